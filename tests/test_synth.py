@@ -1,0 +1,43 @@
+"""Host-side checks of the synthetic workloads (no method arithmetic).
+
+Routing: each token goes to 22 distinct experts out of 512, so the row
+counts sum to tokens*22, no expert exceeds the token count, and MaxVio stays
+under experts/topk ("Nemotron 3 Ultra" report, section 2.7).
+"""
+import numpy as np
+
+from nvfp4_block_scaled_07_amd import synth
+
+
+def test_routing_properties_small():
+    counts, tok, off = synth.zipf_routing(512, 64, 6, 1.1, seed=0)
+    assert counts.sum() == 512 * 6 and off[-1] == 512 * 6
+    assert counts.max() <= 512
+    assert synth.max_vio(counts, 6) <= 64 / 6 + 1e-9
+    for e in range(64):
+        t = tok[off[e]:off[e + 1]]
+        assert len(np.unique(t)) == len(t)  # a token reaches an expert once
+
+
+def test_routing_super_shape():
+    w = synth.WORKLOADS["grouped_super"]
+    counts, tok, off = synth.zipf_routing(w["tokens"], w["experts"], w["topk"], w["zipf_s"],
+                                          w["route_seed"])
+    assert counts.sum() == 8192 * 22
+    assert counts.max() <= 8192
+    assert synth.max_vio(counts, 22) <= 512 / 22
+    assert (counts > 0).all()
+
+
+def test_laplace_zero_fraction():
+    x = synth.laplace((1024, 1024), 1e-3, 3, zero_frac=0.07, zero_seed=4)
+    frac = float((x == 0).mean())
+    assert abs(frac - 0.07) < 0.003
+
+
+def test_bf16_bits_roundtrip():
+    x = synth.normal((8, 16), 1.0, 0)
+    t = synth.to_bf16(x)
+    bits = synth.bf16_bits(t)
+    back = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(back, t.float().numpy())
