@@ -1,0 +1,370 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 linear-layer hot path on one MI355X.
+
+One step = the fprop of one Super-width linear layer from bf16 inputs:
+  quantize X bf16 [8192 x 6144] with 1x16 blocks (RNE),
+  quantize W bf16 [6144 x 6144] with 16x16 blocks,
+  Y = X W^T with the NVFP4 GEMM (NT), bf16 out.
+Inputs are resident in HBM before timing starts; four input sets rotate so
+that the 256 MB Infinity Cache cannot serve a step's inputs from the step
+before.  Every kernel launch in the timed region is bracketed by HIP events on
+the stream the library launches on (torch's current stream), which gives the
+per-kernel averages used for the roofline fractions.
+
+`--rows` adds further rows of the hot path (wgrad with RHT + stochastic
+rounding, routed-expert grouped GEMM, Ultra-width fprop/dgrad), each timed the
+same way and reported under "rows".
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 GEMM TFLOP/s + quantize GB/s at 1 MI355X, % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def q1d_bytes(rows, cols, in_bytes=2):
+    return rows * cols * (in_bytes + 0.5 + 1.0 / 16)
+
+
+def q2d_bytes(rows, cols, in_bytes=2):
+    return rows * cols * (in_bytes + 0.5 + 1.0 / 256)
+
+
+class Timer:
+    """Accumulates HIP-event durations per label within the timed region."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = []
+        self.total = {}
+        self.count = {}
+
+    def run(self, label, fn):
+        t = self.torch
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pending.append((label, e0, e1))
+
+    def collect(self):
+        for label, e0, e1 in self.pending:
+            self.total[label] = self.total.get(label, 0.0) + e0.elapsed_time(e1)
+            self.count[label] = self.count.get(label, 0) + 1
+        self.pending = []
+
+    def avg_ms(self, label):
+        return self.total[label] / self.count[label]
+
+
+def fprop_setup(nv, synth, torch, dev, M, N, K, sets, seed0=1):
+    xs = [synth.normal_device((M, K), 1.0, seed0 + 2 * i, dev) for i in range(sets)]
+    ws = [synth.normal_device((N, K), 0.02, seed0 + 2 * i + 1, dev) for i in range(sets)]
+    qx = nv.quantize_1d(xs[0], "row")
+    qw = nv.quantize_2d(ws[0])
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    return xs, ws, qx, qw, y
+
+
+def fprop_step(nv, timer, xs, ws, qx, qw, y, M, N, K, i):
+    x, w = xs[i % len(xs)], ws[i % len(ws)]
+    timer.run("quantize_1d", lambda: nv.nvfp4_quantize_1d(
+        x, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qx.amax, False, qx.codes, qx.scales,
+        qx.global_dec))
+    timer.run("quantize_2d", lambda: nv.nvfp4_quantize_2d(
+        w, qw.amax, False, qw.codes, qw.scales, qw.global_dec))
+    timer.run("gemm_nt", lambda: nv.nvfp4_gemm("N", "T", M, N, K, qx.operand(), qw.operand(), y,
+                                                nv.NVFP4_BF16))
+
+
+def timed(torch, timer, step, steps, warmup):
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    timer.pending = []
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(warmup + i)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    timer.collect()
+    return start.elapsed_time(stop) / steps, wall
+
+
+def kernel_entry(ms, work, kind):
+    if kind == "bytes":
+        gbs = work / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": int(work)}
+    tf = work / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+            "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 4), "flops": int(work)}
+
+
+def encode_only(nv, torch, qx, x, reps=20):
+    """Quantize with the amax supplied (second pass only)."""
+    for _ in range(3):
+        nv.nvfp4_quantize_1d(x, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qx.amax, True,
+                             qx.codes, qx.scales, qx.global_dec)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        nv.nvfp4_quantize_1d(x, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qx.amax, True,
+                             qx.codes, qx.scales, qx.global_dec)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+# ---- CPU baseline: the oracle on a bounded sample of the same step ---------------------------
+def cpu_baseline(torch, synth, xs, ws, M, N, K):
+    import numpy as np
+
+    import oracle as O
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    rows_x, rows_w, gemm_rows = 256, 256, 8
+    xb = synth.bf16_bits(xs[0][:rows_x].cpu())
+    wb = synth.bf16_bits(ws[0][:rows_w].cpu())
+    amax_x = float(xs[0].float().abs().max())
+    amax_w = float(ws[0].float().abs().max())
+    t0 = time.perf_counter()
+    qa = O.quantize(xb, "row", amax=amax_x)
+    t_qx = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.quantize(wb, "2d", amax=amax_w)
+    t_qw = time.perf_counter() - t0
+    # GEMM sample: `gemm_rows` full rows of Y, against a full quantized W
+    qw_full = O.quantize(synth.bf16_bits(ws[0].cpu()), "2d", amax=amax_w)
+    A = dict(codes=qa["codes"], scales=qa["scales"], block="row", g=qa["g"])
+    B = dict(codes=qw_full["codes"], scales=qw_full["scales"], block="2d", g=qw_full["g"])
+    ii = np.repeat(np.arange(gemm_rows), N)
+    jj = np.tile(np.arange(N), gemm_rows)
+    t0 = time.perf_counter()
+    O.gemm_entries("N", "T", rows_x, N, K, A, B, ii, jj)
+    t_g = time.perf_counter() - t0
+    est = t_qx * (M / rows_x) + t_qw * (N / rows_w) + t_g * (M / gemm_rows)
+    flops = 2.0 * M * N * K
+    return {
+        "value": round(flops / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"oracle quantize of {rows_x} rows of X (1 core) and {rows_w} rows of W "
+                   f"(1 core), fp64 GEMM reference of {gemm_rows} full rows of Y "
+                   f"({threads} OpenMP threads); scaled to the full step"),
+        "est_step_s": round(est, 2),
+        "sample_seconds": round(t_qx + t_qw + t_g, 2),
+    }
+
+
+# ---- further rows ------------------------------------------------------------------------------
+def row_wgrad(nv, synth, torch, dev, steps, warmup):
+    T, Mo, Ni = 8192, 6144, 6144
+    mask = synth.rht_mask(6)
+    dys = [synth.laplace_device((T, Mo), 1e-3, 30 + i, dev, zero_frac=0.07) for i in range(3)]
+    xs = [synth.normal_device((T, Ni), 1.0, 40 + i, dev) for i in range(3)]
+    qdy = nv.quantize_1d(dys[0], "col", "sr", nv.Philox(7), mask)
+    qx = nv.quantize_1d(xs[0], "col", "rne", None, mask)
+    dw = torch.empty((Mo, Ni), dtype=torch.float32, device=dev)
+    timer = Timer(torch)
+    rng = nv.Philox(7)
+
+    def step(i):
+        dy, x = dys[i % 3], xs[i % 3]
+        rng.offset = i
+        timer.run("quantize_col_rht_sr", lambda: nv.nvfp4_quantize_1d(
+            dy, nv.NVFP4_BLOCK_COL, nv.NVFP4_SR, rng, mask, qdy.amax, False, qdy.codes,
+            qdy.scales, qdy.global_dec))
+        timer.run("quantize_col_rht", lambda: nv.nvfp4_quantize_1d(
+            x, nv.NVFP4_BLOCK_COL, nv.NVFP4_RNE, None, mask, qx.amax, False, qx.codes, qx.scales,
+            qx.global_dec))
+        timer.run("gemm_tn", lambda: nv.nvfp4_gemm("T", "N", Mo, Ni, T, qdy.operand(),
+                                                    qx.operand(), dw, nv.NVFP4_FP32))
+
+    ms, _ = timed(torch, timer, step, steps, warmup)
+    return {"workload": "wgrad_super: dY, X bf16 [8192x6144] COL+RHT16 (SR on dY) -> dW fp32 TN",
+            "ms_per_step": round(ms, 4),
+            "quantize_col_rht_sr": kernel_entry(timer.avg_ms("quantize_col_rht_sr"),
+                                                q1d_bytes(T, Mo), "bytes"),
+            "quantize_col_rht": kernel_entry(timer.avg_ms("quantize_col_rht"), q1d_bytes(T, Ni),
+                                             "bytes"),
+            "gemm_tn": kernel_entry(timer.avg_ms("gemm_tn"), 2.0 * Mo * Ni * T, "flops")}
+
+
+def row_grouped(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688, route_seed=9,
+                name="grouped_super"):
+    counts, tok, offsets = synth.zipf_routing(8192, 512, 22, 1.1, route_seed)
+    x = synth.normal_device((8192, latent), 1.0, 8, dev)
+    a = x[torch.from_numpy(tok).to(dev)].contiguous()
+    w = synth.normal_device((512, hidden, latent), 0.02, 10, dev)
+    qa = nv.quantize_1d(a, "row")
+    qw = nv.quantize_2d(w)
+    off = torch.from_numpy(offsets).to(dev)
+    total = int(offsets[-1])
+    y = torch.empty((total, hidden), dtype=torch.bfloat16, device=dev)
+    timer = Timer(torch)
+
+    def step(i):
+        timer.run("quantize_1d", lambda: nv.nvfp4_quantize_1d(
+            a, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qa.amax, False, qa.codes, qa.scales,
+            qa.global_dec))
+        timer.run("quantize_2d_experts", lambda: nv.nvfp4_quantize_2d(
+            w, qw.amax, False, qw.codes, qw.scales, qw.global_dec))
+        timer.run("grouped_gemm", lambda: nv.nvfp4_grouped_gemm(
+            512, off, total, hidden, latent, qa.operand(), qw.operand(), y, nv.NVFP4_BF16))
+
+    ms, _ = timed(torch, timer, step, steps, warmup)
+    return {"workload": f"{name}: 8192 tokens top-22 of 512 experts (Zipf 1.1), "
+                        f"{latent} -> {hidden}",
+            "ms_per_step": round(ms, 4), "max_vio": round(synth.max_vio(counts, 22), 3),
+            "rows_per_expert_min_max": [int(counts.min()), int(counts.max())],
+            "quantize_1d": kernel_entry(timer.avg_ms("quantize_1d"), q1d_bytes(total, latent),
+                                        "bytes"),
+            "quantize_2d_experts": kernel_entry(timer.avg_ms("quantize_2d_experts"),
+                                                q2d_bytes(512 * hidden, latent), "bytes"),
+            "grouped_gemm": kernel_entry(timer.avg_ms("grouped_gemm"),
+                                         2.0 * total * hidden * latent, "flops")}
+
+
+def row_ultra(nv, synth, torch, dev, steps, warmup):
+    M = N = K = 8192
+    xs = [synth.normal_device((M, K), 1.0, 11 + i, dev) for i in range(2)]
+    w = synth.normal_device((N, K), 0.015, 12, dev)
+    dys = [synth.laplace_device((M, N), 1e-3, 13 + i, dev) for i in range(2)]
+    qx = nv.quantize_1d(xs[0], "row")
+    qw = nv.quantize_2d(w)
+    qdy = nv.quantize_1d(dys[0], "row", "sr", nv.Philox(14))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    timer = Timer(torch)
+    rng = nv.Philox(14)
+
+    def step(i):
+        x, dy = xs[i % 2], dys[i % 2]
+        rng.offset = i
+        timer.run("quantize_x", lambda: nv.nvfp4_quantize_1d(
+            x, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qx.amax, False, qx.codes, qx.scales,
+            qx.global_dec))
+        timer.run("quantize_w", lambda: nv.nvfp4_quantize_2d(
+            w, qw.amax, False, qw.codes, qw.scales, qw.global_dec))
+        timer.run("quantize_dy_sr", lambda: nv.nvfp4_quantize_1d(
+            dy, nv.NVFP4_BLOCK_ROW, nv.NVFP4_SR, rng, -1, qdy.amax, False, qdy.codes, qdy.scales,
+            qdy.global_dec))
+        timer.run("gemm_nt", lambda: nv.nvfp4_gemm("N", "T", M, N, K, qx.operand(), qw.operand(),
+                                                    y, nv.NVFP4_BF16))
+        timer.run("gemm_nn", lambda: nv.nvfp4_gemm("N", "N", M, K, N, qdy.operand(),
+                                                    qw.operand(), dx, nv.NVFP4_BF16))
+
+    ms, _ = timed(torch, timer, step, steps, warmup)
+    return {"workload": "ultra: X, dY bf16 [8192x8192], W [8192x8192]; fprop NT + dgrad NN",
+            "ms_per_step": round(ms, 4),
+            "quantize_x": kernel_entry(timer.avg_ms("quantize_x"), q1d_bytes(M, K), "bytes"),
+            "quantize_w": kernel_entry(timer.avg_ms("quantize_w"), q2d_bytes(N, K), "bytes"),
+            "quantize_dy_sr": kernel_entry(timer.avg_ms("quantize_dy_sr"), q1d_bytes(M, N),
+                                           "bytes"),
+            "gemm_nt": kernel_entry(timer.avg_ms("gemm_nt"), 2.0 * M * N * K, "flops"),
+            "gemm_nn": kernel_entry(timer.avg_ms("gemm_nn"), 2.0 * M * N * K, "flops")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,grouped,ultra,all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the hot path has no "
+                                   "multi-GPU mode (see DESIGN.md for how it would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import nvfp4_block_scaled_07_amd as nv
+    from nvfp4_block_scaled_07_amd import synth
+
+    nv.load()  # the HIP library must be present; no fallback
+    dev = torch.device("cuda:0")
+    M, N, K = 8192, 6144, 6144
+    log("generating inputs")
+    xs, ws, qx, qw, y = fprop_setup(nv, synth, torch, dev, M, N, K, sets=4)
+    timer = Timer(torch)
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms, wall = timed(torch, timer,
+                     lambda i: fprop_step(nv, timer, xs, ws, qx, qw, y, M, N, K, i),
+                     args.steps, args.warmup)
+    flops = 2.0 * M * N * K
+    g = kernel_entry(timer.avg_ms("gemm_nt"), flops, "flops")
+    qx_e = kernel_entry(timer.avg_ms("quantize_1d"), q1d_bytes(M, K), "bytes")
+    qw_e = kernel_entry(timer.avg_ms("quantize_2d"), q2d_bytes(N, K), "bytes")
+    enc_ms = encode_only(nv, torch, qx, xs[1])
+    qx_e["encode_only"] = kernel_entry(enc_ms, q1d_bytes(M, K), "bytes")
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "nvfp4 codes -> f16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, on-device generator)",
+        "config": {"workload": "fprop_super: X bf16 [8192x6144] 1x16 RNE + W bf16 [6144x6144] "
+                               "16x16 + Y = X W^T (NT) bf16", "M": M, "N": N, "K": K,
+                   "input_sets_rotated": 4},
+        "roofline": {"bound": "mfma", "achieved": g["TFLOP/s"], "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": g["frac_mfma"], "traffic": None,
+                     "kernel": "gemm_kernel NT 256x256 (fp16 MFMA 32x32x16)"},
+        "kernels": {"gemm_nt": g, "quantize_1d_x": qx_e, "quantize_2d_w": qw_e},
+        "wall_s_timed": round(wall, 3),
+    }
+    extra = [r.strip() for r in args.rows.split(",") if r.strip()]
+    if "all" in extra:
+        extra = ["wgrad", "grouped", "ultra"]
+    rows = {}
+    del xs, ws
+    torch.cuda.empty_cache()
+    for r in extra:
+        log(f"row {r}")
+        if r == "wgrad":
+            rows[r] = row_wgrad(nv, synth, torch, dev, max(5, args.steps // 5), 2)
+        elif r == "grouped":
+            rows[r] = row_grouped(nv, synth, torch, dev, max(5, args.steps // 5), 2)
+        elif r == "grouped_ultra":
+            rows[r] = row_grouped(nv, synth, torch, dev, max(3, args.steps // 10), 1, latent=2048,
+                                  hidden=5120, route_seed=16, name="grouped_ultra")
+        elif r == "ultra":
+            rows[r] = row_ultra(nv, synth, torch, dev, max(5, args.steps // 5), 2)
+        torch.cuda.empty_cache()
+    if rows:
+        out["rows"] = rows
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, bounded sample)")
+        xs1 = [synth.normal_device((M, K), 1.0, 1, dev)]
+        ws1 = [synth.normal_device((N, K), 0.02, 2, dev)]
+        out["cpu_baseline"] = cpu_baseline(torch, synth, xs1, ws1, M, N, K)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4: NVFP4 quantizers and GEMMs for AMD MI355X
+ * (gfx950).
+ *
+ * What the library computes comes from the pages on the Nemotron 3 NVFP4
+ * pretraining recipe:
+ *  - NVFP4 = E2M1 elements in 16-element micro-blocks, each block with one
+ *    E4M3 scale ("Nemotron 3 Super" summary, gkm0120.cn/p/20617,
+ *    pretraining-recipe table, training-precision row);
+ *  - fprop, dgrad and wgrad GEMMs all run in NVFP4; weights use 2D block
+ *    scaling, activations and gradients 1D block scaling; the wgrad inputs
+ *    get a Random Hadamard Transform and gradients stochastic rounding (same
+ *    page, Infra table; "Nemotron 3 Ultra" report, section 2.2);
+ *  - stochastic rounding draws Philox random bits, five rounds balancing
+ *    quality and cost ("Nemotron 3 Super" report summary at
+ *    papers.lianghsun.dev/paper/2604.12374v1, section 4.3);
+ *  - routed-expert GEMMs run in NVFP4 (same summary, section 2.2).
+ * The pages leave the 2D block size, the transform size, the per-tensor
+ * scale, the random-bit layout and all tie rules open; the readings used are
+ * stated at each call below and are the same as the CPU oracle's.
+ *
+ * Conventions for every call:
+ *  - Every pointer argument except the nvfp4_operand / nvfp4_philox structs
+ *    themselves is DEVICE memory owned by the caller.  The library allocates
+ *    nothing, keeps no global state and never synchronizes the device.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it and the call returns; outputs are valid in stream
+ *    order.
+ *  - Return value: NVFP4_OK (0) or a negative nvfp4_status.  Argument errors
+ *    are reported before anything is launched; NVFP4_ERR_DEVICE means a HIP
+ *    launch failed.  No C++ exception crosses this interface.
+ *  - Inputs must be finite.  Results are bit-identical for identical
+ *    arguments (no atomics whose order could change a value).
+ *  - Matrices are row-major: "[R x C]" means C is the contiguous dimension.
+ *
+ * Encoding reading (identical in the CPU oracle):
+ *   A   = max |v| over the tensor (over each slice when batched), v being the
+ *         input in fp32 after the optional Hadamard transform;
+ *   S   = RN32(2688 / A)   (1 if A == 0, FLT_MAX if it overflows),
+ *   k   = RN32(S / 6),  g = RN32(A / 2688)        (2688 = 6 * 448);
+ *   per 16-element block: a = max |v|, scale byte e = E4M3(RN32(a * k)) with
+ *   round-to-nearest-even and saturation at 448, d = value(e),
+ *   r = RN32(S / d) (0 when d == 0, FLT_MAX on overflow);
+ *   per element: y = RN32(v * r), rounded onto the E2M1 grid
+ *   {0, .5, 1, 1.5, 2, 3, 4, 6} (nearest-even, or stochastic), saturating at
+ *   6; code = sign << 3 | magnitude index (-0 keeps its sign: code 0x8).
+ *   Dequantized value = RN32(RN32(val(code) * d) * g).
+ * Storage: codes two per byte along the contiguous dimension, even element in
+ * the low nibble ([R x C/2] bytes).  Scale bytes: ROW blocks [R x C/16], COL
+ * blocks [R/16 x C], 2D blocks [R/16 x C/16].
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+
+/* Status codes. */
+#define NVFP4_OK 0
+#define NVFP4_ERR_NULL (-1)        /* a required pointer is NULL            */
+#define NVFP4_ERR_SHAPE (-2)       /* sizes the blocks or tiles cannot take */
+#define NVFP4_ERR_ALIGN (-3)       /* a pointer misses its alignment        */
+#define NVFP4_ERR_LAYOUT (-4)      /* op letters / block kind do not fit    */
+#define NVFP4_ERR_UNSUPPORTED (-5) /* a valid-looking but unsupported mode  */
+#define NVFP4_ERR_DEVICE (-6)      /* a HIP launch failed                   */
+
+/* Element types of unquantized tensors. */
+#define NVFP4_BF16 0
+#define NVFP4_FP32 1
+
+/* Rounding of elements onto the E2M1 grid. */
+#define NVFP4_RNE 0 /* nearest, ties to the even code (activations, weights) */
+#define NVFP4_SR 1  /* stochastic rounding (gradients)                       */
+
+/* Block kinds (16 elements along the contraction dimension K). */
+#define NVFP4_BLOCK_ROW 0 /* 1x16 along the contiguous dimension       */
+#define NVFP4_BLOCK_COL 1 /* 16x1 along the row dimension              */
+#define NVFP4_BLOCK_2D 2  /* 16x16                                     */
+
+/* Philox4x32 stream for stochastic rounding (host struct, read at the call).
+ * Reading of the pages' "Philox" with five rounds: key = (lo32(seed),
+ * hi32(seed)); block id b makes two calls j = 0, 1 with counter
+ * (lo32(2b+j), hi32(2b+j), lo32(offset), hi32(offset)); element e of the
+ * block (0..15 along the block axis) uses call e>>3, output word (e>>1)&3,
+ * low 16 bits for even e, high for odd; it rounds up iff
+ * u16 < 65536 * (m - lo) / (hi - lo) with lo <= m < hi neighbouring grid
+ * values.  Block ids: ROW b = r*(C/16) + c/16; COL b = c*(R/16) + r/16. */
+typedef struct {
+  uint64_t seed;
+  uint64_t offset;
+  uint32_t rounds; /* 1..16; 5 is the recipe's value, 10 matches cuRAND/rocRAND */
+  uint32_t reserved;
+} nvfp4_philox;
+
+/* A quantized operand: device pointers to its codes, its scale bytes and its
+ * fp32 decode scale g, with the stored shape [rows x cols] and block kind. */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* global_dec;
+  int64_t rows;
+  int64_t cols;
+  int32_t block; /* NVFP4_BLOCK_* */
+  int32_t reserved;
+} nvfp4_operand;
+
+/* Version of this ABI (NVFP4_ABI_VERSION). */
+int32_t nvfp4_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* nvfp4_status_string(int32_t status);
+
+/*
+ * 1D block quantization of activations and gradients (Super summary, Infra
+ * table; Ultra report section 2.2), with the optional 16-point Random
+ * Hadamard Transform of the wgrad inputs and stochastic rounding of
+ * gradients.
+ *   x        [rows x cols] input, NVFP4_BF16 or NVFP4_FP32 (x_dtype).
+ *   axis     NVFP4_BLOCK_ROW (blocks along cols) or NVFP4_BLOCK_COL (blocks
+ *            along rows, used for the token dimension of wgrad inputs).
+ *   rounding NVFP4_RNE, or NVFP4_SR with `rng` (host struct) non-NULL.
+ *   rht_sign_mask  -1 for no transform, else a 16-bit mask: each block v is
+ *            replaced by (1/4) H16 diag(s) v, H16 the Sylvester Hadamard
+ *            matrix, s_i = -1 where bit i is set; evaluated as butterflies of
+ *            stride 1, 2, 4, 8 (RN32 sums/differences) then an exact * 1/4.
+ *            Both wgrad operands must use the same mask.
+ *   amax     device float: read when amax_is_input != 0, else written with
+ *            the tensor amax (after the transform).
+ *   codes    [rows x cols/2] bytes out;  scales ROW [rows x cols/16] or COL
+ *            [rows/16 x cols] bytes out;  global_dec: device float out (g).
+ * Shapes: cols % 32 == 0; COL also rows % 16 == 0; rows == 0 is a no-op.
+ * Alignment: x, codes 16 bytes; scales 4 bytes.
+ */
+int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                          int32_t axis, int32_t rounding, const nvfp4_philox* rng,
+                          int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                          uint8_t* codes, uint8_t* scales, float* global_dec, void* stream);
+
+/*
+ * 2D (16x16) block quantization of weights (Super summary, Infra table: 2D
+ * block scaling for weights; the 16x16 size is the reading).  Round to
+ * nearest even, no transform.  A batch of `batch` independent slices
+ * [rows x cols] (e.g. the routed experts' weights) each gets its own amax and
+ * g.  Because the blocks are square, the same codes and scales serve W and
+ * W^T.
+ *   w [batch x rows x cols]; amax, global_dec: [batch] device floats;
+ *   codes [batch x rows x cols/2]; scales [batch x rows/16 x cols/16].
+ * Shapes: rows % 16 == 0, cols % 32 == 0.  Alignment as nvfp4_quantize_1d.
+ */
+int32_t nvfp4_quantize_2d(const void* w, int32_t w_dtype, int64_t batch, int64_t rows,
+                          int64_t cols, float* amax, int32_t amax_is_input, uint8_t* codes,
+                          uint8_t* scales, float* global_dec, void* stream);
+
+/*
+ * The 16-point Random Hadamard Transform alone, fp32 out (Super summary,
+ * Infra table; the size is the reading): y = (1/4) H16 diag(s) x on every
+ * 16-element block along `axis` (ROW or COL), same evaluation order as in
+ * nvfp4_quantize_1d.  x [rows x cols] bf16/fp32, y [rows x cols] fp32.
+ * Shapes: cols % 32 == 0; COL also rows % 16 == 0.  Alignment 16 bytes.
+ */
+int32_t nvfp4_rht16(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int32_t axis,
+                    uint32_t sign_mask, float* y, void* stream);
+
+/*
+ * Dequantize one operand (one slice): y[r][c] = RN32(RN32(val(code) * d) * g)
+ * as fp32 [rows x cols].  `q` is a host struct of device pointers.
+ */
+int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream);
+
+/*
+ * NVFP4 GEMM (Super summary, Infra table: fprop, dgrad and wgrad GEMMs in
+ * NVFP4; Ultra report section 2.2).  C [M x N] = op(A) op(B) * gA * gB with
+ * row-major op letters:
+ *   opA 'N': A stored [M x K];  'T': A stored [K x M];
+ *   opB 'T': B stored [N x K];  'N': B stored [K x N].
+ * Supported: NT (fprop Y = X W^T), NN (dgrad dX = dY W), TN (wgrad
+ * dW = dY^T X).  TT returns NVFP4_ERR_UNSUPPORTED.  Each operand's blocks
+ * must lie along K: ROW iff K is its contiguous dimension, COL iff K is its
+ * row dimension, 2D either way.
+ * Arithmetic: every decoded element val(code) * d is exact in fp16 (at most
+ * 6 significant bits, range 2^-10 .. 2688); products are summed by MFMA with
+ * fp32 accumulation (the pages trace a divergence to bf16 accumulation,
+ * Ultra report section 2.7); epilogue C = RN32(acc * RN32(gA * gB)), then
+ * bf16 (RNE) or fp32 per c_dtype.
+ * Shapes: K % 32 == 0; M, N >= 0 (the contiguous dimension of a stored
+ * operand must be a multiple of 32).  Alignment: codes 16 bytes, scales 4,
+ * C 16 bytes (bf16) / 16 bytes (fp32) with N % 8 == 0.
+ */
+int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nvfp4_operand* A,
+                   const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream);
+
+/*
+ * Grouped NVFP4 GEMM for the routed experts (Super report summary, sections
+ * 2.1 and 2.2: routed-expert GEMMs in NVFP4, 512 experts with 22 active).
+ * For every group e: C[o_e : o_{e+1}] = A[o_e : o_{e+1}] B_e^T * gA * gB_e,
+ * with o = row_offsets (device int64 [groups + 1], o_0 = 0, non-decreasing,
+ * o_groups = total_rows; ragged, empty groups allowed).
+ *   A: [total_rows x K], ROW blocks, one g.
+ *   B: `groups` slices [N x K] (B->rows = N, B->cols = K), 2D or ROW blocks,
+ *      codes/scales consecutive per slice, global_dec [groups].
+ *   C: [total_rows x N], bf16 or fp32.
+ * Shapes: K % 32 == 0, N % 16 == 0.  A row_offsets entry outside
+ * [0, total_rows] or decreasing is a precondition violation (rows outside
+ * [0, total_rows) are never touched).
+ */
+int32_t nvfp4_grouped_gemm(int64_t groups, const int64_t* row_offsets, int64_t total_rows,
+                           int64_t N, int64_t K, const nvfp4_operand* A, const nvfp4_operand* B,
+                           void* C, int32_t c_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H */

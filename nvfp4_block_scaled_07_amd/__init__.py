@@ -1,0 +1,17 @@
+"""libnvfp4: NVFP4 quantizers and GEMMs for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libnvfp4.so`` (C ABI in
+``include/nvfp4.h``).  This package only marshals torch tensors into that ABI:
+``nvfp4_*`` functions mirror the C entry points one to one, and the
+convenience wrappers (``quantize_1d``, ``quantize_2d``, ``rht16``,
+``dequantize``, ``gemm``, ``grouped_gemm``) allocate outputs with torch and
+call them.  Nothing here computes a value of the method; if the library is
+missing, every call raises.
+"""
+from ._binding import (  # noqa: F401
+    NVFP4_BF16, NVFP4_FP32, NVFP4_RNE, NVFP4_SR, NVFP4_BLOCK_ROW, NVFP4_BLOCK_COL, NVFP4_BLOCK_2D,
+    NVFP4Error, Philox, QTensor, library_path, load,
+    nvfp4_abi_version, nvfp4_status_string, nvfp4_quantize_1d, nvfp4_quantize_2d, nvfp4_rht16,
+    nvfp4_dequantize, nvfp4_gemm, nvfp4_grouped_gemm,
+    quantize_1d, quantize_2d, rht16, dequantize, gemm, grouped_gemm,
+)

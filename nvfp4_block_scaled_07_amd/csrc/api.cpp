@@ -1,0 +1,222 @@
+// api.cpp -- the C ABI of libnvfp4 (declared in include/nvfp4.h): argument
+// validation, then kernel launches on the caller's stream.  Validation runs
+// entirely on the host before any HIP call, so a rejected call launches
+// nothing and touches no device state.
+#include "nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+using nvfp4::DevOperand;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t device_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE; }
+
+bool valid_dtype(int32_t t) { return t == NVFP4_BF16 || t == NVFP4_FP32; }
+
+// The stored shape an operand must have, and the block kinds that tile K.
+struct Expect {
+  int64_t rows, cols;
+  bool kmajor;
+};
+
+int32_t check_operand(const nvfp4_operand* q, const Expect& e) {
+  if (!q || !q->codes || !q->scales || !q->global_dec) return NVFP4_ERR_NULL;
+  if (q->rows != e.rows || q->cols != e.cols) return NVFP4_ERR_SHAPE;
+  if (q->block == NVFP4_BLOCK_ROW && !e.kmajor) return NVFP4_ERR_LAYOUT;
+  if (q->block == NVFP4_BLOCK_COL && e.kmajor) return NVFP4_ERR_LAYOUT;
+  if (q->block != NVFP4_BLOCK_ROW && q->block != NVFP4_BLOCK_COL && q->block != NVFP4_BLOCK_2D)
+    return NVFP4_ERR_LAYOUT;
+  if (q->cols % 32 != 0) return NVFP4_ERR_SHAPE;  // contiguous dim: 16-byte code rows
+  if ((q->block == NVFP4_BLOCK_COL || q->block == NVFP4_BLOCK_2D) && q->rows % 16 != 0)
+    return NVFP4_ERR_SHAPE;
+  if (!aligned(q->codes, 16) || !aligned(q->scales, 4) || !aligned(q->global_dec, 4))
+    return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+DevOperand dev(const nvfp4_operand* q) {
+  return DevOperand{q->codes, q->scales, q->global_dec, q->block};
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_string(int32_t s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "shape not supported by the block or tile sizes";
+    case NVFP4_ERR_ALIGN: return "pointer misaligned";
+    case NVFP4_ERR_LAYOUT: return "operand layout or block kind does not fit the op letters";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported mode";
+    case NVFP4_ERR_DEVICE: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                          int32_t axis, int32_t rounding, const nvfp4_philox* rng,
+                          int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                          uint8_t* codes, uint8_t* scales, float* global_dec, void* stream) {
+  if (!valid_dtype(x_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (axis != NVFP4_BLOCK_ROW && axis != NVFP4_BLOCK_COL) return NVFP4_ERR_LAYOUT;
+  if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_UNSUPPORTED;
+  if (rht_sign_mask < -1 || rht_sign_mask > 0xFFFF) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (axis == NVFP4_BLOCK_COL && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rounding == NVFP4_SR && !rng) return NVFP4_ERR_NULL;
+  if (rng && rounding == NVFP4_SR && (rng->rounds < 1 || rng->rounds > 16))
+    return NVFP4_ERR_UNSUPPORTED;
+  if (!x || !amax || !codes || !scales || !global_dec) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
+      !aligned(global_dec, 4))
+    return NVFP4_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  nvfp4::QuantArgs a{};
+  a.x = x;
+  a.x_fp32 = x_dtype == NVFP4_FP32;
+  a.rows = rows;
+  a.cols = cols;
+  a.axis = axis == NVFP4_BLOCK_ROW ? nvfp4::kBlockRow : nvfp4::kBlockCol;
+  a.sr = rounding == NVFP4_SR;
+  a.rht = rht_sign_mask >= 0;
+  a.mask = a.rht ? (uint32_t)rht_sign_mask : 0u;
+  a.seed = a.sr ? rng->seed : 0;
+  a.offset = a.sr ? rng->offset : 0;
+  a.rounds = a.sr ? rng->rounds : 0;
+  a.amax = amax;
+  a.amax_is_input = amax_is_input != 0;
+  a.codes = codes;
+  a.scales = scales;
+  a.gdec = global_dec;
+  return device_status(nvfp4::launch_quantize_1d(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_quantize_2d(const void* w, int32_t w_dtype, int64_t batch, int64_t rows,
+                          int64_t cols, float* amax, int32_t amax_is_input, uint8_t* codes,
+                          uint8_t* scales, float* global_dec, void* stream) {
+  if (!valid_dtype(w_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (batch < 0 || rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  if (rows % 16 != 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (batch > 65535) return NVFP4_ERR_SHAPE;
+  if (!w || !amax || !codes || !scales || !global_dec) return NVFP4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
+      !aligned(global_dec, 4))
+    return NVFP4_ERR_ALIGN;
+  if (batch == 0) return NVFP4_OK;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  nvfp4::Quant2dArgs a{};
+  a.w = w;
+  a.w_fp32 = w_dtype == NVFP4_FP32;
+  a.batch = batch;
+  a.rows = rows;
+  a.cols = cols;
+  a.amax = amax;
+  a.amax_is_input = amax_is_input != 0;
+  a.codes = codes;
+  a.scales = scales;
+  a.gdec = global_dec;
+  return device_status(nvfp4::launch_quantize_2d(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_rht16(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int32_t axis,
+                    uint32_t sign_mask, float* y, void* stream) {
+  if (!valid_dtype(x_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (axis != NVFP4_BLOCK_ROW && axis != NVFP4_BLOCK_COL) return NVFP4_ERR_LAYOUT;
+  if (sign_mask > 0xFFFFu) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (axis == NVFP4_BLOCK_COL && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (!x || !y) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return NVFP4_OK;
+  return device_status(nvfp4::launch_rht16(x, x_dtype == NVFP4_FP32, rows, cols,
+                                           axis == NVFP4_BLOCK_ROW ? nvfp4::kBlockRow
+                                                                   : nvfp4::kBlockCol,
+                                           sign_mask, y, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream) {
+  if (!q || !y) return NVFP4_ERR_NULL;
+  if (q->rows < 0 || q->cols < 0) return NVFP4_ERR_SHAPE;
+  Expect e{q->rows, q->cols, q->block != NVFP4_BLOCK_COL};
+  int32_t s = check_operand(q, e);
+  if (s != NVFP4_OK) return s;
+  if (!aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  if (q->rows == 0 || q->cols == 0) return NVFP4_OK;
+  return device_status(nvfp4::launch_dequantize(q->codes, q->scales, q->global_dec, q->rows,
+                                                q->cols, q->block, y,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nvfp4_operand* A,
+                   const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream) {
+  if ((opA != 'N' && opA != 'T') || (opB != 'N' && opB != 'T')) return NVFP4_ERR_LAYOUT;
+  if (opA == 'T' && opB == 'T') return NVFP4_ERR_UNSUPPORTED;
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0) return NVFP4_ERR_SHAPE;
+  if (!A || !B || !C) return NVFP4_ERR_NULL;
+  const bool a_k = opA == 'N', b_k = opB == 'T';
+  Expect ea = a_k ? Expect{M, K, true} : Expect{K, M, false};
+  Expect eb = b_k ? Expect{N, K, true} : Expect{K, N, false};
+  int32_t s = check_operand(A, ea);
+  if (s != NVFP4_OK) return s;
+  s = check_operand(B, eb);
+  if (s != NVFP4_OK) return s;
+  if (N % 8 != 0) return NVFP4_ERR_SHAPE;
+  if (!aligned(C, 16)) return NVFP4_ERR_ALIGN;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (K == 0) return NVFP4_ERR_SHAPE;  // nothing to contract: caller should fill C
+  nvfp4::GemmArgs a{};
+  a.a_kmajor = a_k;
+  a.b_kmajor = b_k;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.A = dev(A);
+  a.B = dev(B);
+  a.C = C;
+  a.c_bf16 = c_dtype == NVFP4_BF16;
+  return device_status(nvfp4::launch_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_grouped_gemm(int64_t groups, const int64_t* row_offsets, int64_t total_rows,
+                           int64_t N, int64_t K, const nvfp4_operand* A, const nvfp4_operand* B,
+                           void* C, int32_t c_dtype, void* stream) {
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (groups < 0 || total_rows < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
+  if (groups > 4096) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || N % 16 != 0 || K == 0) return NVFP4_ERR_SHAPE;
+  if (!row_offsets || !A || !B || !C) return NVFP4_ERR_NULL;
+  if (!aligned(row_offsets, 8) || !aligned(C, 16)) return NVFP4_ERR_ALIGN;
+  int32_t s = check_operand(A, Expect{total_rows, K, true});
+  if (s != NVFP4_OK) return s;
+  if (A->block != NVFP4_BLOCK_ROW) return NVFP4_ERR_LAYOUT;
+  s = check_operand(B, Expect{N, K, true});
+  if (s != NVFP4_OK) return s;
+  if (groups == 0 || total_rows == 0 || N == 0) return NVFP4_OK;
+  nvfp4::GroupedArgs a{};
+  a.groups = groups;
+  a.offsets = row_offsets;
+  a.total_rows = total_rows;
+  a.N = N;
+  a.K = K;
+  a.A = dev(A);
+  a.B = dev(B);
+  a.C = C;
+  a.c_bf16 = c_dtype == NVFP4_BF16;
+  return device_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

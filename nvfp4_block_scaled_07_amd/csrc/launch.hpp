@@ -1,0 +1,77 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the
+// kernels.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kBlockRow = 0;
+constexpr int kBlockCol = 1;
+constexpr int kBlock2d = 2;
+
+struct QuantArgs {
+  const void* x;
+  bool x_fp32;
+  int64_t rows, cols;
+  int axis;  // kBlockRow / kBlockCol
+  bool sr, rht;
+  uint32_t mask;
+  uint64_t seed, offset;
+  uint32_t rounds;
+  float* amax;
+  bool amax_is_input;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* gdec;
+};
+
+struct Quant2dArgs {
+  const void* w;
+  bool w_fp32;
+  int64_t batch, rows, cols;
+  float* amax;
+  bool amax_is_input;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* gdec;
+};
+
+// One GEMM operand as the kernels see it.  kmajor: stored [MN][K] (K
+// contiguous), else stored [K][MN].  block: kBlockRow/kBlockCol/kBlock2d.
+struct DevOperand {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gdec;
+  int block;
+};
+
+struct GemmArgs {
+  bool a_kmajor, b_kmajor;  // NT: true,true  NN: true,false  TN: false,false
+  int64_t M, N, K;
+  DevOperand A, B;
+  void* C;
+  bool c_bf16;
+};
+
+struct GroupedArgs {
+  int64_t groups;
+  const int64_t* offsets;  // device [groups + 1]
+  int64_t total_rows, N, K;
+  DevOperand A;  // [total_rows x K] ROW
+  DevOperand B;  // groups x [N x K], 2D or ROW; gdec [groups]
+  void* C;
+  bool c_bf16;
+};
+
+hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st);
+hipError_t launch_quantize_2d(const Quant2dArgs& a, hipStream_t st);
+hipError_t launch_rht16(const void* x, bool x_fp32, int64_t rows, int64_t cols, int axis,
+                        uint32_t mask, float* y, hipStream_t st);
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gdec,
+                             int64_t rows, int64_t cols, int block, float* y, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st);
+
+}  // namespace nvfp4

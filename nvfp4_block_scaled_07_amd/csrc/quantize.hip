@@ -1,0 +1,469 @@
+// quantize.hip -- NVFP4 quantizers, Hadamard transform and dequantizer for
+// gfx950 (bandwidth-bound passes).
+//
+// Work mapping (wave64):
+//  * ROW blocks (1x16 along the contiguous dim): the tensor is a flat stream
+//    of 16-element blocks.  Each lane owns 8 consecutive elements (one 16-byte
+//    bf16 load), so lanes 2t and 2t+1 share a block: its max takes one
+//    xor-1 shuffle, the 16-point transform's stride-8 stage one exchange of
+//    8 values.  A lane stores one dword of codes; even lanes store the scale.
+//  * COL blocks (16x1 along rows) and 2D blocks (16x16): each lane owns 8
+//    columns x 16 rows, loading one 16-byte row segment per row, so each load
+//    instruction reads 1 KiB of a row contiguously across the wave.  COL
+//    blocks live entirely in one lane; 2D blocks span lanes 2t and 2t+1.
+//  * The per-tensor amax runs first: a fill kernel zeroes it (no memset, so
+//    the sequence can be captured in a graph), then every workgroup does one
+//    atomicMax on the fp32 bits (non-negative floats order like integers, so
+//    the result does not depend on the order).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- loads ---------------------------------------------------------------------------
+template <typename T>
+struct In;
+
+template <>
+struct In<uint16_t> {  // bf16 bits
+  static __device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+    uint4 q = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+};
+
+template <>
+struct In<float> {
+  static __device__ __forceinline__ void load8(const float* p, float v[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+__device__ __forceinline__ float max8(const float v[8]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = fmaxf(m, __builtin_fabsf(v[i]));
+  return m;
+}
+
+// Stride-8 butterfly across the lane pair (2t holds positions 0..7, 2t+1
+// positions 8..15), then the exact * 1/4.
+__device__ __forceinline__ void rht_pair_stage8(float v[8], int odd) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    float other = __shfl_xor(v[i], 1);
+    float lo = odd ? other : v[i];
+    float hi = odd ? v[i] : other;
+    v[i] = (odd ? (lo - hi) : (lo + hi)) * 0.25f;
+  }
+}
+
+// ---- workgroup max -> atomicMax ---------------------------------------------------------
+__device__ __forceinline__ void block_max_to(float m, float* out) {
+  __shared__ float red[kThreads / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; i++) r = fmaxf(r, red[i]);
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(r));
+  }
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// ---- amax over flat 8-element chunks (ROW blocks, or no transform) -----------------------
+// chunks: number of 8-element chunks per slice; slice = blockIdx.y.
+template <typename T, bool kRHT>
+__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T* __restrict__ x,
+                                                             int64_t chunks, uint32_t mask,
+                                                             float* __restrict__ amax) {
+  const T* xs = x + (int64_t)blockIdx.y * chunks * 8;
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks; i += stride) {
+    float v[8];
+    In<T>::load8(xs + i * 8, v);
+    if (kRHT) {
+      rht_signs_and_low_stages(v, mask, (int)(i & 1) * 8);
+      rht_pair_stage8(v, (int)(i & 1));
+    }
+    m = fmaxf(m, max8(v));
+  }
+  block_max_to(m, amax + blockIdx.y);
+}
+
+// ---- amax of COL blocks with the transform (lane: 8 cols x 16 rows) ---------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restrict__ x,
+                                                                int64_t rows, int64_t cols,
+                                                                uint32_t mask,
+                                                                float* __restrict__ amax) {
+  const int64_t cg = cols / 8;
+  const int64_t units = (rows / 16) * cg;
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
+    int64_t g = u / cg, c0 = (u % cg) * 8;
+    float v[16][8];
+#pragma unroll
+    for (int r = 0; r < 16; r++) In<T>::load8(x + (g * 16 + r) * cols + c0, v[r]);
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+      float col[16];
+#pragma unroll
+      for (int r = 0; r < 16; r++) col[r] = v[r][c];
+      rht16_inreg(col, mask);
+#pragma unroll
+      for (int r = 0; r < 16; r++) m = fmaxf(m, __builtin_fabsf(col[r]));
+    }
+  }
+  block_max_to(m, amax);
+}
+
+// ---- ROW quantizer ---------------------------------------------------------------------------
+// Lane chunk i (8 elements) belongs to block i >> 1; with stochastic rounding
+// its Philox counter is 2 * block + (i & 1) = i.
+template <typename T, bool kSR, bool kRHT>
+__global__ __launch_bounds__(kThreads) void quant_row_kernel(
+    const T* __restrict__ x, int64_t chunks, const float* __restrict__ amax,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
+    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
+  const TensorScales ts = tensor_scales(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
+  constexpr int kUnroll = 4;
+  const int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+  float v[kUnroll][8];
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    int64_t i = base + (int64_t)u * kThreads;
+    if (i < chunks) In<T>::load8(x + i * 8, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; u++) {
+    int64_t i = base + (int64_t)u * kThreads;
+    if (i >= chunks) continue;  // chunks is even: both lanes of a pair agree
+    const int odd = (int)(i & 1);
+    if (kRHT) {
+      rht_signs_and_low_stages(v[u], mask, odd * 8);
+      rht_pair_stage8(v[u], odd);
+    }
+    float bm = max8(v[u]);
+    bm = fmaxf(bm, __shfl_xor(bm, 1));
+    uint32_t e = e4m3_encode(bm * ts.k);
+    float r = block_recip(ts.S, e4m3_decode(e));
+    uint32_t packed = 0;
+    if (kSR) {
+      Philox4 p = sr_call((uint64_t)i, seed, offset, rounds);
+#pragma unroll
+      for (int t = 0; t < 8; t++) packed |= e2m1_sr(v[u][t] * r, sr_slot(p, t)) << (4 * t);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; t++) packed |= e2m1_rne(v[u][t] * r) << (4 * t);
+    }
+    codes[i] = packed;
+    if (!odd) scales[i >> 1] = (uint8_t)e;
+  }
+}
+
+// ---- COL quantizer (lane: 8 cols x 16 rows = 8 blocks) ---------------------------------------
+template <typename T, bool kSR, bool kRHT>
+__global__ __launch_bounds__(kThreads) void quant_col_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
+    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
+  const TensorScales ts = tensor_scales(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
+  const int64_t cg = cols / 8;
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (u >= (rows / 16) * cg) return;
+  const int64_t g = u / cg, c0 = (u % cg) * 8;
+  float v[16][8];
+#pragma unroll
+  for (int r = 0; r < 16; r++) In<T>::load8(x + (g * 16 + r) * cols + c0, v[r]);
+  uint32_t out[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) out[r] = 0;
+  uint32_t sc[2] = {0, 0};
+#pragma unroll
+  for (int c = 0; c < 8; c++) {
+    float col[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) col[r] = v[r][c];
+    if (kRHT) rht16_inreg(col, mask);
+    float bm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[r]));
+    uint32_t e = e4m3_encode(bm * ts.k);
+    float rcp = block_recip(ts.S, e4m3_decode(e));
+    sc[c >> 2] |= e << (8 * (c & 3));
+    if (kSR) {
+      const uint64_t blk = (uint64_t)(c0 + c) * (uint64_t)(rows / 16) + (uint64_t)g;
+      Philox4 p0 = sr_call(2 * blk, seed, offset, rounds);
+      Philox4 p1 = sr_call(2 * blk + 1, seed, offset, rounds);
+#pragma unroll
+      for (int r = 0; r < 8; r++) out[r] |= e2m1_sr(col[r] * rcp, sr_slot(p0, r)) << (4 * c);
+#pragma unroll
+      for (int r = 0; r < 8; r++)
+        out[r + 8] |= e2m1_sr(col[r + 8] * rcp, sr_slot(p1, r)) << (4 * c);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; r++) out[r] |= e2m1_rne(col[r] * rcp) << (4 * c);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; r++)
+    *reinterpret_cast<uint32_t*>(codes + (g * 16 + r) * (cols / 2) + c0 / 2) = out[r];
+  uint32_t* sp = reinterpret_cast<uint32_t*>(scales + g * cols + c0);
+  sp[0] = sc[0];
+  sp[1] = sc[1];
+}
+
+// ---- 2D quantizer (lane: 8 cols x 16 rows; lanes 2t, 2t+1 = one 16x16 block) ------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quant_2d_kernel(
+    const T* __restrict__ w, int64_t rows, int64_t cols, const float* __restrict__ amax,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec) {
+  const int64_t slice = blockIdx.y;
+  const TensorScales ts = tensor_scales(amax[slice]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) gdec[slice] = ts.g;
+  const T* ws = w + slice * rows * cols;
+  uint8_t* cs = codes + slice * rows * (cols / 2);
+  uint8_t* ss = scales + slice * (rows / 16) * (cols / 16);
+  const int64_t cg = cols / 8;  // a multiple of 4, so pairs never straddle rows
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool active = u < (rows / 16) * cg;  // uniform per lane pair
+  const int64_t g = active ? u / cg : 0, c0 = active ? (u % cg) * 8 : 0;
+  float v[16][8];
+  float bm = 0.0f;
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      In<T>::load8(ws + (g * 16 + r) * cols + c0, v[r]);
+      bm = fmaxf(bm, max8(v[r]));
+    }
+  }
+  bm = fmaxf(bm, __shfl_xor(bm, 1));
+  if (!active) return;
+  uint32_t e = e4m3_encode(bm * ts.k);
+  float rcp = block_recip(ts.S, e4m3_decode(e));
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int t = 0; t < 8; t++) packed |= e2m1_rne(v[r][t] * rcp) << (4 * t);
+    *reinterpret_cast<uint32_t*>(cs + (g * 16 + r) * (cols / 2) + c0 / 2) = packed;
+  }
+  if (((u % cg) & 1) == 0) ss[g * (cols / 16) + c0 / 16] = (uint8_t)e;
+}
+
+// ---- standalone transform ------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rht_row_kernel(const T* __restrict__ x, int64_t chunks,
+                                                           uint32_t mask, float* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= chunks) return;  // chunks even: lane pairs agree
+  float v[8];
+  In<T>::load8(x + i * 8, v);
+  const int odd = (int)(i & 1);
+  rht_signs_and_low_stages(v, mask, odd * 8);
+  rht_pair_stage8(v, odd);
+  float4* o = reinterpret_cast<float4*>(y + i * 8);
+  o[0] = make_float4(v[0], v[1], v[2], v[3]);
+  o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rht_col_kernel(const T* __restrict__ x, int64_t rows,
+                                                           int64_t cols, uint32_t mask,
+                                                           float* __restrict__ y) {
+  const int64_t cg = cols / 8;
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (u >= (rows / 16) * cg) return;
+  const int64_t g = u / cg, c0 = (u % cg) * 8;
+  float v[16][8];
+#pragma unroll
+  for (int r = 0; r < 16; r++) In<T>::load8(x + (g * 16 + r) * cols + c0, v[r]);
+#pragma unroll
+  for (int c = 0; c < 8; c++) {
+    float col[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) col[r] = v[r][c];
+    rht16_inreg(col, mask);
+#pragma unroll
+    for (int r = 0; r < 16; r++) v[r][c] = col[r];
+  }
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    float4* o = reinterpret_cast<float4*>(y + (g * 16 + r) * cols + c0);
+    o[0] = make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
+    o[1] = make_float4(v[r][4], v[r][5], v[r][6], v[r][7]);
+  }
+}
+
+// ---- dequantize ------------------------------------------------------------------------------
+// Lane: one dword of codes = 8 elements of one row.
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ gdec,
+                                                          int64_t rows, int64_t cols, int block,
+                                                          float* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= rows * cols / 8) return;
+  const float g = *gdec;
+  const int64_t r = (i * 8) / cols, c0 = (i * 8) % cols;
+  const uint32_t q = codes[i];
+  float out[8];
+#pragma unroll
+  for (int t = 0; t < 8; t++) {
+    const int64_t c = c0 + t;
+    int64_t si = block == kBlockRow ? r * (cols / 16) + c / 16
+                 : block == kBlockCol ? (r / 16) * cols + c
+                                      : (r / 16) * (cols / 16) + c / 16;
+    const float d = e4m3_decode(scales[si]);
+    const uint32_t code = (q >> (4 * t)) & 15u;
+    const uint32_t mi = code & 7u;
+    float mag = mi < 4u ? (float)mi * 0.5f : (mi < 6u ? (float)(mi - 2u) : (mi == 6u ? 4.0f : 6.0f));
+    float val = (code & 8u) ? -mag : mag;
+    float ed = val * d;  // exact
+    out[t] = ed * g;
+  }
+  float4* o = reinterpret_cast<float4*>(y + i * 8);
+  o[0] = make_float4(out[0], out[1], out[2], out[3]);
+  o[1] = make_float4(out[4], out[5], out[6], out[7]);
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int amax_grid(int64_t units) {
+  // Enough workgroups to fill 256 CUs several times over; each thread then
+  // loops over a strided range, so the atomics stay few.
+  int64_t g = cdiv(units, kThreads);
+  return (int)(g < 4096 ? (g > 0 ? g : 1) : 4096);
+}
+
+template <typename T>
+hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
+  const T* x = static_cast<const T*>(a.x);
+  if (!a.amax_is_input) {
+    fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 1);
+    if (a.axis == kBlockCol && a.rht) {
+      int64_t units = (a.rows / 16) * (a.cols / 8);
+      amax_col_rht_kernel<T><<<amax_grid(units), kThreads, 0, st>>>(x, a.rows, a.cols, a.mask,
+                                                                     a.amax);
+    } else {
+      int64_t chunks = a.rows * a.cols / 8;
+      dim3 grid(amax_grid(chunks), 1);
+      // ROW with the transform needs the pair exchange; COL amax without the
+      // transform is the plain max.
+      if (a.rht && a.axis == kBlockRow)
+        amax_flat_kernel<T, true><<<grid, kThreads, 0, st>>>(x, chunks, a.mask, a.amax);
+      else
+        amax_flat_kernel<T, false><<<grid, kThreads, 0, st>>>(x, chunks, 0, a.amax);
+    }
+  }
+  if (a.axis == kBlockRow) {
+    int64_t chunks = a.rows * a.cols / 8;
+    int grid = (int)cdiv(chunks, (int64_t)kThreads * 4);
+    uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
+#define NVFP4_ROW(SR, RHT)                                                                   \
+  quant_row_kernel<T, SR, RHT><<<grid, kThreads, 0, st>>>(x, chunks, a.amax, cd, a.scales,   \
+                                                          a.gdec, a.mask, a.seed, a.offset, \
+                                                          a.rounds)
+    if (a.sr && a.rht) NVFP4_ROW(true, true);
+    else if (a.sr) NVFP4_ROW(true, false);
+    else if (a.rht) NVFP4_ROW(false, true);
+    else NVFP4_ROW(false, false);
+#undef NVFP4_ROW
+  } else {
+    int64_t units = (a.rows / 16) * (a.cols / 8);
+    int grid = (int)cdiv(units, kThreads);
+#define NVFP4_COL(SR, RHT)                                                                     \
+  quant_col_kernel<T, SR, RHT><<<grid, kThreads, 0, st>>>(x, a.rows, a.cols, a.amax, a.codes, \
+                                                          a.scales, a.gdec, a.mask, a.seed,   \
+                                                          a.offset, a.rounds)
+    if (a.sr && a.rht) NVFP4_COL(true, true);
+    else if (a.sr) NVFP4_COL(true, false);
+    else if (a.rht) NVFP4_COL(false, true);
+    else NVFP4_COL(false, false);
+#undef NVFP4_COL
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
+  const T* w = static_cast<const T*>(a.w);
+  if (!a.amax_is_input) {
+    fill_zero_kernel<<<(unsigned)cdiv(a.batch, 256), 256, 0, st>>>(a.amax, a.batch);
+    int64_t chunks = a.rows * a.cols / 8;
+    dim3 grid(amax_grid(chunks) > 512 ? 512 : amax_grid(chunks), (unsigned)a.batch);
+    amax_flat_kernel<T, false><<<grid, kThreads, 0, st>>>(w, chunks, 0, a.amax);
+  }
+  int64_t units = (a.rows / 16) * (a.cols / 8);
+  dim3 grid((unsigned)cdiv(units, kThreads), (unsigned)a.batch);
+  quant_2d_kernel<T><<<grid, kThreads, 0, st>>>(w, a.rows, a.cols, a.amax, a.codes, a.scales,
+                                                a.gdec);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_rht16_t(const void* xv, int64_t rows, int64_t cols, int axis, uint32_t mask,
+                          float* y, hipStream_t st) {
+  const T* x = static_cast<const T*>(xv);
+  if (axis == kBlockRow) {
+    int64_t chunks = rows * cols / 8;
+    rht_row_kernel<T><<<(unsigned)cdiv(chunks, kThreads), kThreads, 0, st>>>(x, chunks, mask, y);
+  } else {
+    int64_t units = (rows / 16) * (cols / 8);
+    rht_col_kernel<T><<<(unsigned)cdiv(units, kThreads), kThreads, 0, st>>>(x, rows, cols, mask,
+                                                                            y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st) {
+  return a.x_fp32 ? launch_quantize_1d_t<float>(a, st) : launch_quantize_1d_t<uint16_t>(a, st);
+}
+
+hipError_t launch_quantize_2d(const Quant2dArgs& a, hipStream_t st) {
+  return a.w_fp32 ? launch_quantize_2d_t<float>(a, st) : launch_quantize_2d_t<uint16_t>(a, st);
+}
+
+hipError_t launch_rht16(const void* x, bool x_fp32, int64_t rows, int64_t cols, int axis,
+                        uint32_t mask, float* y, hipStream_t st) {
+  return x_fp32 ? launch_rht16_t<float>(x, rows, cols, axis, mask, y, st)
+                : launch_rht16_t<uint16_t>(x, rows, cols, axis, mask, y, st);
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gdec,
+                             int64_t rows, int64_t cols, int block, float* y, hipStream_t st) {
+  int64_t n = rows * cols / 8;
+  dequant_kernel<<<(unsigned)cdiv(n, kThreads), kThreads, 0, st>>>(
+      reinterpret_cast<const uint32_t*>(codes), scales, gdec, rows, cols, block, y);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

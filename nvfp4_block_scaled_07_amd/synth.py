@@ -97,3 +97,24 @@ WORKLOADS = {
                   dy_seed=13, dy_b=1e-3, philox_seed=14, glat=2048,
                   ghidden=5120, gx_seed=15, groute_seed=16, gw_seed=17),
 }
+
+
+def normal_device(shape, std, seed, device, dtype=torch.bfloat16):
+    """N(0, std^2) drawn by torch's generator on the device (used for large
+    benchmark inputs, where host generation would dominate set-up time)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(dtype)
+
+
+def laplace_device(shape, b, seed, device, zero_frac=0.0, dtype=torch.bfloat16):
+    """Laplace(0, b) on the device (inverse CDF of a uniform), optionally with
+    a Bernoulli(zero_frac) mask of exact zeros."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    u = torch.rand(shape, generator=g, device=device, dtype=torch.float32) - 0.5
+    x = -b * torch.sign(u) * torch.log1p(-2.0 * u.abs())
+    if zero_frac > 0.0:
+        z = torch.rand(shape, generator=g, device=device, dtype=torch.float32) < zero_frac
+        x = x.masked_fill(z, 0.0)
+    return x.to(dtype)

@@ -1,0 +1,91 @@
+"""The C-ABI library loads and exports every entry point that include/nvfp4.h
+declares, and its host-side argument checks reject bad calls with the
+documented status codes before touching a device (runs without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+LIB = os.path.join(ROOT, "nvfp4_block_scaled_07_amd", "libnvfp4.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libnvfp4.so not built")
+    from nvfp4_block_scaled_07_amd import _binding
+    return _binding.load()
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for f in ["nvfp4_abi_version", "nvfp4_status_string", "nvfp4_quantize_1d",
+              "nvfp4_quantize_2d", "nvfp4_rht16", "nvfp4_dequantize", "nvfp4_gemm",
+              "nvfp4_grouped_gemm"]:
+        assert f in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+
+
+def test_version_and_status_strings(lib):
+    assert lib.nvfp4_abi_version() == 1
+    for s in range(-6, 1):
+        assert lib.nvfp4_status_string(s)
+    assert lib.nvfp4_status_string(-99) == b"unknown status"
+
+
+FAKE = C.c_void_p(0x100000)  # never dereferenced: every call below fails validation
+
+
+def test_quantize_1d_validation(lib):
+    q = lib.nvfp4_quantize_1d
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("dt", 0), kw.get("rows", 64), kw.get("cols", 64),
+                         kw.get("axis", 0), kw.get("rnd", 0), kw.get("rng", None),
+                         kw.get("mask", -1), kw.get("amax", FAKE), 0, kw.get("codes", FAKE),
+                         kw.get("scales", FAKE), kw.get("g", FAKE), None]
+    assert q(*args(x=None)) == -1
+    assert q(*args(cols=48)) == -2          # cols % 32
+    assert q(*args(axis=1, rows=40)) == -2  # COL needs rows % 16
+    assert q(*args(axis=2)) == -4           # 2D goes through quantize_2d
+    assert q(*args(rnd=1)) == -1            # SR without a Philox stream
+    assert q(*args(mask=0x10000)) == -5
+    assert q(*args(dt=7)) == -5
+    assert q(*args(x=C.c_void_p(0x100004))) == -3
+    assert q(*args(rows=0)) == 0            # empty: nothing to do
+
+
+def test_gemm_validation(lib):
+    from nvfp4_block_scaled_07_amd._binding import _Operand
+    A = _Operand(0x100000, 0x200000, 0x300000, 64, 128, 0, 0)
+    B = _Operand(0x100000, 0x200000, 0x300000, 64, 128, 2, 0)
+    g = lib.nvfp4_gemm
+    assert g(b"T", b"T", 64, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -5
+    assert g(b"X", b"T", 64, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -4
+    assert g(b"N", b"T", 64, 64, 96, C.byref(A), C.byref(B), FAKE, 0, None) == -2   # K % 64
+    assert g(b"N", b"T", 64, 64, 128, C.byref(A), C.byref(B), None, 0, None) == -1
+    bad = _Operand(0x100000, 0x200000, 0x300000, 64, 128, 1, 0)  # COL blocks on a K-major A
+    assert g(b"N", b"T", 64, 64, 128, C.byref(bad), C.byref(B), FAKE, 0, None) == -4
+    wrong = _Operand(0x100000, 0x200000, 0x300000, 65, 128, 0, 0)
+    assert g(b"N", b"T", 64, 64, 128, C.byref(wrong), C.byref(B), FAKE, 0, None) == -2
+
+
+def test_grouped_validation(lib):
+    from nvfp4_block_scaled_07_amd._binding import _Operand
+    A = _Operand(0x100000, 0x200000, 0x300000, 100, 128, 0, 0)
+    B = _Operand(0x100000, 0x200000, 0x300000, 64, 128, 2, 0)
+    f = lib.nvfp4_grouped_gemm
+    assert f(4, None, 100, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -1
+    assert f(5000, FAKE, 100, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -2
+    assert f(4, FAKE, 100, 60, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -2

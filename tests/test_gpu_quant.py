@@ -1,0 +1,182 @@
+"""GPU parity: quantizers, Hadamard transform and dequantizer, bit-exact
+against the CPU oracle (codes, scale bytes, amax, decode scale), called
+through the C ABI.
+
+Small cases span several workgroups and ragged tails with every combination
+of block axis, rounding, transform and input type; full-size cases use the
+workloads' own shapes and distributions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_07_amd as nv
+import oracle as O
+from nvfp4_block_scaled_07_amd import synth
+from _gpu import assert_same, device, device_input, make_input, to_np
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(16, 32), (48, 96), (1000, 64), (64, 2080), (272, 160)]
+
+
+def _check_1d(x, dtype, axis, rounding, mask, seed=0, offset=0, rounds=5, amax=None):
+    dev = device()
+    t, xo = device_input(x, dtype, dev)
+    rng = nv.Philox(seed, offset, rounds) if rounding == "sr" else None
+    a_t = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=dev)
+    q = nv.quantize_1d(t, axis, rounding, rng, mask, amax=a_t)
+    got = to_np(q)
+    ref = O.quantize(xo, axis, rounding=O.SR if rounding == "sr" else O.RNE, seed=seed,
+                     offset=offset, rounds=rounds, rht_mask=mask, amax=amax)
+    assert_same(got["amax"][0], ref["amax"], "amax")
+    assert_same(np.float32(got["g"]), ref["g"], "global decode scale")
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+    return q, ref
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_1d_small(shape, axis, rounding, rht, dtype):
+    if axis == "col" and shape[0] % 16:
+        pytest.skip("COL blocks need rows % 16 == 0")
+    x = make_input("normal", shape, seed=shape[0] * 7 + shape[1])
+    _check_1d(x, dtype, axis, rounding, 0xA5C3 if rht else -1, seed=123, offset=9)
+
+
+@pytest.mark.parametrize("kind", ["laplace_zeros", "wide", "tiny", "zeros"])
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_quantize_1d_distributions(kind, axis, rounding):
+    x = make_input(kind, (64, 256), seed=5)
+    _check_1d(x, "bf16", axis, rounding, 0x1234 if axis == "col" else -1, seed=77)
+    _check_1d(x, "fp32", axis, rounding, -1, seed=77)
+
+
+def test_quantize_1d_philox_rounds_and_offsets():
+    x = make_input("normal", (32, 128), seed=3)
+    for rounds in (1, 5, 10, 16):
+        _check_1d(x, "bf16", "row", "sr", -1, seed=2**40 + 3, offset=2**33 + 1, rounds=rounds)
+    _check_1d(x, "bf16", "col", "sr", 0xFFFF, seed=1, offset=0, rounds=10)
+
+
+def test_quantize_1d_amax_input():
+    x = make_input("normal", (64, 128), seed=4)
+    # a supplied amax larger than the data: smaller codes, still bit-exact
+    _check_1d(x, "bf16", "row", "rne", -1, amax=50.0)
+    _check_1d(x, "fp32", "col", "sr", 0x00FF, amax=12.5)
+
+
+def test_quantize_1d_empty():
+    dev = device()
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    q = nv.quantize_1d(x, "row")
+    assert q.codes.numel() == 0
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(1, 16, 32), (1, 48, 96), (3, 32, 160),
+                                             (5, 272, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_2d_small(batch, rows, cols, dtype):
+    dev = device()
+    x = make_input("normal", (batch, rows, cols), seed=batch + rows)
+    x *= np.float32(10.0) ** np.arange(batch, dtype=np.float32)[:, None, None]
+    t, xo = device_input(x, dtype, dev)
+    q = nv.quantize_2d(t)
+    got = to_np(q)
+    ref = O.quantize(xo, "2d")
+    assert_same(got["amax"], ref["amax"], "amax")
+    assert_same(q.global_dec.cpu().numpy(), ref["g"], "g")
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+
+
+@pytest.mark.parametrize("axis", ["row", "col"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_rht16_standalone(axis, dtype):
+    dev = device()
+    x = make_input("normal", (48, 96), seed=8)
+    t, xo = device_input(x, dtype, dev)
+    y = nv.rht16(t, axis, 0x5A5A)
+    assert_same(y.cpu().numpy(), O.rht16(xo, axis, 0x5A5A), "rht16")
+
+
+@pytest.mark.parametrize("axis", ["row", "col", "2d"])
+def test_dequantize(axis):
+    dev = device()
+    x = make_input("normal", (64, 96), seed=9)
+    t, xo = device_input(x, "bf16", dev)
+    q = nv.quantize_2d(t) if axis == "2d" else nv.quantize_1d(t, axis, "sr", nv.Philox(4))
+    got = nv.dequantize(q, index=None).cpu().numpy()
+    r = to_np(q)
+    want = O.dequantize(r["codes"], r["scales"], r["g"] if axis != "2d" else r["g"], axis)
+    assert_same(got.view(np.uint32), want.view(np.uint32), "dequantized bits")
+
+
+def test_tiny_config():
+    """X fp32 [256x512] ~N(0,1), seed 0, 1x16 RNE, dequantize."""
+    dev = device()
+    x = synth.normal((256, 512), 1.0, 0)
+    q, ref = _check_1d(x, "fp32", "row", "rne", -1)
+    got = nv.dequantize(q).cpu().numpy()
+    want = O.dequantize(ref["codes"], ref["scales"], ref["g"], "row")
+    assert_same(got.view(np.uint32), want.view(np.uint32), "dequantized bits")
+
+
+# ---- full-size workloads -------------------------------------------------------------------------
+def test_full_fprop_super_inputs():
+    w = synth.WORKLOADS["fprop_super"]
+    dev = device()
+    x = synth.normal((w["M"], w["K"]), w["x_std"], w["x_seed"])
+    _check_1d(x, "bf16", "row", "rne", -1)
+    wt = synth.normal((w["N"], w["K"]), w["w_std"], w["w_seed"])
+    t, xo = device_input(wt, "bf16", dev)
+    q = nv.quantize_2d(t)
+    got = to_np(q)
+    ref = O.quantize(xo, "2d")
+    assert_same(got["scales"], ref["scales"], "W scales")
+    assert_same(got["codes"], ref["codes"], "W codes")
+    assert_same(np.float32(got["g"]), ref["g"], "W g")
+
+
+def test_full_wgrad_super_inputs():
+    w = synth.WORKLOADS["wgrad_super"]
+    shape = (w["tokens"], w["out"])
+    dy = synth.laplace(shape, w["dy_b"], w["dy_seed"], w["zero_frac"], w["zero_seed"])
+    mask = synth.rht_mask(w["mask_seed"])
+    q, ref = _check_1d(dy, "bf16", "col", "sr", mask, seed=w["philox_seed"])
+    zero_codes = (np.stack([ref["codes"] & 7, (ref["codes"] >> 4) & 7]) == 0).mean()
+    print(f"dY zero-code fraction {zero_codes:.4f}")
+    x = synth.normal((w["tokens"], w["inp"]), 1.0, w["x_seed"])
+    _check_1d(x, "bf16", "col", "rne", mask)
+
+
+def test_full_ultra_dgrad_input():
+    w = synth.WORKLOADS["ultra"]
+    dy = synth.laplace((w["M"], w["N"]), w["dy_b"], w["dy_seed"])
+    _check_1d(dy, "bf16", "row", "sr", -1, seed=w["philox_seed"])
+
+
+def test_full_grouped_super_weights_sampled():
+    """W [512 x 2688 x 1024] 2D-quantized in one call; per-slice amax and g
+    for all 512 experts, codes and scales for a sample of slices."""
+    w = synth.WORKLOADS["grouped_super"]
+    dev = device()
+    shape = (w["experts"], w["hidden"], w["latent"])
+    x = synth.normal(shape, w["w_std"], w["w_seed"])
+    t, xo = device_input(x, "bf16", dev)
+    del x
+    q = nv.quantize_2d(t)
+    torch.cuda.synchronize()
+    ref_amax = O.amax(xo, "2d")
+    assert_same(q.amax.cpu().numpy(), ref_amax, "per-expert amax")
+    g = q.global_dec.cpu().numpy()
+    for e in [0, 1, 255, 511]:
+        ref = O.quantize(xo[e], "2d")
+        assert_same(q.codes[e].cpu().numpy(), ref["codes"], f"codes of expert {e}")
+        assert_same(q.scales[e].cpu().numpy(), ref["scales"], f"scales of expert {e}")
+        assert g[e] == ref["g"]
