@@ -78,11 +78,11 @@ int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t 
   if (rounding == NVFP4_SR && !rng) return NVFP4_ERR_NULL;
   if (rng && rounding == NVFP4_SR && (rng->rounds < 1 || rng->rounds > 16))
     return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return NVFP4_OK;  // empty: pointers may be NULL
   if (!x || !amax || !codes || !scales || !global_dec) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
       !aligned(global_dec, 4))
     return NVFP4_ERR_ALIGN;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
   nvfp4::QuantArgs a{};
   a.x = x;
   a.x_fp32 = x_dtype == NVFP4_FP32;
@@ -110,12 +110,11 @@ int32_t nvfp4_quantize_2d(const void* w, int32_t w_dtype, int64_t batch, int64_t
   if (batch < 0 || rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
   if (rows % 16 != 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
   if (batch > 65535) return NVFP4_ERR_SHAPE;
+  if (batch == 0 || rows == 0 || cols == 0) return NVFP4_OK;  // empty: pointers may be NULL
   if (!w || !amax || !codes || !scales || !global_dec) return NVFP4_ERR_NULL;
   if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
       !aligned(global_dec, 4))
     return NVFP4_ERR_ALIGN;
-  if (batch == 0) return NVFP4_OK;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
   nvfp4::Quant2dArgs a{};
   a.w = w;
   a.w_fp32 = w_dtype == NVFP4_FP32;
@@ -137,9 +136,9 @@ int32_t nvfp4_rht16(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, 
   if (sign_mask > 0xFFFFu) return NVFP4_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
   if (axis == NVFP4_BLOCK_COL && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;  // empty: pointers may be NULL
   if (!x || !y) return NVFP4_ERR_NULL;
   if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
-  if (rows == 0 || cols == 0) return NVFP4_OK;
   return device_status(nvfp4::launch_rht16(x, x_dtype == NVFP4_FP32, rows, cols,
                                            axis == NVFP4_BLOCK_ROW ? nvfp4::kBlockRow
                                                                    : nvfp4::kBlockCol,

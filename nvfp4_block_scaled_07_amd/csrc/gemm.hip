@@ -33,6 +33,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
 constexpr int BK = 64;  // k per LDS stage
 
@@ -58,17 +59,22 @@ struct OpView {
 
 __device__ __forceinline__ uint32_t bits_of(half2 h) { return __builtin_bit_cast(uint32_t, h); }
 
-// 4 E4M3 scale bytes -> 4 packed fp16 pairs (d, d).
-__device__ __forceinline__ uint4 expand_scales(uint32_t s4) {
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    float d = e4m3_decode((s4 >> (8 * i)) & 0xFFu);
-    _Float16 h = (_Float16)d;  // exact: every E4M3 value is an fp16 value
-    half2 p = {h, h};
-    o[i] = bits_of(p);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+// Every E4M3 byte -> its packed fp16 pair (d, d), for the 256-entry table each
+// workgroup keeps in LDS (exact: every E4M3 value is an fp16 value).
+__device__ __forceinline__ uint32_t e4m3_pair_f16(uint32_t e) {
+  _Float16 h = (_Float16)e4m3_decode(e & 0x7Fu);
+  half2 p = {h, h};
+  return bits_of(p);
+}
+
+__device__ __forceinline__ void build_scale_table(uint32_t* table, int tid, int nt) {
+  for (int i = tid; i < 256; i += nt) table[i] = e4m3_pair_f16((uint32_t)i);
+}
+
+// 4 E4M3 scale bytes -> 4 packed fp16 pairs, through the LDS table.
+__device__ __forceinline__ uint4 expand_scales(uint32_t s4, const uint32_t* table) {
+  return make_uint4(table[s4 & 0xFFu], table[(s4 >> 8) & 0xFFu], table[(s4 >> 16) & 0xFFu],
+                    table[s4 >> 24]);
 }
 
 // Swizzled LDS addresses (bytes within one operand's region).
@@ -104,12 +110,19 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t d[8]) {
 }
 
 // ---- staging: global -> registers -> LDS ---------------------------------------------------
+// Loads are branch-free and unmasked: a row past the operand's edge re-reads
+// the last valid row (always in bounds).  Row i of A only reaches row i of C
+// and row j of B only column j, so such rows only feed outputs that are never
+// stored.  The main loop stays one basic block the scheduler can interleave,
+// and the prefetched values are not consumed until the stage is written out.
+
 // K-major operand, ROWS rows of the tile, NT threads.
 template <int ROWS, int NT>
 struct StageK {
+  static_assert((ROWS * 2) % NT == 0 && ROWS % NT == 0, "tile rows must divide evenly");
   static constexpr int CN = ROWS * 2 / NT;  // uint4 of codes per thread
-  static constexpr int SN = (ROWS + NT - 1) / NT;
-  uint4 c[CN];
+  static constexpr int SN = ROWS / NT;      // scale dwords per thread
+  u32x4 c[CN];
   uint32_t s[SN];
 
   __device__ __forceinline__ void load(const OpView& op, int64_t mn0, int64_t mn_lim,
@@ -118,36 +131,40 @@ struct StageK {
     for (int j = 0; j < CN; j++) {
       int idx = tid + j * NT;
       int64_t mn = mn0 + (idx >> 1);
-      c[j] = make_uint4(0, 0, 0, 0);
-      if (mn < mn_lim)
-        c[j] = *reinterpret_cast<const uint4*>(op.codes + mn * (K / 2) + k0 / 2 + 16 * (idx & 1));
+      int64_t mc = mn < mn_lim ? mn : mn_lim - 1;
+      c[j] = *reinterpret_cast<const u32x4*>(op.codes + mc * (K / 2) + k0 / 2 + 16 * (idx & 1));
     }
 #pragma unroll
     for (int j = 0; j < SN; j++) {
-      int idx = tid + j * NT;
-      int64_t mn = mn0 + idx;
-      s[j] = 0;
-      if (idx < ROWS && mn < mn_lim) {
-        int64_t off = op.block == kBlock2d ? (mn / 16) * (K / 16) : mn * (K / 16);
-        s[j] = *reinterpret_cast<const uint32_t*>(op.scales + off + k0 / 16);
-      }
+      int64_t mn = mn0 + tid + j * NT;
+      int64_t mc = mn < mn_lim ? mn : mn_lim - 1;
+      int64_t off = op.block == kBlock2d ? (mc / 16) * (K / 16) : mc * (K / 16);
+      s[j] = *reinterpret_cast<const uint32_t*>(op.scales + off + k0 / 16);
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* lds_codes, uint8_t* lds_scales, int tid) const {
+  __device__ __forceinline__ void store(uint8_t* lds_codes, uint8_t* lds_scales, int tid,
+                                        const uint32_t* table) const {
+    store_codes(lds_codes, tid);
+    store_scales(lds_scales, tid, table);
+  }
+
+  __device__ __forceinline__ void store_codes(uint8_t* lds_codes, int tid) const {
 #pragma unroll
     for (int j = 0; j < CN; j++) {
       int idx = tid + j * NT;
-      *reinterpret_cast<uint4*>(lds_codes + code_addr(idx >> 1, idx & 1)) = c[j];
+      *reinterpret_cast<u32x4*>(lds_codes + code_addr(idx >> 1, idx & 1)) = c[j];
     }
+  }
+
+  __device__ __forceinline__ void store_scales(uint8_t* lds_scales, int tid,
+                                               const uint32_t* table) const {
 #pragma unroll
     for (int j = 0; j < SN; j++) {
       int idx = tid + j * NT;
-      if (idx < ROWS) {
-        uint4 e = expand_scales(s[j]);
-        *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 0)) = make_uint2(e.x, e.y);
-        *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 1)) = make_uint2(e.z, e.w);
-      }
+      uint4 e = expand_scales(s[j], table);
+      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 0)) = make_uint2(e.x, e.y);
+      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 1)) = make_uint2(e.z, e.w);
     }
   }
 };
@@ -157,8 +174,9 @@ struct StageK {
 template <int ROWS, int NT>
 struct StageMN {
   static constexpr int UNITS = (BK / 8) * (ROWS / 8);
-  static constexpr int UN = (UNITS + NT - 1) / NT;
-  static constexpr int SN = (ROWS + NT - 1) / NT;
+  static_assert(UNITS % NT == 0 && ROWS % NT == 0, "tile must divide evenly");
+  static constexpr int UN = UNITS / NT;
+  static constexpr int SN = ROWS / NT;
   uint32_t c[UN][8];
   uint32_t s[SN];
 
@@ -171,37 +189,37 @@ struct StageMN {
       int u = tid + j * NT;
       int kg = u / (ROWS / 8), md = u % (ROWS / 8);
       int64_t mn = mn0 + 8 * md;
-      bool ok = u < UNITS && mn < mn_lim;  // mn_lim is a multiple of 8
+      int64_t mc = mn < mn_lim ? mn : mn_lim - 8;  // mn_lim is a multiple of 8
 #pragma unroll
-      for (int r = 0; r < 8; r++) {
-        c[j][r] = 0;
-        if (ok)
-          c[j][r] = *reinterpret_cast<const uint32_t*>(op.codes + (k0 + 8 * kg + r) * (W / 2) +
-                                                        mn / 2);
-      }
+      for (int r = 0; r < 8; r++)
+        c[j][r] = *reinterpret_cast<const uint32_t*>(op.codes + (k0 + 8 * kg + r) * (W / 2) +
+                                                      mc / 2);
     }
 #pragma unroll
     for (int j = 0; j < SN; j++) {
-      int idx = tid + j * NT;
-      int64_t mn = mn0 + idx;
+      int64_t mn = mn0 + tid + j * NT;
+      int64_t mc = mn < mn_lim ? mn : mn_lim - 1;
       uint32_t v = 0;
-      if (idx < ROWS && mn < mn_lim) {
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
-          int64_t row = k0 / 16 + kb;
-          int64_t off = op.block == kBlock2d ? row * (W / 16) + mn / 16 : row * W + mn;
-          v |= (uint32_t)op.scales[off] << (8 * kb);
-        }
+      for (int kb = 0; kb < 4; kb++) {
+        int64_t row = k0 / 16 + kb;
+        int64_t off = op.block == kBlock2d ? row * (W / 16) + mc / 16 : row * W + mc;
+        v |= (uint32_t)op.scales[off] << (8 * kb);
       }
       s[j] = v;
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* lds_codes, uint8_t* lds_scales, int tid) {
+  __device__ __forceinline__ void store(uint8_t* lds_codes, uint8_t* lds_scales, int tid,
+                                        const uint32_t* table) {
+    store_codes(lds_codes, tid);
+    store_scales(lds_scales, tid, table);
+  }
+
+  __device__ __forceinline__ void store_codes(uint8_t* lds_codes, int tid) {
 #pragma unroll
     for (int j = 0; j < UN; j++) {
       int u = tid + j * NT;
-      if (u >= UNITS) continue;
       int kg = u / (ROWS / 8), md = u % (ROWS / 8);
       transpose8x8_nibbles(c[j]);
 #pragma unroll
@@ -211,14 +229,16 @@ struct StageMN {
             c[j][i];
       }
     }
+  }
+
+  __device__ __forceinline__ void store_scales(uint8_t* lds_scales, int tid,
+                                               const uint32_t* table) const {
 #pragma unroll
     for (int j = 0; j < SN; j++) {
       int idx = tid + j * NT;
-      if (idx < ROWS) {
-        uint4 e = expand_scales(s[j]);
-        *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 0)) = make_uint2(e.x, e.y);
-        *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 1)) = make_uint2(e.z, e.w);
-      }
+      uint4 e = expand_scales(s[j], table);
+      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 0)) = make_uint2(e.x, e.y);
+      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 1)) = make_uint2(e.z, e.w);
     }
   }
 };
@@ -226,7 +246,9 @@ struct StageMN {
 template <bool KMAJOR, int ROWS, int NT>
 using Stage = typename std::conditional<KMAJOR, StageK<ROWS, NT>, StageMN<ROWS, NT>>::type;
 
-// Decode 8 nibbles (one dword) scaled by the packed pair sc = (d, d).
+// Decode 8 nibbles (one dword) scaled by the packed pair sc = (d, d).  The
+// conversion's own scale operand only applies a power of two, so it stays 1
+// and the E4M3 scale is a separate exact fp16 multiply.
 __device__ __forceinline__ half8 decode8(uint32_t q, uint32_t sc) {
   half2 d = __builtin_bit_cast(half2, sc);
   half2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * d;
@@ -242,8 +264,19 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+__device__ __forceinline__ uint32_t pick(const uint4& v, int s) {
+  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+}
+
 // One output tile: C[m0 : m0+BM) x [n0 : n0+BN) restricted to rows < m_lim,
-// cols < N.  lds must hold 2 stages.
+// cols < N.  lds holds 2 stages and then the 256-entry scale table, which
+// the caller has built (and synchronized) before the first tile.
+//
+// Per 64-k stage each wave: loads the next stage from global memory (held in
+// registers), reads its fragments' codes and scales from LDS, decodes the
+// first 16-k step, then runs the four steps' MFMAs while decoding the next
+// step between them, and writes the next stage to the other LDS buffer
+// during the last step.
 template <class C, bool AK, bool BKM>
 __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int64_t m0,
                                           int64_t m_lim, int64_t n0, int64_t N, int64_t K,
@@ -265,69 +298,104 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
   Stage<AK, C::BM, C::NT> sa;
   Stage<BKM, C::BN, C::NT> sb;
   const int64_t KT = K / BK;
+  const uint32_t* table = reinterpret_cast<const uint32_t*>(lds + 2 * C::kStage);
 
-  auto lds_stage = [&](int buf) { return lds + buf * C::kStage; };
+  // Fragment rows of one wave step by 32, which keeps both swizzles (they
+  // depend on row bits 2 and 3), so each operand needs one base address.
+  const int a_row0 = wm * (C::BM / C::WM) + lrow, b_row0 = wn * (C::BN / C::WN) + lrow;
+  const int a_code0 = code_addr(a_row0, lhalf);
+  const int a_sc0 = C::kACodes + scale_addr(a_row0, lhalf);
+  const int b_code0 = C::kACodes + C::kAScales + code_addr(b_row0, lhalf);
+  const int b_sc0 = C::kACodes + C::kAScales + C::kBCodes + scale_addr(b_row0, lhalf);
 
   sa.load(A, m0, m_lim, 0, K, tid);
   sb.load(B, n0, N, 0, K, tid);
-  {
-    uint8_t* s0 = lds_stage(0);
-    sa.store(s0, s0 + C::kACodes, tid);
-    sb.store(s0 + C::kACodes + C::kAScales, s0 + C::kACodes + C::kAScales + C::kBCodes, tid);
-  }
+  sa.store(lds, lds + C::kACodes, tid, table);
+  sb.store(lds + C::kACodes + C::kAScales, lds + C::kACodes + C::kAScales + C::kBCodes, tid,
+           table);
   __syncthreads();
 
   for (int64_t kt = 0; kt < KT; kt++) {
     const int buf = (int)(kt & 1);
-    if (kt + 1 < KT) {
-      sa.load(A, m0, m_lim, (kt + 1) * BK, K, tid);
-      sb.load(B, n0, N, (kt + 1) * BK, K, tid);
-    }
-    const uint8_t* st = lds_stage(buf);
-    const uint8_t* a_codes = st;
-    const uint8_t* a_sc = st + C::kACodes;
-    const uint8_t* b_codes = a_sc + C::kAScales;
-    const uint8_t* b_sc = b_codes + C::kBCodes;
+    // Next stage (the last iteration reloads the final stage into the idle
+    // buffer, which keeps the loop free of branches).
+    const int64_t kn = (kt + 1 < KT ? kt + 1 : kt) * BK;
+    sa.load(A, m0, m_lim, kn, K, tid);
+    sb.load(B, n0, N, kn, K, tid);
 
+    const uint8_t* st = lds + buf * C::kStage;
     uint4 aq[C::TM], bq[C::TN];
     uint2 as[C::TM], bs[C::TN];
 #pragma unroll
     for (int i = 0; i < C::TM; i++) {
-      int row = wm * (C::BM / C::WM) + i * 32 + lrow;
-      aq[i] = *reinterpret_cast<const uint4*>(a_codes + code_addr(row, lhalf));
-      as[i] = *reinterpret_cast<const uint2*>(a_sc + scale_addr(row, lhalf));
+      aq[i] = *reinterpret_cast<const uint4*>(st + a_code0 + i * 32 * 32);
+      as[i] = *reinterpret_cast<const uint2*>(st + a_sc0 + i * 32 * 16);
     }
 #pragma unroll
     for (int j = 0; j < C::TN; j++) {
-      int row = wn * (C::BN / C::WN) + j * 32 + lrow;
-      bq[j] = *reinterpret_cast<const uint4*>(b_codes + code_addr(row, lhalf));
-      bs[j] = *reinterpret_cast<const uint2*>(b_sc + scale_addr(row, lhalf));
-    }
-#pragma unroll
-    for (int s = 0; s < 4; s++) {
-      half8 af[C::TM], bf[C::TN];
-#pragma unroll
-      for (int i = 0; i < C::TM; i++) {
-        uint32_t q = s == 0 ? aq[i].x : s == 1 ? aq[i].y : s == 2 ? aq[i].z : aq[i].w;
-        af[i] = decode8(q, s < 2 ? as[i].x : as[i].y);
-      }
-#pragma unroll
-      for (int j = 0; j < C::TN; j++) {
-        uint32_t q = s == 0 ? bq[j].x : s == 1 ? bq[j].y : s == 2 ? bq[j].z : bq[j].w;
-        bf[j] = decode8(q, s < 2 ? bs[j].x : bs[j].y);
-      }
-#pragma unroll
-      for (int i = 0; i < C::TM; i++)
-#pragma unroll
-        for (int j = 0; j < C::TN; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      bq[j] = *reinterpret_cast<const uint4*>(st + b_code0 + j * 32 * 32);
+      bs[j] = *reinterpret_cast<const uint2*>(st + b_sc0 + j * 32 * 16);
     }
 
-    if (kt + 1 < KT) {
-      uint8_t* sn = lds_stage(buf ^ 1);
-      sa.store(sn, sn + C::kACodes, tid);
-      sb.store(sn + C::kACodes + C::kAScales, sn + C::kACodes + C::kAScales + C::kBCodes, tid);
+    // A fragments are single-buffered: fragment i of the next step is decoded
+    // once row i's MFMAs of this step have issued.  B fragments, used by every
+    // row, are double-buffered.
+    half8 af[C::TM], bf[2][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; i++) af[i] = decode8(aq[i].x, as[i].x);
+#pragma unroll
+    for (int j = 0; j < C::TN; j++) bf[0][j] = decode8(bq[j].x, bs[j].x);
+
+    // Steps 0..3 of the stage.  The order is fixed in the source and fenced
+    // with sched_barrier: after every second MFMA one fragment of the next
+    // step is decoded (8 VALU ops that issue while the MFMAs run) -- first the
+    // B fragments, then A fragment f once row f is done; during the last step
+    // the next stage is written to the other LDS buffer instead.
+    uint8_t* sn = lds + (buf ^ 1) * C::kStage;
+    static_assert(C::TM == 4 && C::TN == 4, "interleave expects 4x4 MFMA tiles per wave");
+#pragma unroll
+    for (int s = 0; s < 3; s++) {
+      const int cur = s & 1, nxt = cur ^ 1;
+#pragma unroll
+      for (int i = 0; i < C::TM; i++) {
+#pragma unroll
+        for (int j = 0; j < C::TN; j++) {
+          acc[i][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[cur][j], acc[i][j], 0, 0, 0);
+          const int t = i * C::TN + j;
+          if (t & 1) {
+            const int f = t >> 1;  // 0..3: B fragment f; 4..7: A fragment f-4
+            if (f < C::TN)
+              bf[nxt][f] = decode8(pick(bq[f], s + 1), s + 1 < 2 ? bs[f].x : bs[f].y);
+            else
+              af[f - C::TN] = decode8(pick(aq[f - C::TN], s + 1),
+                                      s + 1 < 2 ? as[f - C::TN].x : as[f - C::TN].y);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
     }
+    // Step 3 (uses bf[1]): one row of MFMAs, then a quarter of the next
+    // stage's LDS writes.
+#pragma unroll
+    for (int j = 0; j < C::TN; j++)
+      acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0], bf[1][j], acc[0][j], 0, 0, 0);
+    sa.store_codes(sn, tid);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < C::TN; j++)
+      acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1], bf[1][j], acc[1][j], 0, 0, 0);
+    sa.store_scales(sn + C::kACodes, tid, table);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < C::TN; j++)
+      acc[2][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[2], bf[1][j], acc[2][j], 0, 0, 0);
+    sb.store_codes(sn + C::kACodes + C::kAScales, tid);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < C::TN; j++)
+      acc[3][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[3], bf[1][j], acc[3][j], 0, 0, 0);
+    sb.store_scales(sn + C::kACodes + C::kAScales + C::kBCodes, tid, table);
     __syncthreads();
   }
 
@@ -376,17 +444,18 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   OpView A{a.A.codes, a.A.scales, a.M, a.A.block};
   OpView B{a.B.codes, a.B.scales, a.N, a.B.block};
   const float gs = *a.A.gdec * *a.B.gdec;
+  build_scale_table(reinterpret_cast<uint32_t*>(lds + 2 * C::kStage), threadIdx.x, C::NT);
+  __syncthreads();
   gemm_tile<C, AK, BKM>(A, B, tm * C::BM, a.M, tn * C::BN, a.N, a.K, gs, a.C, a.c_bf16, a.N, lds);
 }
 
 // Persistent grouped kernel: every workgroup builds the prefix of per-group
 // tile counts in LDS, then walks tiles blockIdx.x, +gridDim.x, ...
-constexpr int kMaxGroups = 4096;
-
 template <class C>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  int32_t* prefix = reinterpret_cast<int32_t*>(lds + 2 * C::kStage);  // [groups + 1]
+  build_scale_table(reinterpret_cast<uint32_t*>(lds + 2 * C::kStage), threadIdx.x, C::NT);
+  int32_t* prefix = reinterpret_cast<int32_t*>(lds + 2 * C::kStage + 1024);  // [groups + 1]
   __shared__ int32_t part[C::NT];
   const int tid = threadIdx.x;
   const int64_t G = a.groups;
@@ -451,7 +520,7 @@ using Grouped = Cfg<256, 256, 2, 2>;
 template <class C, bool AK, bool BKM>
 hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
-  const size_t smem = 2 * C::kStage;
+  const size_t smem = 2 * C::kStage + 1024;
   auto kern = gemm_kernel<C, AK, BKM>;
   if (smem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -483,7 +552,7 @@ hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st) {
   const int64_t max_tiles = ((a.total_rows + C::BM - 1) / C::BM + a.groups) * ntn;
   int64_t grid = cus > 0 ? cus : 256;
   if (grid > max_tiles) grid = max_tiles;
-  const size_t smem = 2 * C::kStage + sizeof(int32_t) * (size_t)(a.groups + 1);
+  const size_t smem = 2 * C::kStage + 1024 + sizeof(int32_t) * (size_t)(a.groups + 1);
   auto kern = grouped_gemm_kernel<C>;
   if (smem > 65536) {
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
