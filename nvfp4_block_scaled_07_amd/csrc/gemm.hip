@@ -7,17 +7,19 @@
 //    bits, an E4M3 scale 4, so their product has at most 6 and lies in
 //    [2^-10, 2688] -- and fed to v_mfma_f32_32x32x16_f16 with fp32
 //    accumulation.
-//  * Codes and scales (0.5625 B per element) are staged global -> VGPR ->
-//    LDS in a canonical K-major layout: 32 code bytes (64 k) per row per stage
-//    and the scales pre-expanded to packed fp16 pairs (d, d).  MN-major
-//    operands (the TN/NN layouts) are transposed on the way in with an 8x8
-//    nibble transpose in registers.
+//  * Codes and scale bytes (0.5625 B per element) are staged in LDS in a
+//    canonical K-major layout per 64-k stage: 32 code bytes per row (two
+//    16-byte halves, swapped on rows with bit 2 set to spread LDS banks) and
+//    4 raw scale bytes per row.  K-major operands go global -> LDS directly
+//    (4-byte LDS DMA, no registers); MN-major operands (the TN/NN layouts)
+//    go through registers and an 8x8 nibble transpose.
 //  * Each wave decodes only the fragments it multiplies: lane l reads 16 code
-//    bytes of row l%32 (k = 32*(l/32) .. +32 of the stage) and the two scale
-//    pairs, and for each of the four 16-k MFMA steps converts 8 nibbles with
-//    v_cvt_scalef32_pk_f16_fp4 (scale 1) and v_pk_mul_f16 by (d, d).  The k
-//    order inside an MFMA is a permutation shared by A and B, so the sum is
-//    unchanged.
+//    bytes of row l%32 (k = 32*(l/32) .. +32 of the stage) and the row's two
+//    scale bytes for those k, converts the scales to an fp16 pair with
+//    v_cvt_scalef32_pk_f16_fp8 and, for each 16-k MFMA step, 8 nibbles with
+//    v_cvt_scalef32_pk_f16_fp4 (both with scale 1: their scale operand only
+//    applies a power of two) and v_pk_mul_f16.  The k order inside an MFMA
+//    is a permutation shared by A and B, so the sum is unchanged.
 //  * Epilogue: C = RN32(acc * RN32(gA * gB)), stored as bf16 (RNE) or fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,19 +35,22 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
-constexpr int BK = 64;  // k per LDS stage
+constexpr int BK = 64;       // k per LDS stage
+constexpr int kStages = 4;   // LDS ring depth
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, bool FENCE_ = true>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr bool kFence = FENCE_;  // fence the MFMA/decode order with sched_barrier
   static constexpr int NT = WM * WN * 64;
+  static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM / 32;  // 32x32 MFMA tiles per wave along M
   static constexpr int TN = BN / WN / 32;
-  static constexpr int kACodes = BM * 32, kAScales = BM * 16;
-  static constexpr int kBCodes = BN * 32, kBScales = BN * 16;
+  static constexpr int kACodes = BM * 32, kAScales = BM * 4;
+  static constexpr int kBCodes = BN * 32, kBScales = BN * 4;
   static constexpr int kStage = kACodes + kAScales + kBCodes + kBScales;
+  static constexpr int kLds = kStages * kStage;
 };
 
 // Operand view for one tile: base pointers and the strides of its stored
@@ -57,32 +62,24 @@ struct OpView {
   int block;
 };
 
-__device__ __forceinline__ uint32_t bits_of(half2 h) { return __builtin_bit_cast(uint32_t, h); }
-
-// Every E4M3 byte -> its packed fp16 pair (d, d), for the 256-entry table each
-// workgroup keeps in LDS (exact: every E4M3 value is an fp16 value).
-__device__ __forceinline__ uint32_t e4m3_pair_f16(uint32_t e) {
-  _Float16 h = (_Float16)e4m3_decode(e & 0x7Fu);
-  half2 p = {h, h};
-  return bits_of(p);
+// Makes v look redefined here, so arithmetic on a prefetched value cannot be
+// hoisted up to its load (which would wait for the load right away).
+template <typename T>
+__device__ __forceinline__ void pin(T& v) {
+  asm volatile("" : "+v"(v));
 }
 
-__device__ __forceinline__ void build_scale_table(uint32_t* table, int tid, int nt) {
-  for (int i = tid; i < 256; i += nt) table[i] = e4m3_pair_f16((uint32_t)i);
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  // gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// 4 E4M3 scale bytes -> 4 packed fp16 pairs, through the LDS table.
-__device__ __forceinline__ uint4 expand_scales(uint32_t s4, const uint32_t* table) {
-  return make_uint4(table[s4 & 0xFFu], table[(s4 >> 8) & 0xFFu], table[(s4 >> 16) & 0xFFu],
-                    table[s4 >> 24]);
-}
-
-// Swizzled LDS addresses (bytes within one operand's region).
+// Swizzled byte address of half `half` (16 bytes) of code row `row`.
 __device__ __forceinline__ int code_addr(int row, int half) {
   return row * 32 + 16 * (half ^ ((row >> 2) & 1));
-}
-__device__ __forceinline__ int scale_addr(int row, int half) {
-  return row * 16 + 8 * (half ^ ((row >> 3) & 1));
 }
 
 // In-register transpose of an 8x8 matrix of nibbles: d[i] nibble j -> d[j]
@@ -109,80 +106,81 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t d[8]) {
   }
 }
 
-// ---- staging: global -> registers -> LDS ---------------------------------------------------
-// Loads are branch-free and unmasked: a row past the operand's edge re-reads
-// the last valid row (always in bounds).  Row i of A only reaches row i of C
-// and row j of B only column j, so such rows only feed outputs that are never
-// stored.  The main loop stays one basic block the scheduler can interleave,
-// and the prefetched values are not consumed until the stage is written out.
+// ---- staging: K-major operands by LDS DMA ----------------------------------------------------
+// buffer_load_dword{,x4} ... lds moves 4 or 16 bytes per lane into LDS at
+// (wave-uniform base + size * lane); the lane's source offset is chosen so
+// that the LDS image is the swizzled canonical layout.  A row past the
+// operand's edge re-reads the last valid row (always in bounds): row i of A
+// only reaches row i of C, row j of B only column j, so such rows only feed
+// outputs that are never stored.
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
 
-// K-major operand, ROWS rows of the tile, NT threads.
-template <int ROWS, int NT>
-struct StageK {
-  static_assert((ROWS * 2) % NT == 0 && ROWS % NT == 0, "tile rows must divide evenly");
-  static constexpr int CN = ROWS * 2 / NT;  // uint4 of codes per thread
-  static constexpr int SN = ROWS / NT;      // scale dwords per thread
-  u32x4 c[CN];
-  uint32_t s[SN];
+template <int ROWS, int NW, int SW0, int SWN>
+struct DmaK {
+  // Code chunks (1 KiB = 32 rows, 16 bytes per lane) spread over all NW
+  // waves; scale chunks (256 B = 64 rows, 4 bytes per lane) over waves
+  // [SW0, SW0 + SWN), one each.
+  static constexpr int kCodeChunks = ROWS * 32 / 1024;
+  static_assert(kCodeChunks % NW == 0, "code chunks must split over waves");
+  static_assert(ROWS * 4 / 256 == SWN, "one scale chunk per scale wave");
+  static constexpr int CPW = kCodeChunks / NW;
+  uint32_t coff[CPW];  // lane byte offsets from the tile's first code row
+  uint32_t soff;       // lane byte offset from the tile's first scale row
+  __amdgpu_buffer_rsrc_t crsrc, srsrc;
+  int wave;
 
-  __device__ __forceinline__ void load(const OpView& op, int64_t mn0, int64_t mn_lim,
-                                       int64_t k0, int64_t K, int tid) {
+  __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
+                                       int lane, int wv) {
+    wave = wv;
+    const int64_t kc = K / 2, ks = K / 16;
 #pragma unroll
-    for (int j = 0; j < CN; j++) {
-      int idx = tid + j * NT;
-      int64_t mn = mn0 + (idx >> 1);
-      int64_t mc = mn < mn_lim ? mn : mn_lim - 1;
-      c[j] = *reinterpret_cast<const u32x4*>(op.codes + mc * (K / 2) + k0 / 2 + 16 * (idx & 1));
+    for (int q = 0; q < CPW; q++) {
+      const int c = wave * CPW + q;
+      const int row = 32 * c + (lane >> 1);
+      const int h = (lane & 1) ^ ((row >> 2) & 1);
+      const int64_t mn = mn0 + row < mn_lim ? mn0 + row : mn_lim - 1;
+      coff[q] = (uint32_t)((mn - mn0) * kc + 16 * h);
     }
-#pragma unroll
-    for (int j = 0; j < SN; j++) {
-      int64_t mn = mn0 + tid + j * NT;
-      int64_t mc = mn < mn_lim ? mn : mn_lim - 1;
-      int64_t off = op.block == kBlock2d ? (mc / 16) * (K / 16) : mc * (K / 16);
-      s[j] = *reinterpret_cast<const uint32_t*>(op.scales + off + k0 / 16);
-    }
+    const bool two_d = op.block == kBlock2d;
+    const int srow = (wave - SW0) * 64 + lane;  // meaningful on scale waves only
+    const int64_t smn = mn0 + srow < mn_lim ? mn0 + srow : mn_lim - 1;
+    const int64_t sbase = two_d ? (mn0 / 16) * ks : mn0 * ks;
+    const int64_t slim = two_d ? ((mn_lim + 15) / 16) * ks : mn_lim * ks;
+    soff = (uint32_t)((two_d ? (smn / 16) * ks : smn * ks) - sbase);
+    crsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.codes + mn0 * kc), 0,
+                                              (int)((mn_lim - mn0) * kc), kBufferFlags);
+    srsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.scales + sbase), 0,
+                                              (int)(slim - sbase), kBufferFlags);
   }
 
-  __device__ __forceinline__ void store(uint8_t* lds_codes, uint8_t* lds_scales, int tid,
-                                        const uint32_t* table) const {
-    store_codes(lds_codes, tid);
-    store_scales(lds_scales, tid, table);
-  }
-
-  __device__ __forceinline__ void store_codes(uint8_t* lds_codes, int tid) const {
+  __device__ __forceinline__ void issue(int64_t k0, uint8_t* lds_codes, uint8_t* lds_scales) const {
 #pragma unroll
-    for (int j = 0; j < CN; j++) {
-      int idx = tid + j * NT;
-      *reinterpret_cast<u32x4*>(lds_codes + code_addr(idx >> 1, idx & 1)) = c[j];
-    }
-  }
-
-  __device__ __forceinline__ void store_scales(uint8_t* lds_scales, int tid,
-                                               const uint32_t* table) const {
-#pragma unroll
-    for (int j = 0; j < SN; j++) {
-      int idx = tid + j * NT;
-      uint4 e = expand_scales(s[j], table);
-      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 0)) = make_uint2(e.x, e.y);
-      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 1)) = make_uint2(e.z, e.w);
-    }
+    for (int q = 0; q < CPW; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, lds_codes + (wave * CPW + q) * 1024, 16,
+                                               coff[q], (int)(k0 / 2), 0, 0);
+    if (wave >= SW0 && wave < SW0 + SWN)  // wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, lds_scales + (wave - SW0) * 256, 4, soff,
+                                               (int)(k0 / 16), 0, 0);
   }
 };
 
-// MN-major operand: the stage is BK rows (k) x ROWS columns (mn).  A unit is
-// 8 k x 8 mn (8 dwords, one per k row), transposed to 8 dwords along k.
-template <int ROWS, int NT>
+// ---- staging: MN-major operands through registers ------------------------------------------
+// The stage is BK rows (k) x ROWS columns (mn).  A unit is 8 k x 8 mn (8
+// dwords, one per k row), transposed to 8 dwords along k.
+// Threads [T0, T0 + NT) take part (a wave-uniform predicate).
+template <int ROWS, int T0, int NT>
 struct StageMN {
   static constexpr int UNITS = (BK / 8) * (ROWS / 8);
   static_assert(UNITS % NT == 0 && ROWS % NT == 0, "tile must divide evenly");
   static constexpr int UN = UNITS / NT;
   static constexpr int SN = ROWS / NT;
   uint32_t c[UN][8];
-  uint32_t s[SN];
+  uint32_t s[SN][4];  // the four k-block scale bytes of each row, assembled at store time
 
   __device__ __forceinline__ void load(const OpView& op, int64_t mn0, int64_t mn_lim,
-                                       int64_t k0, int64_t K, int tid) {
-    (void)K;
+                                       int64_t k0, int tid_all) {
+    const int tid = tid_all - T0;
+    if (tid < 0 || tid >= NT) return;
     const int64_t W = op.mn_total;
 #pragma unroll
     for (int j = 0; j < UN; j++) {
@@ -199,28 +197,24 @@ struct StageMN {
     for (int j = 0; j < SN; j++) {
       int64_t mn = mn0 + tid + j * NT;
       int64_t mc = mn < mn_lim ? mn : mn_lim - 1;
-      uint32_t v = 0;
 #pragma unroll
       for (int kb = 0; kb < 4; kb++) {
         int64_t row = k0 / 16 + kb;
         int64_t off = op.block == kBlock2d ? row * (W / 16) + mc / 16 : row * W + mc;
-        v |= (uint32_t)op.scales[off] << (8 * kb);
+        s[j][kb] = op.scales[off];
       }
-      s[j] = v;
     }
   }
 
-  __device__ __forceinline__ void store(uint8_t* lds_codes, uint8_t* lds_scales, int tid,
-                                        const uint32_t* table) {
-    store_codes(lds_codes, tid);
-    store_scales(lds_scales, tid, table);
-  }
-
-  __device__ __forceinline__ void store_codes(uint8_t* lds_codes, int tid) {
+  __device__ __forceinline__ void store_codes(uint8_t* lds_codes, int tid_all) {
+    const int tid = tid_all - T0;
+    if (tid < 0 || tid >= NT) return;
 #pragma unroll
     for (int j = 0; j < UN; j++) {
       int u = tid + j * NT;
       int kg = u / (ROWS / 8), md = u % (ROWS / 8);
+#pragma unroll
+      for (int r = 0; r < 8; r++) pin(c[j][r]);
       transpose8x8_nibbles(c[j]);
 #pragma unroll
       for (int i = 0; i < 8; i++) {
@@ -231,32 +225,36 @@ struct StageMN {
     }
   }
 
-  __device__ __forceinline__ void store_scales(uint8_t* lds_scales, int tid,
-                                               const uint32_t* table) const {
+  __device__ __forceinline__ void store_scales(uint8_t* lds_scales, int tid_all) {
+    const int tid = tid_all - T0;
+    if (tid < 0 || tid >= NT) return;
 #pragma unroll
     for (int j = 0; j < SN; j++) {
-      int idx = tid + j * NT;
-      uint4 e = expand_scales(s[j], table);
-      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 0)) = make_uint2(e.x, e.y);
-      *reinterpret_cast<uint2*>(lds_scales + scale_addr(idx, 1)) = make_uint2(e.z, e.w);
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) pin(s[j][kb]);
+      *reinterpret_cast<uint32_t*>(lds_scales + 4 * (tid + j * NT)) =
+          s[j][0] | (s[j][1] << 8) | (s[j][2] << 16) | (s[j][3] << 24);
     }
   }
 };
 
-template <bool KMAJOR, int ROWS, int NT>
-using Stage = typename std::conditional<KMAJOR, StageK<ROWS, NT>, StageMN<ROWS, NT>>::type;
-
-// Decode 8 nibbles (one dword) scaled by the packed pair sc = (d, d).  The
-// conversion's own scale operand only applies a power of two, so it stays 1
-// and the E4M3 scale is a separate exact fp16 multiply.
-__device__ __forceinline__ half8 decode8(uint32_t q, uint32_t sc) {
-  half2 d = __builtin_bit_cast(half2, sc);
+// Decode 8 nibbles (one dword) scaled by the packed pair d = (d, d).
+__device__ __forceinline__ half8 decode8(uint32_t q, half2 d) {
   half2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * d;
   half2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1) * d;
   half2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2) * d;
   half2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3) * d;
   half8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
   return r;
+}
+
+// Two E4M3 scale bytes (low 16 bits) -> fp16 pair, exact.
+__device__ __forceinline__ half2 scale_pair(uint32_t two_bytes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_bytes, 1.0f, false);
+}
+
+__device__ __forceinline__ half2 splat(half2 d, int hi) {
+  return hi ? half2{d[1], d[1]} : half2{d[0], d[0]};
 }
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -268,15 +266,85 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int s) {
   return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
 
+// Decode schedule within a 16-k step of TM x TN MFMAs (t = i*TN + j): B
+// fragment j (double-buffered) is decoded after MFMA `b_slot`, A fragment i
+// (single-buffered) once row i's MFMAs have issued.  In the last step the
+// fragments come from LDS reads issued at the step's start, so decodes wait
+// for two MFMAs first.
+template <int TM, int TN>
+__device__ __forceinline__ constexpr int b_slot(int s, int j) {
+  return s < 3 ? j : (2 + j < TM * TN ? 2 + j : TM * TN - 1);
+}
+template <int TM, int TN>
+__device__ __forceinline__ constexpr int a_slot(int s, int i) {
+  return s < 3 || i * TN + TN - 1 >= 2 ? i * TN + TN - 1 : 2;
+}
+
+// Per-operand staging: DMA for K-major, registers for MN-major.  OPB
+// selects operand B's share of waves/threads (A uses the first half of the
+// scale waves and MN threads, B the second).
+template <bool KMAJOR, int ROWS, class C, int OPB>
+struct Staging;
+
+template <int ROWS, class C, int OPB>
+struct Staging<true, ROWS, C, OPB> {
+  static constexpr int kSW = ROWS * 4 / 256;  // scale waves
+  static_assert(kSW <= C::NW, "one scale chunk per wave at most");
+  // Both operands' scale chunks on disjoint waves when there are enough
+  // waves, else on the same ones.
+  static constexpr int kSW0 = (2 * kSW <= C::NW) ? OPB * kSW : 0;
+  DmaK<ROWS, C::NW, kSW0, kSW> d;
+  static constexpr int kCodeDma = DmaK<ROWS, C::NW, kSW0, kSW>::CPW;
+  __device__ __forceinline__ int scale_dma(int wave) const {
+    return wave >= kSW0 && wave < kSW0 + kSW ? 1 : 0;
+  }
+  __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
+                                       int tid) {
+    d.init(op, mn0, mn_lim, K, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6));
+  }
+  __device__ __forceinline__ void load_regs(const OpView&, int64_t, int64_t, int64_t, int) {}
+  __device__ __forceinline__ void load_dma(int64_t k0, uint8_t* codes, uint8_t* scales) {
+    d.issue(k0, codes, scales);
+  }
+  __device__ __forceinline__ void store_codes(uint8_t*, int) {}
+  __device__ __forceinline__ void store_scales(uint8_t*, int) {}
+};
+
+template <int ROWS, class C, int OPB>
+struct Staging<false, ROWS, C, OPB> {
+  static constexpr int kThreads = C::NT >= 2 * ROWS ? ROWS : C::NT;
+  static constexpr int kT0 = C::NT >= 2 * ROWS ? OPB * ROWS : 0;
+  StageMN<ROWS, kT0, kThreads> r;
+  static constexpr int kCodeDma = 0;
+  __device__ __forceinline__ int scale_dma(int) const { return 0; }
+  __device__ __forceinline__ void init(const OpView&, int64_t, int64_t, int64_t, int) {}
+  __device__ __forceinline__ void load_regs(const OpView& op, int64_t mn0, int64_t mn_lim,
+                                            int64_t k0, int tid) {
+    r.load(op, mn0, mn_lim, k0, tid);
+  }
+  __device__ __forceinline__ void load_dma(int64_t, uint8_t*, uint8_t*) {}
+  __device__ __forceinline__ void store_codes(uint8_t* codes, int tid) { r.store_codes(codes, tid); }
+  __device__ __forceinline__ void store_scales(uint8_t* scales, int tid) {
+    r.store_scales(scales, tid);
+  }
+};
+
 // One output tile: C[m0 : m0+BM) x [n0 : n0+BN) restricted to rows < m_lim,
-// cols < N.  lds holds 2 stages and then the 256-entry scale table, which
-// the caller has built (and synchronized) before the first tile.
+// cols < N, using lds (kLds bytes).
 //
-// Per 64-k stage each wave: loads the next stage from global memory (held in
-// registers), reads its fragments' codes and scales from LDS, decodes the
-// first 16-k step, then runs the four steps' MFMAs while decoding the next
-// step between them, and writes the next stage to the other LDS buffer
-// during the last step.
+// Software pipeline over 64-k stages (stage s lives in LDS buffer s % 4):
+//  * iteration kt starts stage kt+3's transfer: register loads for MN-major
+//    operands at its start (written to LDS during steps 2 and 3), DMA for
+//    K-major ones during its last step;
+//  * its four 16-k steps run TM x TN MFMAs each; between MFMAs it decodes
+//    the fragments of the following step -- for the last step, those of step
+//    0 of stage kt+1, read from LDS at that step's start;
+//  * it ends with one barrier, after waiting for this wave's transfers of
+//    stage kt+2 (issued an iteration ago): stage kt+2 is read in the next
+//    iteration, and the buffer stage kt+3 overwrites (stage kt-1's) was last
+//    read two iterations ago.
+// Decoded fragments: B double-buffered (every row uses them), A single-
+// buffered, fragment i of the next step decoded once row i's MFMAs issued.
 template <class C, bool AK, bool BKM>
 __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int64_t m0,
                                           int64_t m_lim, int64_t n0, int64_t N, int64_t K,
@@ -295,67 +363,95 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  Stage<AK, C::BM, C::NT> sa;
-  Stage<BKM, C::BN, C::NT> sb;
+  Staging<AK, C::BM, C, 0> sa;
+  Staging<BKM, C::BN, C, 1> sb;
+  sa.init(A, m0, m_lim, K, tid);
+  sb.init(B, n0, N, K, tid);
+  // DMA instructions this wave issues per stage (wave-uniform): the code
+  // chunks plus one scale chunk per operand whose scales this wave moves.
+  constexpr int kCodeDma = Staging<AK, C::BM, C, 0>::kCodeDma + Staging<BKM, C::BN, C, 1>::kCodeDma;
+  const int n_scale_dma = sa.scale_dma(wave) + sb.scale_dma(wave);
   const int64_t KT = K / BK;
-  const uint32_t* table = reinterpret_cast<const uint32_t*>(lds + 2 * C::kStage);
 
-  // Fragment rows of one wave step by 32, which keeps both swizzles (they
-  // depend on row bits 2 and 3), so each operand needs one base address.
+  constexpr int oAS = C::kACodes, oBC = C::kACodes + C::kAScales,
+                oBS = C::kACodes + C::kAScales + C::kBCodes;
+  // Fragment rows of one wave step by 32, which keeps the code swizzle (it
+  // depends on row bit 2), so each operand needs one base address.
   const int a_row0 = wm * (C::BM / C::WM) + lrow, b_row0 = wn * (C::BN / C::WN) + lrow;
-  const int a_code0 = code_addr(a_row0, lhalf);
-  const int a_sc0 = C::kACodes + scale_addr(a_row0, lhalf);
-  const int b_code0 = C::kACodes + C::kAScales + code_addr(b_row0, lhalf);
-  const int b_sc0 = C::kACodes + C::kAScales + C::kBCodes + scale_addr(b_row0, lhalf);
+  const int a_code0 = code_addr(a_row0, lhalf), b_code0 = oBC + code_addr(b_row0, lhalf);
+  const int a_sc0 = oAS + 4 * a_row0 + 2 * lhalf, b_sc0 = oBS + 4 * b_row0 + 2 * lhalf;
 
-  sa.load(A, m0, m_lim, 0, K, tid);
-  sb.load(B, n0, N, 0, K, tid);
-  sa.store(lds, lds + C::kACodes, tid, table);
-  sb.store(lds + C::kACodes + C::kAScales, lds + C::kACodes + C::kAScales + C::kBCodes, tid,
-           table);
-  __syncthreads();
+  auto buffer = [&](int idx) { return lds + idx * C::kStage; };
+  auto load_regs = [&](int64_t k0) {
+    sa.load_regs(A, m0, m_lim, k0, tid);
+    sb.load_regs(B, n0, N, k0, tid);
+  };
+  auto load_dma = [&](int64_t k0, uint8_t* dst) {
+    sa.load_dma(k0, dst, dst + oAS);
+    sb.load_dma(k0, dst + oBC, dst + oBS);
+  };
 
-  for (int64_t kt = 0; kt < KT; kt++) {
-    const int buf = (int)(kt & 1);
-    // Next stage (the last iteration reloads the final stage into the idle
-    // buffer, which keeps the loop free of branches).
-    const int64_t kn = (kt + 1 < KT ? kt + 1 : kt) * BK;
-    sa.load(A, m0, m_lim, kn, K, tid);
-    sb.load(B, n0, N, kn, K, tid);
-
-    const uint8_t* st = lds + buf * C::kStage;
-    uint4 aq[C::TM], bq[C::TN];
-    uint2 as[C::TM], bs[C::TN];
+  uint4 aq[C::TM], bq[C::TN];
+  half2 as[C::TM], bs[C::TN];
+  auto read_frags = [&](const uint8_t* st) {
+    uint32_t ar[C::TM], br[C::TN];
 #pragma unroll
     for (int i = 0; i < C::TM; i++) {
       aq[i] = *reinterpret_cast<const uint4*>(st + a_code0 + i * 32 * 32);
-      as[i] = *reinterpret_cast<const uint2*>(st + a_sc0 + i * 32 * 16);
+      ar[i] = *reinterpret_cast<const uint16_t*>(st + a_sc0 + i * 32 * 4);
     }
 #pragma unroll
     for (int j = 0; j < C::TN; j++) {
       bq[j] = *reinterpret_cast<const uint4*>(st + b_code0 + j * 32 * 32);
-      bs[j] = *reinterpret_cast<const uint2*>(st + b_sc0 + j * 32 * 16);
+      br[j] = *reinterpret_cast<const uint16_t*>(st + b_sc0 + j * 32 * 4);
     }
+#pragma unroll
+    for (int i = 0; i < C::TM; i++) as[i] = scale_pair(ar[i]);
+#pragma unroll
+    for (int j = 0; j < C::TN; j++) bs[j] = scale_pair(br[j]);
+  };
 
-    // A fragments are single-buffered: fragment i of the next step is decoded
-    // once row i's MFMAs of this step have issued.  B fragments, used by every
-    // row, are double-buffered.
-    half8 af[C::TM], bf[2][C::TN];
+  // Prologue: stages 0, 1 and 2 in LDS, step 0 of stage 0 decoded.
+  auto stage_k = [&](int64_t st) { return (st < KT ? st : KT - 1) * BK; };
 #pragma unroll
-    for (int i = 0; i < C::TM; i++) af[i] = decode8(aq[i].x, as[i].x);
+  for (int st = 0; st < kStages - 1; st++) {
+    load_regs(stage_k(st));
+    load_dma(stage_k(st), buffer(st));
+    sa.store_codes(buffer(st), tid);
+    sa.store_scales(buffer(st) + oAS, tid);
+    sb.store_codes(buffer(st) + oBC, tid);
+    sb.store_scales(buffer(st) + oBS, tid);
+  }
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(buffer(0));
+  half8 af[C::TM], bf[2][C::TN];
 #pragma unroll
-    for (int j = 0; j < C::TN; j++) bf[0][j] = decode8(bq[j].x, bs[j].x);
+  for (int i = 0; i < C::TM; i++) af[i] = decode8(aq[i].x, splat(as[i], 0));
+#pragma unroll
+  for (int j = 0; j < C::TN; j++) bf[0][j] = decode8(bq[j].x, splat(bs[j], 0));
+  int b_next = 1, b_load = kStages - 1;  // buffers of stages kt+1 and kt+3
 
-    // Steps 0..3 of the stage.  The order is fixed in the source and fenced
-    // with sched_barrier: after every second MFMA one fragment of the next
-    // step is decoded (8 VALU ops that issue while the MFMAs run) -- first the
-    // B fragments, then A fragment f once row f is done; during the last step
-    // the next stage is written to the other LDS buffer instead.
-    uint8_t* sn = lds + (buf ^ 1) * C::kStage;
-    static_assert(C::TM == 4 && C::TN == 4, "interleave expects 4x4 MFMA tiles per wave");
+  for (int64_t kt = 0; kt < KT; kt++) {
+    // Stage kt+3 (clamped: near the end the last stage is reloaded into an
+    // idle buffer, which keeps the loop free of branches).
+    const int64_t kl = stage_k(kt + kStages - 1);
+    uint8_t* dst = buffer(b_load);
+    load_regs(kl);
+
 #pragma unroll
-    for (int s = 0; s < 3; s++) {
+    for (int s = 0; s < 4; s++) {
       const int cur = s & 1, nxt = cur ^ 1;
+      // Step s+1 of this stage, or step 0 of the next stage (read now).
+      const int ns = s < 3 ? s + 1 : 0;
+      if (s == 3) {
+        // The compiler may make these LDS reads wait for every outstanding
+        // LDS DMA; issuing stage kt+3's DMA only after them keeps that wait
+        // to transfers issued an iteration ago or earlier.
+        read_frags(buffer(b_next));
+        load_dma(kl, dst);
+        if (C::kFence) __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < C::TM; i++) {
 #pragma unroll
@@ -363,41 +459,47 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
           acc[i][j] =
               __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[cur][j], acc[i][j], 0, 0, 0);
           const int t = i * C::TN + j;
-          if (t & 1) {
-            const int f = t >> 1;  // 0..3: B fragment f; 4..7: A fragment f-4
-            if (f < C::TN)
-              bf[nxt][f] = decode8(pick(bq[f], s + 1), s + 1 < 2 ? bs[f].x : bs[f].y);
-            else
-              af[f - C::TN] = decode8(pick(aq[f - C::TN], s + 1),
-                                      s + 1 < 2 ? as[f - C::TN].x : as[f - C::TN].y);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          bool any = false;
+#pragma unroll
+          for (int jj = 0; jj < C::TN; jj++)
+            if (b_slot<C::TM, C::TN>(s, jj) == t) {
+              bf[nxt][jj] = decode8(pick(bq[jj], ns), splat(bs[jj], ns >= 2));
+              any = true;
+            }
+#pragma unroll
+          for (int ii = 0; ii < C::TM; ii++)
+            if (a_slot<C::TM, C::TN>(s, ii) == t) {
+              af[ii] = decode8(pick(aq[ii], ns), splat(as[ii], ns >= 2));
+              any = true;
+            }
+          // MN-major operands write stage kt+2 to LDS during steps 2 and 3.
+          constexpr int kLast = C::TM * C::TN - 1;
+          const bool st = (s == 2 && (t == kLast / 2 || t == kLast)) ||
+                          (s == 3 && (t == kLast / 4 || t == (3 * kLast) / 4));
+          if (s == 2 && t == kLast / 2) sa.store_codes(dst, tid);
+          if (s == 2 && t == kLast) sa.store_scales(dst + oAS, tid);
+          if (s == 3 && t == kLast / 4) sb.store_codes(dst + oBC, tid);
+          if (s == 3 && t == (3 * kLast) / 4) sb.store_scales(dst + oBS, tid);
+          if (C::kFence && (any || (st && (!AK || !BKM)))) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    // Step 3 (uses bf[1]): one row of MFMAs, then a quarter of the next
-    // stage's LDS writes.
-#pragma unroll
-    for (int j = 0; j < C::TN; j++)
-      acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0], bf[1][j], acc[0][j], 0, 0, 0);
-    sa.store_codes(sn, tid);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < C::TN; j++)
-      acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1], bf[1][j], acc[1][j], 0, 0, 0);
-    sa.store_scales(sn + C::kACodes, tid, table);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < C::TN; j++)
-      acc[2][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[2], bf[1][j], acc[2][j], 0, 0, 0);
-    sb.store_codes(sn + C::kACodes + C::kAScales, tid);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < C::TN; j++)
-      acc[3][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[3], bf[1][j], acc[3][j], 0, 0, 0);
-    sb.store_scales(sn + C::kACodes + C::kAScales + C::kBCodes, tid, table);
-    __syncthreads();
+    b_next = b_next == kStages - 1 ? 0 : b_next + 1;
+    b_load = b_load == kStages - 1 ? 0 : b_load + 1;
+    // Stage kt+2, read in the next iteration, complete: this wave's DMA for
+    // it was issued an iteration ago, so only this iteration's transfers may
+    // still be in flight; then every wave's (barrier).
+    if (n_scale_dma == 0)
+      wait_vm_lgkm0<kCodeDma>();
+    else if (n_scale_dma == 1)
+      wait_vm_lgkm0<kCodeDma + 1>();
+    else
+      wait_vm_lgkm0<kCodeDma + 2>();
+    __builtin_amdgcn_s_barrier();
   }
+  // No transfer may still target this workgroup's LDS when it is reused.
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
 
   // Epilogue.  32x32 accumulator layout: lane l holds column l%32 and rows
   // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
@@ -444,8 +546,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   OpView A{a.A.codes, a.A.scales, a.M, a.A.block};
   OpView B{a.B.codes, a.B.scales, a.N, a.B.block};
   const float gs = *a.A.gdec * *a.B.gdec;
-  build_scale_table(reinterpret_cast<uint32_t*>(lds + 2 * C::kStage), threadIdx.x, C::NT);
-  __syncthreads();
   gemm_tile<C, AK, BKM>(A, B, tm * C::BM, a.M, tn * C::BN, a.N, a.K, gs, a.C, a.c_bf16, a.N, lds);
 }
 
@@ -454,8 +554,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 template <class C>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  build_scale_table(reinterpret_cast<uint32_t*>(lds + 2 * C::kStage), threadIdx.x, C::NT);
-  int32_t* prefix = reinterpret_cast<int32_t*>(lds + 2 * C::kStage + 1024);  // [groups + 1]
+  int32_t* prefix = reinterpret_cast<int32_t*>(lds + C::kLds);  // [groups + 1]
   __shared__ int32_t part[C::NT];
   const int tid = threadIdx.x;
   const int64_t G = a.groups;
@@ -514,13 +613,13 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   }
 }
 
-using Dense = Cfg<256, 256, 2, 2>;
-using Grouped = Cfg<256, 256, 2, 2>;
+using Dense = Cfg<256, 256, 2, 4, false>;
+using Grouped = Cfg<256, 256, 2, 4, false>;
 
 template <class C, bool AK, bool BKM>
 hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
-  const size_t smem = 2 * C::kStage + 1024;
+  const size_t smem = C::kLds;
   auto kern = gemm_kernel<C, AK, BKM>;
   if (smem > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -552,7 +651,7 @@ hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st) {
   const int64_t max_tiles = ((a.total_rows + C::BM - 1) / C::BM + a.groups) * ntn;
   int64_t grid = cus > 0 ? cus : 256;
   if (grid > max_tiles) grid = max_tiles;
-  const size_t smem = 2 * C::kStage + 1024 + sizeof(int32_t) * (size_t)(a.groups + 1);
+  const size_t smem = C::kLds + sizeof(int32_t) * (size_t)(a.groups + 1);
   auto kern = grouped_gemm_kernel<C>;
   if (smem > 65536) {
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,

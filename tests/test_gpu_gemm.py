@@ -182,8 +182,17 @@ def test_full_ultra_dgrad():
     _sampled_check("NN", qa, qb, M, N, K, c)
 
 
-def test_gemm_deterministic():
-    qa, qb = _operands("NT", 512, 512, 512, seed=5)
-    c1 = nv.gemm("N", "T", qa, qb, out_dtype=torch.float32)
-    c2 = nv.gemm("N", "T", qa, qb, out_dtype=torch.float32)
-    assert torch.equal(c1, c2)
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_gemm_deterministic_long_k(layout):
+    """Repeated runs with many pipeline stages give identical bits (a race
+    between the LDS stage buffers would show up as run-to-run differences),
+    and bf16 output stays the RNE rounding of the fp32 result."""
+    M, N, K = 1024, 768, 8192
+    qa, qb = _operands(layout, M, N, K, seed=5, sr=layout != "NT",
+                       mask=0x1111 if layout == "TN" else -1)
+    c1 = nv.gemm(layout[0], layout[1], qa, qb, out_dtype=torch.float32)
+    for _ in range(4):
+        c2 = nv.gemm(layout[0], layout[1], qa, qb, out_dtype=torch.float32)
+        assert torch.equal(c1, c2)
+        check_bf16_is_rne_of_fp32(nv.gemm(layout[0], layout[1], qa, qb,
+                                          out_dtype=torch.bfloat16), c1)
