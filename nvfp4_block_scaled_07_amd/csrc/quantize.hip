@@ -4,9 +4,9 @@
 // Work mapping (wave64):
 //  * ROW blocks (1x16 along the contiguous dim): the tensor is a flat stream
 //    of 16-element blocks.  Each lane owns 8 consecutive elements (one 16-byte
-//    bf16 load), so lanes 2t and 2t+1 share a block: its max takes one
-//    xor-1 shuffle, the 16-point transform's stride-8 stage one exchange of
-//    8 values.  A lane stores one dword of codes; even lanes store the scale.
+//    bf16 load), so lanes 2t and 2t+1 share a block: its max takes one DPP
+//    exchange, the 16-point transform's stride-8 stage one exchange of 8
+//    values.  A lane stores one dword of codes; even lanes store the scale.
 //  * COL blocks (16x1 along rows) and 2D blocks (16x16): each lane owns 8
 //    columns x 16 rows, loading one 16-byte row segment per row, so each load
 //    instruction reads 1 KiB of a row contiguously across the wave.  COL
@@ -14,7 +14,19 @@
 //  * The per-tensor amax runs first: a fill kernel zeroes it (no memset, so
 //    the sequence can be captured in a graph), then every workgroup does one
 //    atomicMax on the fp32 bits (non-negative floats order like integers, so
-//    the result does not depend on the order).
+//    the result does not depend on the order).  For bf16 input the max of
+//    |x| is taken on the 15 magnitude bits with packed 16-bit integer max.
+//
+// Arithmetic of the encoders (identical results to the element-wise
+// definitions in nvfp4_device.hpp, which the oracle also follows):
+//  * E2M1 round-to-nearest-even: v_cvt_scalef32_pk_fp4_f32 with scale 1,
+//    which rounds every finite fp32 input exactly like the nearest-even
+//    definition (ties to the even code, saturation at 6, signed zero);
+//  * E4M3 block scale: v_cvt_scalef32_pk_fp8_f32 with scale 1 on
+//    min(s, 448): the instruction rounds to nearest even but gives NaN
+//    instead of saturating above 464, which the clamp removes;
+//  * block reciprocal RN32(S / d) for all 127 E4M3 values d, computed once
+//    per workgroup into an LDS table by IEEE division, then looked up.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,12 +38,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef short short2v __attribute__((ext_vector_type(2)));
+
 // ---- loads ---------------------------------------------------------------------------
 template <typename T>
 struct In;
 
 template <>
 struct In<uint16_t> {  // bf16 bits
+  static constexpr bool kBf16 = true;
   static __device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
     uint4 q = *reinterpret_cast<const uint4*>(p);
     uint32_t w[4] = {q.x, q.y, q.z, q.w};
@@ -41,10 +56,14 @@ struct In<uint16_t> {  // bf16 bits
       v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
   }
+  static __device__ __forceinline__ uint4 raw(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
 };
 
 template <>
 struct In<float> {
+  static constexpr bool kBf16 = false;
   static __device__ __forceinline__ void load8(const float* p, float v[8]) {
     float4 a = *reinterpret_cast<const float4*>(p);
     float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -60,16 +79,73 @@ __device__ __forceinline__ float max8(const float v[8]) {
   return m;
 }
 
+// Max of |x| over 8 bf16 values given as 4 raw dwords, exact: non-negative
+// bf16 bit patterns order like integers.
+__device__ __forceinline__ float max8_bf16_bits(uint4 q) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 a = __builtin_bit_cast(u16x2, q.x & 0x7FFF7FFFu);
+  u16x2 b = __builtin_bit_cast(u16x2, q.y & 0x7FFF7FFFu);
+  u16x2 c = __builtin_bit_cast(u16x2, q.z & 0x7FFF7FFFu);
+  u16x2 d = __builtin_bit_cast(u16x2, q.w & 0x7FFF7FFFu);
+  u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                      __builtin_elementwise_max(c, d));
+  uint32_t hi = m[0] > m[1] ? m[0] : m[1];
+  return __uint_as_float(hi << 16);
+}
+
+// Value of the partner lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ float xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+
 // Stride-8 butterfly across the lane pair (2t holds positions 0..7, 2t+1
 // positions 8..15), then the exact * 1/4.
 __device__ __forceinline__ void rht_pair_stage8(float v[8], int odd) {
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    float other = __shfl_xor(v[i], 1);
+    float other = xor1(v[i]);
     float lo = odd ? other : v[i];
     float hi = odd ? v[i] : other;
     v[i] = (odd ? (lo - hi) : (lo + hi)) * 0.25f;
   }
+}
+
+// ---- block scale and reciprocal ---------------------------------------------------------
+// LDS table of r = RN32(S / value(e)) (0 for e = 0, FLT_MAX on overflow) for
+// the E4M3 codes e = 0..127; entry 127 (NaN code) is never looked up.
+__device__ __forceinline__ void build_recip_table(float* tab, float S) {
+  for (int e = threadIdx.x; e < 128; e += blockDim.x)
+    tab[e] = block_recip(S, e4m3_decode((uint32_t)e));
+  __syncthreads();
+}
+
+// E4M3 code of the block scale s = RN32(a * k): hardware RNE on min(s, 448).
+__device__ __forceinline__ uint32_t block_code(float a, float k) {
+  float s = fminf(a * k, 448.0f);
+  short2v z = {0, 0};
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, s, s, 1.0f, false)) &
+         0xFFu;
+}
+
+// Two values -> two RNE codes in byte `sel` of `old` (sel folds to a
+// constant once the caller's loop is unrolled).
+__device__ __forceinline__ uint32_t cvt_fp4_byte(uint32_t old, float a, float b, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
+  }
+}
+
+// 8 values (already multiplied by the block reciprocal) -> 8 RNE codes.
+__device__ __forceinline__ uint32_t pack8_rne(const float y[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
 }
 
 // ---- workgroup max -> atomicMax ---------------------------------------------------------
@@ -83,7 +159,12 @@ __device__ __forceinline__ void block_max_to(float m, float* out) {
   if (threadIdx.x == 0) {
     float r = red[0];
     for (int i = 1; i < kThreads / 64; i++) r = fmaxf(r, red[i]);
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(r));
+    // Thousands of workgroups target one address: skip the atomic when the
+    // value already there is at least ours (it only grows, and the max of the
+    // atomics performed is the same), which removes most of the contention.
+    unsigned int* p = reinterpret_cast<unsigned int*>(out);
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < __float_as_uint(r))
+      atomicMax(p, __float_as_uint(r));
   }
 }
 
@@ -93,7 +174,10 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 }
 
 // ---- amax over flat 8-element chunks (ROW blocks, or no transform) -----------------------
-// chunks: number of 8-element chunks per slice; slice = blockIdx.y.
+// chunks: number of 8-element chunks per slice; slice = blockIdx.y.  Each
+// thread keeps kUnroll loads in flight per trip.
+constexpr int kAmaxUnroll = 4;
+
 template <typename T, bool kRHT>
 __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T* __restrict__ x,
                                                              int64_t chunks, uint32_t mask,
@@ -101,14 +185,28 @@ __global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T* __restrict
   const T* xs = x + (int64_t)blockIdx.y * chunks * 8;
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks; i += stride) {
-    float v[8];
-    In<T>::load8(xs + i * 8, v);
-    if (kRHT) {
-      rht_signs_and_low_stages(v, mask, (int)(i & 1) * 8);
-      rht_pair_stage8(v, (int)(i & 1));
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (In<T>::kBf16 && !kRHT) {
+    for (; i + (kAmaxUnroll - 1) * stride < chunks; i += kAmaxUnroll * stride) {
+      uint4 q[kAmaxUnroll];
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; u++)
+        q[u] = *reinterpret_cast<const uint4*>(xs + (i + u * stride) * 8);
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; u++) m = fmaxf(m, max8_bf16_bits(q[u]));
     }
-    m = fmaxf(m, max8(v));
+    for (; i < chunks; i += stride)
+      m = fmaxf(m, max8_bf16_bits(*reinterpret_cast<const uint4*>(xs + i * 8)));
+  } else {
+    for (; i < chunks; i += stride) {
+      float v[8];
+      In<T>::load8(xs + i * 8, v);
+      if (kRHT) {
+        rht_signs_and_low_stages(v, mask, (int)(i & 1) * 8);
+        rht_pair_stage8(v, (int)(i & 1));
+      }
+      m = fmaxf(m, max8(v));
+    }
   }
   block_max_to(m, amax + blockIdx.y);
 }
@@ -144,42 +242,55 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
 // ---- ROW quantizer ---------------------------------------------------------------------------
 // Lane chunk i (8 elements) belongs to block i >> 1; with stochastic rounding
 // its Philox counter is 2 * block + (i & 1) = i.
+constexpr int kRowUnroll = 4;
+
 template <typename T, bool kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(
     const T* __restrict__ x, int64_t chunks, const float* __restrict__ amax,
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
     uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
+  __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
-  constexpr int kUnroll = 4;
-  const int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
-  float v[kUnroll][8];
+  const int64_t base = (int64_t)blockIdx.x * kThreads * kRowUnroll + threadIdx.x;
+  // Loads first (kRowUnroll 16-byte loads in flight), then the table.
+  float v[kRowUnroll][8];
+  float bm[kRowUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; u++) {
+  for (int u = 0; u < kRowUnroll; u++) {
     int64_t i = base + (int64_t)u * kThreads;
-    if (i < chunks) In<T>::load8(x + i * 8, v[u]);
+    int64_t ic = i < chunks ? i : chunks - 1;  // chunks is even: pairs agree
+    In<T>::load8(x + ic * 8, v[u]);
   }
+  build_recip_table(rtab, ts.S);
 #pragma unroll
-  for (int u = 0; u < kUnroll; u++) {
+  for (int u = 0; u < kRowUnroll; u++) {
     int64_t i = base + (int64_t)u * kThreads;
-    if (i >= chunks) continue;  // chunks is even: both lanes of a pair agree
     const int odd = (int)(i & 1);
     if (kRHT) {
       rht_signs_and_low_stages(v[u], mask, odd * 8);
       rht_pair_stage8(v[u], odd);
     }
-    float bm = max8(v[u]);
-    bm = fmaxf(bm, __shfl_xor(bm, 1));
-    uint32_t e = e4m3_encode(bm * ts.k);
-    float r = block_recip(ts.S, e4m3_decode(e));
+    float m = max8(v[u]);
+    bm[u] = fmaxf(m, xor1(m));
+  }
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; u++) {
+    int64_t i = base + (int64_t)u * kThreads;
+    if (i >= chunks) continue;  // chunks is even: both lanes of a pair agree
+    const int odd = (int)(i & 1);
+    uint32_t e = block_code(bm[u], ts.k);
+    float r = rtab[e];
+    float y[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) y[t] = v[u][t] * r;
     uint32_t packed = 0;
     if (kSR) {
       Philox4 p = sr_call((uint64_t)i, seed, offset, rounds);
 #pragma unroll
-      for (int t = 0; t < 8; t++) packed |= e2m1_sr(v[u][t] * r, sr_slot(p, t)) << (4 * t);
+      for (int t = 0; t < 8; t++) packed |= e2m1_sr(y[t], sr_slot(p, t)) << (4 * t);
     } else {
-#pragma unroll
-      for (int t = 0; t < 8; t++) packed |= e2m1_rne(v[u][t] * r) << (4 * t);
+      packed = pack8_rne(y);
     }
     codes[i] = packed;
     if (!odd) scales[i >> 1] = (uint8_t)e;
@@ -192,43 +303,60 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
     uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
+  __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
   const int64_t cg = cols / 8;
+  const int64_t units = (rows / 16) * cg;
   const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (u >= (rows / 16) * cg) return;
-  const int64_t g = u / cg, c0 = (u % cg) * 8;
+  const int64_t uc = u < units ? u : units - 1;
+  const int64_t g = uc / cg, c0 = (uc % cg) * 8;
   float v[16][8];
 #pragma unroll
   for (int r = 0; r < 16; r++) In<T>::load8(x + (g * 16 + r) * cols + c0, v[r]);
+  build_recip_table(rtab, ts.S);
+  if (u >= units) return;
   uint32_t out[16];
 #pragma unroll
   for (int r = 0; r < 16; r++) out[r] = 0;
   uint32_t sc[2] = {0, 0};
 #pragma unroll
-  for (int c = 0; c < 8; c++) {
-    float col[16];
+  for (int cp = 0; cp < 4; cp++) {  // column pairs (c, c+1) share one code byte per row
+    float col[2][16];
+    uint32_t e[2];
+    float rcp[2];
 #pragma unroll
-    for (int r = 0; r < 16; r++) col[r] = v[r][c];
-    if (kRHT) rht16_inreg(col, mask);
-    float bm = 0.0f;
+    for (int h = 0; h < 2; h++) {
+      const int c = 2 * cp + h;
 #pragma unroll
-    for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[r]));
-    uint32_t e = e4m3_encode(bm * ts.k);
-    float rcp = block_recip(ts.S, e4m3_decode(e));
-    sc[c >> 2] |= e << (8 * (c & 3));
+      for (int r = 0; r < 16; r++) col[h][r] = v[r][c];
+      if (kRHT) rht16_inreg(col[h], mask);
+      float bm = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[h][r]));
+      e[h] = block_code(bm, ts.k);
+      rcp[h] = rtab[e[h]];
+      sc[c >> 2] |= e[h] << (8 * (c & 3));
+#pragma unroll
+      for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp[h];
+    }
     if (kSR) {
-      const uint64_t blk = (uint64_t)(c0 + c) * (uint64_t)(rows / 16) + (uint64_t)g;
-      Philox4 p0 = sr_call(2 * blk, seed, offset, rounds);
-      Philox4 p1 = sr_call(2 * blk + 1, seed, offset, rounds);
 #pragma unroll
-      for (int r = 0; r < 8; r++) out[r] |= e2m1_sr(col[r] * rcp, sr_slot(p0, r)) << (4 * c);
+      for (int h = 0; h < 2; h++) {
+        const int c = 2 * cp + h;
+        const uint64_t blk = (uint64_t)(c0 + c) * (uint64_t)(rows / 16) + (uint64_t)g;
+        Philox4 p0 = sr_call(2 * blk, seed, offset, rounds);
+        Philox4 p1 = sr_call(2 * blk + 1, seed, offset, rounds);
 #pragma unroll
-      for (int r = 0; r < 8; r++)
-        out[r + 8] |= e2m1_sr(col[r + 8] * rcp, sr_slot(p1, r)) << (4 * c);
+        for (int r = 0; r < 8; r++) out[r] |= e2m1_sr(col[h][r], sr_slot(p0, r)) << (4 * c);
+#pragma unroll
+        for (int r = 0; r < 8; r++)
+          out[r + 8] |= e2m1_sr(col[h][r + 8], sr_slot(p1, r)) << (4 * c);
+      }
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; r++) out[r] |= e2m1_rne(col[r] * rcp) << (4 * c);
+      for (int r = 0; r < 16; r++)
+        out[r] = cvt_fp4_byte(out[r], col[0][r], col[1][r], cp);
     }
   }
 #pragma unroll
@@ -244,6 +372,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
     const T* __restrict__ w, int64_t rows, int64_t cols, const float* __restrict__ amax,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec) {
+  __shared__ float rtab[128];
   const int64_t slice = blockIdx.y;
   const TensorScales ts = tensor_scales(amax[slice]);
   if (blockIdx.x == 0 && threadIdx.x == 0) gdec[slice] = ts.g;
@@ -251,30 +380,30 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
   uint8_t* cs = codes + slice * rows * (cols / 2);
   uint8_t* ss = scales + slice * (rows / 16) * (cols / 16);
   const int64_t cg = cols / 8;  // a multiple of 4, so pairs never straddle rows
+  const int64_t units = (rows / 16) * cg;
   const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool active = u < (rows / 16) * cg;  // uniform per lane pair
-  const int64_t g = active ? u / cg : 0, c0 = active ? (u % cg) * 8 : 0;
+  const int64_t uc = u < units ? u : units - 1;  // units is even: pairs agree
+  const int64_t g = uc / cg, c0 = (uc % cg) * 8;
   float v[16][8];
   float bm = 0.0f;
-  if (active) {
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      In<T>::load8(ws + (g * 16 + r) * cols + c0, v[r]);
-      bm = fmaxf(bm, max8(v[r]));
-    }
-  }
-  bm = fmaxf(bm, __shfl_xor(bm, 1));
-  if (!active) return;
-  uint32_t e = e4m3_encode(bm * ts.k);
-  float rcp = block_recip(ts.S, e4m3_decode(e));
 #pragma unroll
   for (int r = 0; r < 16; r++) {
-    uint32_t packed = 0;
-#pragma unroll
-    for (int t = 0; t < 8; t++) packed |= e2m1_rne(v[r][t] * rcp) << (4 * t);
-    *reinterpret_cast<uint32_t*>(cs + (g * 16 + r) * (cols / 2) + c0 / 2) = packed;
+    In<T>::load8(ws + (g * 16 + r) * cols + c0, v[r]);
+    bm = fmaxf(bm, max8(v[r]));
   }
-  if (((u % cg) & 1) == 0) ss[g * (cols / 16) + c0 / 16] = (uint8_t)e;
+  bm = fmaxf(bm, xor1(bm));
+  build_recip_table(rtab, ts.S);
+  if (u >= units) return;
+  uint32_t e = block_code(bm, ts.k);
+  float rcp = rtab[e];
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    float y[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) y[t] = v[r][t] * rcp;
+    *reinterpret_cast<uint32_t*>(cs + (g * 16 + r) * (cols / 2) + c0 / 2) = pack8_rne(y);
+  }
+  if (((uc % cg) & 1) == 0) ss[g * (cols / 16) + c0 / 16] = (uint8_t)e;
 }
 
 // ---- standalone transform ------------------------------------------------------------------
@@ -355,11 +484,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int amax_grid(int64_t units) {
-  // Enough workgroups to fill 256 CUs several times over; each thread then
-  // loops over a strided range, so the atomics stay few.
-  int64_t g = cdiv(units, kThreads);
-  return (int)(g < 4096 ? (g > 0 ? g : 1) : 4096);
+// Grid of a grid-stride amax pass: enough workgroups to fill 256 CUs a few
+// times over with kAmaxUnroll loads in flight per thread.
+int amax_grid(int64_t units, int unroll) {
+  int64_t g = cdiv(units, (int64_t)kThreads * unroll);
+  return (int)(g < 2048 ? (g > 0 ? g : 1) : 2048);
 }
 
 template <typename T>
@@ -369,22 +498,23 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 1);
     if (a.axis == kBlockCol && a.rht) {
       int64_t units = (a.rows / 16) * (a.cols / 8);
-      amax_col_rht_kernel<T><<<amax_grid(units), kThreads, 0, st>>>(x, a.rows, a.cols, a.mask,
-                                                                     a.amax);
+      amax_col_rht_kernel<T><<<amax_grid(units, 1), kThreads, 0, st>>>(x, a.rows, a.cols, a.mask,
+                                                                        a.amax);
     } else {
       int64_t chunks = a.rows * a.cols / 8;
-      dim3 grid(amax_grid(chunks), 1);
       // ROW with the transform needs the pair exchange; COL amax without the
       // transform is the plain max.
       if (a.rht && a.axis == kBlockRow)
-        amax_flat_kernel<T, true><<<grid, kThreads, 0, st>>>(x, chunks, a.mask, a.amax);
+        amax_flat_kernel<T, true><<<dim3(amax_grid(chunks, 1), 1), kThreads, 0, st>>>(
+            x, chunks, a.mask, a.amax);
       else
-        amax_flat_kernel<T, false><<<grid, kThreads, 0, st>>>(x, chunks, 0, a.amax);
+        amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, kAmaxUnroll), 1), kThreads, 0, st>>>(
+            x, chunks, 0, a.amax);
     }
   }
   if (a.axis == kBlockRow) {
     int64_t chunks = a.rows * a.cols / 8;
-    int grid = (int)cdiv(chunks, (int64_t)kThreads * 4);
+    int grid = (int)cdiv(chunks, (int64_t)kThreads * kRowUnroll);
     uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
 #define NVFP4_ROW(SR, RHT)                                                                   \
   quant_row_kernel<T, SR, RHT><<<grid, kThreads, 0, st>>>(x, chunks, a.amax, cd, a.scales,   \
@@ -417,7 +547,11 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
   if (!a.amax_is_input) {
     fill_zero_kernel<<<(unsigned)cdiv(a.batch, 256), 256, 0, st>>>(a.amax, a.batch);
     int64_t chunks = a.rows * a.cols / 8;
-    dim3 grid(amax_grid(chunks) > 512 ? 512 : amax_grid(chunks), (unsigned)a.batch);
+    int per_slice = amax_grid(chunks, kAmaxUnroll);
+    // spread about 2048 workgroups over the slices
+    int64_t cap = a.batch > 1 ? cdiv(2048, a.batch) : 2048;
+    if (per_slice > cap) per_slice = (int)cap;
+    dim3 grid((unsigned)per_slice, (unsigned)a.batch);
     amax_flat_kernel<T, false><<<grid, kThreads, 0, st>>>(w, chunks, 0, a.amax);
   }
   int64_t units = (a.rows / 16) * (a.cols / 8);
