@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NVFP4 GEMM TFLOP/s + quantize GB/s at 1 MI355X, % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+COPY_BYTES = 256 * 1024 * 1024  # calibration copy: reads and writes this many bytes
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
 
@@ -292,6 +293,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,grouped,ultra,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (a known-size kernel for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; the hot path has no "
@@ -306,6 +310,13 @@ def main():
 
     nv.load()  # the HIP library must be present; no fallback
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     M, N, K = 8192, 6144, 6144
     log("generating inputs")
     xs, ws, qx, qw, y = fprop_setup(nv, synth, torch, dev, M, N, K, sets=4)

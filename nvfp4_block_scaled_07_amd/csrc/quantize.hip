@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -149,8 +151,12 @@ __device__ __forceinline__ uint32_t pack8_rne(const float y[8]) {
 }
 
 // ---- workgroup max -> atomicMax ---------------------------------------------------------
+// Same-address atomics serialize in L2 (several ns each), so the amax passes
+// run few, large workgroups (kAmaxThreads) and one atomic per workgroup.
+constexpr int kAmaxThreads = 1024;
+
 __device__ __forceinline__ void block_max_to(float m, float* out) {
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kAmaxThreads / 64];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   int w = threadIdx.x >> 6;
@@ -158,7 +164,7 @@ __device__ __forceinline__ void block_max_to(float m, float* out) {
   __syncthreads();
   if (threadIdx.x == 0) {
     float r = red[0];
-    for (int i = 1; i < kThreads / 64; i++) r = fmaxf(r, red[i]);
+    for (int i = 1; i < (int)(blockDim.x >> 6); i++) r = fmaxf(r, red[i]);
     // Thousands of workgroups target one address: skip the atomic when the
     // value already there is at least ours (it only grows, and the max of the
     // atomics performed is the same), which removes most of the contention.
@@ -174,44 +180,56 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 }
 
 // ---- amax over flat 8-element chunks (ROW blocks, or no transform) -----------------------
-// chunks: number of 8-element chunks per slice; slice = blockIdx.y.  Each
-// thread keeps kUnroll loads in flight per trip.
-constexpr int kAmaxUnroll = 4;
+// chunks: number of 8-element chunks per slice; slice = blockIdx.y.  A grid-
+// stride loop in which each thread issues all its loads of a trip (U 16-byte
+// loads, strided by the workgroup size so each load instruction is
+// contiguous across the wave) before reducing them.
+constexpr int kAmaxUnroll = 8;
 
 template <typename T, bool kRHT>
-__global__ __launch_bounds__(kThreads) void amax_flat_kernel(const T* __restrict__ x,
-                                                             int64_t chunks, uint32_t mask,
-                                                             float* __restrict__ amax) {
+__global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __restrict__ x,
+                                                                 int64_t chunks, uint32_t mask,
+                                                                 float* __restrict__ amax) {
   const T* xs = x + (int64_t)blockIdx.y * chunks * 8;
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (In<T>::kBf16 && !kRHT) {
-    for (; i + (kAmaxUnroll - 1) * stride < chunks; i += kAmaxUnroll * stride) {
-      uint4 q[kAmaxUnroll];
+  constexpr int U = (In<T>::kBf16 && !kRHT) ? kAmaxUnroll : 2;
+  constexpr int NT = kAmaxThreads;
+  for (int64_t b = blockIdx.x; b * NT * U < chunks; b += gridDim.x) {
+    const int64_t base = b * NT * U + threadIdx.x;
+    if (In<T>::kBf16 && !kRHT) {
+      uint4 q[U];
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; u++)
-        q[u] = *reinterpret_cast<const uint4*>(xs + (i + u * stride) * 8);
-#pragma unroll
-      for (int u = 0; u < kAmaxUnroll; u++) m = fmaxf(m, max8_bf16_bits(q[u]));
-    }
-    for (; i < chunks; i += stride)
-      m = fmaxf(m, max8_bf16_bits(*reinterpret_cast<const uint4*>(xs + i * 8)));
-  } else {
-    for (; i < chunks; i += stride) {
-      float v[8];
-      In<T>::load8(xs + i * 8, v);
-      if (kRHT) {
-        rht_signs_and_low_stages(v, mask, (int)(i & 1) * 8);
-        rht_pair_stage8(v, (int)(i & 1));
+      for (int u = 0; u < U; u++) {
+        int64_t i = base + (int64_t)u * NT;
+        q[u] = i < chunks ? *reinterpret_cast<const uint4*>(xs + i * 8) : make_uint4(0, 0, 0, 0);
       }
-      m = fmaxf(m, max8(v));
+#pragma unroll
+      for (int u = 0; u < U; u++) m = fmaxf(m, max8_bf16_bits(q[u]));
+    } else {
+      float v[U][8];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        int64_t i = base + (int64_t)u * NT;
+        int64_t ic = i < chunks ? i : chunks - 1;  // duplicates do not change a max
+        In<T>::load8(xs + ic * 8, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        if (kRHT) {
+          const int odd = (int)((base + (int64_t)u * NT) & 1);
+          rht_signs_and_low_stages(v[u], mask, odd * 8);
+          rht_pair_stage8(v[u], odd);
+        }
+        m = fmaxf(m, max8(v[u]));
+      }
     }
   }
   block_max_to(m, amax + blockIdx.y);
 }
 
 // ---- amax of COL blocks with the transform (lane: 8 cols x 16 rows) ---------------------
+// 256-thread workgroups: each lane holds a 16 x 8 tile and its transform,
+// too many registers for the large amax workgroups.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restrict__ x,
                                                                 int64_t rows, int64_t cols,
@@ -484,11 +502,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Grid of a grid-stride amax pass: enough workgroups to fill 256 CUs a few
-// times over with kAmaxUnroll loads in flight per thread.
-int amax_grid(int64_t units, int unroll) {
-  int64_t g = cdiv(units, (int64_t)kThreads * unroll);
-  return (int)(g < 2048 ? (g > 0 ? g : 1) : 2048);
+// Workgroups of an amax pass: one per kAmaxThreads * unroll units, capped
+// near the CU count (the kernels loop over the rest) to keep the atomics few.
+int amax_grid(int64_t units, int unroll, int64_t cap = 256) {
+  int64_t g = cdiv(units, (int64_t)kAmaxThreads * unroll);
+  return (int)(g < cap ? (g > 0 ? g : 1) : cap);
 }
 
 template <typename T>
@@ -498,17 +516,18 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 1);
     if (a.axis == kBlockCol && a.rht) {
       int64_t units = (a.rows / 16) * (a.cols / 8);
-      amax_col_rht_kernel<T><<<amax_grid(units, 1), kThreads, 0, st>>>(x, a.rows, a.cols, a.mask,
-                                                                        a.amax);
+      amax_col_rht_kernel<T><<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads,
+                               0, st>>>(x, a.rows, a.cols, a.mask, a.amax);
     } else {
       int64_t chunks = a.rows * a.cols / 8;
       // ROW with the transform needs the pair exchange; COL amax without the
       // transform is the plain max.
+      const int u = (!a.x_fp32 && !(a.rht && a.axis == kBlockRow)) ? kAmaxUnroll : 2;
       if (a.rht && a.axis == kBlockRow)
-        amax_flat_kernel<T, true><<<dim3(amax_grid(chunks, 1), 1), kThreads, 0, st>>>(
+        amax_flat_kernel<T, true><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
             x, chunks, a.mask, a.amax);
       else
-        amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, kAmaxUnroll), 1), kThreads, 0, st>>>(
+        amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
             x, chunks, 0, a.amax);
     }
   }
@@ -547,12 +566,11 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
   if (!a.amax_is_input) {
     fill_zero_kernel<<<(unsigned)cdiv(a.batch, 256), 256, 0, st>>>(a.amax, a.batch);
     int64_t chunks = a.rows * a.cols / 8;
-    int per_slice = amax_grid(chunks, kAmaxUnroll);
-    // spread about 2048 workgroups over the slices
-    int64_t cap = a.batch > 1 ? cdiv(2048, a.batch) : 2048;
-    if (per_slice > cap) per_slice = (int)cap;
-    dim3 grid((unsigned)per_slice, (unsigned)a.batch);
-    amax_flat_kernel<T, false><<<grid, kThreads, 0, st>>>(w, chunks, 0, a.amax);
+    const int u = a.w_fp32 ? 2 : kAmaxUnroll;
+    // about 256 workgroups in all, at least one per slice
+    const int64_t per = a.batch >= 256 ? 1 : 256 / a.batch;
+    dim3 grid((unsigned)amax_grid(chunks, u, per), (unsigned)a.batch);
+    amax_flat_kernel<T, false><<<grid, kAmaxThreads, 0, st>>>(w, chunks, 0, a.amax);
   }
   int64_t units = (a.rows / 16) * (a.cols / 8);
   dim3 grid((unsigned)cdiv(units, kThreads), (unsigned)a.batch);
