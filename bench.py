@@ -18,8 +18,10 @@ same way and reported under "rows".
 Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,6 +32,10 @@ METRIC = "NVFP4 GEMM TFLOP/s + quantize GB/s at 1 MI355X, % of MFMA/HBM roofline
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 COPY_BYTES = 256 * 1024 * 1024  # calibration copy: reads and writes this many bytes
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fprop_super_hbm_traffic.txt")
+GEMM_SOURCE = os.path.join(ROOT, "nvfp4_block_scaled_07_amd", "csrc", "gemm.hip")
 
 
 def log(msg):
@@ -137,41 +143,71 @@ def encode_only(nv, torch, qx, x, reps=20):
     return e0.elapsed_time(e1) / reps
 
 
+def gemm_traffic():
+    """HBM bytes per NT launch from the committed FETCH_SIZE/WRITE_SIZE summary,
+    or None when that summary is missing or was taken on another version of
+    the GEMM source (its sha256 is recorded in the summary)."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    h = re.search(r"source sha256 gemm.hip: ([0-9a-f]{64})", text)
+    t = re.search(r"gemm_nt traffic_bytes_per_launch: (\d+)", text)
+    if not h or not t or h.group(1) != src:
+        return None
+    return int(t.group(1))
+
+
 # ---- CPU baseline: the oracle on a bounded sample of the same step ---------------------------
-def cpu_baseline(torch, synth, xs, ws, M, N, K):
+def cpu_baseline(torch, synth, xs, ws, M, N, K, budget_s=(3.0, 3.0, 12.0)):
+    """Times the oracle on growing slices of the fprop step until each part
+    has run for about its share of `budget_s` seconds, then scales each part
+    to the full step."""
     import numpy as np
 
     import oracle as O
     threads = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    rows_x, rows_w, gemm_rows = 256, 256, 8
-    xb = synth.bf16_bits(xs[0][:rows_x].cpu())
-    wb = synth.bf16_bits(ws[0][:rows_w].cpu())
+    xb_all = synth.bf16_bits(xs[0].cpu())
+    wb_all = synth.bf16_bits(ws[0].cpu())
     amax_x = float(xs[0].float().abs().max())
     amax_w = float(ws[0].float().abs().max())
-    t0 = time.perf_counter()
-    qa = O.quantize(xb, "row", amax=amax_x)
-    t_qx = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.quantize(wb, "2d", amax=amax_w)
-    t_qw = time.perf_counter() - t0
-    # GEMM sample: `gemm_rows` full rows of Y, against a full quantized W
-    qw_full = O.quantize(synth.bf16_bits(ws[0].cpu()), "2d", amax=amax_w)
+
+    def run_chunks(fn, total, chunk, budget):
+        done, spent = 0, 0.0
+        while done < total and spent < budget:
+            hi = min(done + chunk, total)
+            t0 = time.perf_counter()
+            fn(done, hi)
+            spent += time.perf_counter() - t0
+            done = hi
+        return done, spent
+
+    # ROW and 16x16 blocks only see their own rows once the amax is given.
+    rows_x, t_qx = run_chunks(lambda a, b: O.quantize(xb_all[a:b], "row", amax=amax_x), M, 256,
+                              budget_s[0])
+    rows_w, t_qw = run_chunks(lambda a, b: O.quantize(wb_all[a:b], "2d", amax=amax_w), N, 256,
+                              budget_s[1])
+    qa = O.quantize(xb_all[:256], "row", amax=amax_x)
+    qw_full = O.quantize(wb_all, "2d", amax=amax_w)
     A = dict(codes=qa["codes"], scales=qa["scales"], block="row", g=qa["g"])
     B = dict(codes=qw_full["codes"], scales=qw_full["scales"], block="2d", g=qw_full["g"])
-    ii = np.repeat(np.arange(gemm_rows), N)
-    jj = np.tile(np.arange(N), gemm_rows)
-    t0 = time.perf_counter()
-    O.gemm_entries("N", "T", rows_x, N, K, A, B, ii, jj)
-    t_g = time.perf_counter() - t0
-    est = t_qx * (M / rows_x) + t_qw * (N / rows_w) + t_g * (M / gemm_rows)
+
+    def gemm_rows(a, b):
+        ii = np.repeat(np.arange(a, b) % 256, N)
+        jj = np.tile(np.arange(N), b - a)
+        O.gemm_entries("N", "T", 256, N, K, A, B, ii, jj)
+
+    rows_g, t_g = run_chunks(gemm_rows, M, 8, budget_s[2])
+    est = t_qx * (M / rows_x) + t_qw * (N / rows_w) + t_g * (M / rows_g)
     flops = 2.0 * M * N * K
     return {
         "value": round(flops / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle quantize of {rows_x} rows of X (1 core) and {rows_w} rows of W "
-                   f"(1 core), fp64 GEMM reference of {gemm_rows} full rows of Y "
-                   f"({threads} OpenMP threads); scaled to the full step"),
+        "sample": (f"oracle quantize of {rows_x} of {M} rows of X and {rows_w} of {N} rows of W "
+                   f"(1 core each), fp64 GEMM reference of {rows_g} of {M} rows of Y "
+                   f"({threads} OpenMP threads); each part scaled to the full step"),
         "est_step_s": round(est, 2),
         "sample_seconds": round(t_qx + t_qw + t_g, 2),
     }
@@ -291,7 +327,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,grouped,ultra,all")
+    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,grouped,ultra,grouped_ultra,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel for scaling "
@@ -344,14 +380,14 @@ def main():
                                "16x16 + Y = X W^T (NT) bf16", "M": M, "N": N, "K": K,
                    "input_sets_rotated": 4},
         "roofline": {"bound": "mfma", "achieved": g["TFLOP/s"], "peak": MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": g["frac_mfma"], "traffic": None,
+                     "unit": "TFLOP/s", "frac": g["frac_mfma"], "traffic": gemm_traffic(),
                      "kernel": "gemm_kernel NT 256x256 (fp16 MFMA 32x32x16)"},
         "kernels": {"gemm_nt": g, "quantize_1d_x": qx_e, "quantize_2d_w": qw_e},
         "wall_s_timed": round(wall, 3),
     }
     extra = [r.strip() for r in args.rows.split(",") if r.strip()]
     if "all" in extra:
-        extra = ["wgrad", "grouped", "ultra"]
+        extra = ["wgrad", "grouped", "ultra", "grouped_ultra"]
     rows = {}
     del xs, ws
     torch.cuda.empty_cache()

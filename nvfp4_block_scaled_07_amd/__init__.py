@@ -10,6 +10,8 @@ missing, every call raises.
 """
 from ._binding import (  # noqa: F401
     NVFP4_BF16, NVFP4_FP32, NVFP4_RNE, NVFP4_SR, NVFP4_BLOCK_ROW, NVFP4_BLOCK_COL, NVFP4_BLOCK_2D,
+    NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_LAYOUT,
+    NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_DEVICE,
     NVFP4Error, Philox, QTensor, library_path, load,
     nvfp4_abi_version, nvfp4_status_string, nvfp4_quantize_1d, nvfp4_quantize_2d, nvfp4_rht16,
     nvfp4_dequantize, nvfp4_gemm, nvfp4_grouped_gemm,

@@ -14,6 +14,8 @@ import torch
 NVFP4_BF16, NVFP4_FP32 = 0, 1
 NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_BLOCK_ROW, NVFP4_BLOCK_COL, NVFP4_BLOCK_2D = 0, 1, 2
+NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN = 0, -1, -2, -3
+NVFP4_ERR_LAYOUT, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_DEVICE = -4, -5, -6
 _BLOCKS = {"row": NVFP4_BLOCK_ROW, "col": NVFP4_BLOCK_COL, "2d": NVFP4_BLOCK_2D}
 _BLOCK_NAMES = {v: k for k, v in _BLOCKS.items()}
 

@@ -34,6 +34,18 @@ def test_header_declares_the_boundary():
         assert f in fns
 
 
+def test_binding_constants_match_header():
+    """The Python binding's enum values are the header's #defines."""
+    from nvfp4_block_scaled_07_amd import _binding
+    text = open(HEADER).read()
+    defs = dict((k, int(v)) for k, v in re.findall(r"#define\s+(NVFP4_[A-Z0-9_]+)\s+\(?(-?\d+)\)?",
+                                                   text))
+    names = [n for n in dir(_binding) if n.startswith("NVFP4_") and n != "NVFP4Error"]
+    assert len(names) >= 14
+    for n in names:
+        assert defs[n] == getattr(_binding, n), n
+
+
 def test_every_declared_symbol_is_exported(lib):
     for f in declared_functions():
         assert hasattr(lib, f), f

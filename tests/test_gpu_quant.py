@@ -43,7 +43,13 @@ def _check_1d(x, dtype, axis, rounding, mask, seed=0, offset=0, rounds=5, amax=N
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_quantize_1d_small(shape, axis, rounding, rht, dtype):
     if axis == "col" and shape[0] % 16:
-        pytest.skip("COL blocks need rows % 16 == 0")
+        # COL blocks need rows % 16 == 0: the call is rejected before launch.
+        t, _ = device_input(make_input("normal", shape, seed=1), dtype, device())
+        with pytest.raises(nv.NVFP4Error) as e:
+            nv.quantize_1d(t, axis, rounding, nv.Philox(1) if rounding == "sr" else None,
+                           0xA5C3 if rht else -1)
+        assert e.value.status == nv.NVFP4_ERR_SHAPE
+        return
     x = make_input("normal", shape, seed=shape[0] * 7 + shape[1])
     _check_1d(x, dtype, axis, rounding, 0xA5C3 if rht else -1, seed=123, offset=9)
 
