@@ -11,8 +11,10 @@
 //    canonical K-major layout per 64-k stage: 32 code bytes per row (two
 //    16-byte halves, swapped on rows with bit 2 set to spread LDS banks) and
 //    4 raw scale bytes per row.  K-major operands go global -> LDS directly
-//    (4-byte LDS DMA, no registers); MN-major operands (the TN/NN layouts)
-//    go through registers and an 8x8 nibble transpose.
+//    by LDS DMA.  MN-major operands (the TN/NN layouts) also go by LDS DMA,
+//    as stored rows of k, and are transposed by the LDS read itself
+//    (ds_read_b64_tr_b4), which hands each lane 16 consecutive k of one
+//    column.
 //  * Each wave decodes only the fragments it multiplies: lane l reads 16 code
 //    bytes of row l%32 (k = 32*(l/32) .. +32 of the stage) and the row's two
 //    scale bytes for those k, converts the scales to an fp16 pair with
@@ -82,30 +84,6 @@ __device__ __forceinline__ int code_addr(int row, int half) {
   return row * 32 + 16 * (half ^ ((row >> 2) & 1));
 }
 
-// In-register transpose of an 8x8 matrix of nibbles: d[i] nibble j -> d[j]
-// nibble i (three rounds of block swaps: 4x4, 2x2, 1x1).
-__device__ __forceinline__ void transpose8x8_nibbles(uint32_t d[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    uint32_t t = ((d[i] >> 16) ^ d[i + 4]) & 0x0000FFFFu;
-    d[i + 4] ^= t;
-    d[i] ^= t << 16;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    if (i & 2) continue;
-    uint32_t t = ((d[i] >> 8) ^ d[i + 2]) & 0x00FF00FFu;
-    d[i + 2] ^= t;
-    d[i] ^= t << 8;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    uint32_t t = ((d[i] >> 4) ^ d[i + 1]) & 0x0F0F0F0Fu;
-    d[i + 1] ^= t;
-    d[i] ^= t << 4;
-  }
-}
-
 // ---- staging: K-major operands by LDS DMA ----------------------------------------------------
 // buffer_load_dword{,x4} ... lds moves 4 or 16 bytes per lane into LDS at
 // (wave-uniform base + size * lane); the lane's source offset is chosen so
@@ -164,79 +142,87 @@ struct DmaK {
   }
 };
 
-// ---- staging: MN-major operands through registers ------------------------------------------
-// The stage is BK rows (k) x ROWS columns (mn).  A unit is 8 k x 8 mn (8
-// dwords, one per k row), transposed to 8 dwords along k.
-// Threads [T0, T0 + NT) take part (a wave-uniform predicate).
-template <int ROWS, int T0, int NT>
-struct StageMN {
-  static constexpr int UNITS = (BK / 8) * (ROWS / 8);
-  static_assert(UNITS % NT == 0 && ROWS % NT == 0, "tile must divide evenly");
-  static constexpr int UN = UNITS / NT;
-  static constexpr int SN = ROWS / NT;
-  uint32_t c[UN][8];
-  uint32_t s[SN][4];  // the four k-block scale bytes of each row, assembled at store time
+// ---- staging: MN-major operands by LDS DMA, transposed when read ----------------------------
+// The stage of an operand stored [K][W] is 64 stored rows (k) of the tile's
+// 256 columns (mn): 64 x 128 code bytes.  16-byte unit c (32 columns) of
+// stage row k lands in LDS unit 8k + (c ^ ((k >> 1) & 7)): the 16 rows that
+// one transposing read gathers (below) then sit in 16 different 16-byte
+// slots of a 256-byte span.  Columns past the operand's edge re-read its last
+// valid unit (W is a multiple of 32), which only feeds unstored outputs.
+// Scales of stage row kb (k-block k0/16 + kb) go to LDS bytes 256*kb: COL
+// blocks as the tile's 256 bytes of that row; 2D blocks as the 4-byte words
+// holding the row's (up to) 16 bytes for the tile, read from the aligned word
+// at or below their start, so a reader adds that start's offset (0 or 2).
+template <int ROWS, int NW, int SW0, int SWN>
+struct DmaMN {
+  static_assert(ROWS == 256, "a stage row of codes is 128 bytes, a scale row 256");
+  static constexpr int kCodeChunks = BK * ROWS / 2 / 1024;
+  static_assert(kCodeChunks % NW == 0, "code chunks must split over waves");
+  static_assert(SWN == BK / 16, "one scale row per scale wave");
+  static constexpr int CPW = kCodeChunks / NW;
+  uint32_t coff[CPW];
+  uint32_t soff;
+  uint32_t crow, srow;  // bytes per stored code row, per scale row
+  __amdgpu_buffer_rsrc_t crsrc, srsrc;
+  int wave;
 
-  __device__ __forceinline__ void load(const OpView& op, int64_t mn0, int64_t mn_lim,
-                                       int64_t k0, int tid_all) {
-    const int tid = tid_all - T0;
-    if (tid < 0 || tid >= NT) return;
+  __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
+                                       int lane, int wv) {
+    wave = wv;
     const int64_t W = op.mn_total;
+    const int64_t last_unit = W / 32 - 1;
+    crow = (uint32_t)(W / 2);
 #pragma unroll
-    for (int j = 0; j < UN; j++) {
-      int u = tid + j * NT;
-      int kg = u / (ROWS / 8), md = u % (ROWS / 8);
-      int64_t mn = mn0 + 8 * md;
-      int64_t mc = mn < mn_lim ? mn : mn_lim - 8;  // mn_lim is a multiple of 8
-#pragma unroll
-      for (int r = 0; r < 8; r++)
-        c[j][r] = *reinterpret_cast<const uint32_t*>(op.codes + (k0 + 8 * kg + r) * (W / 2) +
-                                                      mc / 2);
+    for (int q = 0; q < CPW; q++) {
+      const int unit = 64 * (wave * CPW + q) + lane;  // LDS 16-byte unit of the stage
+      const int k = unit >> 3;
+      const int c = (unit & 7) ^ ((k >> 1) & 7);
+      int64_t cg = mn0 / 32 + c;
+      cg = cg < last_unit ? cg : last_unit;
+      coff[q] = (uint32_t)(k * (W / 2) + 16 * cg);
     }
-#pragma unroll
-    for (int j = 0; j < SN; j++) {
-      int64_t mn = mn0 + tid + j * NT;
-      int64_t mc = mn < mn_lim ? mn : mn_lim - 1;
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
-        int64_t row = k0 / 16 + kb;
-        int64_t off = op.block == kBlock2d ? row * (W / 16) + mc / 16 : row * W + mc;
-        s[j][kb] = op.scales[off];
-      }
+    const int kb = wave - SW0;  // meaningful on scale waves only
+    if (op.block == kBlock2d) {
+      const int64_t w16 = W / 16;
+      const int64_t rel = kb * w16 + mn0 / 16;
+      const int64_t rel4 = rel & ~(int64_t)3;
+      const int64_t need = w16 - mn0 / 16 < 16 ? w16 - mn0 / 16 : 16;
+      const int nd = (int)((rel - rel4 + need + 3) / 4);
+      const int d = (lane & 7) < nd - 1 ? (lane & 7) : nd - 1;
+      soff = (uint32_t)(rel4 + 4 * d);
+      srow = (uint32_t)w16;
+    } else {
+      int64_t col = mn0 + 4 * lane;
+      col = col < W - 4 ? col : W - 4;
+      soff = (uint32_t)(kb * W + col);
+      srow = (uint32_t)W;
     }
+    (void)mn_lim;
+    crsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.codes), 0,
+                                              (int)(K * (W / 2)), kBufferFlags);
+    srsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.scales), 0,
+                                              (int)((K / 16) * srow), kBufferFlags);
   }
 
-  __device__ __forceinline__ void store_codes(uint8_t* lds_codes, int tid_all) {
-    const int tid = tid_all - T0;
-    if (tid < 0 || tid >= NT) return;
+  __device__ __forceinline__ void issue(int64_t k0, uint8_t* lds_codes, uint8_t* lds_scales) const {
 #pragma unroll
-    for (int j = 0; j < UN; j++) {
-      int u = tid + j * NT;
-      int kg = u / (ROWS / 8), md = u % (ROWS / 8);
-#pragma unroll
-      for (int r = 0; r < 8; r++) pin(c[j][r]);
-      transpose8x8_nibbles(c[j]);
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        int row = 8 * md + i;
-        *reinterpret_cast<uint32_t*>(lds_codes + code_addr(row, kg >> 2) + 4 * (kg & 3)) =
-            c[j][i];
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store_scales(uint8_t* lds_scales, int tid_all) {
-    const int tid = tid_all - T0;
-    if (tid < 0 || tid >= NT) return;
-#pragma unroll
-    for (int j = 0; j < SN; j++) {
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++) pin(s[j][kb]);
-      *reinterpret_cast<uint32_t*>(lds_scales + 4 * (tid + j * NT)) =
-          s[j][0] | (s[j][1] << 8) | (s[j][2] << 16) | (s[j][3] << 24);
-    }
+    for (int q = 0; q < CPW; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, lds_codes + (wave * CPW + q) * 1024, 16,
+                                               coff[q], (int)(k0 * crow), 0, 0);
+    if (wave >= SW0 && wave < SW0 + SWN)  // wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, lds_scales + (wave - SW0) * 256, 4, soff,
+                                               (int)((k0 / 16) * srow), 0, 0);
   }
 };
+
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b4: in each group of 16 lanes, lane i receives nibble i of
+// the 8-byte rows addressed by lanes 0..15 of its group, in lane order.
+__device__ __forceinline__ v2i32 lds_read_tr4(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+      (__attribute__((address_space(3))) v2i32*)(p));
+}
 
 // Decode 8 nibbles (one dword) scaled by the packed pair d = (d, d).
 __device__ __forceinline__ half8 decode8(uint32_t q, half2 d) {
@@ -280,9 +266,11 @@ __device__ __forceinline__ constexpr int a_slot(int s, int i) {
   return s < 3 || i * TN + TN - 1 >= 2 ? i * TN + TN - 1 : 2;
 }
 
-// Per-operand staging: DMA for K-major, registers for MN-major.  OPB
-// selects operand B's share of waves/threads (A uses the first half of the
-// scale waves and MN threads, B the second).
+// Per-operand staging, both layouts by LDS DMA.  OPB selects operand B's
+// share of the scale waves (A uses the first half, B the second).  A
+// fragment is what one lane multiplies in one 64-k stage: 32 nibbles of its
+// row (row l%32 of the fragment, k = 32*(l/32) .. +32 of the stage; dword s
+// holds the k of 16-k step s) and the two scale bytes of those k.
 template <bool KMAJOR, int ROWS, class C, int OPB>
 struct Staging;
 
@@ -295,37 +283,74 @@ struct Staging<true, ROWS, C, OPB> {
   static constexpr int kSW0 = (2 * kSW <= C::NW) ? OPB * kSW : 0;
   DmaK<ROWS, C::NW, kSW0, kSW> d;
   static constexpr int kCodeDma = DmaK<ROWS, C::NW, kSW0, kSW>::CPW;
+  int code0, sc0;  // this lane's LDS offsets for fragment 0
   __device__ __forceinline__ int scale_dma(int wave) const {
     return wave >= kSW0 && wave < kSW0 + kSW ? 1 : 0;
   }
+  // row0: first row (of the tile) of this wave's fragments; fragment i
+  // starts 32*i rows further.
   __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
-                                       int tid) {
+                                       int tid, int row0) {
     d.init(op, mn0, mn_lim, K, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6));
+    const int lane = tid & 63;
+    code0 = code_addr(row0 + (lane & 31), lane >> 5);  // rows step by 32: same swizzle
+    sc0 = 4 * (row0 + (lane & 31)) + 2 * (lane >> 5);
   }
-  __device__ __forceinline__ void load_regs(const OpView&, int64_t, int64_t, int64_t, int) {}
   __device__ __forceinline__ void load_dma(int64_t k0, uint8_t* codes, uint8_t* scales) {
     d.issue(k0, codes, scales);
   }
-  __device__ __forceinline__ void store_codes(uint8_t*, int) {}
-  __device__ __forceinline__ void store_scales(uint8_t*, int) {}
+  __device__ __forceinline__ void frag(const uint8_t* codes, const uint8_t* scales, int i,
+                                       uint4& q, uint32_t& sc) const {
+    q = *reinterpret_cast<const uint4*>(codes + code0 + i * 32 * 32);
+    sc = *reinterpret_cast<const uint16_t*>(scales + sc0 + i * 32 * 4);
+  }
 };
 
 template <int ROWS, class C, int OPB>
 struct Staging<false, ROWS, C, OPB> {
-  static constexpr int kThreads = C::NT >= 2 * ROWS ? ROWS : C::NT;
-  static constexpr int kT0 = C::NT >= 2 * ROWS ? OPB * ROWS : 0;
-  StageMN<ROWS, kT0, kThreads> r;
-  static constexpr int kCodeDma = 0;
-  __device__ __forceinline__ int scale_dma(int) const { return 0; }
-  __device__ __forceinline__ void init(const OpView&, int64_t, int64_t, int64_t, int) {}
-  __device__ __forceinline__ void load_regs(const OpView& op, int64_t mn0, int64_t mn_lim,
-                                            int64_t k0, int tid) {
-    r.load(op, mn0, mn_lim, k0, tid);
+  static constexpr int kSW = BK / 16;  // scale waves: one per k-block row
+  static_assert(kSW <= C::NW, "one scale row per wave at most");
+  static constexpr int kSW0 = (2 * kSW <= C::NW) ? OPB * kSW : 0;
+  DmaMN<ROWS, C::NW, kSW0, kSW> d;
+  static constexpr int kCodeDma = DmaMN<ROWS, C::NW, kSW0, kSW>::CPW;
+  // Lane l (group g = l/16, j = l%16, half h = l/32) addresses, for read
+  // r = 0, 1, stage row k = 32h + 16r + j at the 8 bytes of columns
+  // [row0 + 32i + 16(g&1), +16): it receives the 16 k of its own column.
+  uint32_t tr_base[2];
+  int tr_c[2];
+  int sc_off[2], sc_step;
+  __device__ __forceinline__ int scale_dma(int wave) const {
+    return wave >= kSW0 && wave < kSW0 + kSW ? 1 : 0;
   }
-  __device__ __forceinline__ void load_dma(int64_t, uint8_t*, uint8_t*) {}
-  __device__ __forceinline__ void store_codes(uint8_t* codes, int tid) { r.store_codes(codes, tid); }
-  __device__ __forceinline__ void store_scales(uint8_t* scales, int tid) {
-    r.store_scales(scales, tid);
+  __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
+                                       int tid, int row0) {
+    d.init(op, mn0, mn_lim, K, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6));
+    const int lane = tid & 63;
+    const int g = lane >> 4, j = lane & 15, h = lane >> 5;
+    const int c0 = row0 / 32;  // a multiple of the fragment count: c0 + i == c0 ^ i
+    const bool two_d = op.block == kBlock2d;
+    const int64_t w16 = op.mn_total / 16;
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      const int k = 32 * h + 16 * r + j;
+      tr_base[r] = 128 * k + 8 * (g & 1);
+      tr_c[r] = c0 ^ ((k >> 1) & 7);
+      const int kb = 2 * h + r;
+      sc_off[r] = two_d ? 256 * kb + (int)((kb * w16 + mn0 / 16) & 3) + (row0 + (lane & 31)) / 16
+                        : 256 * kb + row0 + (lane & 31);
+    }
+    sc_step = two_d ? 2 : 32;
+  }
+  __device__ __forceinline__ void load_dma(int64_t k0, uint8_t* codes, uint8_t* scales) {
+    d.issue(k0, codes, scales);
+  }
+  __device__ __forceinline__ void frag(const uint8_t* codes, const uint8_t* scales, int i,
+                                       uint4& q, uint32_t& sc) const {
+    const v2i32 lo = lds_read_tr4(codes + tr_base[0] + 16 * (tr_c[0] ^ i));
+    const v2i32 hi = lds_read_tr4(codes + tr_base[1] + 16 * (tr_c[1] ^ i));
+    q = uint4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
+    sc = (uint32_t)scales[sc_off[0] + i * sc_step] |
+         ((uint32_t)scales[sc_off[1] + i * sc_step] << 8);
   }
 };
 
@@ -333,9 +358,7 @@ struct Staging<false, ROWS, C, OPB> {
 // cols < N, using lds (kLds bytes).
 //
 // Software pipeline over 64-k stages (stage s lives in LDS buffer s % 4):
-//  * iteration kt starts stage kt+3's transfer: register loads for MN-major
-//    operands at its start (written to LDS during steps 2 and 3), DMA for
-//    K-major ones during its last step;
+//  * iteration kt issues stage kt+3's LDS DMA during its last step;
 //  * its four 16-k steps run TM x TN MFMAs each; between MFMAs it decodes
 //    the fragments of the following step -- for the last step, those of step
 //    0 of stage kt+1, read from LDS at that step's start;
@@ -365,8 +388,8 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
 
   Staging<AK, C::BM, C, 0> sa;
   Staging<BKM, C::BN, C, 1> sb;
-  sa.init(A, m0, m_lim, K, tid);
-  sb.init(B, n0, N, K, tid);
+  sa.init(A, m0, m_lim, K, tid, wm * (C::BM / C::WM));
+  sb.init(B, n0, N, K, tid, wn * (C::BN / C::WN));
   // DMA instructions this wave issues per stage (wave-uniform): the code
   // chunks plus one scale chunk per operand whose scales this wave moves.
   constexpr int kCodeDma = Staging<AK, C::BM, C, 0>::kCodeDma + Staging<BKM, C::BN, C, 1>::kCodeDma;
@@ -375,17 +398,8 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
 
   constexpr int oAS = C::kACodes, oBC = C::kACodes + C::kAScales,
                 oBS = C::kACodes + C::kAScales + C::kBCodes;
-  // Fragment rows of one wave step by 32, which keeps the code swizzle (it
-  // depends on row bit 2), so each operand needs one base address.
-  const int a_row0 = wm * (C::BM / C::WM) + lrow, b_row0 = wn * (C::BN / C::WN) + lrow;
-  const int a_code0 = code_addr(a_row0, lhalf), b_code0 = oBC + code_addr(b_row0, lhalf);
-  const int a_sc0 = oAS + 4 * a_row0 + 2 * lhalf, b_sc0 = oBS + 4 * b_row0 + 2 * lhalf;
 
   auto buffer = [&](int idx) { return lds + idx * C::kStage; };
-  auto load_regs = [&](int64_t k0) {
-    sa.load_regs(A, m0, m_lim, k0, tid);
-    sb.load_regs(B, n0, N, k0, tid);
-  };
   auto load_dma = [&](int64_t k0, uint8_t* dst) {
     sa.load_dma(k0, dst, dst + oAS);
     sb.load_dma(k0, dst + oBC, dst + oBS);
@@ -396,15 +410,9 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
   auto read_frags = [&](const uint8_t* st) {
     uint32_t ar[C::TM], br[C::TN];
 #pragma unroll
-    for (int i = 0; i < C::TM; i++) {
-      aq[i] = *reinterpret_cast<const uint4*>(st + a_code0 + i * 32 * 32);
-      ar[i] = *reinterpret_cast<const uint16_t*>(st + a_sc0 + i * 32 * 4);
-    }
+    for (int i = 0; i < C::TM; i++) sa.frag(st, st + oAS, i, aq[i], ar[i]);
 #pragma unroll
-    for (int j = 0; j < C::TN; j++) {
-      bq[j] = *reinterpret_cast<const uint4*>(st + b_code0 + j * 32 * 32);
-      br[j] = *reinterpret_cast<const uint16_t*>(st + b_sc0 + j * 32 * 4);
-    }
+    for (int j = 0; j < C::TN; j++) sb.frag(st + oBC, st + oBS, j, bq[j], br[j]);
 #pragma unroll
     for (int i = 0; i < C::TM; i++) as[i] = scale_pair(ar[i]);
 #pragma unroll
@@ -414,14 +422,7 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
   // Prologue: stages 0, 1 and 2 in LDS, step 0 of stage 0 decoded.
   auto stage_k = [&](int64_t st) { return (st < KT ? st : KT - 1) * BK; };
 #pragma unroll
-  for (int st = 0; st < kStages - 1; st++) {
-    load_regs(stage_k(st));
-    load_dma(stage_k(st), buffer(st));
-    sa.store_codes(buffer(st), tid);
-    sa.store_scales(buffer(st) + oAS, tid);
-    sb.store_codes(buffer(st) + oBC, tid);
-    sb.store_scales(buffer(st) + oBS, tid);
-  }
+  for (int st = 0; st < kStages - 1; st++) load_dma(stage_k(st), buffer(st));
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   read_frags(buffer(0));
@@ -437,7 +438,6 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
     // idle buffer, which keeps the loop free of branches).
     const int64_t kl = stage_k(kt + kStages - 1);
     uint8_t* dst = buffer(b_load);
-    load_regs(kl);
 
 #pragma unroll
     for (int s = 0; s < 4; s++) {
@@ -472,15 +472,7 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
               af[ii] = decode8(pick(aq[ii], ns), splat(as[ii], ns >= 2));
               any = true;
             }
-          // MN-major operands write stage kt+2 to LDS during steps 2 and 3.
-          constexpr int kLast = C::TM * C::TN - 1;
-          const bool st = (s == 2 && (t == kLast / 2 || t == kLast)) ||
-                          (s == 3 && (t == kLast / 4 || t == (3 * kLast) / 4));
-          if (s == 2 && t == kLast / 2) sa.store_codes(dst, tid);
-          if (s == 2 && t == kLast) sa.store_scales(dst + oAS, tid);
-          if (s == 3 && t == kLast / 4) sb.store_codes(dst + oBC, tid);
-          if (s == 3 && t == (3 * kLast) / 4) sb.store_scales(dst + oBS, tid);
-          if (C::kFence && (any || (st && (!AK || !BKM)))) __builtin_amdgcn_sched_barrier(0);
+          if (C::kFence && any) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -523,7 +515,7 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
   }
 }
 
-// Tile order: groups of 8 M-tiles sweep N, so a wave of workgroups shares
+// Tile order: groups of 8 M-tiles sweep N, so tiles that run together share
 // both operands' panels in L2.
 __device__ __forceinline__ void tile_coords(int64_t t, int64_t ntm, int64_t ntn, int64_t& tm,
                                             int64_t& tn) {
@@ -537,12 +529,21 @@ __device__ __forceinline__ void tile_coords(int64_t t, int64_t ntm, int64_t ntn,
   tn = r / gsize;
 }
 
+// Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b % 8) and
+// every XCD has its own L2: give each XCD a contiguous run of the tile order,
+// so the tiles running together on one XCD share panels in its L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t total) {
+  constexpr int64_t kXcds = 8;
+  const int64_t per = total / kXcds;
+  return b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
+}
+
 template <class C, bool AK, bool BKM>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
   int64_t tm, tn;
-  tile_coords(blockIdx.x, ntm, ntn, tm, tn);
+  tile_coords(xcd_tile(blockIdx.x, ntm * ntn), ntm, ntn, tm, tn);
   OpView A{a.A.codes, a.A.scales, a.M, a.A.block};
   OpView B{a.B.codes, a.B.scales, a.N, a.B.block};
   const float gs = *a.A.gdec * *a.B.gdec;
