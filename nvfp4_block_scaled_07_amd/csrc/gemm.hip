@@ -7,26 +7,25 @@
 //    bits, an E4M3 scale 4, so their product has at most 6 and lies in
 //    [2^-10, 2688] -- and fed to v_mfma_f32_32x32x16_f16 with fp32
 //    accumulation.
-//  * Codes and scale bytes (0.5625 B per element) are staged in LDS in a
-//    canonical K-major layout per 64-k stage: 32 code bytes per row (two
-//    16-byte halves, swapped on rows with bit 2 set to spread LDS banks) and
-//    4 raw scale bytes per row.  K-major operands go global -> LDS directly
-//    by LDS DMA.  MN-major operands (the TN/NN layouts) also go by LDS DMA,
-//    as stored rows of k, and are transposed by the LDS read itself
-//    (ds_read_b64_tr_b4), which hands each lane 16 consecutive k of one
-//    column.
-//  * Each wave decodes only the fragments it multiplies: lane l reads 16 code
-//    bytes of row l%32 (k = 32*(l/32) .. +32 of the stage) and the row's two
-//    scale bytes for those k, converts the scales to an fp16 pair with
-//    v_cvt_scalef32_pk_f16_fp8 and, for each 16-k MFMA step, 8 nibbles with
-//    v_cvt_scalef32_pk_f16_fp4 (both with scale 1: their scale operand only
-//    applies a power of two) and v_pk_mul_f16.  The k order inside an MFMA
-//    is a permutation shared by A and B, so the sum is unchanged.
+//  * Codes and scale bytes (0.5625 B per element) reach LDS by LDS DMA
+//    (buffer loads that write LDS directly), one stage of BK = 128 (or 64)
+//    k at a time, in a ring of three stage buffers.  K-major operands keep
+//    their rows: BK/2 code bytes per row in 16-byte units whose order is
+//    swizzled per row, and BK/16 scale bytes per row.  MN-major operands
+//    (the TN/NN layouts) are staged as stored, rows of k, and transposed by
+//    the LDS read itself (ds_read_b64_tr_b4), which hands each lane 16
+//    consecutive k of one column.
+//  * Each wave decodes only the fragments it multiplies.  Lane l owns row
+//    l%32 of a 32-row fragment and, in each 64-k half of a stage, the 32 k
+//    at 32*(l/32); per 16-k MFMA step it decodes 8 nibbles with
+//    v_cvt_scalef32_pk_f16_fp4 and scales them by the fp16 value of their
+//    E4M3 scale byte (v_cvt_scalef32_pk_f16_fp8, then v_pk_mul_f16; both
+//    converts with scale 1, since their scale operand only applies a power
+//    of two).  The k order inside an MFMA is a permutation shared by A and
+//    B, so every output is the same sum whatever the tile shape or depth.
 //  * Epilogue: C = RN32(acc * RN32(gA * gB)), stored as bf16 (RNE) or fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
@@ -37,20 +36,26 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 64;       // k per LDS stage
-constexpr int kStages = 4;   // LDS ring depth
+constexpr int kStages = 3;  // LDS ring depth
 
-template <int BM_, int BN_, int WM_, int WN_, bool FENCE_ = true>
+template <int BM_, int BN_, int WM_, int WN_, int BK_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr bool kFence = FENCE_;  // fence the MFMA/decode order with sched_barrier
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile sizes");
+  static_assert(BK == 64 || BK == 128, "stage depth");
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM / 32;  // 32x32 MFMA tiles per wave along M
   static constexpr int TN = BN / WN / 32;
-  static constexpr int kACodes = BM * 32, kAScales = BM * 4;
-  static constexpr int kBCodes = BN * 32, kBScales = BN * 4;
+  static constexpr int H = BK / 64;        // 64-k halves per stage
+  static constexpr int STEPS = BK / 16;    // MFMA steps per stage
+  static constexpr int RB = BK / 2;        // code bytes per row per stage
+  static constexpr int SB = BK / 16;       // scale bytes per row (k-blocks) per stage
+  // Scales: SB bytes per row (K-major) or SB rows of 256 bytes (MN-major).
+  static constexpr int kACodes = BM * RB, kAScales = BM * SB > SB * 256 ? BM * SB : SB * 256;
+  static constexpr int kBCodes = BN * RB, kBScales = BN * SB > SB * 256 ? BN * SB : SB * 256;
   static constexpr int kStage = kACodes + kAScales + kBCodes + kBScales;
   static constexpr int kLds = kStages * kStage;
 };
@@ -64,13 +69,6 @@ struct OpView {
   int block;
 };
 
-// Makes v look redefined here, so arithmetic on a prefetched value cannot be
-// hoisted up to its load (which would wait for the load right away).
-template <typename T>
-__device__ __forceinline__ void pin(T& v) {
-  asm volatile("" : "+v"(v));
-}
-
 // s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt not waited on).
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -79,52 +77,113 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// Swizzled byte address of half `half` (16 bytes) of code row `row`.
-__device__ __forceinline__ int code_addr(int row, int half) {
-  return row * 32 + 16 * (half ^ ((row >> 2) & 1));
+// The same with a wave-uniform count (a count above 15 waits for all).
+__device__ __forceinline__ void wait_vm_lgkm0_upto(int n) {
+  switch (n) {
+    case 1: wait_vm_lgkm0<1>(); break;
+    case 2: wait_vm_lgkm0<2>(); break;
+    case 3: wait_vm_lgkm0<3>(); break;
+    case 4: wait_vm_lgkm0<4>(); break;
+    case 5: wait_vm_lgkm0<5>(); break;
+    case 6: wait_vm_lgkm0<6>(); break;
+    case 7: wait_vm_lgkm0<7>(); break;
+    case 8: wait_vm_lgkm0<8>(); break;
+    case 9: wait_vm_lgkm0<9>(); break;
+    case 10: wait_vm_lgkm0<10>(); break;
+    case 11: wait_vm_lgkm0<11>(); break;
+    case 12: wait_vm_lgkm0<12>(); break;
+    case 13: wait_vm_lgkm0<13>(); break;
+    case 14: wait_vm_lgkm0<14>(); break;
+    case 15: wait_vm_lgkm0<15>(); break;
+    default: wait_vm_lgkm0<0>(); break;
+  }
 }
 
-// ---- staging: K-major operands by LDS DMA ----------------------------------------------------
+// ---- K-major stage layout --------------------------------------------------------------------
+// Row r of a stage holds RB code bytes as UR = RB/16 units of 16 bytes; unit
+// u (k = 32u .. 32u+31 of the stage) sits in slot u ^ kmaj_swz(r).  A 16-byte
+// LDS read is served 16 lanes at a time over a 256-byte bank window, and the
+// 16 lanes of a fragment read take 16 consecutive rows and the same unit:
+// the swizzle spreads them over 16 distinct 16-byte slots of the window.
+template <int RB>
+__device__ __forceinline__ int kmaj_swz(int row) {
+  static_assert(RB == 32 || RB == 64, "row bytes");
+  return RB == 32 ? (row >> 3) & 1 : (row >> 2) & 3;
+}
+
+template <int RB>
+__device__ __forceinline__ int kmaj_code_addr(int row, int unit) {
+  return row * RB + 16 * (unit ^ kmaj_swz<RB>(row));
+}
+
+// ---- staging plans -----------------------------------------------------------------------------
 // buffer_load_dword{,x4} ... lds moves 4 or 16 bytes per lane into LDS at
-// (wave-uniform base + size * lane); the lane's source offset is chosen so
-// that the LDS image is the swizzled canonical layout.  A row past the
-// operand's edge re-reads the last valid row (always in bounds): row i of A
-// only reaches row i of C, row j of B only column j, so such rows only feed
-// outputs that are never stored.
+// (wave-uniform base + size * lane).  Code chunks (1 KiB: 64 lanes x 16
+// bytes) go to wave c % NW; scale chunks (256 bytes: 64 lanes x 4 bytes) to
+// wave (W0 + j) % NW.
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
 
-template <int ROWS, int NW, int SW0, int SWN>
+template <int NW, int CHUNKS, int SCHUNKS, int W0>
+struct DmaPlan {
+  static constexpr int CPW = (CHUNKS + NW - 1) / NW;   // most code chunks on one wave
+  static constexpr int SPW = (SCHUNKS + NW - 1) / NW;  // most scale chunks on one wave
+  __device__ __forceinline__ static bool code_on(int wave, int q) {
+    return wave + q * NW < CHUNKS;
+  }
+  __device__ __forceinline__ static int scale_chunk(int wave, int q) {
+    return ((wave - W0) % NW + NW) % NW + q * NW;  // valid if < SCHUNKS
+  }
+  __device__ __forceinline__ static int count(int wave) {
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < CPW; q++) n += code_on(wave, q) ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < SPW; q++) n += scale_chunk(wave, q) < SCHUNKS ? 1 : 0;
+    return n;
+  }
+};
+
+// ---- staging: K-major operands ----------------------------------------------------------------
+// The lane's source offset is chosen so that the LDS image is the swizzled
+// layout above.  A row past the operand's edge re-reads the last valid row
+// (always in bounds): row i of A only reaches row i of C, row j of B only
+// column j, so such rows only feed outputs that are never stored.
+template <class C, int ROWS, int W0>
 struct DmaK {
-  // Code chunks (1 KiB = 32 rows, 16 bytes per lane) spread over all NW
-  // waves; scale chunks (256 B = 64 rows, 4 bytes per lane) over waves
-  // [SW0, SW0 + SWN), one each.
-  static constexpr int kCodeChunks = ROWS * 32 / 1024;
-  static_assert(kCodeChunks % NW == 0, "code chunks must split over waves");
-  static_assert(ROWS * 4 / 256 == SWN, "one scale chunk per scale wave");
-  static constexpr int CPW = kCodeChunks / NW;
-  uint32_t coff[CPW];  // lane byte offsets from the tile's first code row
-  uint32_t soff;       // lane byte offset from the tile's first scale row
+  static constexpr int RB = C::RB, SB = C::SB, UR = RB / 16;
+  static constexpr int kCodeChunks = ROWS * RB / 1024;
+  static constexpr int kScaleChunks = ROWS * SB / 256;
+  using Plan = DmaPlan<C::NW, kCodeChunks, kScaleChunks, W0>;
+  uint32_t coff[Plan::CPW];
+  uint32_t soff[Plan::SPW];
   __amdgpu_buffer_rsrc_t crsrc, srsrc;
   int wave;
+
+  __device__ __forceinline__ int count(int w) const { return Plan::count(w); }
 
   __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
                                        int lane, int wv) {
     wave = wv;
     const int64_t kc = K / 2, ks = K / 16;
 #pragma unroll
-    for (int q = 0; q < CPW; q++) {
-      const int c = wave * CPW + q;
-      const int row = 32 * c + (lane >> 1);
-      const int h = (lane & 1) ^ ((row >> 2) & 1);
+    for (int q = 0; q < Plan::CPW; q++) {
+      const int row = (1024 / RB) * (wave + q * C::NW) + lane / UR;
+      const int unit = (lane % UR) ^ kmaj_swz<RB>(row);
       const int64_t mn = mn0 + row < mn_lim ? mn0 + row : mn_lim - 1;
-      coff[q] = (uint32_t)((mn - mn0) * kc + 16 * h);
+      coff[q] = (uint32_t)((mn - mn0) * kc + 16 * unit);
     }
     const bool two_d = op.block == kBlock2d;
-    const int srow = (wave - SW0) * 64 + lane;  // meaningful on scale waves only
-    const int64_t smn = mn0 + srow < mn_lim ? mn0 + srow : mn_lim - 1;
     const int64_t sbase = two_d ? (mn0 / 16) * ks : mn0 * ks;
     const int64_t slim = two_d ? ((mn_lim + 15) / 16) * ks : mn_lim * ks;
-    soff = (uint32_t)((two_d ? (smn / 16) * ks : smn * ks) - sbase);
+#pragma unroll
+    for (int q = 0; q < Plan::SPW; q++) {
+      // Row SB bytes = SB/4 lanes of 4 bytes (the stage's k-blocks).
+      const int j = Plan::scale_chunk(wave, q);
+      const int row = (256 / SB) * j + lane / (SB / 4);
+      const int part = lane % (SB / 4);
+      const int64_t mn = mn0 + row < mn_lim ? mn0 + row : mn_lim - 1;
+      soff[q] = (uint32_t)((two_d ? (mn / 16) * ks : mn * ks) - sbase + 4 * part);
+    }
     crsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.codes + mn0 * kc), 0,
                                               (int)((mn_lim - mn0) * kc), kBufferFlags);
     srsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.scales + sbase), 0,
@@ -133,71 +192,89 @@ struct DmaK {
 
   __device__ __forceinline__ void issue(int64_t k0, uint8_t* lds_codes, uint8_t* lds_scales) const {
 #pragma unroll
-    for (int q = 0; q < CPW; q++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, lds_codes + (wave * CPW + q) * 1024, 16,
-                                               coff[q], (int)(k0 / 2), 0, 0);
-    if (wave >= SW0 && wave < SW0 + SWN)  // wave-uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, lds_scales + (wave - SW0) * 256, 4, soff,
-                                               (int)(k0 / 16), 0, 0);
+    for (int q = 0; q < Plan::CPW; q++)
+      if (Plan::code_on(wave, q))  // wave-uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, lds_codes + (wave + q * C::NW) * 1024, 16,
+                                                 coff[q], (int)(k0 / 2), 0, 0);
+#pragma unroll
+    for (int q = 0; q < Plan::SPW; q++) {
+      const int j = Plan::scale_chunk(wave, q);
+      if (j < kScaleChunks)  // wave-uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, lds_scales + j * 256, 4, soff[q],
+                                                 (int)(k0 / 16), 0, 0);
+    }
   }
 };
 
-// ---- staging: MN-major operands by LDS DMA, transposed when read ----------------------------
-// The stage of an operand stored [K][W] is 64 stored rows (k) of the tile's
-// 256 columns (mn): 64 x 128 code bytes.  16-byte unit c (32 columns) of
-// stage row k lands in LDS unit 8k + (c ^ ((k >> 1) & 7)): the 16 rows that
-// one transposing read gathers (below) then sit in 16 different 16-byte
-// slots of a 256-byte span.  Columns past the operand's edge re-read its last
-// valid unit (W is a multiple of 32), which only feeds unstored outputs.
+// ---- staging: MN-major operands, transposed when read ------------------------------------------
+// The stage of an operand stored [K][W] is BK stored rows (k) of the tile's
+// ROWS columns (mn): rows of U = ROWS/32 16-byte units.  Unit c of stage row
+// k lands in LDS unit U*k + mn_swz(c, k).  A transposing read (below)
+// gathers the same unit of 16 consecutive rows; the swizzle puts them in 16
+// different 16-byte slots of a 256-byte span (U = 8: XOR with bits 1..3 of
+// k; U = 6: 6k already spreads 8 rows, XOR with bit 3 of k separates the
+// two octets).  Columns past the operand's edge re-read its last valid unit
+// (W is a multiple of 32), which only feeds unstored outputs.
 // Scales of stage row kb (k-block k0/16 + kb) go to LDS bytes 256*kb: COL
-// blocks as the tile's 256 bytes of that row; 2D blocks as the 4-byte words
-// holding the row's (up to) 16 bytes for the tile, read from the aligned word
-// at or below their start, so a reader adds that start's offset (0 or 2).
-template <int ROWS, int NW, int SW0, int SWN>
+// blocks as the tile's ROWS bytes of that row; 2D blocks as the 4-byte words
+// holding the row's (up to) ROWS/16 bytes for the tile, read from the aligned
+// word at or below their start, so a reader adds that start's offset (0 or
+// 2).
+template <int U>
+__device__ __forceinline__ int mn_swz(int c, int k) {
+  static_assert(U == 8 || U == 6, "units per stage row");
+  return U == 8 ? c ^ ((k >> 1) & 7) : c ^ ((k >> 3) & 1);
+}
+
+template <class C, int ROWS, int W0>
 struct DmaMN {
-  static_assert(ROWS == 256, "a stage row of codes is 128 bytes, a scale row 256");
-  static constexpr int kCodeChunks = BK * ROWS / 2 / 1024;
-  static_assert(kCodeChunks % NW == 0, "code chunks must split over waves");
-  static_assert(SWN == BK / 16, "one scale row per scale wave");
-  static constexpr int CPW = kCodeChunks / NW;
-  uint32_t coff[CPW];
-  uint32_t soff;
+  static constexpr int U = ROWS / 32;  // 16-byte units per stage row
+  static constexpr int kCodeChunks = C::BK * U / 64;
+  static constexpr int kScaleChunks = C::SB;  // one per k-block row
+  static_assert(ROWS <= 256, "a scale row holds at most 256 bytes");
+  using Plan = DmaPlan<C::NW, kCodeChunks, kScaleChunks, W0>;
+  uint32_t coff[Plan::CPW];
+  uint32_t soff[Plan::SPW];
   uint32_t crow, srow;  // bytes per stored code row, per scale row
   __amdgpu_buffer_rsrc_t crsrc, srsrc;
   int wave;
 
-  __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
+  __device__ __forceinline__ int count(int w) const { return Plan::count(w); }
+
+  __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t, int64_t K,
                                        int lane, int wv) {
     wave = wv;
     const int64_t W = op.mn_total;
     const int64_t last_unit = W / 32 - 1;
     crow = (uint32_t)(W / 2);
 #pragma unroll
-    for (int q = 0; q < CPW; q++) {
-      const int unit = 64 * (wave * CPW + q) + lane;  // LDS 16-byte unit of the stage
-      const int k = unit >> 3;
-      const int c = (unit & 7) ^ ((k >> 1) & 7);
+    for (int q = 0; q < Plan::CPW; q++) {
+      const int unit = 64 * (wave + q * C::NW) + lane;  // LDS 16-byte unit of the stage
+      const int k = unit / U;
+      const int c = mn_swz<U>(unit % U, k);
       int64_t cg = mn0 / 32 + c;
       cg = cg < last_unit ? cg : last_unit;
       coff[q] = (uint32_t)(k * (W / 2) + 16 * cg);
     }
-    const int kb = wave - SW0;  // meaningful on scale waves only
-    if (op.block == kBlock2d) {
-      const int64_t w16 = W / 16;
-      const int64_t rel = kb * w16 + mn0 / 16;
-      const int64_t rel4 = rel & ~(int64_t)3;
-      const int64_t need = w16 - mn0 / 16 < 16 ? w16 - mn0 / 16 : 16;
-      const int nd = (int)((rel - rel4 + need + 3) / 4);
-      const int d = (lane & 7) < nd - 1 ? (lane & 7) : nd - 1;
-      soff = (uint32_t)(rel4 + 4 * d);
-      srow = (uint32_t)w16;
-    } else {
-      int64_t col = mn0 + 4 * lane;
-      col = col < W - 4 ? col : W - 4;
-      soff = (uint32_t)(kb * W + col);
-      srow = (uint32_t)W;
+    const bool two_d = op.block == kBlock2d;
+    srow = (uint32_t)(two_d ? W / 16 : W);
+#pragma unroll
+    for (int q = 0; q < Plan::SPW; q++) {
+      const int kb = Plan::scale_chunk(wave, q);  // meaningful if < kScaleChunks
+      if (two_d) {
+        const int64_t w16 = W / 16;
+        const int64_t rel = kb * w16 + mn0 / 16;
+        const int64_t rel4 = rel & ~(int64_t)3;
+        const int64_t need = w16 - mn0 / 16 < ROWS / 16 ? w16 - mn0 / 16 : ROWS / 16;
+        const int nd = (int)((rel - rel4 + need + 3) / 4);
+        const int d = (lane & 7) < nd - 1 ? (lane & 7) : nd - 1;
+        soff[q] = (uint32_t)(rel4 + 4 * d);
+      } else {
+        int64_t col = mn0 + 4 * lane;
+        col = col < W - 4 ? col : W - 4;
+        soff[q] = (uint32_t)(kb * W + col);
+      }
     }
-    (void)mn_lim;
     crsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.codes), 0,
                                               (int)(K * (W / 2)), kBufferFlags);
     srsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.scales), 0,
@@ -206,16 +283,19 @@ struct DmaMN {
 
   __device__ __forceinline__ void issue(int64_t k0, uint8_t* lds_codes, uint8_t* lds_scales) const {
 #pragma unroll
-    for (int q = 0; q < CPW; q++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, lds_codes + (wave * CPW + q) * 1024, 16,
-                                               coff[q], (int)(k0 * crow), 0, 0);
-    if (wave >= SW0 && wave < SW0 + SWN)  // wave-uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, lds_scales + (wave - SW0) * 256, 4, soff,
-                                               (int)((k0 / 16) * srow), 0, 0);
+    for (int q = 0; q < Plan::CPW; q++)
+      if (Plan::code_on(wave, q))  // wave-uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crsrc, lds_codes + (wave + q * C::NW) * 1024, 16,
+                                                 coff[q], (int)(k0 * crow), 0, 0);
+#pragma unroll
+    for (int q = 0; q < Plan::SPW; q++) {
+      const int kb = Plan::scale_chunk(wave, q);
+      if (kb < kScaleChunks)  // wave-uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, lds_scales + kb * 256, 4, soff[q],
+                                                 (int)((k0 / 16) * srow), 0, 0);
+    }
   }
 };
-
-typedef int v2i32 __attribute__((ext_vector_type(2)));
 
 // ds_read_b64_tr_b4: in each group of 16 lanes, lane i receives nibble i of
 // the 8-byte rows addressed by lanes 0..15 of its group, in lane order.
@@ -224,6 +304,7 @@ __device__ __forceinline__ v2i32 lds_read_tr4(const uint8_t* p) {
       (__attribute__((address_space(3))) v2i32*)(p));
 }
 
+// ---- decode -----------------------------------------------------------------------------------
 // Decode 8 nibbles (one dword) scaled by the packed pair d = (d, d).
 __device__ __forceinline__ half8 decode8(uint32_t q, half2 d) {
   half2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * d;
@@ -252,120 +333,121 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int s) {
   return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
 }
 
-// Decode schedule within a 16-k step of TM x TN MFMAs (t = i*TN + j): B
-// fragment j (double-buffered) is decoded after MFMA `b_slot`, A fragment i
-// (single-buffered) once row i's MFMAs have issued.  In the last step the
-// fragments come from LDS reads issued at the step's start, so decodes wait
-// for two MFMAs first.
-template <int TM, int TN>
-__device__ __forceinline__ constexpr int b_slot(int s, int j) {
-  return s < 3 ? j : (2 + j < TM * TN ? 2 + j : TM * TN - 1);
-}
-template <int TM, int TN>
-__device__ __forceinline__ constexpr int a_slot(int s, int i) {
-  return s < 3 || i * TN + TN - 1 >= 2 ? i * TN + TN - 1 : 2;
-}
-
-// Per-operand staging, both layouts by LDS DMA.  OPB selects operand B's
-// share of the scale waves (A uses the first half, B the second).  A
-// fragment is what one lane multiplies in one 64-k stage: 32 nibbles of its
-// row (row l%32 of the fragment, k = 32*(l/32) .. +32 of the stage; dword s
-// holds the k of 16-k step s) and the two scale bytes of those k.
-template <bool KMAJOR, int ROWS, class C, int OPB>
+// ---- per-operand staging ------------------------------------------------------------------------
+// A fragment half is what one lane multiplies in one 64-k half of a stage:
+// 32 nibbles of its row (row l%32 of the fragment, k = 32*(l/32) .. +32 of
+// the half; dword s holds the k of 16-k step s) and the two scale bytes of
+// those k.  W0 places the operand's scale chunks on the waves (B after A's).
+template <bool KMAJOR, int ROWS, class C, int W0, int NF>
 struct Staging;
 
-template <int ROWS, class C, int OPB>
-struct Staging<true, ROWS, C, OPB> {
-  static constexpr int kSW = ROWS * 4 / 256;  // scale waves
-  static_assert(kSW <= C::NW, "one scale chunk per wave at most");
-  // Both operands' scale chunks on disjoint waves when there are enough
-  // waves, else on the same ones.
-  static constexpr int kSW0 = (2 * kSW <= C::NW) ? OPB * kSW : 0;
-  DmaK<ROWS, C::NW, kSW0, kSW> d;
-  static constexpr int kCodeDma = DmaK<ROWS, C::NW, kSW0, kSW>::CPW;
-  int code0, sc0;  // this lane's LDS offsets for fragment 0
-  __device__ __forceinline__ int scale_dma(int wave) const {
-    return wave >= kSW0 && wave < kSW0 + kSW ? 1 : 0;
-  }
+template <int ROWS, class C, int W0, int NF>
+struct Staging<true, ROWS, C, W0, NF> {
+  using Dma = DmaK<C, ROWS, W0>;
+  static constexpr int kScaleChunks = Dma::kScaleChunks;
+  Dma d;
+  int code0[C::H];  // this lane's LDS code offsets for fragment 0, per half
+  int sc0;          // this lane's LDS scale offset for fragment 0, half 0
+  __device__ __forceinline__ int dma_count(int wave) const { return d.count(wave); }
   // row0: first row (of the tile) of this wave's fragments; fragment i
-  // starts 32*i rows further.
+  // starts 32*i rows further (which keeps the row swizzle).
   __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
                                        int tid, int row0) {
     d.init(op, mn0, mn_lim, K, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6));
     const int lane = tid & 63;
-    code0 = code_addr(row0 + (lane & 31), lane >> 5);  // rows step by 32: same swizzle
-    sc0 = 4 * (row0 + (lane & 31)) + 2 * (lane >> 5);
+    const int row = row0 + (lane & 31);
+#pragma unroll
+    for (int hs = 0; hs < C::H; hs++)
+      code0[hs] = kmaj_code_addr<C::RB>(row, 2 * hs + (lane >> 5));
+    sc0 = C::SB * row + 2 * (lane >> 5);
   }
   __device__ __forceinline__ void load_dma(int64_t k0, uint8_t* codes, uint8_t* scales) {
     d.issue(k0, codes, scales);
   }
-  __device__ __forceinline__ void frag(const uint8_t* codes, const uint8_t* scales, int i,
+  __device__ __forceinline__ void frag(const uint8_t* codes, const uint8_t* scales, int i, int hs,
                                        uint4& q, uint32_t& sc) const {
-    q = *reinterpret_cast<const uint4*>(codes + code0 + i * 32 * 32);
-    sc = *reinterpret_cast<const uint16_t*>(scales + sc0 + i * 32 * 4);
+    q = *reinterpret_cast<const uint4*>(codes + code0[hs] + i * 32 * C::RB);
+    sc = *reinterpret_cast<const uint16_t*>(scales + sc0 + 4 * hs + i * 32 * C::SB);
   }
 };
 
-template <int ROWS, class C, int OPB>
-struct Staging<false, ROWS, C, OPB> {
-  static constexpr int kSW = BK / 16;  // scale waves: one per k-block row
-  static_assert(kSW <= C::NW, "one scale row per wave at most");
-  static constexpr int kSW0 = (2 * kSW <= C::NW) ? OPB * kSW : 0;
-  DmaMN<ROWS, C::NW, kSW0, kSW> d;
-  static constexpr int kCodeDma = DmaMN<ROWS, C::NW, kSW0, kSW>::CPW;
-  // Lane l (group g = l/16, j = l%16, half h = l/32) addresses, for read
-  // r = 0, 1, stage row k = 32h + 16r + j at the 8 bytes of columns
-  // [row0 + 32i + 16(g&1), +16): it receives the 16 k of its own column.
-  uint32_t tr_base[2];
-  int tr_c[2];
-  int sc_off[2], sc_step;
-  __device__ __forceinline__ int scale_dma(int wave) const {
-    return wave >= kSW0 && wave < kSW0 + kSW ? 1 : 0;
-  }
+template <int ROWS, class C, int W0, int NF>
+struct Staging<false, ROWS, C, W0, NF> {
+  using Dma = DmaMN<C, ROWS, W0>;
+  static constexpr int kScaleChunks = Dma::kScaleChunks;
+  static constexpr int U = ROWS / 32;
+  Dma d;
+  // Lane l (group g = l/16, half h = l/32) addresses, for stage half hs and
+  // read r = 0, 1, stage row k = 64hs + 32h + 16r + l%16 at the 8 bytes of
+  // columns [row0 + 32i + 16(g&1), +16) of fragment i: it receives the 16 k
+  // of its own column.  The row swizzle only depends on k mod 16, so hs and
+  // r only add constants.  The lane's scale bytes are those of k-blocks
+  // kb = 4hs + 2h + r of its column.
+  int col[NF];   // LDS offset of the tr-read row for hs = 0, r = 0
+  int scb;       // LDS offset of the scale byte for fragment 0, hs = 0, r = 0
+  int sc_step;   // from fragment i to i + 1 (wave-uniform)
+  int sc_d;      // from the r = 0 scale byte to the r = 1 byte (wave-uniform)
+  __device__ __forceinline__ int dma_count(int wave) const { return d.count(wave); }
   __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
                                        int tid, int row0) {
     d.init(op, mn0, mn_lim, K, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6));
     const int lane = tid & 63;
-    const int g = lane >> 4, j = lane & 15, h = lane >> 5;
-    const int c0 = row0 / 32;  // a multiple of the fragment count: c0 + i == c0 ^ i
+    const int g = lane >> 4, h = lane >> 5;
+    const int krow0 = 32 * h + (lane & 15);
+    const int sw = mn_swz<U>(0, krow0);
     const bool two_d = op.block == kBlock2d;
     const int64_t w16 = op.mn_total / 16;
-#pragma unroll
-    for (int r = 0; r < 2; r++) {
-      const int k = 32 * h + 16 * r + j;
-      tr_base[r] = 128 * k + 8 * (g & 1);
-      tr_c[r] = c0 ^ ((k >> 1) & 7);
-      const int kb = 2 * h + r;
-      sc_off[r] = two_d ? 256 * kb + (int)((kb * w16 + mn0 / 16) & 3) + (row0 + (lane & 31)) / 16
-                        : 256 * kb + row0 + (lane & 31);
-    }
+    // 2D scale rows start 2 bytes past a 4-byte word on odd k-block rows when
+    // w16 = 2 mod 4 (every other start offset is 0; see the DMA).
+    const int m1 = two_d && (w16 & 3) == 2 ? 2 : 0;
+    sc_d = 256 + m1;
     sc_step = two_d ? 2 : 32;
+    scb = 256 * 2 * h + (two_d ? (row0 + (lane & 31)) / 16 : row0 + (lane & 31));
+#pragma unroll
+    for (int i = 0; i < NF; i++) col[i] = 16 * (U * krow0 + ((row0 / 32 + i) ^ sw)) + 8 * (g & 1);
   }
   __device__ __forceinline__ void load_dma(int64_t k0, uint8_t* codes, uint8_t* scales) {
     d.issue(k0, codes, scales);
   }
-  __device__ __forceinline__ void frag(const uint8_t* codes, const uint8_t* scales, int i,
+  __device__ __forceinline__ void frag(const uint8_t* codes, const uint8_t* scales, int i, int hs,
                                        uint4& q, uint32_t& sc) const {
-    const v2i32 lo = lds_read_tr4(codes + tr_base[0] + 16 * (tr_c[0] ^ i));
-    const v2i32 hi = lds_read_tr4(codes + tr_base[1] + 16 * (tr_c[1] ^ i));
+    const uint8_t* p = codes + col[i];
+    const v2i32 lo = lds_read_tr4(p + 16 * U * 64 * hs);
+    const v2i32 hi = lds_read_tr4(p + 16 * U * (64 * hs + 16));
     q = uint4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
-    sc = (uint32_t)scales[sc_off[0] + i * sc_step] |
-         ((uint32_t)scales[sc_off[1] + i * sc_step] << 8);
+    const uint8_t* ps = scales + scb + i * sc_step + 1024 * hs;
+    sc = (uint32_t)ps[0] | ((uint32_t)ps[sc_d] << 8);
   }
 };
+
+// Decode schedule within a 16-k step of TM x TN MFMAs (t = i*TN + j): B
+// fragment j (double-buffered) is decoded after MFMA `b_slot`, A fragment i
+// (single-buffered) once row i's MFMAs have issued.  In a stage's last step
+// the fragments come from LDS reads issued at the step's start, so decodes
+// wait for two MFMAs first.
+template <int TM, int TN>
+__device__ __forceinline__ constexpr int b_slot(bool last, int j) {
+  return !last ? j : (2 + j < TM * TN ? 2 + j : TM * TN - 1);
+}
+template <int TM, int TN>
+__device__ __forceinline__ constexpr int a_slot(bool last, int i) {
+  return !last || i * TN + TN - 1 >= 2 ? i * TN + TN - 1 : 2;
+}
 
 // One output tile: C[m0 : m0+BM) x [n0 : n0+BN) restricted to rows < m_lim,
 // cols < N, using lds (kLds bytes).
 //
-// Software pipeline over 64-k stages (stage s lives in LDS buffer s % 4):
-//  * iteration kt issues stage kt+3's LDS DMA during its last step;
-//  * its four 16-k steps run TM x TN MFMAs each; between MFMAs it decodes
-//    the fragments of the following step -- for the last step, those of step
-//    0 of stage kt+1, read from LDS at that step's start;
+// Software pipeline over stages of BK k (stage s lives in LDS buffer s % 3):
+//  * a stage's fragments (both halves) are read from LDS into registers in
+//    the last step of the stage before, so stage kt's buffer is idle while kt
+//    is multiplied;
+//  * iteration kt runs the stage's STEPS 16-k steps of TM x TN MFMAs; between
+//    MFMAs it decodes the fragments of the following step;
+//  * in its last step it reads stage kt+1's fragments and then issues stage
+//    kt+3's LDS DMA into stage kt's buffer (every wave read it before the
+//    previous barrier);
 //  * it ends with one barrier, after waiting for this wave's transfers of
-//    stage kt+2 (issued an iteration ago): stage kt+2 is read in the next
-//    iteration, and the buffer stage kt+3 overwrites (stage kt-1's) was last
-//    read two iterations ago.
+//    stage kt+2 (issued an iteration ago), which the next iteration reads.
 // Decoded fragments: B double-buffered (every row uses them), A single-
 // buffered, fragment i of the next step decoded once row i's MFMAs issued.
 template <class C, bool AK, bool BKM>
@@ -386,15 +468,16 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  Staging<AK, C::BM, C, 0> sa;
-  Staging<BKM, C::BN, C, 1> sb;
+  using SA = Staging<AK, C::BM, C, 0, C::TM>;
+  constexpr int kBW0 = SA::kScaleChunks % C::NW;  // B's scale chunks after A's
+  using SB = Staging<BKM, C::BN, C, kBW0, C::TN>;
+  SA sa;
+  SB sb;
   sa.init(A, m0, m_lim, K, tid, wm * (C::BM / C::WM));
   sb.init(B, n0, N, K, tid, wn * (C::BN / C::WN));
-  // DMA instructions this wave issues per stage (wave-uniform): the code
-  // chunks plus one scale chunk per operand whose scales this wave moves.
-  constexpr int kCodeDma = Staging<AK, C::BM, C, 0>::kCodeDma + Staging<BKM, C::BN, C, 1>::kCodeDma;
-  const int n_scale_dma = sa.scale_dma(wave) + sb.scale_dma(wave);
-  const int64_t KT = K / BK;
+  // DMA instructions this wave issues per stage (wave-uniform).
+  const int n_dma = sa.dma_count(wave) + sb.dma_count(wave);
+  const int64_t KT = K / C::BK;
 
   constexpr int oAS = C::kACodes, oBC = C::kACodes + C::kAScales,
                 oBS = C::kACodes + C::kAScales + C::kBCodes;
@@ -405,52 +488,62 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
     sb.load_dma(k0, dst + oBC, dst + oBS);
   };
 
-  uint4 aq[C::TM], bq[C::TN];
-  half2 as[C::TM], bs[C::TN];
+  uint4 aq[C::H][C::TM], bq[C::H][C::TN];
+  half2 as[C::H][C::TM], bs[C::H][C::TN];
   auto read_frags = [&](const uint8_t* st) {
-    uint32_t ar[C::TM], br[C::TN];
+    uint32_t ar[C::H][C::TM], br[C::H][C::TN];
 #pragma unroll
-    for (int i = 0; i < C::TM; i++) sa.frag(st, st + oAS, i, aq[i], ar[i]);
+    for (int hs = 0; hs < C::H; hs++) {
 #pragma unroll
-    for (int j = 0; j < C::TN; j++) sb.frag(st + oBC, st + oBS, j, bq[j], br[j]);
+      for (int i = 0; i < C::TM; i++) sa.frag(st, st + oAS, i, hs, aq[hs][i], ar[hs][i]);
 #pragma unroll
-    for (int i = 0; i < C::TM; i++) as[i] = scale_pair(ar[i]);
+      for (int j = 0; j < C::TN; j++) sb.frag(st + oBC, st + oBS, j, hs, bq[hs][j], br[hs][j]);
+    }
 #pragma unroll
-    for (int j = 0; j < C::TN; j++) bs[j] = scale_pair(br[j]);
+    for (int hs = 0; hs < C::H; hs++) {
+#pragma unroll
+      for (int i = 0; i < C::TM; i++) as[hs][i] = scale_pair(ar[hs][i]);
+#pragma unroll
+      for (int j = 0; j < C::TN; j++) bs[hs][j] = scale_pair(br[hs][j]);
+    }
   };
 
-  // Prologue: stages 0, 1 and 2 in LDS, step 0 of stage 0 decoded.
-  auto stage_k = [&](int64_t st) { return (st < KT ? st : KT - 1) * BK; };
+  // Prologue: stages 0, 1, 2 issued; stage 0 read and its step 0 decoded.
+  auto stage_k = [&](int64_t st) { return (st < KT ? st : KT - 1) * C::BK; };
 #pragma unroll
-  for (int st = 0; st < kStages - 1; st++) load_dma(stage_k(st), buffer(st));
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
+  for (int st = 0; st < kStages; st++) load_dma(stage_k(st), buffer(st));
+  wait_vm_lgkm0_upto(2 * n_dma);  // this wave's stage 0 transfers landed
+  __builtin_amdgcn_s_barrier();   // ... and every wave's
   read_frags(buffer(0));
   half8 af[C::TM], bf[2][C::TN];
 #pragma unroll
-  for (int i = 0; i < C::TM; i++) af[i] = decode8(aq[i].x, splat(as[i], 0));
+  for (int i = 0; i < C::TM; i++) af[i] = decode8(aq[0][i].x, splat(as[0][i], 0));
 #pragma unroll
-  for (int j = 0; j < C::TN; j++) bf[0][j] = decode8(bq[j].x, splat(bs[j], 0));
-  int b_next = 1, b_load = kStages - 1;  // buffers of stages kt+1 and kt+3
+  for (int j = 0; j < C::TN; j++) bf[0][j] = decode8(bq[0][j].x, splat(bs[0][j], 0));
+  wait_vm_lgkm0_upto(n_dma);  // stage 1 (stage 2 may still be in flight)
+  __builtin_amdgcn_s_barrier();
+  int b_cur = 0;  // buffer of stage kt
 
   for (int64_t kt = 0; kt < KT; kt++) {
-    // Stage kt+3 (clamped: near the end the last stage is reloaded into an
+    // Stage kt+3 (clamped: near the end the last stage is reloaded into the
     // idle buffer, which keeps the loop free of branches).
-    const int64_t kl = stage_k(kt + kStages - 1);
-    uint8_t* dst = buffer(b_load);
+    const int64_t kl = stage_k(kt + kStages);
+    uint8_t* dst = buffer(b_cur);
+    const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
 
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
+    for (int s = 0; s < C::STEPS; s++) {
+      const bool last = s == C::STEPS - 1;
       const int cur = s & 1, nxt = cur ^ 1;
       // Step s+1 of this stage, or step 0 of the next stage (read now).
-      const int ns = s < 3 ? s + 1 : 0;
-      if (s == 3) {
+      const int ns = last ? 0 : s + 1;
+      const int nh = ns / 4, nd = ns % 4;
+      if (last) {
         // The compiler may make these LDS reads wait for every outstanding
         // LDS DMA; issuing stage kt+3's DMA only after them keeps that wait
-        // to transfers issued an iteration ago or earlier.
+        // to transfers issued an iteration ago.
         read_frags(buffer(b_next));
         load_dma(kl, dst);
-        if (C::kFence) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < C::TM; i++) {
@@ -459,34 +552,22 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
           acc[i][j] =
               __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[cur][j], acc[i][j], 0, 0, 0);
           const int t = i * C::TN + j;
-          bool any = false;
 #pragma unroll
           for (int jj = 0; jj < C::TN; jj++)
-            if (b_slot<C::TM, C::TN>(s, jj) == t) {
-              bf[nxt][jj] = decode8(pick(bq[jj], ns), splat(bs[jj], ns >= 2));
-              any = true;
-            }
+            if (b_slot<C::TM, C::TN>(last, jj) == t)
+              bf[nxt][jj] = decode8(pick(bq[nh][jj], nd), splat(bs[nh][jj], nd >= 2));
 #pragma unroll
           for (int ii = 0; ii < C::TM; ii++)
-            if (a_slot<C::TM, C::TN>(s, ii) == t) {
-              af[ii] = decode8(pick(aq[ii], ns), splat(as[ii], ns >= 2));
-              any = true;
-            }
-          if (C::kFence && any) __builtin_amdgcn_sched_barrier(0);
+            if (a_slot<C::TM, C::TN>(last, ii) == t)
+              af[ii] = decode8(pick(aq[nh][ii], nd), splat(as[nh][ii], nd >= 2));
         }
       }
     }
-    b_next = b_next == kStages - 1 ? 0 : b_next + 1;
-    b_load = b_load == kStages - 1 ? 0 : b_load + 1;
+    b_cur = b_next;
     // Stage kt+2, read in the next iteration, complete: this wave's DMA for
     // it was issued an iteration ago, so only this iteration's transfers may
     // still be in flight; then every wave's (barrier).
-    if (n_scale_dma == 0)
-      wait_vm_lgkm0<kCodeDma>();
-    else if (n_scale_dma == 1)
-      wait_vm_lgkm0<kCodeDma + 1>();
-    else
-      wait_vm_lgkm0<kCodeDma + 2>();
+    wait_vm_lgkm0_upto(n_dma);
     __builtin_amdgcn_s_barrier();
   }
   // No transfer may still target this workgroup's LDS when it is reused.
@@ -614,9 +695,6 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   }
 }
 
-using Dense = Cfg<256, 256, 2, 4, false>;
-using Grouped = Cfg<256, 256, 2, 4, false>;
-
 template <class C, bool AK, bool BKM>
 hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
@@ -631,36 +709,74 @@ hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (a.a_kmajor && a.b_kmajor) return launch_dense<Dense, true, true>(a, st);
-  if (a.a_kmajor && !a.b_kmajor) return launch_dense<Dense, true, false>(a, st);
-  return launch_dense<Dense, false, false>(a, st);
-}
-
-hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st) {
-  if (a.total_rows == 0 || a.N == 0 || a.groups == 0) return hipSuccess;
-  using C = Grouped;
-  int dev = 0, cus = 0;
+// Compute units of the current device (one workgroup of these tiles runs
+// per CU).
+hipError_t device_cus(int* cus) {
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && *cus <= 0) *cus = 256;
+  return e;
+}
+
+template <class C>
+hipError_t launch_layout(const GemmArgs& a, hipStream_t st) {
+  if (a.a_kmajor && a.b_kmajor) return launch_dense<C, true, true>(a, st);
+  if (a.a_kmajor && !a.b_kmajor) return launch_dense<C, true, false>(a, st);
+  return launch_dense<C, false, false>(a, st);
+}
+
+template <int BK>
+hipError_t launch_depth(const GemmArgs& a, int cus, hipStream_t st) {
+  auto cost = [&](int64_t bm, int64_t bn) {
+    const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    return ((tiles + cus - 1) / cus) * bm * bn;
+  };
+  if (cost(192, 256) < cost(256, 256)) return launch_layout<Cfg<192, 256, 2, 4, BK>>(a, st);
+  return launch_layout<Cfg<256, 256, 2, 4, BK>>(a, st);
+}
+
+template <class C>
+hipError_t launch_grouped(const GroupedArgs& a, int cus, hipStream_t st) {
   const int64_t ntn = (a.N + C::BN - 1) / C::BN;
   const int64_t max_tiles = ((a.total_rows + C::BM - 1) / C::BM + a.groups) * ntn;
-  int64_t grid = cus > 0 ? cus : 256;
+  int64_t grid = cus;
   if (grid > max_tiles) grid = max_tiles;
   const size_t smem = C::kLds + sizeof(int32_t) * (size_t)(a.groups + 1);
   auto kern = grouped_gemm_kernel<C>;
   if (smem > 65536) {
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)smem);
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
   kern<<<(unsigned)grid, C::NT, smem, st>>>(a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Stage depth: 128 k when K allows (longer row segments per transfer and
+// half the barriers), else 64.  Tile: both tile shapes run at about the same
+// rate per output, so take the one whose last round of workgroups leaves
+// the fewest CUs idle (cost = rounds of tiles times tile area).  Every output
+// is the same sum in the same order whatever the choice.
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  if (a.M == 0 || a.N == 0) return hipSuccess;
+  int cus = 256;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  if (a.K % 128 == 0) return launch_depth<128>(a, cus, st);
+  return launch_depth<64>(a, cus, st);
+}
+
+hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st) {
+  if (a.total_rows == 0 || a.N == 0 || a.groups == 0) return hipSuccess;
+  int cus = 256;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  if (a.K % 128 == 0) return launch_grouped<Cfg<256, 256, 2, 4, 128>>(a, cus, st);
+  return launch_grouped<Cfg<256, 256, 2, 4, 64>>(a, cus, st);
 }
 
 }  // namespace nvfp4

@@ -183,6 +183,44 @@ def test_full_ultra_dgrad():
 
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_gemm_large_tiles_full(layout):
+    """4096 x 4096 fills exactly one round of 256 x 256 tiles on 256 CUs, so
+    the launch takes the 256-row tile; every output is checked."""
+    M, N, K = 4096, 4096, 128
+    qa, qb = _operands(layout, M, N, K, seed=17, sr=layout != "NT",
+                       mask=0x0F0F if layout == "TN" else -1)
+    _full_check(layout, qa, qb, M, N, K, torch.bfloat16)
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN"])
+def test_gemm_tile_shape_does_not_change_bits(layout):
+    """C for A's first 768 rows (192-row tiles) equals those rows of the
+    4096 x 4096 product (256-row tiles) bit for bit: each output is the same
+    sum in the same order whatever the tile shape."""
+    M, N, K = 4096, 4096, 256
+    qa, qb = _operands(layout, M, N, K, seed=23, sr=layout != "NT")
+    full = nv.gemm(layout[0], layout[1], qa, qb, out_dtype=torch.float32)
+    sub = nv.QTensor(qa.codes[:768], qa.scales[:768], qa.global_dec, qa.amax, 768, K, "row")
+    part = nv.gemm(layout[0], layout[1], sub, qb, out_dtype=torch.float32)
+    assert torch.equal(part, full[:768])
+
+
+def test_full_ultra_wgrad():
+    """dW = dY^T X at the Ultra width (8192 tokens, 8192 x 8192), COL blocks
+    with the transform on both operands and SR on dY (256-row tiles)."""
+    w = synth.WORKLOADS["ultra"]
+    dev = device()
+    T, Mo, Ni = w["K"], w["M"], w["N"]
+    mask = synth.rht_mask(6)
+    dy = synth.to_bf16(synth.laplace((T, Mo), w["dy_b"], w["dy_seed"])).to(dev)
+    x = synth.to_bf16(synth.normal((T, Ni), 1.0, w["x_seed"])).to(dev)
+    qa = nv.quantize_1d(dy, "col", "sr", nv.Philox(w["philox_seed"]), mask)
+    qb = nv.quantize_1d(x, "col", "rne", None, mask)
+    c = nv.gemm("T", "N", qa, qb, out_dtype=torch.float32)
+    _sampled_check("TN", qa, qb, Mo, Ni, T, c)
+
+
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 def test_gemm_deterministic_long_k(layout):
     """Repeated runs with many pipeline stages give identical bits (a race
     between the LDS stage buffers would show up as run-to-run differences),
