@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -37,8 +39,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
-
-constexpr int kStages = 3;  // LDS ring depth
 
 template <int BM_, int BN_, int WM_, int WN_, int BK_>
 struct Cfg {
@@ -56,8 +56,8 @@ struct Cfg {
   // Scales: SB bytes per row (K-major) or SB rows of 256 bytes (MN-major).
   static constexpr int kACodes = BM * RB, kAScales = BM * SB > SB * 256 ? BM * SB : SB * 256;
   static constexpr int kBCodes = BN * RB, kBScales = BN * SB > SB * 256 ? BN * SB : SB * 256;
-  static constexpr int kStage = kACodes + kAScales + kBCodes + kBScales;
-  static constexpr int kLds = kStages * kStage;
+  static constexpr int kStage = kACodes + kAScales + kBCodes + kBScales;  // one raw stage
+  static constexpr int kA16 = BM * 128;  // A of one 64-k half, decoded to fp16
 };
 
 // Operand view for one tile: base pointers and the strides of its stored
@@ -69,7 +69,8 @@ struct OpView {
   int block;
 };
 
-// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt not waited on).
+// s_waitcnt with vmcnt <= N and lgkmcnt == 0 (expcnt not waited on); N = 63
+// does not wait for vector memory.
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
@@ -420,156 +421,203 @@ struct Staging<false, ROWS, C, W0, NF> {
   }
 };
 
-// Decode schedule within a 16-k step of TM x TN MFMAs (t = i*TN + j): B
-// fragment j (double-buffered) is decoded after MFMA `b_slot`, A fragment i
-// (single-buffered) once row i's MFMAs have issued.  In a stage's last step
-// the fragments come from LDS reads issued at the step's start, so decodes
-// wait for two MFMAs first.
-template <int TM, int TN>
-__device__ __forceinline__ constexpr int b_slot(bool last, int j) {
-  return !last ? j : (2 + j < TM * TN ? 2 + j : TM * TN - 1);
-}
-template <int TM, int TN>
-__device__ __forceinline__ constexpr int a_slot(bool last, int i) {
-  return !last || i * TN + TN - 1 >= 2 ? i * TN + TN - 1 : 2;
+// LDS buffers of one workgroup: two raw stages (codes and scale bytes as
+// staged by LDS DMA) and two fp16 images of A, each one 64-k half.  They are
+// separate variables so that the compiler can tell a read of one buffer from
+// an LDS DMA into another.
+struct TileLds {
+  uint8_t* raw[2];
+  uint8_t* a16[2];
+};
+
+// fp16 image of A for one 64-k half: row r holds 64 halves as 8 units of 16
+// bytes (unit v = k 8v .. 8v+7); unit v sits in slot v ^ ((r >> 1) & 7), so
+// the 16 consecutive rows a fragment read or write touches at one unit fall
+// in 16 distinct slots of a 256-byte bank window.
+__device__ __forceinline__ int a16_addr(int row, int unit) {
+  return row * 128 + 16 * (unit ^ ((row >> 1) & 7));
 }
 
 // One output tile: C[m0 : m0+BM) x [n0 : n0+BN) restricted to rows < m_lim,
-// cols < N, using lds (kLds bytes).
+// cols < N.
 //
-// Software pipeline over stages of BK k (stage s lives in LDS buffer s % 3):
-//  * a stage's fragments (both halves) are read from LDS into registers in
-//    the last step of the stage before, so stage kt's buffer is idle while kt
-//    is multiplied;
-//  * iteration kt runs the stage's STEPS 16-k steps of TM x TN MFMAs; between
-//    MFMAs it decodes the fragments of the following step;
-//  * in its last step it reads stage kt+1's fragments and then issues stage
-//    kt+3's LDS DMA into stage kt's buffer (every wave read it before the
-//    previous barrier);
-//  * it ends with one barrier, after waiting for this wave's transfers of
-//    stage kt+2 (issued an iteration ago), which the next iteration reads.
-// Decoded fragments: B double-buffered (every row uses them), A single-
-// buffered, fragment i of the next step decoded once row i's MFMAs issued.
+// Work is split in phases of 64 k (H = BK/64 phases per stage).  In phase p:
+//  * every wave multiplies its 128 x 64 (or 96 x 64) share of the tile in
+//    4 steps of 16 k: A fragments come ready-made from the fp16 image a16[p%2]
+//    (read one step ahead); B fragments are decoded by the wave itself from
+//    registers, one step ahead;
+//  * every wave also decodes its 32 rows of A for phase p+1 (one fragment
+//    half: 32 nibbles and 2 scale bytes per lane, read from the raw stage)
+//    into a16[(p+1)%2], one 8-k dword per step -- so each A element is decoded
+//    once per workgroup instead of once per wave that multiplies it;
+//  * the last phase of a stage reads the next stage's B fragments (both
+//    halves) into registers;
+//  * a barrier ends the phase; a16[(p+1)%2] is then complete and a16[p%2]
+//    free.
+// Raw stage S is used during phases H*S - 1 .. H*S + H - 2 (its A decoded
+// for phases H*S .. H*S+H-1; its B read at the end of phase H*S - 1), so its
+// buffer is refilled with stage S+2 at the start of phase H*S + H - 1, and
+// the end of phase H*(S+1) + H - 2 waits for that transfer.
 template <class C, bool AK, bool BKM>
 __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int64_t m0,
                                           int64_t m_lim, int64_t n0, int64_t N, int64_t K,
                                           float gscale, void* Cout, bool c_bf16, int64_t ldc,
-                                          uint8_t* lds) {
+                                          const TileLds& L) {
+  constexpr int H = C::H, TM = C::TM, TN = C::TN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lrow = lane & 31, lhalf = lane >> 5;
+  const bool decodes_a = wave < C::BM / 32;  // wave-uniform: this wave owns 32 rows of A
 
-  f32x16 acc[C::TM][C::TN];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < C::TM; i++)
+  for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int j = 0; j < C::TN; j++)
+    for (int j = 0; j < TN; j++)
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-  using SA = Staging<AK, C::BM, C, 0, C::TM>;
+  using SA = Staging<AK, C::BM, C, 0, 1>;
   constexpr int kBW0 = SA::kScaleChunks % C::NW;  // B's scale chunks after A's
-  using SB = Staging<BKM, C::BN, C, kBW0, C::TN>;
+  using SB = Staging<BKM, C::BN, C, kBW0, TN>;
   SA sa;
   SB sb;
-  sa.init(A, m0, m_lim, K, tid, wm * (C::BM / C::WM));
+  sa.init(A, m0, m_lim, K, tid, 32 * wave);  // the rows this wave decodes
   sb.init(B, n0, N, K, tid, wn * (C::BN / C::WN));
-  // DMA instructions this wave issues per stage (wave-uniform).
-  const int n_dma = sa.dma_count(wave) + sb.dma_count(wave);
   const int64_t KT = K / C::BK;
 
   constexpr int oAS = C::kACodes, oBC = C::kACodes + C::kAScales,
                 oBS = C::kACodes + C::kAScales + C::kBCodes;
 
-  auto buffer = [&](int idx) { return lds + idx * C::kStage; };
-  auto load_dma = [&](int64_t k0, uint8_t* dst) {
+  // A16 offsets: fragment reads (row wm*BM/WM + 32i + lrow, unit 4*lhalf + nd)
+  // and this wave's decode writes (row 32*wave + lrow, same units); the slot
+  // swizzle only depends on lrow.
+  const int a_row0 = wm * (C::BM / C::WM);
+  int a16_rd[4];
+#pragma unroll
+  for (int nd = 0; nd < 4; nd++) a16_rd[nd] = a16_addr(a_row0 + lrow, 4 * lhalf + nd);
+  const int a16_wr_delta = 128 * (32 * wave - a_row0);  // wave-uniform
+
+  auto load_dma = [&](int64_t st, uint8_t* dst) {
+    const int64_t k0 = st * C::BK;
     sa.load_dma(k0, dst, dst + oAS);
     sb.load_dma(k0, dst + oBC, dst + oBS);
   };
 
-  uint4 aq[C::H][C::TM], bq[C::H][C::TN];
-  half2 as[C::H][C::TM], bs[C::H][C::TN];
-  auto read_frags = [&](const uint8_t* st) {
-    uint32_t ar[C::H][C::TM], br[C::H][C::TN];
+  uint4 bq[H][TN];
+  half2 bs[H][TN];
+  auto read_b = [&](const uint8_t* st) {
+    uint32_t br[H][TN];
 #pragma unroll
-    for (int hs = 0; hs < C::H; hs++) {
+    for (int hs = 0; hs < H; hs++)
 #pragma unroll
-      for (int i = 0; i < C::TM; i++) sa.frag(st, st + oAS, i, hs, aq[hs][i], ar[hs][i]);
+      for (int j = 0; j < TN; j++) sb.frag(st + oBC, st + oBS, j, hs, bq[hs][j], br[hs][j]);
 #pragma unroll
-      for (int j = 0; j < C::TN; j++) sb.frag(st + oBC, st + oBS, j, hs, bq[hs][j], br[hs][j]);
-    }
+    for (int hs = 0; hs < H; hs++)
 #pragma unroll
-    for (int hs = 0; hs < C::H; hs++) {
+      for (int j = 0; j < TN; j++) bs[hs][j] = scale_pair(br[hs][j]);
+  };
+
+  // This wave's raw A for one half: 32 nibbles and the scale pair.
+  uint4 dq;
+  half2 ds;
+  auto read_a = [&](const uint8_t* st, int hs) {
+    uint32_t sc;
+    sa.frag(st, st + oAS, 0, hs, dq, sc);
+    ds = scale_pair(sc);
+  };
+  auto decode_a = [&](uint8_t* a16, int nd) {
+    const half8 v = decode8(pick(dq, nd), splat(ds, nd >= 2));
+    *reinterpret_cast<half8*>(a16 + a16_rd[nd] + a16_wr_delta) = v;
+  };
+
+  half8 af[2][TM], bf[2][TN];
+  auto read_af = [&](const uint8_t* a16, int nd, int buf) {
 #pragma unroll
-      for (int i = 0; i < C::TM; i++) as[hs][i] = scale_pair(ar[hs][i]);
+    for (int i = 0; i < TM; i++)
+      af[buf][i] = *reinterpret_cast<const half8*>(a16 + a16_rd[nd] + i * 32 * 128);
+  };
+
+  // Prologue: stages 0 and 1 in LDS, phase 0's A image, stage 0's B.
+  load_dma(0, L.raw[0]);
+  if (KT > 1) load_dma(1, L.raw[1]);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  if (decodes_a) {
+    read_a(L.raw[0], 0);
 #pragma unroll
-      for (int j = 0; j < C::TN; j++) bs[hs][j] = scale_pair(br[hs][j]);
+    for (int nd = 0; nd < 4; nd++) decode_a(L.a16[0], nd);
+  }
+  read_b(L.raw[0]);
+  wait_vm_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
+  read_af(L.a16[0], 0, 0);
+#pragma unroll
+  for (int j = 0; j < TN; j++) bf[0][j] = decode8(bq[0][j].x, splat(bs[0][j], 0));
+
+  // One stage S whose raw buffer is raw[PAR] (the next stage's is raw[1-PAR]).
+  auto stage = [&](int64_t S, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    uint8_t* raw_cur = L.raw[PAR];
+    uint8_t* raw_nxt = L.raw[1 - PAR];
+#pragma unroll
+    for (int h = 0; h < H; h++) {
+      // Phase p = H*S + h uses a16[p%2] and fills a16[(p+1)%2].
+      const int ab = H == 2 ? h : PAR;  // (H*S + h) % 2 with S % 2 == PAR
+      uint8_t* a16_cur = L.a16[ab];
+      uint8_t* a16_nxt = L.a16[1 - ab];
+      if (h == H - 1 && S + 2 < KT) load_dma(S + 2, raw_cur);  // raw[PAR] is free
+      // A of phase p+1: the next half of this stage, or the first of the next.
+      if (decodes_a) read_a(h + 1 < H ? raw_cur : raw_nxt, h + 1 < H ? h + 1 : 0);
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        const int cur = s & 1, nxt = cur ^ 1;
+        const bool last_step = s == 3;
+        const bool stage_end = last_step && h == H - 1;  // next step is the next stage's
+        if (stage_end) read_b(raw_nxt);
+        // B fragment of the next step: dword (s+1) of this half, or dword 0
+        // of the next half (this stage's, or the next stage's just read).
+        const int nh = last_step ? (h + 1 < H ? h + 1 : 0) : h;
+        const int nd = last_step ? 0 : s + 1;
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+#pragma unroll
+          for (int j = 0; j < TN; j++) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j],
+                                                               acc[i][j], 0, 0, 0);
+            const int t = i * TN + j;
+            if (t == 0 && !last_step) read_af(a16_cur, s + 1, nxt);
+            // B decodes after MFMAs j (2 + j when the raw registers were
+            // just reloaded, to leave the LDS reads time to land).
+#pragma unroll
+            for (int jj = 0; jj < TN; jj++) {
+              const int slot = stage_end ? (2 + jj < TM * TN ? 2 + jj : TM * TN - 1) : jj;
+              if (slot == t) bf[nxt][jj] = decode8(pick(bq[nh][jj], nd), splat(bs[nh][jj], nd >= 2));
+            }
+            if (t == TM * TN - 1 && decodes_a) decode_a(a16_nxt, s);
+          }
+        }
+      }
+      // End of phase: A image of phase p+1 written, a16_cur read by all.
+      // The next phase reads raw stage S+1 (H = 2: from its start; H = 1:
+      // it is the stage after), whose transfer is this wave's only one in
+      // flight here.
+      if ((h + 2) % H == 0)
+        wait_vm_lgkm0<0>();
+      else
+        wait_vm_lgkm0<63>();
+      __builtin_amdgcn_s_barrier();
+      read_af(a16_nxt, 0, 0);
     }
   };
 
-  // Prologue: stages 0, 1, 2 issued; stage 0 read and its step 0 decoded.
-  auto stage_k = [&](int64_t st) { return (st < KT ? st : KT - 1) * C::BK; };
-#pragma unroll
-  for (int st = 0; st < kStages; st++) load_dma(stage_k(st), buffer(st));
-  wait_vm_lgkm0_upto(2 * n_dma);  // this wave's stage 0 transfers landed
-  __builtin_amdgcn_s_barrier();   // ... and every wave's
-  read_frags(buffer(0));
-  half8 af[C::TM], bf[2][C::TN];
-#pragma unroll
-  for (int i = 0; i < C::TM; i++) af[i] = decode8(aq[0][i].x, splat(as[0][i], 0));
-#pragma unroll
-  for (int j = 0; j < C::TN; j++) bf[0][j] = decode8(bq[0][j].x, splat(bs[0][j], 0));
-  wait_vm_lgkm0_upto(n_dma);  // stage 1 (stage 2 may still be in flight)
-  __builtin_amdgcn_s_barrier();
-  int b_cur = 0;  // buffer of stage kt
-
-  for (int64_t kt = 0; kt < KT; kt++) {
-    // Stage kt+3 (clamped: near the end the last stage is reloaded into the
-    // idle buffer, which keeps the loop free of branches).
-    const int64_t kl = stage_k(kt + kStages);
-    uint8_t* dst = buffer(b_cur);
-    const int b_next = b_cur == kStages - 1 ? 0 : b_cur + 1;
-
-#pragma unroll
-    for (int s = 0; s < C::STEPS; s++) {
-      const bool last = s == C::STEPS - 1;
-      const int cur = s & 1, nxt = cur ^ 1;
-      // Step s+1 of this stage, or step 0 of the next stage (read now).
-      const int ns = last ? 0 : s + 1;
-      const int nh = ns / 4, nd = ns % 4;
-      if (last) {
-        // The compiler may make these LDS reads wait for every outstanding
-        // LDS DMA; issuing stage kt+3's DMA only after them keeps that wait
-        // to transfers issued an iteration ago.
-        read_frags(buffer(b_next));
-        load_dma(kl, dst);
-      }
-#pragma unroll
-      for (int i = 0; i < C::TM; i++) {
-#pragma unroll
-        for (int j = 0; j < C::TN; j++) {
-          acc[i][j] =
-              __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[cur][j], acc[i][j], 0, 0, 0);
-          const int t = i * C::TN + j;
-#pragma unroll
-          for (int jj = 0; jj < C::TN; jj++)
-            if (b_slot<C::TM, C::TN>(last, jj) == t)
-              bf[nxt][jj] = decode8(pick(bq[nh][jj], nd), splat(bs[nh][jj], nd >= 2));
-#pragma unroll
-          for (int ii = 0; ii < C::TM; ii++)
-            if (a_slot<C::TM, C::TN>(last, ii) == t)
-              af[ii] = decode8(pick(aq[nh][ii], nd), splat(as[nh][ii], nd >= 2));
-        }
-      }
-    }
-    b_cur = b_next;
-    // Stage kt+2, read in the next iteration, complete: this wave's DMA for
-    // it was issued an iteration ago, so only this iteration's transfers may
-    // still be in flight; then every wave's (barrier).
-    wait_vm_lgkm0_upto(n_dma);
-    __builtin_amdgcn_s_barrier();
+  int64_t S = 0;
+  for (; S + 1 < KT; S += 2) {
+    stage(S, std::integral_constant<int, 0>{});
+    stage(S + 1, std::integral_constant<int, 1>{});
   }
+  if (S < KT) stage(S, std::integral_constant<int, 0>{});
   // No transfer may still target this workgroup's LDS when it is reused.
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
@@ -577,13 +625,13 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
   // Epilogue.  32x32 accumulator layout: lane l holds column l%32 and rows
   // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
 #pragma unroll
-  for (int i = 0; i < C::TM; i++) {
+  for (int i = 0; i < TM; i++) {
 #pragma unroll
-    for (int j = 0; j < C::TN; j++) {
+    for (int j = 0; j < TN; j++) {
       const int64_t col = n0 + wn * (C::BN / C::WN) + j * 32 + lrow;
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int64_t row = m0 + wm * (C::BM / C::WM) + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+        const int64_t row = m0 + a_row0 + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
         if (row < m_lim && col < N) {
           float v = acc[i][j][r] * gscale;
           if (c_bf16)
@@ -619,9 +667,17 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t total) {
   return b < per * kXcds ? (b % kXcds) * per + b / kXcds : b;
 }
 
+// The workgroup's LDS buffers (static, so that each is its own variable).
+#define NVFP4_TILE_LDS(C)                                            \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw0[C::kStage]; \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw1[C::kStage]; \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a16a[C::kA16];   \
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a16b[C::kA16];   \
+  const TileLds lds{{lds_raw0, lds_raw1}, {lds_a16a, lds_a16b}}
+
 template <class C, bool AK, bool BKM>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  NVFP4_TILE_LDS(C);
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
   int64_t tm, tn;
   tile_coords(xcd_tile(blockIdx.x, ntm * ntn), ntm, ntn, tm, tn);
@@ -631,12 +687,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   gemm_tile<C, AK, BKM>(A, B, tm * C::BM, a.M, tn * C::BN, a.N, a.K, gs, a.C, a.c_bf16, a.N, lds);
 }
 
+constexpr int kMaxGroups = 4096;  // the ABI's limit on groups
+
 // Persistent grouped kernel: every workgroup builds the prefix of per-group
 // tile counts in LDS, then walks tiles blockIdx.x, +gridDim.x, ...
 template <class C>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  int32_t* prefix = reinterpret_cast<int32_t*>(lds + C::kLds);  // [groups + 1]
+  NVFP4_TILE_LDS(C);
+  __shared__ int32_t prefix[kMaxGroups + 1];
   __shared__ int32_t part[C::NT];
   const int tid = threadIdx.x;
   const int64_t G = a.groups;
@@ -698,14 +756,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
 template <class C, bool AK, bool BKM>
 hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
-  const size_t smem = C::kLds;
-  auto kern = gemm_kernel<C, AK, BKM>;
-  if (smem > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-  }
-  kern<<<(unsigned)(ntm * ntn), C::NT, smem, st>>>(a);
+  gemm_kernel<C, AK, BKM><<<(unsigned)(ntm * ntn), C::NT, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -739,18 +790,12 @@ hipError_t launch_depth(const GemmArgs& a, int cus, hipStream_t st) {
 
 template <class C>
 hipError_t launch_grouped(const GroupedArgs& a, int cus, hipStream_t st) {
+  if (a.groups > kMaxGroups) return hipErrorInvalidValue;
   const int64_t ntn = (a.N + C::BN - 1) / C::BN;
   const int64_t max_tiles = ((a.total_rows + C::BM - 1) / C::BM + a.groups) * ntn;
   int64_t grid = cus;
   if (grid > max_tiles) grid = max_tiles;
-  const size_t smem = C::kLds + sizeof(int32_t) * (size_t)(a.groups + 1);
-  auto kern = grouped_gemm_kernel<C>;
-  if (smem > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-  }
-  kern<<<(unsigned)grid, C::NT, smem, st>>>(a);
+  grouped_gemm_kernel<C><<<(unsigned)grid, C::NT, 0, st>>>(a);
   return hipGetLastError();
 }
 
