@@ -431,11 +431,14 @@ struct TileLds {
 };
 
 // fp16 image of A for one 64-k half: row r holds 64 halves as 8 units of 16
-// bytes (unit v = k 8v .. 8v+7); unit v sits in slot v ^ ((r >> 1) & 7), so
-// the 16 consecutive rows a fragment read or write touches at one unit fall
-// in 16 distinct slots of a 256-byte bank window.
+// bytes (unit v = k 8v .. 8v+7); unit v sits in slot v ^ (r & 7) ^ ((r >> 3)
+// & 1).  A fragment read or write touches one unit of consecutive rows: 16-byte
+// reads are served 16 lanes (rows) at a time over a 256-byte bank window,
+// 16-byte writes 8 lanes at a time over 128 bytes, and the swizzle puts any 8
+// aligned rows in distinct slots and any 16 in distinct (row parity, slot)
+// pairs.
 __device__ __forceinline__ int a16_addr(int row, int unit) {
-  return row * 128 + 16 * (unit ^ ((row >> 1) & 7));
+  return row * 128 + 16 * (unit ^ (row & 7) ^ ((row >> 3) & 1));
 }
 
 // One output tile: C[m0 : m0+BM) x [n0 : n0+BN) restricted to rows < m_lim,
