@@ -210,8 +210,12 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
 #pragma unroll
       for (int u = 0; u < U; u++) {
         int64_t i = base + (int64_t)u * NT;
-        int64_t ic = i < chunks ? i : chunks - 1;  // duplicates do not change a max
-        In<T>::load8(xs + ic * 8, v[u]);
+        // Past the end: zeros (a duplicated chunk would not change a plain
+        // max, but its transform, paired with its partner, could).
+        In<T>::load8(xs + (i < chunks ? i : chunks - 1) * 8, v[u]);
+        if (i >= chunks)
+#pragma unroll
+          for (int q = 0; q < 8; q++) v[u][q] = 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < U; u++) {

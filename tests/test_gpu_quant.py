@@ -77,6 +77,45 @@ def test_quantize_1d_amax_input():
     _check_1d(x, "fp32", "col", "sr", 0x00FF, amax=12.5)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("mask", [0x0000, 0xA5C3])
+def test_quantize_1d_rht_tail_block(dtype, mask):
+    """Zeros except the last 8 elements (the second half of the last block):
+    the transform of that block, [0 | v], has max |H8 v|/4; a pass that paired
+    the last chunk with a copy of itself would see [v | v] and twice that."""
+    x = np.zeros((16, 64), dtype=np.float32)
+    x[15, 56:] = np.array([3.0, -1.0, 2.5, 0.25, -7.0, 1.5, 0.5, -2.0], dtype=np.float32)
+    _check_1d(x, dtype, "row", "rne", mask)
+
+
+# Mid-size tensors (several amax trips per workgroup and a ragged last trip).
+@pytest.mark.parametrize("rounding,rht", [("rne", False), ("sr", False), ("rne", True),
+                                          ("sr", True)])
+def test_quantize_1d_row_large(rounding, rht):
+    x = make_input("laplace_zeros", (4096, 4160), seed=41)
+    _check_1d(x, "bf16", "row", rounding, 0x9C31 if rht else -1, seed=9, offset=4)
+
+
+def test_quantize_1d_row_large_amax_input():
+    x = make_input("normal", (4096, 4096), seed=42)
+    _check_1d(x, "bf16", "row", "sr", -1, seed=3, amax=40.0)
+
+
+@pytest.mark.parametrize("amax", [None, 0.5])
+def test_quantize_2d_large(amax):
+    dev = device()
+    x = make_input("normal", (4096, 4160), seed=43) * np.float32(0.02)
+    t, xo = device_input(x, "bf16", dev)
+    a_t = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=dev)
+    q = nv.quantize_2d(t, amax=a_t)
+    got = to_np(q)
+    ref = O.quantize(xo, "2d", amax=amax)
+    assert_same(got["amax"], np.atleast_1d(np.float32(ref["amax"])), "amax")
+    assert_same(q.global_dec.cpu().numpy(), np.atleast_1d(np.float32(ref["g"])), "g")
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+
+
 def test_quantize_1d_empty():
     dev = device()
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
