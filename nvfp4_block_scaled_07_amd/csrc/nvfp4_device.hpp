@@ -77,18 +77,28 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
 }
 
 // Stochastic rounding: lo = largest grid value <= |y|, round up iff
-// u16 < 65536 * (|y| - lo) / step; both products are exact (power-of-2
-// factors, Sterbenz subtraction).  |y| >= 6 saturates.
+// u16 < 65536 * (|y| - lo) / step, |y| >= 6 saturating.  On the fp32 bits F
+// of |y|: in [1, 6) lo's code is (F >> 22) - 252 (exponent and the top
+// mantissa bit) and 65536 * (|y| - lo) / step is the 22 lower mantissa bits
+// over 64; in [0.5, 1) lo = 0.5 and it is the 23 mantissa bits over 128;
+// below 0.5 lo = 0 and it is |y| * 2^17 (exact).
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-  float m = __builtin_fabsf(y);
-  uint32_t lo = (uint32_t)(m >= 0.5f) + (uint32_t)(m >= 1.0f) + (uint32_t)(m >= 1.5f) +
-                (uint32_t)(m >= 2.0f) + (uint32_t)(m >= 3.0f) + (uint32_t)(m >= 4.0f) +
-                (uint32_t)(m >= 6.0f);
-  float lov = lo < 4u ? (float)lo * 0.5f : (lo < 6u ? (float)(lo - 2u) : 4.0f);
-  float scale = lo < 4u ? 131072.0f : (lo < 6u ? 65536.0f : 32768.0f);
-  float t = (m - lov) * scale;
-  uint32_t up = (lo < 7u && (float)u16 < t) ? 1u : 0u;
-  return (lo + up) | ((__float_as_uint(y) >> 28) & 8u);
+  const uint32_t F = __float_as_uint(y) & 0x7FFFFFFFu;
+  uint32_t code, up;
+  if (F >= 0x40C00000u) {  // >= 6
+    code = 7u;
+    up = 0u;
+  } else if (F >= 0x3F800000u) {  // [1, 6)
+    code = (F >> 22) - 252u;
+    up = (u16 << 6) < (F & 0x3FFFFFu) ? 1u : 0u;
+  } else if (F >= 0x3F000000u) {  // [0.5, 1)
+    code = 1u;
+    up = (u16 << 7) < (F & 0x7FFFFFu) ? 1u : 0u;
+  } else {
+    code = 0u;
+    up = (float)u16 < __uint_as_float(F) * 131072.0f ? 1u : 0u;
+  }
+  return (code + up) | ((__float_as_uint(y) >> 28) & 8u);
 }
 
 // ---- Philox4x32 ----------------------------------------------------------------------
@@ -96,19 +106,27 @@ struct Philox4 {
   uint32_t x, y, z, w;
 };
 
+__device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                             uint32_t& c3, uint32_t& k0, uint32_t& k1) {
+  uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
+  uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
+  uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+  c0 = n0;
+  c1 = lo1;
+  c2 = n2;
+  c3 = lo0;
+  k0 += 0x9E3779B9u;
+  k1 += 0xBB67AE85u;
+}
+
 __device__ __forceinline__ Philox4 philox4x32(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                               uint32_t k0, uint32_t k1, uint32_t rounds) {
-  for (uint32_t r = 0; r < rounds; r++) {
-    uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
-    uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
-    uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0;
-    c1 = lo1;
-    c2 = n2;
-    c3 = lo0;
-    k0 += 0x9E3779B9u;
-    k1 += 0xBB67AE85u;
+  if (rounds == 5) {  // the default: unrolled
+#pragma unroll
+    for (int r = 0; r < 5; r++) philox_round(c0, c1, c2, c3, k0, k1);
+    return Philox4{c0, c1, c2, c3};
   }
+  for (uint32_t r = 0; r < rounds; r++) philox_round(c0, c1, c2, c3, k0, k1);
   return Philox4{c0, c1, c2, c3};
 }
 

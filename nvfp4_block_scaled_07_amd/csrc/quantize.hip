@@ -320,6 +320,40 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
 }
 
 // ---- COL quantizer (lane: 8 cols x 16 rows = 8 blocks) ---------------------------------------
+// The 16 rows stay as loaded (raw input words) and are worked one column pair
+// at a time (the loop is kept rolled so that only one pair's transform and
+// random bits are live): with stochastic rounding an unrolled lane would hold
+// all 8 blocks' Philox output and its occupancy would drop to one wave per
+// SIMD.
+template <typename T>
+struct RawRow;
+
+template <>
+struct RawRow<uint16_t> {  // 8 bf16 = 4 words; column pair p is word p
+  uint4 q;
+  __device__ __forceinline__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void pair(int p, float& a, float& b) const {
+    const uint32_t w = p == 0 ? q.x : p == 1 ? q.y : p == 2 ? q.z : q.w;
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xFFFF0000u);
+  }
+};
+
+template <>
+struct RawRow<float> {  // named words (no array, so selects stay in registers)
+  uint4 lo, hi;         // elements 0..3, 4..7
+  __device__ __forceinline__ void load(const float* p) {
+    lo = reinterpret_cast<const uint4*>(p)[0];
+    hi = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void pair(int p, float& a, float& b) const {
+    const uint32_t wa = p == 0 ? lo.x : p == 1 ? lo.z : p == 2 ? hi.x : hi.z;
+    const uint32_t wb = p == 0 ? lo.y : p == 1 ? lo.w : p == 2 ? hi.y : hi.w;
+    a = __uint_as_float(wa);
+    b = __uint_as_float(wb);
+  }
+};
+
 template <typename T, bool kSR, bool kRHT>
 __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
@@ -333,52 +367,48 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
   const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t uc = u < units ? u : units - 1;
   const int64_t g = uc / cg, c0 = (uc % cg) * 8;
-  float v[16][8];
+  RawRow<T> raw[16];
 #pragma unroll
-  for (int r = 0; r < 16; r++) In<T>::load8(x + (g * 16 + r) * cols + c0, v[r]);
+  for (int r = 0; r < 16; r++) raw[r].load(x + (g * 16 + r) * cols + c0);
   build_recip_table(rtab, ts.S);
   if (u >= units) return;
   uint32_t out[16];
 #pragma unroll
   for (int r = 0; r < 16; r++) out[r] = 0;
   uint32_t sc[2] = {0, 0};
-#pragma unroll
+#pragma unroll 1
   for (int cp = 0; cp < 4; cp++) {  // column pairs (c, c+1) share one code byte per row
     float col[2][16];
-    uint32_t e[2];
-    float rcp[2];
+#pragma unroll
+    for (int r = 0; r < 16; r++) raw[r].pair(cp, col[0][r], col[1][r]);
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const int c = 2 * cp + h;
-#pragma unroll
-      for (int r = 0; r < 16; r++) col[h][r] = v[r][c];
       if (kRHT) rht16_inreg(col[h], mask);
       float bm = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[h][r]));
-      e[h] = block_code(bm, ts.k);
-      rcp[h] = rtab[e[h]];
-      sc[c >> 2] |= e[h] << (8 * (c & 3));
+      const uint32_t e = block_code(bm, ts.k);
+      const float rcp = rtab[e];
+      sc[cp >> 1] |= e << (8 * (c & 3));
 #pragma unroll
-      for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp[h];
-    }
-    if (kSR) {
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-        const int c = 2 * cp + h;
+      for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp;
+      if (kSR) {
         const uint64_t blk = (uint64_t)(c0 + c) * (uint64_t)(rows / 16) + (uint64_t)g;
-        Philox4 p0 = sr_call(2 * blk, seed, offset, rounds);
-        Philox4 p1 = sr_call(2 * blk + 1, seed, offset, rounds);
+        const Philox4 p0 = sr_call(2 * blk, seed, offset, rounds);
+        const Philox4 p1 = sr_call(2 * blk + 1, seed, offset, rounds);
 #pragma unroll
         for (int r = 0; r < 8; r++) out[r] |= e2m1_sr(col[h][r], sr_slot(p0, r)) << (4 * c);
 #pragma unroll
         for (int r = 0; r < 8; r++)
           out[r + 8] |= e2m1_sr(col[h][r + 8], sr_slot(p1, r)) << (4 * c);
       }
-    } else {
+    }
+    if (!kSR) {
 #pragma unroll
       for (int r = 0; r < 16; r++)
-        out[r] = cvt_fp4_byte(out[r], col[0][r], col[1][r], cp);
+        out[r] |= __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0)
+                  << (8 * cp);
     }
   }
 #pragma unroll
