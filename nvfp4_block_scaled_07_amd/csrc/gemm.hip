@@ -40,16 +40,19 @@ typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int v2i32 __attribute__((ext_vector_type(2)));
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int PK_ = 64>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, PK = PK_;
   static_assert(BM % 64 == 0 && BN % 64 == 0 && BM <= 256 && BN <= 256, "tile sizes");
   static_assert(BK == 64 || BK == 128, "stage depth");
+  static_assert((PK == 64 || PK == 128) && BK % PK == 0, "phase depth");
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int TM = BM / WM / 32;  // 32x32 MFMA tiles per wave along M
   static constexpr int TN = BN / WN / 32;
   static constexpr int H = BK / 64;        // 64-k halves per stage
+  static constexpr int NPH = BK / PK;      // phases (barrier intervals) per stage
+  static constexpr int PH = PK / 16;       // MFMA steps per phase
   static constexpr int STEPS = BK / 16;    // MFMA steps per stage
   static constexpr int RB = BK / 2;        // code bytes per row per stage
   static constexpr int SB = BK / 16;       // scale bytes per row (k-blocks) per stage
@@ -57,7 +60,7 @@ struct Cfg {
   static constexpr int kACodes = BM * RB, kAScales = BM * SB > SB * 256 ? BM * SB : SB * 256;
   static constexpr int kBCodes = BN * RB, kBScales = BN * SB > SB * 256 ? BN * SB : SB * 256;
   static constexpr int kStage = kACodes + kAScales + kBCodes + kBScales;  // one raw stage
-  static constexpr int kA16 = BM * 128;  // A of one 64-k half, decoded to fp16
+  static constexpr int kA16 = BM * PK * 2;  // A of one phase, decoded to fp16
 };
 
 // Operand view for one tile: base pointers and the strides of its stored
@@ -325,9 +328,16 @@ __device__ __forceinline__ half2 splat(half2 d, int hi) {
   return hi ? half2{d[1], d[1]} : half2{d[0], d[0]};
 }
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two bf16 (round to nearest even: v_cvt_pk_bf16_f32) packed low | high << 16.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(__bf16 lo, __bf16 hi) {
+  const bf16x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Value of the partner lane (lane ^ 1) via DPP quad_perm [1,0,3,2].
+__device__ __forceinline__ float xor1_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ uint32_t pick(const uint4& v, int s) {
@@ -361,6 +371,11 @@ struct Staging<true, ROWS, C, W0, NF> {
     for (int hs = 0; hs < C::H; hs++)
       code0[hs] = kmaj_code_addr<C::RB>(row, 2 * hs + (lane >> 5));
     sc0 = C::SB * row + 2 * (lane >> 5);
+  }
+  // Point the transfers at another tile (the LDS offsets do not change).
+  __device__ __forceinline__ void retarget(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
+                                           int tid) {
+    d.init(op, mn0, mn_lim, K, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6));
   }
   __device__ __forceinline__ void load_dma(int64_t k0, uint8_t* codes, uint8_t* scales) {
     d.issue(k0, codes, scales);
@@ -407,6 +422,10 @@ struct Staging<false, ROWS, C, W0, NF> {
 #pragma unroll
     for (int i = 0; i < NF; i++) col[i] = 16 * (U * krow0 + ((row0 / 32 + i) ^ sw)) + 8 * (g & 1);
   }
+  __device__ __forceinline__ void retarget(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
+                                           int tid) {
+    d.init(op, mn0, mn_lim, K, tid & 63, __builtin_amdgcn_readfirstlane(tid >> 6));
+  }
   __device__ __forceinline__ void load_dma(int64_t k0, uint8_t* codes, uint8_t* scales) {
     d.issue(k0, codes, scales);
   }
@@ -430,25 +449,38 @@ struct TileLds {
   uint8_t* a16[2];
 };
 
-// fp16 image of A for one 64-k half: row r holds 64 halves as 8 units of 16
-// bytes (unit v = k 8v .. 8v+7); unit v sits in slot v ^ (r & 7) ^ ((r >> 3)
-// & 1).  A fragment read or write touches one unit of consecutive rows: 16-byte
-// reads are served 16 lanes (rows) at a time over a 256-byte bank window,
-// 16-byte writes 8 lanes at a time over 128 bytes, and the swizzle puts any 8
-// aligned rows in distinct slots and any 16 in distinct (row parity, slot)
-// pairs.
+// fp16 image of A for one phase of PK k: row r holds PK halves as PK/8 units
+// of 16 bytes (unit v = k 8v .. 8v+7); unit v sits in a swizzled slot.  A
+// fragment read or write touches one unit of consecutive rows: 16-byte reads
+// are served 16 lanes (rows) at a time over a 256-byte bank window, 16-byte
+// writes 8 lanes at a time over 128 bytes.  PK = 64 (128-byte rows): slot
+// v ^ (r & 7) ^ ((r >> 3) & 1) puts any 8 aligned rows in distinct slots and
+// any 16 in distinct (row parity, slot) pairs; PK = 128 (256-byte rows):
+// slot v ^ (r & 15) puts any 16 aligned rows in distinct slots.
+template <int PK>
 __device__ __forceinline__ int a16_addr(int row, int unit) {
-  return row * 128 + 16 * (unit ^ (row & 7) ^ ((row >> 3) & 1));
+  return PK == 64 ? row * 128 + 16 * (unit ^ (row & 7) ^ ((row >> 3) & 1))
+                  : row * 256 + 16 * (unit ^ (row & 15));
 }
 
-// One output tile: C[m0 : m0+BM) x [n0 : n0+BN) restricted to rows < m_lim,
-// cols < N.
+// One output tile: C[m0 : m0+BM) x [n0 : n0+BN) restricted to rows < m_lim
+// (and columns < N); C points at row 0 of the tile's row coordinates.
+struct TileDesc {
+  OpView A, B;
+  int64_t m0, m_lim, n0;
+  float gscale;
+  void* C;
+};
+
+// The output tiles of a workgroup, one after another, as one pipeline of
+// stages (stage g = stage g % KT of tile g / KT), so that the next tile's
+// first stages are fetched and decoded while the current one finishes.
 //
 // Work is split in phases of 64 k (H = BK/64 phases per stage).  In phase p:
-//  * every wave multiplies its 128 x 64 (or 96 x 64) share of the tile in
-//    4 steps of 16 k: A fragments come ready-made from the fp16 image a16[p%2]
-//    (read one step ahead); B fragments are decoded by the wave itself from
-//    registers, one step ahead;
+//  * every wave multiplies its share of the tile in 4 steps of 16 k: A
+//    fragments come ready-made from the fp16 image a16[p%2] (read one step
+//    ahead); B fragments are decoded by the wave itself from registers, one
+//    step ahead;
 //  * every wave also decodes its 32 rows of A for phase p+1 (one fragment
 //    half: 32 nibbles and 2 scale bytes per lane, read from the raw stage)
 //    into a16[(p+1)%2], one 8-k dword per step -- so each A element is decoded
@@ -457,53 +489,80 @@ __device__ __forceinline__ int a16_addr(int row, int unit) {
 //    halves) into registers;
 //  * a barrier ends the phase; a16[(p+1)%2] is then complete and a16[p%2]
 //    free.
-// Raw stage S is used during phases H*S - 1 .. H*S + H - 2 (its A decoded
-// for phases H*S .. H*S+H-1; its B read at the end of phase H*S - 1), so its
-// buffer is refilled with stage S+2 at the start of phase H*S + H - 1, and
-// the end of phase H*(S+1) + H - 2 waits for that transfer.
-template <class C, bool AK, bool BKM>
-__device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int64_t m0,
-                                          int64_t m_lim, int64_t n0, int64_t N, int64_t K,
-                                          float gscale, void* Cout, bool c_bf16, int64_t ldc,
-                                          const TileLds& L) {
+// Raw stage g is used during phases H*g - 1 .. H*g + H - 2 (its A decoded
+// for phases H*g .. H*g+H-1; its B read at the end of phase H*g - 1), so its
+// buffer is refilled with stage g+2 at the start of phase H*g + H - 1, and
+// the end of phase H*(g+1) + H - 2 waits for that transfer.  After a tile's
+// last stage its accumulators are stored and cleared.
+//
+// Src: count() tiles, get(j) -> TileDesc of the j-th (wave-uniform); kSingle
+// when there is always exactly one (its store then follows the loop).
+template <class C, bool AK, bool BKM, class Src>
+__device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K, bool c_bf16,
+                                           int64_t ldc, const TileLds& L) {
   constexpr int H = C::H, TM = C::TM, TN = C::TN;
+  const int64_t NJ = src.count();
+  if (NJ <= 0) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lrow = lane & 31, lhalf = lane >> 5;
   const bool decodes_a = wave < C::BM / 32;  // wave-uniform: this wave owns 32 rows of A
+  const int64_t KT = K / C::BK;
+  const int64_t GT = NJ * KT;
 
   f32x16 acc[TM][TN];
+  auto clear_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < TM; i++)
+    for (int i = 0; i < TM; i++)
 #pragma unroll
-    for (int j = 0; j < TN; j++)
+      for (int j = 0; j < TN; j++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+  };
+  clear_acc();
+
+  // Tiles j0 and j0+1: the current one and the next, which transfers reach
+  // when KT >= 2 (the caller's precondition when NJ > 1).  Separate
+  // variables, not an array, so that they stay in registers.
+  int64_t j0 = 0;
+  TileDesc d0 = src.get(0);
+  TileDesc d1 = src.get(1 < NJ ? 1 : NJ - 1);
 
   using SA = Staging<AK, C::BM, C, 0, 1>;
   constexpr int kBW0 = SA::kScaleChunks % C::NW;  // B's scale chunks after A's
   using SB = Staging<BKM, C::BN, C, kBW0, TN>;
   SA sa;
   SB sb;
-  sa.init(A, m0, m_lim, K, tid, 32 * wave);  // the rows this wave decodes
-  sb.init(B, n0, N, K, tid, wn * (C::BN / C::WN));
-  const int64_t KT = K / C::BK;
+  sa.init(d0.A, d0.m0, d0.m_lim, K, tid, 32 * wave);  // rows this wave decodes
+  sb.init(d0.B, d0.n0, N, K, tid, wn * (C::BN / C::WN));
 
   constexpr int oAS = C::kACodes, oBC = C::kACodes + C::kAScales,
                 oBS = C::kACodes + C::kAScales + C::kBCodes;
 
-  // A16 offsets: fragment reads (row wm*BM/WM + 32i + lrow, unit 4*lhalf + nd)
-  // and this wave's decode writes (row 32*wave + lrow, same units); the slot
-  // swizzle only depends on lrow.
+  // A16 offsets: fragment reads (row wm*BM/WM + 32i + lrow, unit 8q + 4*lhalf
+  // + nd for 64-k half q of the phase and step nd of it) and this wave's
+  // decode writes (row 32*wave + lrow, same units); the slot swizzle only
+  // depends on lrow.
+  constexpr int PQ = C::PK / 64;  // 64-k halves per phase
   const int a_row0 = wm * (C::BM / C::WM);
-  int a16_rd[4];
+  int a16_rd[PQ][4];
 #pragma unroll
-  for (int nd = 0; nd < 4; nd++) a16_rd[nd] = a16_addr(a_row0 + lrow, 4 * lhalf + nd);
-  const int a16_wr_delta = 128 * (32 * wave - a_row0);  // wave-uniform
+  for (int q = 0; q < PQ; q++)
+#pragma unroll
+    for (int nd = 0; nd < 4; nd++)
+      a16_rd[q][nd] = a16_addr<C::PK>(a_row0 + lrow, 8 * q + 4 * lhalf + nd);
+  const int a16_wr_delta = 2 * C::PK * (32 * wave - a_row0);  // wave-uniform
 
-  auto load_dma = [&](int64_t st, uint8_t* dst) {
-    const int64_t k0 = st * C::BK;
+  // Transfer global stage g into dst.  Transfers run two stages ahead of the
+  // multiply, in order, so they move to the next tile (d1, as KT >= 2) at its
+  // first stage.
+  auto load_dma = [&](int64_t g, uint8_t* dst) {
+    if (!Src::kSingle && g > 0 && g % KT == 0) {
+      sa.retarget(d1.A, d1.m0, d1.m_lim, K, tid);
+      sb.retarget(d1.B, d1.n0, N, K, tid);
+    }
+    const int64_t k0 = (g % KT) * C::BK;
     sa.load_dma(k0, dst, dst + oAS);
     sb.load_dma(k0, dst + oBC, dst + oBS);
   };
@@ -522,35 +581,81 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
       for (int j = 0; j < TN; j++) bs[hs][j] = scale_pair(br[hs][j]);
   };
 
-  // This wave's raw A for one half: 32 nibbles and the scale pair.
-  uint4 dq;
-  half2 ds;
-  auto read_a = [&](const uint8_t* st, int hs) {
-    uint32_t sc;
-    sa.frag(st, st + oAS, 0, hs, dq, sc);
-    ds = scale_pair(sc);
+  // This wave's raw A for one phase: per 64-k half, 32 nibbles and the scale
+  // pair (stage halves h0 .. h0+PQ-1).
+  uint4 dq[PQ];
+  half2 ds[PQ];
+  auto read_a = [&](const uint8_t* st, int h0) {
+#pragma unroll
+    for (int q = 0; q < PQ; q++) {
+      uint32_t sc;
+      sa.frag(st, st + oAS, 0, h0 + q, dq[q], sc);
+      ds[q] = scale_pair(sc);
+    }
   };
-  auto decode_a = [&](uint8_t* a16, int nd) {
-    const half8 v = decode8(pick(dq, nd), splat(ds, nd >= 2));
-    *reinterpret_cast<half8*>(a16 + a16_rd[nd] + a16_wr_delta) = v;
+  auto decode_a = [&](uint8_t* a16, int s) {  // step s of the phase: half s/4, dword s%4
+    const int q = s / 4, nd = s % 4;
+    const half8 v = decode8(pick(dq[q], nd), splat(ds[q], nd >= 2));
+    *reinterpret_cast<half8*>(a16 + a16_rd[q][nd] + a16_wr_delta) = v;
   };
 
   half8 af[2][TM], bf[2][TN];
-  auto read_af = [&](const uint8_t* a16, int nd, int buf) {
+  auto read_af = [&](const uint8_t* a16, int s, int buf) {
 #pragma unroll
     for (int i = 0; i < TM; i++)
-      af[buf][i] = *reinterpret_cast<const half8*>(a16 + a16_rd[nd] + i * 32 * 128);
+      af[buf][i] = *reinterpret_cast<const half8*>(a16 + a16_rd[s / 4][s % 4] +
+                                                   i * 32 * 2 * C::PK);
+  };
+
+  // Epilogue of tile d0.  32x32 accumulator layout: lane l holds column
+  // l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  bf16: lanes l and
+  // l^1 hold neighbouring columns of the same rows; they swap one value per
+  // row pair so that the even lane stores rows r (r even) and the odd lane
+  // rows r+1, two columns (4 bytes) at a time.  Offsets are element indices
+  // from C; tiles inside the output skip the bounds checks.
+  auto store_tile = [&]() {
+    const TileDesc& t = d0;
+    const bool full = t.m0 + C::BM <= t.m_lim && t.n0 + C::BN <= N;  // wave-uniform
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+#pragma unroll
+      for (int j = 0; j < TN; j++) {
+        const int64_t col = t.n0 + wn * (C::BN / C::WN) + j * 32 + lrow;
+        const int64_t row0 = t.m0 + a_row0 + i * 32 + 4 * lhalf;
+        if (c_bf16) {
+          uint32_t* cb = static_cast<uint32_t*>(t.C);  // bf16 pairs; ldc and col are even
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float v0 = acc[i][j][r] * t.gscale, v1 = acc[i][j][r + 1] * t.gscale;
+            const float other = xor1_f(odd ? v0 : v1);
+            const __bf16 lo = (__bf16)(odd ? other : v0), hi = (__bf16)(odd ? v1 : other);
+            const int64_t row = row0 + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
+            const int64_t c2 = odd ? col - 1 : col;
+            if (full || row < t.m_lim)  // c2 + 1 < N when c2 < N (N % 8 == 0)
+              if (full || c2 < N) cb[(row * ldc + c2) >> 1] = bf16_pair(lo, hi);
+          }
+        } else {
+          float* cf = static_cast<float*>(t.C);
+#pragma unroll
+          for (int r = 0; r < 16; r++) {
+            const int64_t row = row0 + 8 * (r >> 2) + (r & 3);
+            if (full || (row < t.m_lim && col < N)) cf[row * ldc + col] = acc[i][j][r] * t.gscale;
+          }
+        }
+      }
+    }
   };
 
   // Prologue: stages 0 and 1 in LDS, phase 0's A image, stage 0's B.
   load_dma(0, L.raw[0]);
-  if (KT > 1) load_dma(1, L.raw[1]);
+  if (GT > 1) load_dma(1, L.raw[1]);
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   if (decodes_a) {
     read_a(L.raw[0], 0);
 #pragma unroll
-    for (int nd = 0; nd < 4; nd++) decode_a(L.a16[0], nd);
+    for (int s = 0; s < C::PH; s++) decode_a(L.a16[0], s);
   }
   read_b(L.raw[0]);
   wait_vm_lgkm0<0>();
@@ -559,30 +664,33 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
 #pragma unroll
   for (int j = 0; j < TN; j++) bf[0][j] = decode8(bq[0][j].x, splat(bs[0][j], 0));
 
-  // One stage S whose raw buffer is raw[PAR] (the next stage's is raw[1-PAR]).
-  auto stage = [&](int64_t S, auto par) {
+  // One global stage g whose raw buffer is raw[PAR] (the next one's is
+  // raw[1-PAR]).
+  auto stage = [&](int64_t g, auto par) {
     constexpr int PAR = decltype(par)::value;
+    constexpr int NPH = C::NPH, PH = C::PH;
     uint8_t* raw_cur = L.raw[PAR];
     uint8_t* raw_nxt = L.raw[1 - PAR];
 #pragma unroll
-    for (int h = 0; h < H; h++) {
-      // Phase p = H*S + h uses a16[p%2] and fills a16[(p+1)%2].
-      const int ab = H == 2 ? h : PAR;  // (H*S + h) % 2 with S % 2 == PAR
+    for (int h = 0; h < NPH; h++) {
+      // Phase p = NPH*g + h uses a16[p%2] and fills a16[(p+1)%2].
+      const int ab = NPH == 2 ? h : PAR;  // (NPH*g + h) % 2 with g % 2 == PAR
       uint8_t* a16_cur = L.a16[ab];
       uint8_t* a16_nxt = L.a16[1 - ab];
-      if (h == H - 1 && S + 2 < KT) load_dma(S + 2, raw_cur);  // raw[PAR] is free
-      // A of phase p+1: the next half of this stage, or the first of the next.
-      if (decodes_a) read_a(h + 1 < H ? raw_cur : raw_nxt, h + 1 < H ? h + 1 : 0);
+      if (h == NPH - 1 && g + 2 < GT) load_dma(g + 2, raw_cur);  // raw[PAR] is free
+      // A of phase p+1: the next phase of this stage, or the first of the next.
+      if (decodes_a) read_a(h + 1 < NPH ? raw_cur : raw_nxt, h + 1 < NPH ? (h + 1) * PQ : 0);
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
+      for (int s = 0; s < PH; s++) {
         const int cur = s & 1, nxt = cur ^ 1;
-        const bool last_step = s == 3;
-        const bool stage_end = last_step && h == H - 1;  // next step is the next stage's
+        const bool last_step = s == PH - 1;
+        const bool stage_end = last_step && h == NPH - 1;  // next step is the next stage's
         if (stage_end) read_b(raw_nxt);
-        // B fragment of the next step: dword (s+1) of this half, or dword 0
-        // of the next half (this stage's, or the next stage's just read).
-        const int nh = last_step ? (h + 1 < H ? h + 1 : 0) : h;
-        const int nd = last_step ? 0 : s + 1;
+        // B fragment of the next step: step sg + 1 of this stage (64-k half
+        // (sg+1)/4, dword (sg+1)%4), or step 0 of the next (just read).
+        const int sg = h * PH + s;
+        const int nh = stage_end ? 0 : (sg + 1) / 4;
+        const int nd = stage_end ? 0 : (sg + 1) % 4;
 #pragma unroll
         for (int i = 0; i < TM; i++) {
 #pragma unroll
@@ -603,48 +711,32 @@ __device__ __forceinline__ void gemm_tile(const OpView& A, const OpView& B, int6
         }
       }
       // End of phase: A image of phase p+1 written, a16_cur read by all.
-      // The next phase reads raw stage S+1 (H = 2: from its start; H = 1:
+      // The next phase reads raw stage g+1 (NPH = 2: from its start; NPH = 1:
       // it is the stage after), whose transfer is this wave's only one in
       // flight here.
-      if ((h + 2) % H == 0)
+      if ((h + 2) % NPH == 0)
         wait_vm_lgkm0<0>();
       else
         wait_vm_lgkm0<63>();
       __builtin_amdgcn_s_barrier();
       read_af(a16_nxt, 0, 0);
     }
+    if (!Src::kSingle && (g + 1) % KT == 0) {  // the tile's last stage: store, move on
+      store_tile();
+      clear_acc();
+      j0++;
+      d0 = d1;
+      d1 = src.get(j0 + 1 < NJ ? j0 + 1 : NJ - 1);
+    }
   };
 
-  int64_t S = 0;
-  for (; S + 1 < KT; S += 2) {
-    stage(S, std::integral_constant<int, 0>{});
-    stage(S + 1, std::integral_constant<int, 1>{});
+  int64_t g = 0;
+  for (; g + 1 < GT; g += 2) {
+    stage(g, std::integral_constant<int, 0>{});
+    stage(g + 1, std::integral_constant<int, 1>{});
   }
-  if (S < KT) stage(S, std::integral_constant<int, 0>{});
-  // No transfer may still target this workgroup's LDS when it is reused.
-  wait_vm_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
-
-  // Epilogue.  32x32 accumulator layout: lane l holds column l%32 and rows
-  // 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
-#pragma unroll
-  for (int i = 0; i < TM; i++) {
-#pragma unroll
-    for (int j = 0; j < TN; j++) {
-      const int64_t col = n0 + wn * (C::BN / C::WN) + j * 32 + lrow;
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int64_t row = m0 + a_row0 + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-        if (row < m_lim && col < N) {
-          float v = acc[i][j][r] * gscale;
-          if (c_bf16)
-            static_cast<uint16_t*>(Cout)[row * ldc + col] = (uint16_t)bf16_rne_bits(v);
-          else
-            static_cast<float*>(Cout)[row * ldc + col] = v;
-        }
-      }
-    }
-  }
+  if (g < GT) stage(g, std::integral_constant<int, 0>{});
+  if (Src::kSingle) store_tile();
 }
 
 // Tile order: groups of 8 M-tiles sweep N, so tiles that run together share
@@ -678,19 +770,81 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t total) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_a16b[C::kA16];   \
   const TileLds lds{{lds_raw0, lds_raw1}, {lds_a16a, lds_a16b}}
 
+// One tile per workgroup.
+struct DenseTile {
+  static constexpr bool kSingle = true;
+  TileDesc t;
+  __device__ __forceinline__ int64_t count() const { return 1; }
+  __device__ __forceinline__ TileDesc get(int64_t) const { return t; }
+};
+
 template <class C, bool AK, bool BKM>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   NVFP4_TILE_LDS(C);
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
   int64_t tm, tn;
   tile_coords(xcd_tile(blockIdx.x, ntm * ntn), ntm, ntn, tm, tn);
-  OpView A{a.A.codes, a.A.scales, a.M, a.A.block};
-  OpView B{a.B.codes, a.B.scales, a.N, a.B.block};
-  const float gs = *a.A.gdec * *a.B.gdec;
-  gemm_tile<C, AK, BKM>(A, B, tm * C::BM, a.M, tn * C::BN, a.N, a.K, gs, a.C, a.c_bf16, a.N, lds);
+  DenseTile src;
+  src.t.A = OpView{a.A.codes, a.A.scales, a.M, a.A.block};
+  src.t.B = OpView{a.B.codes, a.B.scales, a.N, a.B.block};
+  src.t.m0 = tm * C::BM;
+  src.t.m_lim = a.M;
+  src.t.n0 = tn * C::BN;
+  src.t.gscale = *a.A.gdec * *a.B.gdec;
+  src.t.C = a.C;
+  gemm_tiles<C, AK, BKM>(src, a.N, a.K, a.c_bf16, a.N, lds);
 }
 
 constexpr int kMaxGroups = 4096;  // the ABI's limit on groups
+
+// The workgroup's tiles of the per-group tile list (group e owns tiles
+// prefix[e] .. prefix[e+1]-1, column tile major, row tiles minor, so that
+// neighbouring tiles share the group's B panel).  Round j runs tiles
+// j*G .. j*G+G-1 (G = grid size) and hands neighbours to the same XCD:
+// workgroup b (on XCD b % 8) takes slot (b % 8) * (G/8) + b / 8.
+template <class C>
+struct GroupedTiles {
+  static constexpr bool kSingle = false;
+  const GroupedArgs* a;
+  const int32_t* prefix;  // LDS, [groups + 1]
+  int64_t ntn;
+  int32_t total;
+  __device__ __forceinline__ int64_t slot() const {
+    const int64_t G = gridDim.x, b = blockIdx.x;
+    return G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
+  }
+  __device__ __forceinline__ int64_t count() const {
+    const int64_t s = slot();
+    return s < total ? (total - 1 - s) / gridDim.x + 1 : 0;
+  }
+  __device__ __forceinline__ TileDesc get(int64_t j) const {
+    const int32_t t = (int32_t)(slot() + j * gridDim.x);
+    // largest e with prefix[e] <= t (empty groups share a prefix value)
+    int64_t lo = 0, hi = a->groups;  // prefix[lo] <= t < prefix[hi]
+    while (hi - lo > 1) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (prefix[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int64_t e = lo;
+    const int32_t lt = t - prefix[e];
+    const int64_t r0 = a->offsets[e], r1 = a->offsets[e + 1];
+    const int64_t mtiles = (r1 - r0 + C::BM - 1) / C::BM;
+    const int64_t nt = lt / mtiles, mt = lt % mtiles;
+    const int64_t K = a->K, N = a->N;
+    const int64_t b_scales_stride =
+        a->B.block == kBlock2d ? (N / 16) * (K / 16) : N * (K / 16);
+    TileDesc d;
+    d.A = OpView{a->A.codes + r0 * (K / 2), a->A.scales + r0 * (K / 16), 0, kBlockRow};
+    d.B = OpView{a->B.codes + e * (N * K / 2), a->B.scales + e * b_scales_stride, 0, a->B.block};
+    d.m0 = mt * C::BM;
+    d.m_lim = r1 - r0;
+    d.n0 = nt * C::BN;
+    d.gscale = *a->A.gdec * a->B.gdec[e];
+    d.C = a->c_bf16 ? (void*)(static_cast<uint16_t*>(a->C) + r0 * N)
+                    : (void*)(static_cast<float*>(a->C) + r0 * N);
+    return d;
+  }
+};
 
 // Persistent grouped kernel: every workgroup builds the prefix of per-group
 // tile counts in LDS, then walks tiles blockIdx.x, +gridDim.x, ...
@@ -730,29 +884,15 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   }
   __syncthreads();
   const int32_t total = prefix[G];
-  const float ga = *a.A.gdec;
-  const int64_t b_codes_stride = a.N * a.K / 2;
-  const int64_t b_scales_stride =
-      a.B.block == kBlock2d ? (a.N / 16) * (a.K / 16) : a.N * (a.K / 16);
-  for (int32_t t = blockIdx.x; t < total; t += gridDim.x) {
-    // largest e with prefix[e] <= t (empty groups share a prefix value)
-    int64_t lo = 0, hi = G;  // prefix[lo] <= t < prefix[hi]
-    while (hi - lo > 1) {
-      int64_t mid = (lo + hi) >> 1;
-      if (prefix[mid] <= t) lo = mid; else hi = mid;
+  GroupedTiles<C> src{&a, prefix, ntn, total};
+  if (a.K >= 2 * C::BK) {
+    gemm_tiles<C, true, true>(src, a.N, a.K, a.c_bf16, a.N, lds);
+  } else {  // one stage per tile: no pipeline across tiles
+    for (int64_t j = 0; j < src.count(); j++) {
+      DenseTile one{src.get(j)};
+      gemm_tiles<C, true, true>(one, a.N, a.K, a.c_bf16, a.N, lds);
+      __syncthreads();
     }
-    const int64_t e = lo;
-    const int32_t lt = t - prefix[e];
-    const int64_t mt = lt / ntn, nt = lt % ntn;
-    const int64_t r0 = a.offsets[e], r1 = a.offsets[e + 1];
-    OpView A{a.A.codes + r0 * (a.K / 2), a.A.scales + r0 * (a.K / 16), 0, kBlockRow};
-    OpView B{a.B.codes + e * b_codes_stride, a.B.scales + e * b_scales_stride, 0, a.B.block};
-    const float gs = ga * a.B.gdec[e];
-    gemm_tile<C, true, true>(A, B, mt * C::BM, r1 - r0, nt * C::BN, a.N, a.K, gs,
-                             a.c_bf16 ? (void*)(static_cast<uint16_t*>(a.C) + r0 * a.N)
-                                      : (void*)(static_cast<float*>(a.C) + r0 * a.N),
-                             a.c_bf16, a.N, lds);
-    __syncthreads();
   }
 }
 
@@ -818,13 +958,22 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   return launch_depth<64>(a, cus, st);
 }
 
+// Grouped tiles: routed experts get few rows each (padding a 256-row tile
+// wastes most of it), so when the average group has fewer than 512 rows the
+// tiles are 128 rows x 256 columns, one 128 x 32 slice per wave (eight waves
+// side by side: each B fragment is decoded by one wave, A comes decoded
+// from LDS); otherwise 256 x 256.
 hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st) {
   if (a.total_rows == 0 || a.N == 0 || a.groups == 0) return hipSuccess;
   int cus = 256;
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
-  if (a.K % 128 == 0) return launch_grouped<Cfg<256, 256, 2, 4, 128>>(a, cus, st);
-  return launch_grouped<Cfg<256, 256, 2, 4, 64>>(a, cus, st);
+  const bool small = a.total_rows < 512 * a.groups;
+  if (a.K % 128 == 0)
+    return small ? launch_grouped<Cfg<128, 256, 1, 8, 128, 128>>(a, cus, st)
+                 : launch_grouped<Cfg<256, 256, 2, 4, 128>>(a, cus, st);
+  return small ? launch_grouped<Cfg<128, 256, 1, 8, 64>>(a, cus, st)
+               : launch_grouped<Cfg<256, 256, 2, 4, 64>>(a, cus, st);
 }
 
 }  // namespace nvfp4

@@ -92,8 +92,28 @@ def test_grouped_matches_dense_per_group():
         assert torch.equal(d, c[r0:r0 + n])
 
 
+@pytest.mark.parametrize("counts,K", [([40, 0, 260, 7], 192),   # few rows per group: 128-row tiles
+                                      ([600, 1100, 0, 700], 256)])  # many: 256-row tiles
+def test_grouped_tile_shapes_match_dense(counts, K):
+    """Both grouped tile shapes give each group exactly the dense GEMM's bits."""
+    N = 272
+    qa, qb, off, c = _grouped_case(counts, N, K, seed=11, out=torch.float32)
+    for e, n in enumerate(counts):
+        if n == 0:
+            continue
+        _check_group(qa, qb, off, c, e, N, K)
+        r0 = int(off[e])
+        sub = nv.QTensor(qa.codes[r0:r0 + n], qa.scales[r0:r0 + n], qa.global_dec, qa.amax, n, K,
+                         "row")
+        be = nv.QTensor(qb.codes[e], qb.scales[e], qb.global_dec[e:e + 1], qb.amax[e:e + 1], N, K,
+                        "2d")
+        d = nv.gemm("N", "T", sub, be, out_dtype=torch.float32)
+        assert torch.equal(d, c[r0:r0 + n])
+
+
 def test_grouped_all_rows_in_one_group_and_many_groups():
-    _grouped_case([700], 64, 64, seed=1)
+    qa, qb, off, c = _grouped_case([700], 64, 64, seed=1)
+    _check_group(qa, qb, off, c, 0, 64, 64)
     counts = np.random.default_rng(2).integers(0, 40, 300)
     qa, qb, off, c = _grouped_case(counts, 32, 64, seed=2)
     for e in range(0, 300, 37):
