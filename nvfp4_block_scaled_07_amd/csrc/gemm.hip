@@ -504,10 +504,12 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   const int64_t NJ = src.count();
   if (NJ <= 0) return;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const bool decodes_a = wave < C::BM / 32;  // wave-uniform: this wave owns 32 rows of A
+  // This wave owns 32 rows of A to decode (all waves do when BM / 32 >= NW;
+  // known at compile time then, which keeps the step code free of branches).
+  const bool decodes_a = C::BM / 32 >= C::NW || wave < C::BM / 32;
   const int64_t KT = K / C::BK;
   const int64_t GT = NJ * KT;
 
