@@ -700,6 +700,11 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][i], bf[cur][j],
                                                                acc[i][j], 0, 0, 0);
             const int t = i * TN + j;
+            // Raised wave priority while the first half of the step's MFMAs
+            // issue: with both waves of a SIMD ready, the one feeding the
+            // matrix core goes first (measured +1-3%).
+            if (t == 0) __builtin_amdgcn_s_setprio(1);
+            if (t == TM * TN / 2) __builtin_amdgcn_s_setprio(0);
             if (t == 0 && !last_step) read_af(a16_cur, s + 1, nxt);
             // B decodes after MFMAs j (2 + j when the raw registers were
             // just reloaded, to leave the LDS reads time to land).
