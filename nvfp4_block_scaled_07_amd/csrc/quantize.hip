@@ -184,7 +184,7 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 // stride loop in which each thread issues all its loads of a trip (U 16-byte
 // loads, strided by the workgroup size so each load instruction is
 // contiguous across the wave) before reducing them.
-constexpr int kAmaxUnroll = 8;
+constexpr int kAmaxUnroll = 4;
 
 template <typename T, bool kRHT>
 __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __restrict__ x,
@@ -538,7 +538,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Workgroups of an amax pass: one per kAmaxThreads * unroll units, capped
 // near the CU count (the kernels loop over the rest) to keep the atomics few.
-int amax_grid(int64_t units, int unroll, int64_t cap = 256) {
+int amax_grid(int64_t units, int unroll, int64_t cap = 512) {
   int64_t g = cdiv(units, (int64_t)kAmaxThreads * unroll);
   return (int)(g < cap ? (g > 0 ? g : 1) : cap);
 }
@@ -601,8 +601,8 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
     fill_zero_kernel<<<(unsigned)cdiv(a.batch, 256), 256, 0, st>>>(a.amax, a.batch);
     int64_t chunks = a.rows * a.cols / 8;
     const int u = a.w_fp32 ? 2 : kAmaxUnroll;
-    // about 256 workgroups in all, at least one per slice
-    const int64_t per = a.batch >= 256 ? 1 : 256 / a.batch;
+    // about 512 workgroups in all, at least one per slice
+    const int64_t per = a.batch >= 512 ? 1 : 512 / a.batch;
     dim3 grid((unsigned)amax_grid(chunks, u, per), (unsigned)a.batch);
     amax_flat_kernel<T, false><<<grid, kAmaxThreads, 0, st>>>(w, chunks, 0, a.amax);
   }
