@@ -483,17 +483,19 @@ struct TileDesc {
 //    step ahead;
 //  * every wave also decodes its 32 rows of A for phase p+1 (one fragment
 //    half: 32 nibbles and 2 scale bytes per lane, read from the raw stage)
-//    into a16[(p+1)%2], one 8-k dword per step -- so each A element is decoded
-//    once per workgroup instead of once per wave that multiplies it;
+//    into a16[(p+1)%2], one 8-k dword per step and the last two together in
+//    the second-last step -- so each A element is decoded once per workgroup
+//    instead of once per wave that multiplies it;
 //  * the last phase of a stage reads the next stage's B fragments (both
 //    halves) into registers;
-//  * a barrier ends the phase; a16[(p+1)%2] is then complete and a16[p%2]
-//    free.
+//  * a barrier precedes the last step: a16[(p+1)%2] is then complete and
+//    every read of a16[p%2] done (the last step's A is already in
+//    registers), so the last step reads the first fragments of phase p+1.
 // Raw stage g is used during phases H*g - 1 .. H*g + H - 2 (its A decoded
-// for phases H*g .. H*g+H-1; its B read at the end of phase H*g - 1), so its
-// buffer is refilled with stage g+2 at the start of phase H*g + H - 1, and
-// the end of phase H*(g+1) + H - 2 waits for that transfer.  After a tile's
-// last stage its accumulators are stored and cleared.
+// for phases H*g .. H*g+H-1; its B read in the last step of phase H*g - 1),
+// so its buffer is refilled with stage g+2 at the start of phase H*g + H - 1,
+// and the barrier of phase H*(g+1) + H - 2 waits for that transfer.  After a
+// tile's last stage its accumulators are stored and cleared.
 //
 // Src: count() tiles, get(j) -> TileDesc of the j-th (wave-uniform); kSingle
 // when there is always exactly one (its store then follows the loop).
@@ -705,7 +707,12 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
             // matrix core goes first (measured +1-3%).
             if (t == 0) __builtin_amdgcn_s_setprio(1);
             if (t == TM * TN / 2) __builtin_amdgcn_s_setprio(0);
-            if (t == 0 && !last_step) read_af(a16_cur, s + 1, nxt);
+            // A fragments of the next step: from this phase's image, or
+            // (last step, after the barrier) step 0 of the next phase's.
+            if (t == 0) {
+              if (!last_step) read_af(a16_cur, s + 1, nxt);
+              else read_af(a16_nxt, 0, nxt);
+            }
             // B decodes after MFMAs j (2 + j when the raw registers were
             // just reloaded, to leave the LDS reads time to land).
 #pragma unroll
@@ -713,20 +720,30 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
               const int slot = stage_end ? (2 + jj < TM * TN ? 2 + jj : TM * TN - 1) : jj;
               if (slot == t) bf[nxt][jj] = decode8(pick(bq[nh][jj], nd), splat(bs[nh][jj], nd >= 2));
             }
-            if (t == TM * TN - 1 && decodes_a) decode_a(a16_nxt, s);
+            // The next phase's A image: one dword per step, the last two in
+            // the step before the barrier.
+            if (t == TM * TN - 1 && decodes_a && !last_step) {
+              decode_a(a16_nxt, s);
+              if (s == PH - 2) decode_a(a16_nxt, PH - 1);
+            }
           }
         }
+        // The barrier sits before the phase's last step, whose operands are
+        // already in registers: once past it, every wave has written its part
+        // of the next image and read the last fragments of this one (so
+        // a16_cur is free for the phase after), and the first reads of the
+        // next image then land behind the last step's MFMAs instead of
+        // stalling every wave after the barrier.  The next phase reads raw
+        // stage g+1 (NPH = 2: from its start; NPH = 1: it is the stage
+        // after), whose transfer is this wave's only one in flight here.
+        if (s == PH - 2) {
+          if ((h + 2) % NPH == 0)
+            wait_vm_lgkm0<0>();
+          else
+            wait_vm_lgkm0<63>();
+          __builtin_amdgcn_s_barrier();
+        }
       }
-      // End of phase: A image of phase p+1 written, a16_cur read by all.
-      // The next phase reads raw stage g+1 (NPH = 2: from its start; NPH = 1:
-      // it is the stage after), whose transfer is this wave's only one in
-      // flight here.
-      if ((h + 2) % NPH == 0)
-        wait_vm_lgkm0<0>();
-      else
-        wait_vm_lgkm0<63>();
-      __builtin_amdgcn_s_barrier();
-      read_af(a16_nxt, 0, 0);
     }
     if (!Src::kSingle && (g + 1) % KT == 0) {  // the tile's last stage: store, move on
       store_tile();
