@@ -558,17 +558,21 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
       a16_rd[q][nd] = a16_addr<C::PK>(a_row0 + lrow, 8 * q + 4 * lhalf + nd);
   const int a16_wr_delta = 2 * C::PK * (32 * wave - a_row0);  // wave-uniform
 
-  // Transfer global stage g into dst.  Transfers run two stages ahead of the
-  // multiply, in order, so they move to the next tile (d1, as KT >= 2) at its
-  // first stage.
-  auto load_dma = [&](int64_t g, uint8_t* dst) {
-    if (!Src::kSingle && g > 0 && g % KT == 0) {
+  // Transfer the next global stage into dst.  Transfers run two stages ahead
+  // of the multiply, in order, so they move to the next tile (d1, as KT >= 2)
+  // at its first stage.  dma_kt: k-stage of the next transfer within its
+  // tile (a running count, not a division per stage).
+  int64_t dma_kt = 0;
+  auto load_dma = [&](uint8_t* dst) {
+    if (!Src::kSingle && dma_kt == KT) {
       sa.retarget(d1.A, d1.m0, d1.m_lim, K, tid);
       sb.retarget(d1.B, d1.n0, N, K, tid);
+      dma_kt = 0;
     }
-    const int64_t k0 = (g % KT) * C::BK;
+    const int64_t k0 = dma_kt * C::BK;
     sa.load_dma(k0, dst, dst + oAS);
     sb.load_dma(k0, dst + oBC, dst + oBS);
+    dma_kt++;
   };
 
   uint4 bq[H][TN];
@@ -652,8 +656,8 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   };
 
   // Prologue: stages 0 and 1 in LDS, phase 0's A image, stage 0's B.
-  load_dma(0, L.raw[0]);
-  if (GT > 1) load_dma(1, L.raw[1]);
+  load_dma(L.raw[0]);
+  if (GT > 1) load_dma(L.raw[1]);
   wait_vm_lgkm0<0>();
   __builtin_amdgcn_s_barrier();
   if (decodes_a) {
@@ -669,7 +673,8 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   for (int j = 0; j < TN; j++) bf[0][j] = decode8(bq[0][j].x, splat(bs[0][j], 0));
 
   // One global stage g whose raw buffer is raw[PAR] (the next one's is
-  // raw[1-PAR]).
+  // raw[1-PAR]); mul_kt is its k-stage within its tile.
+  int64_t mul_kt = 0;
   auto stage = [&](int64_t g, auto par) {
     constexpr int PAR = decltype(par)::value;
     constexpr int NPH = C::NPH, PH = C::PH;
@@ -681,7 +686,7 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
       const int ab = NPH == 2 ? h : PAR;  // (NPH*g + h) % 2 with g % 2 == PAR
       uint8_t* a16_cur = L.a16[ab];
       uint8_t* a16_nxt = L.a16[1 - ab];
-      if (h == NPH - 1 && g + 2 < GT) load_dma(g + 2, raw_cur);  // raw[PAR] is free
+      if (h == NPH - 1 && g + 2 < GT) load_dma(raw_cur);  // stage g+2; raw[PAR] is free
       // A of phase p+1: the next phase of this stage, or the first of the next.
       if (decodes_a) read_a(h + 1 < NPH ? raw_cur : raw_nxt, h + 1 < NPH ? (h + 1) * PQ : 0);
 #pragma unroll
@@ -745,7 +750,8 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
         }
       }
     }
-    if (!Src::kSingle && (g + 1) % KT == 0) {  // the tile's last stage: store, move on
+    if (!Src::kSingle && ++mul_kt == KT) {  // the tile's last stage: store, move on
+      mul_kt = 0;
       store_tile();
       clear_acc();
       j0++;
