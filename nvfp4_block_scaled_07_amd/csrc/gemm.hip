@@ -483,8 +483,8 @@ struct TileDesc {
 //    step ahead;
 //  * every wave also decodes its 32 rows of A for phase p+1 (one fragment
 //    half: 32 nibbles and 2 scale bytes per lane, read from the raw stage)
-//    into a16[(p+1)%2], one 8-k dword per step and the last two together in
-//    the second-last step -- so each A element is decoded once per workgroup
+//    into a16[(p+1)%2], one 8-k dword per half step from the end of the
+//    first step on -- so each A element is decoded once per workgroup
 //    instead of once per wave that multiplies it;
 //  * the last phase of a stage reads the next stage's B fragments (both
 //    halves) into registers;
@@ -575,35 +575,32 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
     dma_kt++;
   };
 
+  // This wave's raw B for one stage: per 64-k half and fragment, 32 nibbles
+  // and two scale bytes (converted where they are used).
   uint4 bq[H][TN];
-  half2 bs[H][TN];
+  uint32_t bsr[H][TN];
   auto read_b = [&](const uint8_t* st) {
-    uint32_t br[H][TN];
 #pragma unroll
     for (int hs = 0; hs < H; hs++)
 #pragma unroll
-      for (int j = 0; j < TN; j++) sb.frag(st + oBC, st + oBS, j, hs, bq[hs][j], br[hs][j]);
-#pragma unroll
-    for (int hs = 0; hs < H; hs++)
-#pragma unroll
-      for (int j = 0; j < TN; j++) bs[hs][j] = scale_pair(br[hs][j]);
+      for (int j = 0; j < TN; j++) sb.frag(st + oBC, st + oBS, j, hs, bq[hs][j], bsr[hs][j]);
+  };
+  auto decode_b = [&](int hs, int j, int nd) {
+    return decode8(pick(bq[hs][j], nd), splat(scale_pair(bsr[hs][j]), nd >= 2));
   };
 
-  // This wave's raw A for one phase: per 64-k half, 32 nibbles and the scale
-  // pair (stage halves h0 .. h0+PQ-1).
+  // This wave's raw A for one phase: per 64-k half, 32 nibbles and the two
+  // scale bytes (stage halves h0 .. h0+PQ-1).  The bytes are converted where
+  // they are used, so that no conversion waits for the read right after it.
   uint4 dq[PQ];
-  half2 ds[PQ];
+  uint32_t dsr[PQ];
   auto read_a = [&](const uint8_t* st, int h0) {
 #pragma unroll
-    for (int q = 0; q < PQ; q++) {
-      uint32_t sc;
-      sa.frag(st, st + oAS, 0, h0 + q, dq[q], sc);
-      ds[q] = scale_pair(sc);
-    }
+    for (int q = 0; q < PQ; q++) sa.frag(st, st + oAS, 0, h0 + q, dq[q], dsr[q]);
   };
   auto decode_a = [&](uint8_t* a16, int s) {  // step s of the phase: half s/4, dword s%4
     const int q = s / 4, nd = s % 4;
-    const half8 v = decode8(pick(dq[q], nd), splat(ds[q], nd >= 2));
+    const half8 v = decode8(pick(dq[q], nd), splat(scale_pair(dsr[q]), nd >= 2));
     *reinterpret_cast<half8*>(a16 + a16_rd[q][nd] + a16_wr_delta) = v;
   };
 
@@ -670,7 +667,7 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   __builtin_amdgcn_s_barrier();
   read_af(L.a16[0], 0, 0);
 #pragma unroll
-  for (int j = 0; j < TN; j++) bf[0][j] = decode8(bq[0][j].x, splat(bs[0][j], 0));
+  for (int j = 0; j < TN; j++) bf[0][j] = decode_b(0, j, 0);
 
   // One global stage g whose raw buffer is raw[PAR] (the next one's is
   // raw[1-PAR]); mul_kt is its k-stage within its tile.
@@ -678,6 +675,7 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   auto stage = [&](int64_t g, auto par) {
     constexpr int PAR = decltype(par)::value;
     constexpr int NPH = C::NPH, PH = C::PH;
+    static_assert(PH >= 4, "the A image is written by the middle of step PH/2 <= PH-2");
     uint8_t* raw_cur = L.raw[PAR];
     uint8_t* raw_nxt = L.raw[1 - PAR];
 #pragma unroll
@@ -723,13 +721,14 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
 #pragma unroll
             for (int jj = 0; jj < TN; jj++) {
               const int slot = stage_end ? (2 + jj < TM * TN ? 2 + jj : TM * TN - 1) : jj;
-              if (slot == t) bf[nxt][jj] = decode8(pick(bq[nh][jj], nd), splat(bs[nh][jj], nd >= 2));
+              if (slot == t) bf[nxt][jj] = decode_b(nh, jj, nd);
             }
-            // The next phase's A image: one dword per step, the last two in
-            // the step before the barrier.
-            if (t == TM * TN - 1 && decodes_a && !last_step) {
-              decode_a(a16_nxt, s);
-              if (s == PH - 2) decode_a(a16_nxt, PH - 1);
+            // The next phase's A image, dword c after half-step c + 1 (the
+            // middle or the end of step (c+1)/2): the last write goes out
+            // half a step or more before the barrier's wait.
+            if (decodes_a && (t == TM * TN / 2 - 1 || t == TM * TN - 1)) {
+              const int c = 2 * s + (t == TM * TN - 1 ? 1 : 0) - 1;
+              if (c >= 0 && c < PH) decode_a(a16_nxt, c);
             }
           }
         }
