@@ -401,8 +401,8 @@ struct Staging<false, ROWS, C, W0, NF> {
   // kb = 4hs + 2h + r of its column.
   int col[NF];   // LDS offset of the tr-read row for hs = 0, r = 0
   int scb;       // LDS offset of the scale byte for fragment 0, hs = 0, r = 0
+  int scb1;      // the same for r = 1
   int sc_step;   // from fragment i to i + 1 (wave-uniform)
-  int sc_d;      // from the r = 0 scale byte to the r = 1 byte (wave-uniform)
   __device__ __forceinline__ int dma_count(int wave) const { return d.count(wave); }
   __device__ __forceinline__ void init(const OpView& op, int64_t mn0, int64_t mn_lim, int64_t K,
                                        int tid, int row0) {
@@ -416,9 +416,9 @@ struct Staging<false, ROWS, C, W0, NF> {
     // 2D scale rows start 2 bytes past a 4-byte word on odd k-block rows when
     // w16 = 2 mod 4 (every other start offset is 0; see the DMA).
     const int m1 = two_d && (w16 & 3) == 2 ? 2 : 0;
-    sc_d = 256 + m1;
     sc_step = two_d ? 2 : 32;
     scb = 256 * 2 * h + (two_d ? (row0 + (lane & 31)) / 16 : row0 + (lane & 31));
+    scb1 = scb + 256 + m1;
 #pragma unroll
     for (int i = 0; i < NF; i++) col[i] = 16 * (U * krow0 + ((row0 / 32 + i) ^ sw)) + 8 * (g & 1);
   }
@@ -435,8 +435,11 @@ struct Staging<false, ROWS, C, W0, NF> {
     const v2i32 lo = lds_read_tr4(p + 16 * U * 64 * hs);
     const v2i32 hi = lds_read_tr4(p + 16 * U * (64 * hs + 16));
     q = uint4{(uint32_t)lo.x, (uint32_t)lo.y, (uint32_t)hi.x, (uint32_t)hi.y};
-    const uint8_t* ps = scales + scb + i * sc_step + 1024 * hs;
-    sc = (uint32_t)ps[0] | ((uint32_t)ps[sc_d] << 8);
+    // Two plain per-lane offsets (not one plus a distance between them):
+    // then the compiler can tell these reads from a transfer into the other
+    // stage buffer, and does not wait for it.
+    const int d = i * sc_step + 1024 * hs;
+    sc = (uint32_t)scales[scb + d] | ((uint32_t)scales[scb1 + d] << 8);
   }
 };
 
@@ -826,6 +829,14 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 
 constexpr int kMaxGroups = 4096;  // the ABI's limit on groups
 
+// Load of a value the kernel never writes, at a wave-uniform address, as a
+// scalar load: it then counts on the scalar counter, so waiting for it does
+// not also wait for the LDS transfers in flight.
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 // The workgroup's tiles of the per-group tile list (group e owns tiles
 // prefix[e] .. prefix[e+1]-1, column tile major, row tiles minor, so that
 // neighbouring tiles share the group's B panel).  Round j runs tiles
@@ -854,9 +865,9 @@ struct GroupedTiles {
       const int64_t mid = (lo + hi) >> 1;
       if (prefix[mid] <= t) lo = mid; else hi = mid;
     }
-    const int64_t e = lo;
-    const int32_t lt = t - prefix[e];
-    const int64_t r0 = a->offsets[e], r1 = a->offsets[e + 1];
+    const int64_t e = __builtin_amdgcn_readfirstlane((int)lo);
+    const int32_t lt = __builtin_amdgcn_readfirstlane(t - prefix[e]);
+    const int64_t r0 = load_uniform(a->offsets + e), r1 = load_uniform(a->offsets + e + 1);
     const int64_t mtiles = (r1 - r0 + C::BM - 1) / C::BM;
     const int64_t nt = lt / mtiles, mt = lt % mtiles;
     const int64_t K = a->K, N = a->N;
@@ -868,7 +879,7 @@ struct GroupedTiles {
     d.m0 = mt * C::BM;
     d.m_lim = r1 - r0;
     d.n0 = nt * C::BN;
-    d.gscale = *a->A.gdec * a->B.gdec[e];
+    d.gscale = load_uniform(a->A.gdec) * load_uniform(a->B.gdec + e);
     d.C = a->c_bf16 ? (void*)(static_cast<uint16_t*>(a->C) + r0 * N)
                     : (void*)(static_cast<float*>(a->C) + r0 * N);
     return d;
