@@ -77,28 +77,26 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
 }
 
 // Stochastic rounding: lo = largest grid value <= |y|, round up iff
-// u16 < 65536 * (|y| - lo) / step, |y| >= 6 saturating.  On the fp32 bits F
-// of |y|: in [1, 6) lo's code is (F >> 22) - 252 (exponent and the top
-// mantissa bit) and 65536 * (|y| - lo) / step is the 22 lower mantissa bits
-// over 64; in [0.5, 1) lo = 0.5 and it is the 23 mantissa bits over 128;
-// below 0.5 lo = 0 and it is |y| * 2^17 (exact).
+// u16 < 65536 * (|y| - lo) / step, |y| >= 6 saturating.  Computed without
+// branches (both candidates, then selects):
+//  * [1, 6) from the fp32 bits F of |y|: lo's code is (F >> 22) - 252
+//    (exponent and the top mantissa bit) and 65536 * (|y| - lo) / step is the
+//    22 lower mantissa bits over 64;
+//    Above 6 the same formula gives a code of at least 7 (F >> 22 is at most
+//    511), so the saturation is a min;
+//  * [0, 1), where the grid step is 0.5: with t = 2|y| (exact), lo's code is
+//    [t >= 1] and the fraction is t - [t >= 1] (exact), scaled by 65536
+//    (exact) and compared with u16 as floats.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-  const uint32_t F = __float_as_uint(y) & 0x7FFFFFFFu;
-  uint32_t code, up;
-  if (F >= 0x40C00000u) {  // >= 6
-    code = 7u;
-    up = 0u;
-  } else if (F >= 0x3F800000u) {  // [1, 6)
-    code = (F >> 22) - 252u;
-    up = (u16 << 6) < (F & 0x3FFFFFu) ? 1u : 0u;
-  } else if (F >= 0x3F000000u) {  // [0.5, 1)
-    code = 1u;
-    up = (u16 << 7) < (F & 0x7FFFFFu) ? 1u : 0u;
-  } else {
-    code = 0u;
-    up = (float)u16 < __uint_as_float(F) * 131072.0f ? 1u : 0u;
-  }
-  return (code + up) | ((__float_as_uint(y) >> 28) & 8u);
+  const uint32_t bits = __float_as_uint(y);
+  const uint32_t F = bits & 0x7FFFFFFFu;
+  const uint32_t hi = ((F >> 22) - 252u) + ((u16 << 6) < (F & 0x3FFFFFu) ? 1u : 0u);
+  const float t = __uint_as_float(F) * 2.0f;
+  const bool t1 = t >= 1.0f;
+  const float frac = t1 ? t - 1.0f : t;
+  const uint32_t lo = (t1 ? 1u : 0u) + ((float)u16 < frac * 65536.0f ? 1u : 0u);
+  const uint32_t code = F >= 0x3F800000u ? __builtin_elementwise_min(hi, 7u) : lo;
+  return code | ((bits >> 28) & 8u);
 }
 
 // ---- Philox4x32 ----------------------------------------------------------------------
@@ -108,8 +106,10 @@ struct Philox4 {
 
 __device__ __forceinline__ void philox_round(uint32_t& c0, uint32_t& c1, uint32_t& c2,
                                              uint32_t& c3, uint32_t& k0, uint32_t& k1) {
-  uint32_t lo0 = c0 * 0xD2511F53u, hi0 = __umulhi(c0, 0xD2511F53u);
-  uint32_t lo1 = c2 * 0xCD9E8D57u, hi1 = __umulhi(c2, 0xCD9E8D57u);
+  // 32 x 32 -> 64-bit products (one v_mad_u64_u32 each)
+  const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
+  const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+  const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
   uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
   c0 = n0;
   c1 = lo1;
