@@ -189,8 +189,9 @@ int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream);
  * bf16 (RNE) or fp32 per c_dtype.
  * Shapes: K % 64 == 0 and K > 0 (one pipeline stage is 64 k); M, N >= 0;
  * the contiguous dimension of a stored operand is a multiple of 32 and a COL
- * or 2D operand has rows % 16 == 0.  M == 0 or N == 0 is a no-op.  Alignment: codes 16 bytes, scales 4,
- * C 16 bytes (bf16) / 16 bytes (fp32) with N % 8 == 0.
+ * or 2D operand has rows % 16 == 0; N % 8 == 0 and N < 2^21 (else
+ * NVFP4_ERR_SHAPE).  M == 0 or N == 0 is a no-op.  Alignment: codes 16
+ * bytes, scales 4, C 16 bytes.
  */
 int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nvfp4_operand* A,
                    const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream);
@@ -205,7 +206,8 @@ int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nv
  *   B: `groups` slices [N x K] (B->rows = N, B->cols = K), 2D or ROW blocks,
  *      codes/scales consecutive per slice, global_dec [groups].
  *   C: [total_rows x N], bf16 or fp32.
- * Shapes: K % 64 == 0, K > 0, N % 16 == 0, groups <= 4096.  A row_offsets entry outside
+ * Shapes: K % 64 == 0, K > 0, N % 16 == 0, N < 2^21, groups <= 4096.  A
+ * row_offsets entry outside
  * [0, total_rows] or decreasing is a precondition violation (rows outside
  * [0, total_rows) are never touched).
  */

@@ -158,6 +158,10 @@ int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream) {
                                                 static_cast<hipStream_t>(stream)));
 }
 
+// Output rows of a GEMM tile (at most 256 of them, 4-byte elements) must span
+// fewer than 2^31 bytes: the epilogue's store offsets are 31-bit.
+constexpr int64_t kMaxN = int64_t(1) << 21;
+
 int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nvfp4_operand* A,
                    const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream) {
   if ((opA != 'N' && opA != 'T') || (opB != 'N' && opB != 'T')) return NVFP4_ERR_LAYOUT;
@@ -173,7 +177,7 @@ int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nv
   if (s != NVFP4_OK) return s;
   s = check_operand(B, eb);
   if (s != NVFP4_OK) return s;
-  if (N % 8 != 0) return NVFP4_ERR_SHAPE;
+  if (N % 8 != 0 || N >= kMaxN) return NVFP4_ERR_SHAPE;
   if (!aligned(C, 16)) return NVFP4_ERR_ALIGN;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (K == 0) return NVFP4_ERR_SHAPE;  // nothing to contract: caller should fill C
@@ -196,7 +200,7 @@ int32_t nvfp4_grouped_gemm(int64_t groups, const int64_t* row_offsets, int64_t t
   if (!valid_dtype(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
   if (groups < 0 || total_rows < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
   if (groups > 4096) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0 || N % 16 != 0 || K == 0) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || N % 16 != 0 || K == 0 || N >= kMaxN) return NVFP4_ERR_SHAPE;
   if (!row_offsets || !A || !B || !C) return NVFP4_ERR_NULL;
   if (!aligned(row_offsets, 8) || !aligned(C, 16)) return NVFP4_ERR_ALIGN;
   int32_t s = check_operand(A, Expect{total_rows, K, true});

@@ -385,6 +385,16 @@ struct Staging<true, ROWS, C, W0, NF> {
     q = *reinterpret_cast<const uint4*>(codes + code0[hs] + i * 32 * C::RB);
     sc = *reinterpret_cast<const uint16_t*>(scales + sc0 + 4 * hs + i * 32 * C::SB);
   }
+  // Fragment 0 of half hs given at run time (wave-uniform).
+  __device__ __forceinline__ void frag_h(const uint8_t* codes, const uint8_t* scales, int hs,
+                                         uint4& q, uint32_t& sc) const {
+    int off = code0[0];
+#pragma unroll
+    for (int x = 1; x < C::H; x++)
+      if (hs == x) off = code0[x];
+    q = *reinterpret_cast<const uint4*>(codes + off);
+    sc = *reinterpret_cast<const uint16_t*>(scales + sc0 + 4 * hs);
+  }
 };
 
 template <int ROWS, class C, int W0, int NF>
@@ -512,9 +522,20 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  // This wave owns 32 rows of A to decode (all waves do when BM / 32 >= NW;
-  // known at compile time then, which keeps the step code free of branches).
-  const bool decodes_a = C::BM / 32 >= C::NW || wave < C::BM / 32;
+  // The A image of a phase is RBLK row blocks of 32 rows, each PQ 64-k halves
+  // of 4 dwords (8 k) per lane.  With at least as many row blocks as waves,
+  // wave w decodes row block w whole (and none when w >= RBLK).  With fewer
+  // row blocks than waves, and the waves a multiple of them, wave w decodes
+  // AD consecutive dwords (within one half) of row block w % RBLK: every wave
+  // then takes part, which keeps the step code free of a branch on it.
+  constexpr int RBLK = C::BM / 32;
+  constexpr int PQ = C::PK / 64;  // 64-k halves per phase
+  constexpr int SPLIT = RBLK < C::NW && C::NW % RBLK == 0 ? C::NW / RBLK : 1;
+  constexpr bool kSplitA = SPLIT > 1 && SPLIT >= PQ && (4 * PQ) % SPLIT == 0;
+  constexpr int AD = kSplitA ? 4 * PQ / SPLIT : 4 * PQ;  // dwords per wave per phase
+  const bool decodes_a = kSplitA || RBLK >= C::NW || wave < RBLK;
+  const int a_rb = kSplitA ? wave % RBLK : wave;      // row block this wave decodes
+  const int a_i0 = kSplitA ? (wave / RBLK) * AD : 0;  // its first dword (4 * half + dword)
   const int64_t KT = K / C::BK;
   const int64_t GT = NJ * KT;
 
@@ -541,7 +562,7 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   using SB = Staging<BKM, C::BN, C, kBW0, TN>;
   SA sa;
   SB sb;
-  sa.init(d0.A, d0.m0, d0.m_lim, K, tid, 32 * wave);  // rows this wave decodes
+  sa.init(d0.A, d0.m0, d0.m_lim, K, tid, 32 * a_rb);  // rows this wave decodes
   sb.init(d0.B, d0.n0, N, K, tid, wn * (C::BN / C::WN));
 
   constexpr int oAS = C::kACodes, oBC = C::kACodes + C::kAScales,
@@ -549,9 +570,8 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
 
   // A16 offsets: fragment reads (row wm*BM/WM + 32i + lrow, unit 8q + 4*lhalf
   // + nd for 64-k half q of the phase and step nd of it) and this wave's
-  // decode writes (row 32*wave + lrow, same units); the slot swizzle only
-  // depends on lrow.
-  constexpr int PQ = C::PK / 64;  // 64-k halves per phase
+  // decode writes (row 32*a_rb + lrow, same units, dword c of its share); the
+  // slot swizzle only depends on lrow.
   const int a_row0 = wm * (C::BM / C::WM);
   int a16_rd[PQ][4];
 #pragma unroll
@@ -559,7 +579,16 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
 #pragma unroll
     for (int nd = 0; nd < 4; nd++)
       a16_rd[q][nd] = a16_addr<C::PK>(a_row0 + lrow, 8 * q + 4 * lhalf + nd);
-  const int a16_wr_delta = 2 * C::PK * (32 * wave - a_row0);  // wave-uniform
+  const int a16_wr_delta = 2 * C::PK * (32 * a_rb - a_row0);  // wave-uniform
+  int a16_wr[AD];
+#pragma unroll
+  for (int c = 0; c < AD; c++) {
+    int v = a16_rd[0][0];
+#pragma unroll
+    for (int it = 0; it < 4 * PQ; it++)
+      if (it == a_i0 + c) v = a16_rd[it / 4][it % 4];  // a_i0 == 0 unless split
+    a16_wr[c] = v + a16_wr_delta;
+  }
 
   // Transfer the next global stage into dst.  Transfers run two stages ahead
   // of the multiply, in order, so they move to the next tile (d1, as KT >= 2)
@@ -593,18 +622,25 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   };
 
   // This wave's raw A for one phase: per 64-k half, 32 nibbles and the two
-  // scale bytes (stage halves h0 .. h0+PQ-1).  The bytes are converted where
-  // they are used, so that no conversion waits for the read right after it.
-  uint4 dq[PQ];
-  uint32_t dsr[PQ];
+  // scale bytes (stage halves h0 .. h0+PQ-1; split: only the half of its
+  // share).  The bytes are converted where they are used, so that no
+  // conversion waits for the read right after it.
+  constexpr int NQ = kSplitA ? 1 : PQ;
+  const int a_q = a_i0 / 4, a_nd0 = AD % 4 == 0 ? 0 : a_i0 % 4;
+  uint4 dq[NQ];
+  uint32_t dsr[NQ];
   auto read_a = [&](const uint8_t* st, int h0) {
+    if constexpr (kSplitA) {
+      sa.frag_h(st, st + oAS, h0 + a_q, dq[0], dsr[0]);
+    } else {
 #pragma unroll
-    for (int q = 0; q < PQ; q++) sa.frag(st, st + oAS, 0, h0 + q, dq[q], dsr[q]);
+      for (int q = 0; q < PQ; q++) sa.frag(st, st + oAS, 0, h0 + q, dq[q], dsr[q]);
+    }
   };
-  auto decode_a = [&](uint8_t* a16, int s) {  // step s of the phase: half s/4, dword s%4
-    const int q = s / 4, nd = s % 4;
+  auto decode_a = [&](uint8_t* a16, int c) {  // dword c of this wave's share
+    const int q = kSplitA ? 0 : c / 4, nd = kSplitA ? a_nd0 + c : c % 4;
     const half8 v = decode8(pick(dq[q], nd), splat(scale_pair(dsr[q]), nd >= 2));
-    *reinterpret_cast<half8*>(a16 + a16_rd[q][nd] + a16_wr_delta) = v;
+    *reinterpret_cast<half8*>(a16 + a16_wr[c]) = v;
   };
 
   half8 af[2][TM], bf[2][TN];
@@ -619,40 +655,62 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   // l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  bf16: lanes l and
   // l^1 hold neighbouring columns of the same rows; they swap one value per
   // row pair so that the even lane stores rows r (r even) and the odd lane
-  // rows r+1, two columns (4 bytes) at a time.  Offsets are element indices
-  // from C; tiles inside the output skip the bounds checks.
+  // rows r+1, two columns (4 bytes) at a time.  Stores go through a buffer
+  // resource based at the tile's first row, with the lane's offset in the
+  // vector operand and the row step of element r (wave-uniform) in the
+  // scalar one; a lane whose element lies past the last row or column gets
+  // a vector offset beyond the resource's range, and the hardware drops that
+  // store -- no branches, full tile or not.  The offsets fit 31 bits as
+  // N < 2^21 (checked by the caller) and a tile has at most 256 rows.
+  const int esz = c_bf16 ? 2 : 4;
+  const int ldc32 = (int)ldc;
   auto store_tile = [&]() {
+    // Kept apart from the surrounding pipeline code by the scheduler, which
+    // would otherwise interleave the two and run out of registers.
+    __builtin_amdgcn_sched_barrier(0);
     const TileDesc& t = d0;
-    const bool full = t.m0 + C::BM <= t.m_lim && t.n0 + C::BN <= N;  // wave-uniform
     const bool odd = lane & 1;
+    const int64_t left = t.m_lim - t.m0;  // rows of the tile that exist (32-bit compare below)
+    const int rows_left = left < C::BM ? (int)left : C::BM;
+    char* base = static_cast<char*>(t.C) + t.m0 * ldc * esz;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7FFFFFFF, kBufferFlags);
+    constexpr uint32_t kDrop = 0x80000000u;  // past the range: not stored
 #pragma unroll
     for (int i = 0; i < TM; i++) {
 #pragma unroll
       for (int j = 0; j < TN; j++) {
-        const int64_t col = t.n0 + wn * (C::BN / C::WN) + j * 32 + lrow;
-        const int64_t row0 = t.m0 + a_row0 + i * 32 + 4 * lhalf;
+        const int col = (int)t.n0 + wn * (C::BN / C::WN) + j * 32 + lrow;
+        const int rl0 = a_row0 + i * 32 + 4 * lhalf;  // row within the tile, r = 0
         if (c_bf16) {
-          uint32_t* cb = static_cast<uint32_t*>(t.C);  // bf16 pairs; ldc and col are even
+          const int lr = rl0 + (odd ? 1 : 0);
+          const int c2 = odd ? col - 1 : col;  // c2 + 1 < N when c2 < N (N % 8 == 0)
+          const uint32_t loff = (uint32_t)(lr * ldc32 + c2) * 2u;
+          const bool cok = c2 < N;
 #pragma unroll
           for (int r = 0; r < 16; r += 2) {
             const float v0 = acc[i][j][r] * t.gscale, v1 = acc[i][j][r + 1] * t.gscale;
             const float other = xor1_f(odd ? v0 : v1);
             const __bf16 lo = (__bf16)(odd ? other : v0), hi = (__bf16)(odd ? v1 : other);
-            const int64_t row = row0 + 8 * (r >> 2) + (r & 3) + (odd ? 1 : 0);
-            const int64_t c2 = odd ? col - 1 : col;
-            if (full || row < t.m_lim)  // c2 + 1 < N when c2 < N (N % 8 == 0)
-              if (full || c2 < N) cb[(row * ldc + c2) >> 1] = bf16_pair(lo, hi);
+            const int dr = 8 * (r >> 2) + (r & 3);
+            const bool ok = cok && lr + dr < rows_left;
+            __builtin_amdgcn_raw_buffer_store_b32(bf16_pair(lo, hi), rs, ok ? loff : kDrop,
+                                                  dr * ldc32 * 2, 0);
           }
         } else {
-          float* cf = static_cast<float*>(t.C);
+          const uint32_t loff = (uint32_t)(rl0 * ldc32 + col) * 4u;
+          const bool cok = col < N;
 #pragma unroll
           for (int r = 0; r < 16; r++) {
-            const int64_t row = row0 + 8 * (r >> 2) + (r & 3);
-            if (full || (row < t.m_lim && col < N)) cf[row * ldc + col] = acc[i][j][r] * t.gscale;
+            const int dr = 8 * (r >> 2) + (r & 3);
+            const bool ok = cok && rl0 + dr < rows_left;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] * t.gscale), rs,
+                                                  ok ? loff : kDrop, dr * ldc32 * 4, 0);
           }
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Prologue: stages 0 and 1 in LDS, phase 0's A image, stage 0's B.
@@ -663,7 +721,7 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   if (decodes_a) {
     read_a(L.raw[0], 0);
 #pragma unroll
-    for (int s = 0; s < C::PH; s++) decode_a(L.a16[0], s);
+    for (int c = 0; c < AD; c++) decode_a(L.a16[0], c);
   }
   read_b(L.raw[0]);
   wait_vm_lgkm0<0>();
@@ -731,7 +789,7 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
             // half a step or more before the barrier's wait.
             if (decodes_a && (t == TM * TN / 2 - 1 || t == TM * TN - 1)) {
               const int c = 2 * s + (t == TM * TN - 1 ? 1 : 0) - 1;
-              if (c >= 0 && c < PH) decode_a(a16_nxt, c);
+              if (c >= 0 && c < AD) decode_a(a16_nxt, c);
             }
           }
         }
@@ -828,6 +886,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 }
 
 constexpr int kMaxGroups = 4096;  // the ABI's limit on groups
+static_assert(kMaxGroups == 64 * 64, "the group search reads prefix[0 .. 4095]: 64 blocks of 64");
 
 // Load of a value the kernel never writes, at a wave-uniform address, as a
 // scalar load: it then counts on the scalar counter, so waiting for it does
@@ -853,19 +912,28 @@ struct GroupedTiles {
     const int64_t G = gridDim.x, b = blockIdx.x;
     return G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
   }
+  // The largest e with prefix[e] <= t (empty groups share a prefix value;
+  // prefix[0] = 0 <= t), by the whole wave at once: prefix is nondecreasing,
+  // so the entries <= t are a leading run, and two ballots over 64 entries
+  // each (the first of every block of 64 groups, then the entries of one
+  // block) count it.  The reads stay inside the LDS array (kMaxGroups + 1
+  // entries); entries past the groups are left out of the counts.
+  __device__ __forceinline__ int find_group(int32_t t) const {
+    const int lane = threadIdx.x & 63;
+    const int G = (int)a->groups;
+    const int32_t v1 = prefix[lane << 6];
+    const int c1 = __popcll(__ballot(lane < ((G + 63) >> 6) && v1 <= t)) - 1;
+    const int i2 = (c1 << 6) + lane;
+    const int32_t v2 = prefix[i2];
+    return (c1 << 6) + __popcll(__ballot(i2 < G && v2 <= t)) - 1;
+  }
   __device__ __forceinline__ int64_t count() const {
     const int64_t s = slot();
     return s < total ? (total - 1 - s) / gridDim.x + 1 : 0;
   }
   __device__ __forceinline__ TileDesc get(int64_t j) const {
     const int32_t t = (int32_t)(slot() + j * gridDim.x);
-    // largest e with prefix[e] <= t (empty groups share a prefix value)
-    int64_t lo = 0, hi = a->groups;  // prefix[lo] <= t < prefix[hi]
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (prefix[mid] <= t) lo = mid; else hi = mid;
-    }
-    const int64_t e = __builtin_amdgcn_readfirstlane((int)lo);
+    const int64_t e = __builtin_amdgcn_readfirstlane(find_group(t));
     const int32_t lt = __builtin_amdgcn_readfirstlane(t - prefix[e]);
     const int64_t r0 = load_uniform(a->offsets + e), r1 = load_uniform(a->offsets + e + 1);
     const int64_t mtiles = (r1 - r0 + C::BM - 1) / C::BM;

@@ -91,6 +91,9 @@ def test_gemm_validation(lib):
     assert g(b"N", b"T", 64, 64, 128, C.byref(bad), C.byref(B), FAKE, 0, None) == -4
     wrong = _Operand(0x100000, 0x200000, 0x300000, 65, 128, 0, 0)
     assert g(b"N", b"T", 64, 64, 128, C.byref(wrong), C.byref(B), FAKE, 0, None) == -2
+    # N < 2^21: a tile's output rows must span fewer than 2^31 bytes
+    wide = _Operand(0x100000, 0x200000, 0x300000, 1 << 21, 128, 2, 0)
+    assert g(b"N", b"T", 64, 1 << 21, 128, C.byref(A), C.byref(wide), FAKE, 0, None) == -2
 
 
 def test_grouped_validation(lib):
@@ -101,3 +104,5 @@ def test_grouped_validation(lib):
     assert f(4, None, 100, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -1
     assert f(5000, FAKE, 100, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -2
     assert f(4, FAKE, 100, 60, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -2
+    wide = _Operand(0x100000, 0x200000, 0x300000, 1 << 21, 128, 2, 0)
+    assert f(4, FAKE, 100, 1 << 21, 128, C.byref(A), C.byref(wide), FAKE, 0, None) == -2
