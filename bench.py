@@ -248,6 +248,54 @@ def row_wgrad(nv, synth, torch, dev, steps, warmup):
             "gemm_tn": kernel_entry(timer.avg_ms("gemm_tn"), 2.0 * Mo * Ni * T, "flops")}
 
 
+def row_dy_dual(nv, synth, torch, dev, steps, warmup):
+    """dY of the Super layer quantized for both backward GEMMs from one read
+    (ROW+SR for dgrad, COL+RHT+SR for wgrad, zero-code counts), against the
+    two separate calls that produce the same bits."""
+    T, Mo = 8192, 6144
+    mask = synth.rht_mask(6)
+    dys = [synth.laplace_device((T, Mo), 1e-3, 30 + i, dev, zero_frac=0.07) for i in range(3)]
+    qr, qc, z = nv.quantize_dual(dys[0], nv.Philox(107), nv.Philox(7), mask)
+    g = torch.empty(2, dtype=torch.float32, device=dev)
+    a = torch.empty(2, dtype=torch.float32, device=dev)
+    rr, rc = nv.Philox(107), nv.Philox(7)
+    timer = Timer(torch)
+
+    def dual(i):
+        rr.offset = rc.offset = i
+        dy = dys[i % 3]
+        timer.run("quantize_dual", lambda: nv.nvfp4_quantize_dual(
+            dy, rr, rc, mask, a, False, qr.codes, qr.scales, g[0:1], qc.codes, qc.scales, g[1:2],
+            z))
+
+    def separate(i):
+        rr.offset = rc.offset = i
+        dy = dys[i % 3]
+        timer.run("separate_row_sr", lambda: nv.nvfp4_quantize_1d(
+            dy, nv.NVFP4_BLOCK_ROW, nv.NVFP4_SR, rr, -1, a[0:1], False, qr.codes, qr.scales,
+            g[0:1]))
+        timer.run("separate_col_rht_sr", lambda: nv.nvfp4_quantize_1d(
+            dy, nv.NVFP4_BLOCK_COL, nv.NVFP4_SR, rc, mask, a[1:2], False, qc.codes, qc.scales,
+            g[1:2]))
+
+    ms, _ = timed(torch, timer, dual, steps, warmup)
+    ms_sep, _ = timed(torch, timer, separate, steps, warmup)
+    dual(0)
+    torch.cuda.synchronize()
+    zeros = z.cpu().tolist()
+    both = T * Mo * (2 + 2 * (0.5 + 1.0 / 16))  # one read, two sets of codes and scales
+    return {"workload": "dy_dual_super: dY bf16 [8192x6144] Laplace(1e-3), 7% zeros -> ROW+SR "
+                        "(dgrad) and COL+RHT16+SR (wgrad) from one read",
+            "ms_per_step": round(ms, 4), "ms_separate_calls": round(ms_sep, 4),
+            "quantize_dual": kernel_entry(timer.avg_ms("quantize_dual"), both, "bytes"),
+            "separate_row_sr": kernel_entry(timer.avg_ms("separate_row_sr"), q1d_bytes(T, Mo),
+                                            "bytes"),
+            "separate_col_rht_sr": kernel_entry(timer.avg_ms("separate_col_rht_sr"),
+                                                q1d_bytes(T, Mo), "bytes"),
+            "zero_code_fraction": {"row": round(zeros[0] / (T * Mo), 4),
+                                   "col_rht": round(zeros[1] / (T * Mo), 4)}}
+
+
 def row_grouped(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688, route_seed=9,
                 name="grouped_super"):
     counts, tok, offsets = synth.zipf_routing(8192, 512, 22, 1.1, route_seed)
@@ -328,7 +376,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,grouped,ultra,grouped_ultra,all")
+    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,ultra,grouped_ultra,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel for scaling "
@@ -388,7 +436,7 @@ def main():
     }
     extra = [r.strip() for r in args.rows.split(",") if r.strip()]
     if "all" in extra:
-        extra = ["wgrad", "grouped", "ultra", "grouped_ultra"]
+        extra = ["wgrad", "dy_dual", "grouped", "ultra", "grouped_ultra"]
     rows = {}
     del xs, ws
     torch.cuda.empty_cache()
@@ -396,6 +444,8 @@ def main():
         log(f"row {r}")
         if r == "wgrad":
             rows[r] = row_wgrad(nv, synth, torch, dev, max(5, args.steps // 5), 2)
+        elif r == "dy_dual":
+            rows[r] = row_dy_dual(nv, synth, torch, dev, max(5, args.steps // 5), 2)
         elif r == "grouped":
             rows[r] = row_grouped(nv, synth, torch, dev, max(5, args.steps // 5), 2)
         elif r == "grouped_ultra":

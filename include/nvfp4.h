@@ -142,6 +142,39 @@ int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t 
                           uint8_t* codes, uint8_t* scales, float* global_dec, void* stream);
 
 /*
+ * Both 1D quantizations of one gradient tensor (dY) from a single read of it
+ * (Super summary, Infra table; Ultra report section 2.2: dgrad and wgrad
+ * both consume dY in NVFP4, stochastically rounded, the wgrad operand after
+ * the Random Hadamard Transform), plus the count of zero-valued codes, the
+ * health signal of the Super report summary, section 2.2 (NVFP4
+ * pretraining: the share of zero-valued gradient elements).
+ * Results are bit-identical to the two calls
+ *   nvfp4_quantize_1d(x, ROW, SR, rng_row, -1,            amax[0], ...row outputs)
+ *   nvfp4_quantize_1d(x, COL, SR, rng_col, rht_sign_mask, amax[1], ...col outputs)
+ * with the same amax_is_input, so dgrad takes the ROW operand (blocks along
+ * the output features) and wgrad the COL one (blocks along the tokens).
+ *   x          [rows x cols], NVFP4_BF16 or NVFP4_FP32.
+ *   rng_row, rng_col  host structs, both required (two independent streams).
+ *   rht_sign_mask     -1 or a 16-bit mask, for the COL output only.
+ *   amax       device float[2]: ROW tensor amax, COL tensor amax (after the
+ *              transform); read when amax_is_input != 0, else written.
+ *   row_codes [rows x cols/2], row_scales [rows x cols/16], row_global_dec;
+ *   col_codes [rows x cols/2], col_scales [rows/16 x cols], col_global_dec.
+ *   zero_codes NULL, or device uint64[2] overwritten with the number of
+ *              codes of magnitude zero (0x0 or 0x8) in the ROW and in the
+ *              COL output.
+ * Shapes: rows % 16 == 0, cols % 32 == 0; rows == 0 or cols == 0 is a no-op
+ * (nothing is written, zero_codes included).  Alignment: x and codes 16
+ * bytes, scales and amax 4, zero_codes 8.
+ */
+int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                            const nvfp4_philox* rng_row, const nvfp4_philox* rng_col,
+                            int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                            uint8_t* row_codes, uint8_t* row_scales, float* row_global_dec,
+                            uint8_t* col_codes, uint8_t* col_scales, float* col_global_dec,
+                            uint64_t* zero_codes, void* stream);
+
+/*
  * 2D (16x16) block quantization of weights (Super summary, Infra table: 2D
  * block scaling for weights; the 16x16 size is the reading).  Round to
  * nearest even, no transform.  A batch of `batch` independent slices

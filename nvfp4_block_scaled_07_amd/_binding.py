@@ -63,6 +63,9 @@ def load():
     L.nvfp4_quantize_1d.restype = i32
     L.nvfp4_quantize_1d.argtypes = [vp, i32, i64, i64, i32, i32, C.POINTER(_Philox), i32, vp, i32,
                                      vp, vp, vp, vp]
+    L.nvfp4_quantize_dual.restype = i32
+    L.nvfp4_quantize_dual.argtypes = [vp, i32, i64, i64, C.POINTER(_Philox), C.POINTER(_Philox),
+                                       i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     L.nvfp4_quantize_2d.restype = i32
     L.nvfp4_quantize_2d.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, vp]
     L.nvfp4_rht16.restype = i32
@@ -151,6 +154,20 @@ def nvfp4_quantize_1d(x, axis, rounding, rng, rht_sign_mask, amax, amax_is_input
     _check("nvfp4_quantize_1d", st)
 
 
+def nvfp4_quantize_dual(x, rng_row, rng_col, rht_sign_mask, amax, amax_is_input, row_codes,
+                        row_scales, row_global_dec, col_codes, col_scales, col_global_dec,
+                        zero_codes, stream=None):
+    rows, cols = x.shape
+    pr = C.byref(_Philox(rng_row.seed, rng_row.offset, rng_row.rounds, 0))
+    pc = C.byref(_Philox(rng_col.seed, rng_col.offset, rng_col.rounds, 0))
+    st = load().nvfp4_quantize_dual(_p(x), _dtype_code(x), rows, cols, pr, pc, int(rht_sign_mask),
+                                    _p(amax), int(bool(amax_is_input)), _p(row_codes),
+                                    _p(row_scales), _p(row_global_dec), _p(col_codes),
+                                    _p(col_scales), _p(col_global_dec), _p(zero_codes),
+                                    _stream(stream))
+    _check("nvfp4_quantize_dual", st)
+
+
 def nvfp4_quantize_2d(w, amax, amax_is_input, codes, scales, global_dec, stream=None):
     if w.dim() == 2:
         batch, (rows, cols) = 1, w.shape
@@ -209,6 +226,27 @@ def quantize_1d(x, axis="row", rounding="rne", rng: Optional[Philox] = None, rht
     rnd = NVFP4_SR if rounding == "sr" else NVFP4_RNE
     nvfp4_quantize_1d(x, _BLOCKS[axis], rnd, rng, rht_sign_mask, a, given, codes, scales, g, stream)
     return QTensor(codes, scales, g, a, rows, cols, axis)
+
+
+def quantize_dual(x, rng_row: Philox, rng_col: Philox, rht_sign_mask=-1, amax=None,
+                  count_zeros=True, stream=None):
+    """ROW (dgrad) and COL (wgrad) quantization of one gradient from one read.
+    Returns (row QTensor, col QTensor, zero-code counts int64[2] or None)."""
+    rows, cols = x.shape
+    dev = x.device
+    rc = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    rs = torch.empty(_scale_shape("row", rows, cols), dtype=torch.uint8, device=dev)
+    cc = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    cs = torch.empty(_scale_shape("col", rows, cols), dtype=torch.uint8, device=dev)
+    g = torch.empty(2, dtype=torch.float32, device=dev)
+    given = amax is not None
+    a = (amax.reshape(2).to(torch.float32).clone() if given
+         else torch.empty(2, dtype=torch.float32, device=dev))
+    z = torch.empty(2, dtype=torch.int64, device=dev) if count_zeros else None
+    nvfp4_quantize_dual(x, rng_row, rng_col, rht_sign_mask, a, given, rc, rs, g[0:1], cc, cs,
+                        g[1:2], z, stream)
+    return (QTensor(rc, rs, g[0:1], a[0:1], rows, cols, "row"),
+            QTensor(cc, cs, g[1:2], a[1:2], rows, cols, "col"), z)
 
 
 def quantize_2d(w, amax=None, stream=None):

@@ -103,6 +103,51 @@ int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t 
   return device_status(nvfp4::launch_quantize_1d(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                            const nvfp4_philox* rng_row, const nvfp4_philox* rng_col,
+                            int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                            uint8_t* row_codes, uint8_t* row_scales, float* row_global_dec,
+                            uint8_t* col_codes, uint8_t* col_scales, float* col_global_dec,
+                            uint64_t* zero_codes, void* stream) {
+  if (!valid_dtype(x_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (rht_sign_mask < -1 || rht_sign_mask > 0xFFFF) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (!rng_row || !rng_col) return NVFP4_ERR_NULL;
+  if (rng_row->rounds < 1 || rng_row->rounds > 16 || rng_col->rounds < 1 || rng_col->rounds > 16)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return NVFP4_OK;  // empty: pointers may be NULL
+  if (!x || !amax || !row_codes || !row_scales || !row_global_dec || !col_codes || !col_scales ||
+      !col_global_dec)
+    return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(row_codes, 16) || !aligned(col_codes, 16) ||
+      !aligned(row_scales, 4) || !aligned(col_scales, 4) || !aligned(amax, 4) ||
+      !aligned(row_global_dec, 4) || !aligned(col_global_dec, 4) || !aligned(zero_codes, 8))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::QuantDualArgs a{};
+  a.x = x;
+  a.x_fp32 = x_dtype == NVFP4_FP32;
+  a.rows = rows;
+  a.cols = cols;
+  a.rht = rht_sign_mask >= 0;
+  a.mask = a.rht ? (uint32_t)rht_sign_mask : 0u;
+  a.seed_r = rng_row->seed;
+  a.offset_r = rng_row->offset;
+  a.rounds_r = rng_row->rounds;
+  a.seed_c = rng_col->seed;
+  a.offset_c = rng_col->offset;
+  a.rounds_c = rng_col->rounds;
+  a.amax = amax;
+  a.amax_is_input = amax_is_input != 0;
+  a.row_codes = row_codes;
+  a.row_scales = row_scales;
+  a.row_gdec = row_global_dec;
+  a.col_codes = col_codes;
+  a.col_scales = col_scales;
+  a.col_gdec = col_global_dec;
+  a.zeros = reinterpret_cast<unsigned long long*>(zero_codes);
+  return device_status(nvfp4::launch_quantize_dual(a, static_cast<hipStream_t>(stream)));
+}
+
 int32_t nvfp4_quantize_2d(const void* w, int32_t w_dtype, int64_t batch, int64_t rows,
                           int64_t cols, float* amax, int32_t amax_is_input, uint8_t* codes,
                           uint8_t* scales, float* global_dec, void* stream) {

@@ -81,28 +81,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// The same with a wave-uniform count (a count above 15 waits for all).
-__device__ __forceinline__ void wait_vm_lgkm0_upto(int n) {
-  switch (n) {
-    case 1: wait_vm_lgkm0<1>(); break;
-    case 2: wait_vm_lgkm0<2>(); break;
-    case 3: wait_vm_lgkm0<3>(); break;
-    case 4: wait_vm_lgkm0<4>(); break;
-    case 5: wait_vm_lgkm0<5>(); break;
-    case 6: wait_vm_lgkm0<6>(); break;
-    case 7: wait_vm_lgkm0<7>(); break;
-    case 8: wait_vm_lgkm0<8>(); break;
-    case 9: wait_vm_lgkm0<9>(); break;
-    case 10: wait_vm_lgkm0<10>(); break;
-    case 11: wait_vm_lgkm0<11>(); break;
-    case 12: wait_vm_lgkm0<12>(); break;
-    case 13: wait_vm_lgkm0<13>(); break;
-    case 14: wait_vm_lgkm0<14>(); break;
-    case 15: wait_vm_lgkm0<15>(); break;
-    default: wait_vm_lgkm0<0>(); break;
-  }
-}
-
 // ---- K-major stage layout --------------------------------------------------------------------
 // Row r of a stage holds RB code bytes as UR = RB/16 units of 16 bytes; unit
 // u (k = 32u .. 32u+31 of the stage) sits in slot u ^ kmaj_swz(r).  A 16-byte

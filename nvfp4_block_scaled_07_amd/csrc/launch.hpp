@@ -27,6 +27,27 @@ struct QuantArgs {
   float* gdec;
 };
 
+// Both 1D quantizations of one gradient tensor from one read: ROW blocks with
+// stochastic rounding (no transform) and COL blocks with stochastic rounding
+// and, when rht, the transform.  amax[0] is the ROW tensor amax, amax[1] the
+// COL one; zeros (nullable) receives the zero-magnitude code counts.
+struct QuantDualArgs {
+  const void* x;
+  bool x_fp32;
+  int64_t rows, cols;
+  bool rht;
+  uint32_t mask;
+  uint64_t seed_r, offset_r, seed_c, offset_c;
+  uint32_t rounds_r, rounds_c;
+  float* amax;  // [2]
+  bool amax_is_input;
+  uint8_t *row_codes, *row_scales;
+  float* row_gdec;
+  uint8_t *col_codes, *col_scales;
+  float* col_gdec;
+  unsigned long long* zeros;  // [2] or null
+};
+
 struct Quant2dArgs {
   const void* w;
   bool w_fp32;
@@ -67,6 +88,7 @@ struct GroupedArgs {
 
 hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st);
 hipError_t launch_quantize_2d(const Quant2dArgs& a, hipStream_t st);
+hipError_t launch_quantize_dual(const QuantDualArgs& a, hipStream_t st);
 hipError_t launch_rht16(const void* x, bool x_fp32, int64_t rows, int64_t cols, int axis,
                         uint32_t mask, float* y, hipStream_t st);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gdec,

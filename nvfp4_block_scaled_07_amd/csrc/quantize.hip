@@ -129,17 +129,6 @@ __device__ __forceinline__ uint32_t block_code(float a, float k) {
          0xFFu;
 }
 
-// Two values -> two RNE codes in byte `sel` of `old` (sel folds to a
-// constant once the caller's loop is unrolled).
-__device__ __forceinline__ uint32_t cvt_fp4_byte(uint32_t old, float a, float b, int sel) {
-  switch (sel) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, 3);
-  }
-}
-
 // 8 values (already multiplied by the block reciprocal) -> 8 RNE codes.
 __device__ __forceinline__ uint32_t pack8_rne(const float y[8]) {
   uint32_t w = 0;
@@ -155,22 +144,33 @@ __device__ __forceinline__ uint32_t pack8_rne(const float y[8]) {
 // run few, large workgroups (kAmaxThreads) and one atomic per workgroup.
 constexpr int kAmaxThreads = 1024;
 
-__device__ __forceinline__ void block_max_to(float m, float* out) {
-  __shared__ float red[kAmaxThreads / 64];
+// m0 -> out0 and, when out1 is given, m1 -> out1 (one reduction pass).
+__device__ __forceinline__ void block_max_to(float m0, float* out0, float m1 = 0.0f,
+                                             float* out1 = nullptr) {
+  __shared__ float red[2][kAmaxThreads / 64];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  for (int o = 32; o > 0; o >>= 1) {
+    m0 = fmaxf(m0, __shfl_xor(m0, o));
+    m1 = fmaxf(m1, __shfl_xor(m1, o));
+  }
   int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = m;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = m0;
+    red[1][w] = m1;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float r = red[0];
-    for (int i = 1; i < (int)(blockDim.x >> 6); i++) r = fmaxf(r, red[i]);
-    // Thousands of workgroups target one address: skip the atomic when the
-    // value already there is at least ours (it only grows, and the max of the
-    // atomics performed is the same), which removes most of the contention.
-    unsigned int* p = reinterpret_cast<unsigned int*>(out);
-    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < __float_as_uint(r))
-      atomicMax(p, __float_as_uint(r));
+    for (int k = 0; k < (out1 ? 2 : 1); k++) {
+      float r = red[k][0];
+      for (int i = 1; i < (int)(blockDim.x >> 6); i++) r = fmaxf(r, red[k][i]);
+      // Thousands of workgroups target one address: skip the atomic when the
+      // value already there is at least ours (it only grows, and the max of
+      // the atomics performed is the same), which removes most of the
+      // contention.
+      unsigned int* p = reinterpret_cast<unsigned int*>(k ? out1 : out0);
+      if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < __float_as_uint(r))
+        atomicMax(p, __float_as_uint(r));
+    }
   }
 }
 
@@ -186,10 +186,12 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 // contiguous across the wave) before reducing them.
 constexpr int kAmaxUnroll = 4;
 
+// amax2 (nullable): a second target that receives the same maximum.
 template <typename T, bool kRHT>
 __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __restrict__ x,
                                                                  int64_t chunks, uint32_t mask,
-                                                                 float* __restrict__ amax) {
+                                                                 float* __restrict__ amax,
+                                                                 float* __restrict__ amax2) {
   const T* xs = x + (int64_t)blockIdx.y * chunks * 8;
   float m = 0.0f;
   constexpr int U = (In<T>::kBf16 && !kRHT) ? kAmaxUnroll : 2;
@@ -228,26 +230,31 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
       }
     }
   }
-  block_max_to(m, amax + blockIdx.y);
+  block_max_to(m, amax + blockIdx.y, m, amax2);
 }
 
 // ---- amax of COL blocks with the transform (lane: 8 cols x 16 rows) ---------------------
 // 256-thread workgroups: each lane holds a 16 x 8 tile and its transform,
-// too many registers for the large amax workgroups.
-template <typename T>
+// too many registers for the large amax workgroups.  kPlain: also the max of
+// |x| itself (into amax_plain), from the same loads.
+template <typename T, bool kPlain>
 __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restrict__ x,
                                                                 int64_t rows, int64_t cols,
                                                                 uint32_t mask,
-                                                                float* __restrict__ amax) {
+                                                                float* __restrict__ amax,
+                                                                float* __restrict__ amax_plain) {
   const int64_t cg = cols / 8;
   const int64_t units = (rows / 16) * cg;
-  float m = 0.0f;
+  float m = 0.0f, mp = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
     int64_t g = u / cg, c0 = (u % cg) * 8;
     float v[16][8];
 #pragma unroll
     for (int r = 0; r < 16; r++) In<T>::load8(x + (g * 16 + r) * cols + c0, v[r]);
+    if (kPlain)
+#pragma unroll
+      for (int r = 0; r < 16; r++) mp = fmaxf(mp, max8(v[r]));
 #pragma unroll
     for (int c = 0; c < 8; c++) {
       float col[16];
@@ -258,7 +265,10 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
       for (int r = 0; r < 16; r++) m = fmaxf(m, __builtin_fabsf(col[r]));
     }
   }
-  block_max_to(m, amax);
+  if (kPlain)
+    block_max_to(m, amax, mp, amax_plain);
+  else
+    block_max_to(m, amax);
 }
 
 // ---- ROW quantizer ---------------------------------------------------------------------------
@@ -337,6 +347,10 @@ struct RawRow<uint16_t> {  // 8 bf16 = 4 words; column pair p is word p
     a = __uint_as_float(w << 16);
     b = __uint_as_float(w & 0xFFFF0000u);
   }
+  __device__ __forceinline__ void all(float v[8]) const {
+#pragma unroll
+    for (int p = 0; p < 4; p++) pair(p, v[2 * p], v[2 * p + 1]);
+  }
 };
 
 template <>
@@ -352,30 +366,23 @@ struct RawRow<float> {  // named words (no array, so selects stay in registers)
     a = __uint_as_float(wa);
     b = __uint_as_float(wb);
   }
+  __device__ __forceinline__ void all(float v[8]) const {
+#pragma unroll
+    for (int p = 0; p < 4; p++) pair(p, v[2 * p], v[2 * p + 1]);
+  }
 };
 
+// COL encode of one lane's 8 columns x 16 rows (8 blocks), from its raw
+// rows: out[r] gets the 8 codes of row r, sc[0..1] the 8 scale bytes.
 template <typename T, bool kSR, bool kRHT>
-__global__ __launch_bounds__(kThreads) void quant_col_kernel(
-    const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
-    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
-  __shared__ float rtab[128];
-  const TensorScales ts = tensor_scales(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
-  const int64_t cg = cols / 8;
-  const int64_t units = (rows / 16) * cg;
-  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t uc = u < units ? u : units - 1;
-  const int64_t g = uc / cg, c0 = (uc % cg) * 8;
-  RawRow<T> raw[16];
-#pragma unroll
-  for (int r = 0; r < 16; r++) raw[r].load(x + (g * 16 + r) * cols + c0);
-  build_recip_table(rtab, ts.S);
-  if (u >= units) return;
-  uint32_t out[16];
+__device__ __forceinline__ void col_encode(const RawRow<T> (&raw)[16], int64_t rows, int64_t g,
+                                           int64_t c0, const TensorScales& ts,
+                                           const float* rtab, uint32_t mask, uint64_t seed,
+                                           uint64_t offset, uint32_t rounds, uint32_t (&out)[16],
+                                           uint32_t (&sc)[2]) {
 #pragma unroll
   for (int r = 0; r < 16; r++) out[r] = 0;
-  uint32_t sc[2] = {0, 0};
+  sc[0] = sc[1] = 0;
 #pragma unroll 1
   for (int cp = 0; cp < 4; cp++) {  // column pairs (c, c+1) share one code byte per row
     float col[2][16];
@@ -411,12 +418,140 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
                   << (8 * cp);
     }
   }
+}
+
+template <typename T, bool kSR, bool kRHT>
+__global__ __launch_bounds__(kThreads) void quant_col_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
+    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
+  __shared__ float rtab[128];
+  const TensorScales ts = tensor_scales(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
+  const int64_t cg = cols / 8;
+  const int64_t units = (rows / 16) * cg;
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t uc = u < units ? u : units - 1;
+  const int64_t g = uc / cg, c0 = (uc % cg) * 8;
+  RawRow<T> raw[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) raw[r].load(x + (g * 16 + r) * cols + c0);
+  build_recip_table(rtab, ts.S);
+  if (u >= units) return;
+  uint32_t out[16], sc[2];
+  col_encode<T, kSR, kRHT>(raw, rows, g, c0, ts, rtab, mask, seed, offset, rounds, out, sc);
 #pragma unroll
   for (int r = 0; r < 16; r++)
     *reinterpret_cast<uint32_t*>(codes + (g * 16 + r) * (cols / 2) + c0 / 2) = out[r];
   uint32_t* sp = reinterpret_cast<uint32_t*>(scales + g * cols + c0);
   sp[0] = sc[0];
   sp[1] = sc[1];
+}
+
+// ---- both 1D quantizations of a gradient from one read ---------------------------------------
+// Zero-magnitude codes (0x0 or 0x8) among the 8 nibbles of w.
+__device__ __forceinline__ uint32_t zero_nibbles(uint32_t w) {
+  const uint32_t m = w & 0x77777777u;
+  return 8u - (uint32_t)__builtin_popcount((m | (m >> 1) | (m >> 2)) & 0x11111111u);
+}
+
+// Lane: 8 columns x 16 rows, as the COL quantizer.  First its COL blocks,
+// exactly as the COL quantizer (transform when kRHT).  Then the ROW blocks
+// (1 x 16 along columns, no transform, stochastic rounding) of each of its 16
+// rows, which span lanes 2t and 2t+1 (cols % 16 == 0 keeps the pairs in one
+// row), exactly as the ROW quantizer forms them: block max across the pair,
+// chunk i = (row * cols + c0) / 8 draws Philox call i of the ROW stream.  The
+// ROW pass takes one row at a time and reads its 16 bytes again (a cache hit:
+// the workgroup has just loaded them), which keeps it out of the COL pass's
+// registers.  Both outputs are bit-identical to the two separate calls.
+// zeros (nullable): the zero-magnitude codes of each output, summed per
+// workgroup and added with one atomic each (an atomic per wave on the same
+// two addresses serializes in L2 and doubled the kernel's time).
+template <typename T, bool kRHT>
+__global__ __launch_bounds__(kThreads) void quant_dual_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
+    uint32_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
+    float* __restrict__ row_gdec, uint8_t* __restrict__ col_codes,
+    uint8_t* __restrict__ col_scales, float* __restrict__ col_gdec, uint32_t mask,
+    uint64_t seed_r, uint64_t offset_r, uint32_t rounds_r, uint64_t seed_c, uint64_t offset_c,
+    uint32_t rounds_c, unsigned long long* __restrict__ zeros) {
+  __shared__ float rtab_r[128], rtab_c[128];
+  const TensorScales tr = tensor_scales(amax[0]), tc = tensor_scales(amax[1]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *row_gdec = tr.g;
+    *col_gdec = tc.g;
+  }
+  const int64_t cg = cols / 8;
+  const int64_t units = (rows / 16) * cg;  // even (cols % 16 == 0): lane pairs agree below
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool active = u < units;
+  const int64_t uc = active ? u : units - 2 + (u & 1);  // the last pair, same parity
+  const int64_t g = uc / cg, c0 = (uc % cg) * 8;
+  RawRow<T> raw[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) raw[r].load(x + (g * 16 + r) * cols + c0);
+  for (int e = threadIdx.x; e < 128; e += blockDim.x) {
+    const float d = e4m3_decode((uint32_t)e);
+    rtab_r[e] = block_recip(tr.S, d);
+    rtab_c[e] = block_recip(tc.S, d);
+  }
+  __syncthreads();
+  uint32_t zr = 0, zc = 0;
+  {
+    uint32_t out[16], sc[2];
+    col_encode<T, true, kRHT>(raw, rows, g, c0, tc, rtab_c, mask, seed_c, offset_c, rounds_c,
+                              out, sc);
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        *reinterpret_cast<uint32_t*>(col_codes + (g * 16 + r) * (cols / 2) + c0 / 2) = out[r];
+        zc += zero_nibbles(out[r]);
+      }
+      uint32_t* sp = reinterpret_cast<uint32_t*>(col_scales + g * cols + c0);
+      sp[0] = sc[0];
+      sp[1] = sc[1];
+    }
+  }
+  const bool even = (uc & 1) == 0;
+#pragma unroll 1
+  for (int r = 0; r < 16; r++) {
+    RawRow<T> rr;  // this row's segment again (just loaded: a cache hit)
+    rr.load(x + (g * 16 + r) * cols + c0);
+    float v[8];
+    rr.all(v);
+    const float m = max8(v);
+    const uint32_t e = block_code(fmaxf(m, xor1(m)), tr.k);
+    const float rc = rtab_r[e];
+    const int64_t chunk = (g * 16 + r) * cg + c0 / 8;
+    const Philox4 p = sr_call((uint64_t)chunk, seed_r, offset_r, rounds_r);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int t = 0; t < 8; t++) packed |= e2m1_sr(v[t] * rc, sr_slot(p, t)) << (4 * t);
+    if (active) {
+      row_codes[chunk] = packed;
+      if (even) row_scales[(g * 16 + r) * (cols / 16) + c0 / 16] = (uint8_t)e;
+      zr += zero_nibbles(packed);
+    }
+  }
+  if (zeros) {  // per workgroup: one atomic per output
+    __shared__ uint32_t wz[2][kThreads / 64];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      zr += __shfl_xor(zr, o);
+      zc += __shfl_xor(zc, o);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      wz[0][threadIdx.x >> 6] = zr;
+      wz[1][threadIdx.x >> 6] = zc;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      unsigned long long t = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; w++) t += wz[threadIdx.x][w];
+      if (t) atomicAdd(zeros + threadIdx.x, t);
+    }
+  }
 }
 
 // ---- 2D quantizer (lane: 8 cols x 16 rows; lanes 2t, 2t+1 = one 16x16 block) ------------------
@@ -550,8 +685,9 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 1);
     if (a.axis == kBlockCol && a.rht) {
       int64_t units = (a.rows / 16) * (a.cols / 8);
-      amax_col_rht_kernel<T><<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads,
-                               0, st>>>(x, a.rows, a.cols, a.mask, a.amax);
+      amax_col_rht_kernel<T, false><<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024),
+                                      kThreads, 0, st>>>(x, a.rows, a.cols, a.mask, a.amax,
+                                                         nullptr);
     } else {
       int64_t chunks = a.rows * a.cols / 8;
       // ROW with the transform needs the pair exchange; COL amax without the
@@ -559,10 +695,10 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
       const int u = (!a.x_fp32 && !(a.rht && a.axis == kBlockRow)) ? kAmaxUnroll : 2;
       if (a.rht && a.axis == kBlockRow)
         amax_flat_kernel<T, true><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-            x, chunks, a.mask, a.amax);
+            x, chunks, a.mask, a.amax, nullptr);
       else
         amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-            x, chunks, 0, a.amax);
+            x, chunks, 0, a.amax, nullptr);
     }
   }
   if (a.axis == kBlockRow) {
@@ -604,7 +740,7 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
     // about 512 workgroups in all, at least one per slice
     const int64_t per = a.batch >= 512 ? 1 : 512 / a.batch;
     dim3 grid((unsigned)amax_grid(chunks, u, per), (unsigned)a.batch);
-    amax_flat_kernel<T, false><<<grid, kAmaxThreads, 0, st>>>(w, chunks, 0, a.amax);
+    amax_flat_kernel<T, false><<<grid, kAmaxThreads, 0, st>>>(w, chunks, 0, a.amax, nullptr);
   }
   int64_t units = (a.rows / 16) * (a.cols / 8);
   dim3 grid((unsigned)cdiv(units, kThreads), (unsigned)a.batch);
@@ -628,7 +764,42 @@ hipError_t launch_rht16_t(const void* xv, int64_t rows, int64_t cols, int axis, 
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_quantize_dual_t(const QuantDualArgs& a, hipStream_t st) {
+  const T* x = static_cast<const T*>(a.x);
+  const int64_t units = (a.rows / 16) * (a.cols / 8);
+  if (!a.amax_is_input) {
+    fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 2);
+    if (a.rht) {  // transform max for COL, plain max for ROW, one read
+      amax_col_rht_kernel<T, true><<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024),
+                                     kThreads, 0, st>>>(x, a.rows, a.cols, a.mask, a.amax + 1,
+                                                        a.amax);
+    } else {  // the same plain max for both
+      const int64_t chunks = a.rows * a.cols / 8;
+      const int u = a.x_fp32 ? 2 : kAmaxUnroll;
+      amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
+          x, chunks, 0, a.amax, a.amax + 1);
+    }
+  }
+  if (a.zeros) fill_zero_kernel<<<1, 64, 0, st>>>(reinterpret_cast<float*>(a.zeros), 4);
+  const int grid = (int)cdiv(units, kThreads);
+  uint32_t* rc = reinterpret_cast<uint32_t*>(a.row_codes);
+#define NVFP4_DUAL(RHT)                                                                       \
+  quant_dual_kernel<T, RHT><<<grid, kThreads, 0, st>>>(                                       \
+      x, a.rows, a.cols, a.amax, rc, a.row_scales, a.row_gdec, a.col_codes, a.col_scales,     \
+      a.col_gdec, a.mask, a.seed_r, a.offset_r, a.rounds_r, a.seed_c, a.offset_c, a.rounds_c, \
+      a.zeros)
+  if (a.rht) NVFP4_DUAL(true);
+  else NVFP4_DUAL(false);
+#undef NVFP4_DUAL
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_quantize_dual(const QuantDualArgs& a, hipStream_t st) {
+  return a.x_fp32 ? launch_quantize_dual_t<float>(a, st) : launch_quantize_dual_t<uint16_t>(a, st);
+}
 
 hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st) {
   return a.x_fp32 ? launch_quantize_1d_t<float>(a, st) : launch_quantize_1d_t<uint16_t>(a, st);

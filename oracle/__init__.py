@@ -189,6 +189,14 @@ def quantize(x, block, rounding=RNE, seed=0, offset=0, rounds=5, rht_mask=-1,
     return dict(codes=codes, scales=scales, amax=amax_out, g=g)
 
 
+def zero_codes(codes):
+    """Number of codes of magnitude zero (0x0 or 0x8) in packed codes, two per
+    byte: the count behind the share of zero-valued gradient elements that the
+    Super report summary, section 2.2 (NVFP4 pretraining), watches."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return int(np.count_nonzero((c & 0x7) == 0) + np.count_nonzero(((c >> 4) & 0x7) == 0))
+
+
 def amax(x, block=ROW, rht_mask=-1):
     x, is_bf16, batch, rows, cols = _as_input(x)
     out = np.zeros(batch, dtype=np.float32)

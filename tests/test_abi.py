@@ -78,6 +78,27 @@ def test_quantize_1d_validation(lib):
     assert q(*args(rows=0)) == 0            # empty: nothing to do
 
 
+def test_quantize_dual_validation(lib):
+    from nvfp4_block_scaled_07_amd._binding import _Philox
+    f = lib.nvfp4_quantize_dual
+    r = C.byref(_Philox(1, 0, 5, 0))
+    bad_rounds = C.byref(_Philox(1, 0, 0, 0))
+    P = FAKE
+
+    def call(rows=64, cols=128, rr=r, rc=r, mask=0x1234, zeros=P, x=P):
+        return f(x, 0, rows, cols, rr, rc, mask, P, 0, P, P, P, P, P, P, zeros, None)
+
+    assert call(rows=40) == -2                   # rows % 16
+    assert call(cols=80) == -2                   # cols % 32
+    assert call(rr=None) == -1 and call(rc=None) == -1
+    assert call(rc=bad_rounds) == -5
+    assert call(mask=0x10000) == -5 and call(mask=-2) == -5
+    assert call(zeros=C.c_void_p(0x100004)) == -3   # zero_codes needs 8-byte alignment
+    assert call(x=None) == -1
+    assert call(rows=0) == 0                     # empty: nothing launched
+    assert f(P, 7, 64, 128, r, r, -1, P, 0, P, P, P, P, P, P, None, None) == -5  # dtype
+
+
 def test_gemm_validation(lib):
     from nvfp4_block_scaled_07_amd._binding import _Operand
     A = _Operand(0x100000, 0x200000, 0x300000, 64, 128, 0, 0)

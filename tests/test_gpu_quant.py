@@ -172,6 +172,56 @@ def test_tiny_config():
     assert_same(got.view(np.uint32), want.view(np.uint32), "dequantized bits")
 
 
+# ---- both quantizations of a gradient from one read -------------------------------------------------
+def _check_dual(x, dtype, mask, seeds=(11, 12), offsets=(3, 0), rounds=(5, 5), amax=None):
+    dev = device()
+    t, xo = device_input(x, dtype, dev)
+    rr = nv.Philox(seeds[0], offsets[0], rounds[0])
+    rc = nv.Philox(seeds[1], offsets[1], rounds[1])
+    a_t = None if amax is None else torch.tensor(amax, dtype=torch.float32, device=dev)
+    qr, qc, z = nv.quantize_dual(t, rr, rc, mask, amax=a_t)
+    ref_r = O.quantize(xo, "row", rounding=O.SR, seed=seeds[0], offset=offsets[0],
+                       rounds=rounds[0], amax=None if amax is None else amax[0])
+    ref_c = O.quantize(xo, "col", rounding=O.SR, seed=seeds[1], offset=offsets[1],
+                       rounds=rounds[1], rht_mask=mask, amax=None if amax is None else amax[1])
+    for got, ref, name in ((to_np(qr), ref_r, "row"), (to_np(qc), ref_c, "col")):
+        assert_same(got["amax"][0], ref["amax"], name + " amax")
+        assert_same(np.float32(got["g"]), ref["g"], name + " g")
+        assert_same(got["scales"], ref["scales"], name + " scales")
+        assert_same(got["codes"], ref["codes"], name + " codes")
+    zeros = z.cpu().numpy()
+    assert zeros[0] == O.zero_codes(ref_r["codes"]) and zeros[1] == O.zero_codes(ref_c["codes"])
+    return qr, qc, zeros
+
+
+@pytest.mark.parametrize("shape", [(16, 32), (48, 96), (272, 160), (64, 2080), (1008, 64)])
+@pytest.mark.parametrize("rht", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_dual_small(shape, rht, dtype):
+    """Several workgroups and a ragged last one (units not a multiple of 256)."""
+    x = make_input("laplace_zeros", shape, seed=shape[0] + 3 * shape[1])
+    _check_dual(x, dtype, 0x6C2B if rht else -1)
+
+
+@pytest.mark.parametrize("kind", ["normal", "wide", "tiny", "zeros"])
+def test_quantize_dual_distributions(kind):
+    x = make_input(kind, (64, 256), seed=17)
+    _check_dual(x, "bf16", 0x0F0F, seeds=(2**40 + 1, 7), offsets=(2**33, 5), rounds=(10, 1))
+
+
+def test_quantize_dual_amax_input():
+    x = make_input("normal", (96, 128), seed=6)
+    _check_dual(x, "bf16", 0x1111, amax=[9.5, 3.25])
+    _check_dual(x, "fp32", -1, amax=[0.5, 40.0])
+
+
+def test_quantize_dual_empty():
+    dev = device()
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    qr, qc, z = nv.quantize_dual(x, nv.Philox(1), nv.Philox(2), 0x5)
+    assert qr.codes.numel() == 0 and qc.codes.numel() == 0
+
+
 # ---- full-size workloads -------------------------------------------------------------------------
 def test_full_fprop_super_inputs():
     w = synth.WORKLOADS["fprop_super"]
@@ -225,3 +275,23 @@ def test_full_grouped_super_weights_sampled():
         assert_same(q.codes[e].cpu().numpy(), ref["codes"], f"codes of expert {e}")
         assert_same(q.scales[e].cpu().numpy(), ref["scales"], f"scales of expert {e}")
         assert g[e] == ref["g"]
+
+
+def test_full_wgrad_super_dy_dual():
+    """dY of the wgrad Super workload [8192 x 6144] (Laplace, 7% exact zeros):
+    the single-read quantizer against the oracle's ROW (dgrad) and COL+RHT
+    (wgrad) quantizations, and equal to the two separate device calls."""
+    w = synth.WORKLOADS["wgrad_super"]
+    dev = device()
+    dy = synth.laplace((w["tokens"], w["out"]), w["dy_b"], w["dy_seed"], w["zero_frac"],
+                       w["zero_seed"])
+    mask = synth.rht_mask(w["mask_seed"])
+    qr, qc, zeros = _check_dual(dy, "bf16", mask, seeds=(w["philox_seed"] + 100, w["philox_seed"]),
+                                offsets=(0, 0))
+    t, _ = device_input(dy, "bf16", dev)
+    sr = nv.quantize_1d(t, "row", "sr", nv.Philox(w["philox_seed"] + 100))
+    sc = nv.quantize_1d(t, "col", "sr", nv.Philox(w["philox_seed"]), mask)
+    for a, b, name in ((qr, sr, "row"), (qc, sc, "col")):
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales), name
+    n = dy.size
+    print(f"dY zero-code fraction: ROW {zeros[0] / n:.4f}, COL+RHT {zeros[1] / n:.4f}")

@@ -5,7 +5,8 @@ closed form of the per-tensor scales, invariants that hold for any input
 (the amax element takes the top code under the top block scale; COL equals
 the transpose of ROW, random bits included; windows equal the full call;
 the fused transform equals transform-then-quantize), the round-to-nearest
-error bound, and exact round trips of representable tensors.
+error bound, exact round trips of representable tensors, and zero-code counts
+of tensors whose zero codes are known by construction.
 """
 import numpy as np
 import pytest
@@ -211,3 +212,58 @@ def test_shape_errors():
         O.quantize(np.zeros((24, 32), dtype=np.float32), "col")
     with pytest.raises(ValueError):
         O.quantize(np.zeros((16, 32), dtype=np.float32), "2d", rounding=O.SR)
+
+
+@pytest.mark.parametrize("rounding", [O.RNE, O.SR])
+def test_zero_codes_row_and_col_count_exact_zeros(rounding):
+    """Exact zeros always encode to magnitude 0 (their fraction is 0, so
+    stochastic rounding never rounds them up); every other element equals its
+    block's max in magnitude and takes a nonzero code.  So the count is the
+    number of exact zeros, whatever the random bits."""
+    rng = np.random.default_rng(21)
+    rows, cols = 64, 96
+    x = np.where(rng.random((rows, cols)) < 0.3, 0.0,
+                 np.where(rng.random((rows, cols)) < 0.5, -1.0, 1.0)).astype(np.float32)
+    # one block of each kind entirely zero, one with a lone nonzero element
+    x[0, :16] = 0.0
+    x[16:32, 5] = 0.0
+    x[2, 16:32] = 0.0
+    x[2, 20] = 3.0  # a lone nonzero element: its block's max
+    zeros = int(np.count_nonzero(x == 0.0))
+    for block in ("row", "col"):
+        # make every nonzero element of a block equal the block max in
+        # magnitude (zeros stay zeros)
+        y = x.copy()
+        if block == "row":
+            b = y.reshape(rows, cols // 16, 16)
+        else:
+            b = y.reshape(rows // 16, 16, cols).transpose(0, 2, 1)
+        m = np.abs(b).max(axis=-1, keepdims=True)
+        b[...] = np.sign(b) * m
+        q = O.quantize(y, block, rounding=rounding, seed=5)
+        assert O.zero_codes(q["codes"]) == zeros, block
+
+
+def test_zero_codes_col_with_transform():
+    """With the 16-point transform a block with one nonzero value v becomes
+    +-v/4 in all 16 places (every Hadamard column is +-1), all at the block
+    max: no zero codes.  An all-zero block stays zero: 16 zero codes."""
+    rows, cols = 64, 64
+    x = np.zeros((rows, cols), dtype=np.float32)
+    rng = np.random.default_rng(3)
+    zero_blocks = 0
+    for gb in range(rows // 16):
+        for c in range(cols):
+            if rng.random() < 0.4:
+                zero_blocks += 1
+            else:
+                x[16 * gb + rng.integers(16), c] = np.float32(rng.choice([-2.0, 0.5, 7.0]))
+    for rounding in (O.RNE, O.SR):
+        q = O.quantize(x, "col", rounding=rounding, seed=9, rht_mask=0xB6D1)
+        assert O.zero_codes(q["codes"]) == 16 * zero_blocks
+
+
+def test_zero_codes_counts_both_nibbles():
+    codes = np.array([[0x00, 0x88, 0x80, 0x17, 0x9F]], dtype=np.uint8)
+    # nibbles: 0,0 | 8,8 | 0,8 | 7,1 | F,9 -> zero magnitude: 6
+    assert O.zero_codes(codes) == 6
