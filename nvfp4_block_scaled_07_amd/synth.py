@@ -107,13 +107,23 @@ def normal_device(shape, std, seed, device, dtype=torch.bfloat16):
     return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(dtype)
 
 
+def laplace_from_uniform(r, b):
+    """Laplace(0, b) by inverse CDF from uniform draws r in [0, 1) (float64),
+    as float32.  |r - 1/2| is kept below 1/2: r = 0 (one draw in 2^24 for
+    float32 draws, so several times in any large tensor) would give
+    log1p(-1) = -inf, and one infinite element makes a whole tensor's amax,
+    scales and codes meaningless."""
+    u = r - 0.5
+    a = u.abs().clamp_(max=0.5 - 2.0 ** -40)
+    return (-b * torch.sign(u) * torch.log1p(-2.0 * a)).to(torch.float32)
+
+
 def laplace_device(shape, b, seed, device, zero_frac=0.0, dtype=torch.bfloat16):
     """Laplace(0, b) on the device (inverse CDF of a uniform), optionally with
     a Bernoulli(zero_frac) mask of exact zeros."""
     g = torch.Generator(device=device)
     g.manual_seed(seed)
-    u = torch.rand(shape, generator=g, device=device, dtype=torch.float32) - 0.5
-    x = -b * torch.sign(u) * torch.log1p(-2.0 * u.abs())
+    x = laplace_from_uniform(torch.rand(shape, generator=g, device=device, dtype=torch.float64), b)
     if zero_frac > 0.0:
         z = torch.rand(shape, generator=g, device=device, dtype=torch.float32) < zero_frac
         x = x.masked_fill(z, 0.0)

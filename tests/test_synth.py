@@ -41,3 +41,14 @@ def test_bf16_bits_roundtrip():
     bits = synth.bf16_bits(t)
     back = (bits.astype(np.uint32) << 16).view(np.float32)
     assert np.array_equal(back, t.float().numpy())
+
+
+def test_device_laplace_is_finite_at_the_uniform_edges():
+    """r = 0 (which float32 draws hit once in 2^24) must not give -inf."""
+    import torch
+    r = torch.tensor([0.0, 2.0 ** -24, 0.25, 0.5, 0.75, 1.0 - 2.0 ** -53], dtype=torch.float64)
+    x = synth.laplace_from_uniform(r, 1e-3)
+    assert torch.isfinite(x).all()
+    assert x[0] < 0 < x[-1] and x[3] == 0.0
+    big = synth.laplace_device((1 << 20,), 1e-3, 3, "cpu", zero_frac=0.07)
+    assert torch.isfinite(big.float()).all()
