@@ -248,6 +248,44 @@ int32_t nvfp4_grouped_gemm(int64_t groups, const int64_t* row_offsets, int64_t t
                            int64_t N, int64_t K, const nvfp4_operand* A, const nvfp4_operand* B,
                            void* C, int32_t c_dtype, void* stream);
 
+/*
+ * Grouped dgrad for the routed experts (Super report summary, section 2.2:
+ * the routed-expert GEMMs run in NVFP4; Ultra report section 2.2: dgrad in
+ * NVFP4 with stochastically rounded gradients).  For every group e:
+ * C[o_e : o_{e+1}] = A[o_e : o_{e+1}] B_e * gA * gB_e, with
+ *   A: dY [total_rows x K], ROW blocks (nvfp4_quantize_1d / _dual, SR), one g;
+ *   B: `groups` slices stored [K x N] (B->rows = K, B->cols = N), 2D or COL
+ *      blocks, global_dec [groups] -- the same 2D codes as the fprop's
+ *      [N x K] slices when the fprop weight is W_e^T (square blocks);
+ *   C: [total_rows x N] bf16 or fp32; row_offsets as nvfp4_grouped_gemm.
+ * Shapes: K % 64 == 0, K > 0, N % 32 == 0, N < 2^21, groups <= 4096.
+ */
+int32_t nvfp4_grouped_gemm_nn(int64_t groups, const int64_t* row_offsets, int64_t total_rows,
+                              int64_t N, int64_t K, const nvfp4_operand* A,
+                              const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream);
+
+/*
+ * Grouped wgrad for the routed experts (Ultra report section 2.2: wgrad in
+ * NVFP4 on Random-Hadamard-transformed inputs, gradients stochastically
+ * rounded; section 2.7: fp32 accumulation).  The contraction runs over each
+ * group's own tokens: for every group e,
+ *   C[e] [M x N] fp32 = A[k_e : k_{e+1}]^T B[k_e : k_{e+1}] * gA * gB,
+ * with k = k_offsets (device int64 [groups + 1], k_0 = 0, non-decreasing,
+ * every entry a multiple of 16, k_groups = total_k), so a group with no
+ * tokens gets C[e] = 0.
+ *   A: dY rows gathered per group, each group's rows padded with zero rows
+ *      to a multiple of 16, stored [total_k x M], COL blocks (so no block
+ *      spans two groups), one g;
+ *   B: X gathered and padded the same way, [total_k x N], COL blocks, one g;
+ *   C: [groups x M x N] fp32.
+ * Shapes: M % 32 == 0, N % 32 == 0, N < 2^21, total_k % 16 == 0,
+ * groups <= 4096.  Offsets that break these rules are a precondition
+ * violation (rows outside [0, total_k) are never read).
+ */
+int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t total_k,
+                              int64_t M, int64_t N, const nvfp4_operand* A,
+                              const nvfp4_operand* B, float* C, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

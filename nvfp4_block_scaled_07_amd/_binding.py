@@ -78,6 +78,12 @@ def load():
     L.nvfp4_grouped_gemm.restype = i32
     L.nvfp4_grouped_gemm.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
                                      C.POINTER(_Operand), vp, i32, vp]
+    L.nvfp4_grouped_gemm_nn.restype = i32
+    L.nvfp4_grouped_gemm_nn.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
+                                        C.POINTER(_Operand), vp, i32, vp]
+    L.nvfp4_grouped_gemm_tn.restype = i32
+    L.nvfp4_grouped_gemm_tn.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
+                                        C.POINTER(_Operand), vp, vp]
     _lib = L
     return L
 
@@ -204,6 +210,21 @@ def nvfp4_grouped_gemm(groups, row_offsets, total_rows, N, K, A_operand, B_opera
     _check("nvfp4_grouped_gemm", st)
 
 
+def nvfp4_grouped_gemm_nn(groups, row_offsets, total_rows, N, K, A_operand, B_operand, C_out,
+                          c_dtype, stream=None):
+    st = load().nvfp4_grouped_gemm_nn(groups, _p(row_offsets), total_rows, N, K,
+                                      C.byref(A_operand), C.byref(B_operand), _p(C_out),
+                                      int(c_dtype), _stream(stream))
+    _check("nvfp4_grouped_gemm_nn", st)
+
+
+def nvfp4_grouped_gemm_tn(groups, k_offsets, total_k, M, N, A_operand, B_operand, C_out,
+                          stream=None):
+    st = load().nvfp4_grouped_gemm_tn(groups, _p(k_offsets), total_k, M, N, C.byref(A_operand),
+                                      C.byref(B_operand), _p(C_out), _stream(stream))
+    _check("nvfp4_grouped_gemm_tn", st)
+
+
 # ---- allocating convenience wrappers ------------------------------------------------------
 def _scale_shape(block, rows, cols):
     if block == "row":
@@ -299,4 +320,28 @@ def grouped_gemm(A: QTensor, B: QTensor, row_offsets, out_dtype=torch.bfloat16, 
         out = torch.empty((total, N), dtype=out_dtype, device=A.codes.device)
     cd = NVFP4_BF16 if out.dtype == torch.bfloat16 else NVFP4_FP32
     nvfp4_grouped_gemm(groups, row_offsets, total, N, K, A.operand(), B.operand(), out, cd, stream)
+    return out
+
+
+def grouped_gemm_nn(A: QTensor, B: QTensor, row_offsets, out_dtype=torch.bfloat16, out=None,
+                    stream=None):
+    """Per group e: C[o_e:o_e+1] = A[o_e:o_e+1] B_e (B batched [groups, K, N])."""
+    groups = B.codes.shape[0]
+    total, K = A.rows, A.cols
+    N = B.cols
+    if out is None:
+        out = torch.empty((total, N), dtype=out_dtype, device=A.codes.device)
+    cd = NVFP4_BF16 if out.dtype == torch.bfloat16 else NVFP4_FP32
+    nvfp4_grouped_gemm_nn(groups, row_offsets, total, N, K, A.operand(), B.operand(), out, cd,
+                          stream)
+    return out
+
+
+def grouped_gemm_tn(A: QTensor, B: QTensor, k_offsets, groups, out=None, stream=None):
+    """Per group e: C[e] = A[k_e:k_e+1]^T B[k_e:k_e+1], fp32 [groups, M, N]."""
+    total, M = A.rows, A.cols
+    N = B.cols
+    if out is None:
+        out = torch.empty((groups, M, N), dtype=torch.float32, device=A.codes.device)
+    nvfp4_grouped_gemm_tn(groups, k_offsets, total, M, N, A.operand(), B.operand(), out, stream)
     return out

@@ -45,6 +45,43 @@ DevOperand dev(const nvfp4_operand* q) {
   return DevOperand{q->codes, q->scales, q->global_dec, q->block};
 }
 
+// Output rows of a GEMM tile (at most 256 of them, 4-byte elements) must span
+// fewer than 2^31 bytes: the epilogue's store offsets are 31-bit.
+constexpr int64_t kMaxN = int64_t(1) << 21;
+
+// Shared by the NT (fprop) and NN (dgrad) grouped GEMMs: B slices stored
+// [N x K] (b_kmajor) or [K x N].
+int32_t grouped_gemm(bool b_kmajor, int64_t groups, const int64_t* row_offsets,
+                     int64_t total_rows, int64_t N, int64_t K, const nvfp4_operand* A,
+                     const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream) {
+  if (!valid_dtype(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (groups < 0 || total_rows < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
+  if (groups > 4096) return NVFP4_ERR_SHAPE;
+  if (K % 64 != 0 || N % 16 != 0 || K == 0 || N >= kMaxN) return NVFP4_ERR_SHAPE;
+  if (!b_kmajor && N % 32 != 0) return NVFP4_ERR_SHAPE;  // B's contiguous dimension
+  if (!row_offsets || !A || !B || !C) return NVFP4_ERR_NULL;
+  if (!aligned(row_offsets, 8) || !aligned(C, 16)) return NVFP4_ERR_ALIGN;
+  int32_t s = check_operand(A, Expect{total_rows, K, true});
+  if (s != NVFP4_OK) return s;
+  if (A->block != NVFP4_BLOCK_ROW) return NVFP4_ERR_LAYOUT;
+  s = check_operand(B, b_kmajor ? Expect{N, K, true} : Expect{K, N, false});
+  if (s != NVFP4_OK) return s;
+  if (groups == 0 || total_rows == 0 || N == 0) return NVFP4_OK;
+  nvfp4::GroupedArgs a{};
+  a.groups = groups;
+  a.offsets = row_offsets;
+  a.total_rows = total_rows;
+  a.N = N;
+  a.K = K;
+  a.A = dev(A);
+  a.B = dev(B);
+  a.b_kmajor = b_kmajor;
+  a.C = C;
+  a.c_bf16 = c_dtype == NVFP4_BF16;
+  return device_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -203,10 +240,6 @@ int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream) {
                                                 static_cast<hipStream_t>(stream)));
 }
 
-// Output rows of a GEMM tile (at most 256 of them, 4-byte elements) must span
-// fewer than 2^31 bytes: the epilogue's store offsets are 31-bit.
-constexpr int64_t kMaxN = int64_t(1) << 21;
-
 int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nvfp4_operand* A,
                    const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream) {
   if ((opA != 'N' && opA != 'T') || (opB != 'N' && opB != 'T')) return NVFP4_ERR_LAYOUT;
@@ -242,29 +275,38 @@ int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nv
 int32_t nvfp4_grouped_gemm(int64_t groups, const int64_t* row_offsets, int64_t total_rows,
                            int64_t N, int64_t K, const nvfp4_operand* A, const nvfp4_operand* B,
                            void* C, int32_t c_dtype, void* stream) {
-  if (!valid_dtype(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
-  if (groups < 0 || total_rows < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
+  return grouped_gemm(true, groups, row_offsets, total_rows, N, K, A, B, C, c_dtype, stream);
+}
+
+int32_t nvfp4_grouped_gemm_nn(int64_t groups, const int64_t* row_offsets, int64_t total_rows,
+                              int64_t N, int64_t K, const nvfp4_operand* A,
+                              const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream) {
+  return grouped_gemm(false, groups, row_offsets, total_rows, N, K, A, B, C, c_dtype, stream);
+}
+
+int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t total_k,
+                              int64_t M, int64_t N, const nvfp4_operand* A,
+                              const nvfp4_operand* B, float* C, void* stream) {
+  if (groups < 0 || total_k < 0 || M < 0 || N < 0) return NVFP4_ERR_SHAPE;
   if (groups > 4096) return NVFP4_ERR_SHAPE;
-  if (K % 64 != 0 || N % 16 != 0 || K == 0 || N >= kMaxN) return NVFP4_ERR_SHAPE;
-  if (!row_offsets || !A || !B || !C) return NVFP4_ERR_NULL;
-  if (!aligned(row_offsets, 8) || !aligned(C, 16)) return NVFP4_ERR_ALIGN;
-  int32_t s = check_operand(A, Expect{total_rows, K, true});
+  if (M % 32 != 0 || N % 32 != 0 || total_k % 16 != 0 || N >= kMaxN) return NVFP4_ERR_SHAPE;
+  if (!k_offsets || !A || !B || !C) return NVFP4_ERR_NULL;
+  if (!aligned(k_offsets, 8) || !aligned(C, 16)) return NVFP4_ERR_ALIGN;
+  int32_t s = check_operand(A, Expect{total_k, M, false});
   if (s != NVFP4_OK) return s;
-  if (A->block != NVFP4_BLOCK_ROW) return NVFP4_ERR_LAYOUT;
-  s = check_operand(B, Expect{N, K, true});
+  s = check_operand(B, Expect{total_k, N, false});
   if (s != NVFP4_OK) return s;
-  if (groups == 0 || total_rows == 0 || N == 0) return NVFP4_OK;
-  nvfp4::GroupedArgs a{};
+  if (groups == 0 || M == 0 || N == 0) return NVFP4_OK;
+  nvfp4::WgradArgs a{};
   a.groups = groups;
-  a.offsets = row_offsets;
-  a.total_rows = total_rows;
+  a.k_offsets = k_offsets;
+  a.total_k = total_k;
+  a.M = M;
   a.N = N;
-  a.K = K;
   a.A = dev(A);
   a.B = dev(B);
   a.C = C;
-  a.c_bf16 = c_dtype == NVFP4_BF16;
-  return device_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)));
+  return device_status(nvfp4::launch_grouped_wgrad(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -514,7 +514,10 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
   const bool decodes_a = kSplitA || RBLK >= C::NW || wave < RBLK;
   const int a_rb = kSplitA ? wave % RBLK : wave;      // row block this wave decodes
   const int a_i0 = kSplitA ? (wave / RBLK) * AD : 0;  // its first dword (4 * half + dword)
-  const int64_t KT = K / C::BK;
+  // Stages per tile.  K need not be a multiple of BK: the operands' buffer
+  // ranges end at K, so the rows of a last, partial stage past K read as
+  // zeros and add nothing (K itself is a multiple of 16, whole blocks).
+  const int64_t KT = (K + C::BK - 1) / C::BK;
   const int64_t GT = NJ * KT;
 
   f32x16 acc[TM][TN];
@@ -921,7 +924,9 @@ struct GroupedTiles {
         a->B.block == kBlock2d ? (N / 16) * (K / 16) : N * (K / 16);
     TileDesc d;
     d.A = OpView{a->A.codes + r0 * (K / 2), a->A.scales + r0 * (K / 16), 0, kBlockRow};
-    d.B = OpView{a->B.codes + e * (N * K / 2), a->B.scales + e * b_scales_stride, 0, a->B.block};
+    // B slice e: stored [N x K] (K-major) or [K x N] (MN-major, width N).
+    d.B = OpView{a->B.codes + e * (N * K / 2), a->B.scales + e * b_scales_stride,
+                 a->b_kmajor ? 0 : N, a->B.block};
     d.m0 = mt * C::BM;
     d.m_lim = r1 - r0;
     d.n0 = nt * C::BN;
@@ -934,7 +939,7 @@ struct GroupedTiles {
 
 // Persistent grouped kernel: every workgroup builds the prefix of per-group
 // tile counts in LDS, then walks tiles blockIdx.x, +gridDim.x, ...
-template <class C>
+template <class C, bool BKM>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   NVFP4_TILE_LDS(C);
   __shared__ int32_t prefix[kMaxGroups + 1];
@@ -972,13 +977,46 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   const int32_t total = prefix[G];
   GroupedTiles<C> src{&a, prefix, ntn, total};
   if (a.K >= 2 * C::BK) {
-    gemm_tiles<C, true, true>(src, a.N, a.K, a.c_bf16, a.N, lds);
+    gemm_tiles<C, true, BKM>(src, a.N, a.K, a.c_bf16, a.N, lds);
   } else {  // one stage per tile: no pipeline across tiles
     for (int64_t j = 0; j < src.count(); j++) {
       DenseTile one{src.get(j)};
-      gemm_tiles<C, true, true>(one, a.N, a.K, a.c_bf16, a.N, lds);
+      gemm_tiles<C, true, BKM>(one, a.N, a.K, a.c_bf16, a.N, lds);
       __syncthreads();
     }
+  }
+}
+
+// Grouped wgrad: for every group e, C_e [M x N] (fp32) = A_e^T B_e with A_e
+// = A rows k_e .. k_{e+1}-1 (stored [tokens x M], COL blocks) and B_e the
+// same rows of B ([tokens x N], COL blocks): the contraction runs over the
+// group's own tokens, so K differs per group (a multiple of 16; zero gives
+// C_e = 0).  Tiles (e, tm, tn) are spread over a persistent grid, XCD-aware
+// (workgroup b on XCD b % 8 takes a contiguous run of the tile list), each
+// a pipeline of its own (its stage count is its group's).  The operand views
+// start at the group's first row, with buffer ranges that end at its last.
+template <class C>
+__global__ __launch_bounds__(C::NT) void grouped_wgrad_kernel(WgradArgs a) {
+  NVFP4_TILE_LDS(C);
+  const int64_t M = a.M, N = a.N;
+  const int64_t mt = (M + C::BM - 1) / C::BM, nt = (N + C::BN - 1) / C::BN;
+  const int64_t per = mt * nt, total = a.groups * per;
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  const int64_t slot = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
+  const float gscale = load_uniform(a.A.gdec) * load_uniform(a.B.gdec);
+  for (int64_t t = slot; t < total; t += G) {
+    const int64_t e = t / per, r = t % per;
+    const int64_t k0 = load_uniform(a.k_offsets + e), k1 = load_uniform(a.k_offsets + e + 1);
+    DenseTile one;
+    one.t.A = OpView{a.A.codes + k0 * (M / 2), a.A.scales + (k0 / 16) * M, M, a.A.block};
+    one.t.B = OpView{a.B.codes + k0 * (N / 2), a.B.scales + (k0 / 16) * N, N, a.B.block};
+    one.t.m0 = (r % mt) * C::BM;
+    one.t.m_lim = M;
+    one.t.n0 = (r / mt) * C::BN;
+    one.t.gscale = gscale;
+    one.t.C = a.C + e * M * N;
+    gemm_tiles<C, false, false>(one, N, k1 - k0, false, N, lds);
+    __syncthreads();  // the next tile reuses the LDS buffers
   }
 }
 
@@ -1024,7 +1062,10 @@ hipError_t launch_grouped(const GroupedArgs& a, int cus, hipStream_t st) {
   const int64_t max_tiles = ((a.total_rows + C::BM - 1) / C::BM + a.groups) * ntn;
   int64_t grid = cus;
   if (grid > max_tiles) grid = max_tiles;
-  grouped_gemm_kernel<C><<<(unsigned)grid, C::NT, 0, st>>>(a);
+  if (a.b_kmajor)
+    grouped_gemm_kernel<C, true><<<(unsigned)grid, C::NT, 0, st>>>(a);
+  else
+    grouped_gemm_kernel<C, false><<<(unsigned)grid, C::NT, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1060,6 +1101,21 @@ hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st) {
                  : launch_grouped<Cfg<256, 256, 2, 4, 128>>(a, cus, st);
   return small ? launch_grouped<Cfg<128, 256, 1, 8, 64>>(a, cus, st)
                : launch_grouped<Cfg<256, 256, 2, 4, 64>>(a, cus, st);
+}
+
+// Grouped wgrad: 256 x 256 tiles, stages of 64 k (the groups' token counts
+// are ragged, and a partial last stage is work on zeros: the shallow stage
+// keeps that small).
+hipError_t launch_grouped_wgrad(const WgradArgs& a, hipStream_t st) {
+  if (a.groups == 0 || a.M == 0 || a.N == 0) return hipSuccess;
+  int cus = 256;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  using C = Cfg<256, 256, 2, 4, 64>;
+  const int64_t tiles = a.groups * ((a.M + C::BM - 1) / C::BM) * ((a.N + C::BN - 1) / C::BN);
+  const int64_t grid = tiles < cus ? tiles : cus;
+  grouped_wgrad_kernel<C><<<(unsigned)grid, C::NT, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

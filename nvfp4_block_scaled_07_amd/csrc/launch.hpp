@@ -80,10 +80,21 @@ struct GroupedArgs {
   int64_t groups;
   const int64_t* offsets;  // device [groups + 1]
   int64_t total_rows, N, K;
-  DevOperand A;  // [total_rows x K] ROW
-  DevOperand B;  // groups x [N x K], 2D or ROW; gdec [groups]
+  DevOperand A;   // [total_rows x K] ROW
+  DevOperand B;   // groups x [N x K] (b_kmajor; 2D or ROW) or [K x N] (2D or COL); gdec [groups]
+  bool b_kmajor;  // NT (fprop) when true, NN (dgrad) when false
   void* C;
   bool c_bf16;
+};
+
+// Grouped wgrad: C[e] [M x N] fp32 = A[k_e : k_{e+1}]^T B[k_e : k_{e+1}].
+struct WgradArgs {
+  int64_t groups;
+  const int64_t* k_offsets;  // device [groups + 1], multiples of 16
+  int64_t total_k, M, N;
+  DevOperand A;  // [total_k x M] COL (or 2D)
+  DevOperand B;  // [total_k x N] COL (or 2D)
+  float* C;      // [groups x M x N]
 };
 
 hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st);
@@ -95,5 +106,6 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
                              int64_t rows, int64_t cols, int block, float* y, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st);
+hipError_t launch_grouped_wgrad(const WgradArgs& a, hipStream_t st);
 
 }  // namespace nvfp4

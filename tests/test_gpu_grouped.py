@@ -143,3 +143,174 @@ def test_full_grouped_super_sampled():
     for e in sorted({0, 1, big, small, 257, 511}):
         n = int(counts[e])
         _check_group(qa, qb, offsets, c, e, w["hidden"], w["latent"], rows=[0, n // 2, n - 1])
+
+
+# ---- routed-expert backward: grouped dgrad (NN) and grouped wgrad (TN) -------------------------
+def _offsets(counts):
+    off = np.zeros(len(counts) + 1, dtype=np.int64)
+    off[1:] = np.cumsum(counts)
+    return off
+
+
+def _stack_col(ws, dev):
+    """COL-blocked slices [G, K, N]: one 1D quantization per slice."""
+    qs = [nv.quantize_1d(synth.to_bf16(w).to(dev), "col") for w in ws]
+    K, N = ws[0].shape
+    return nv.QTensor(torch.stack([q.codes for q in qs]), torch.stack([q.scales for q in qs]),
+                      torch.cat([q.global_dec for q in qs]), torch.cat([q.amax for q in qs]),
+                      K, N, "col")
+
+
+@pytest.mark.parametrize("b_block", ["2d", "col"])
+def test_grouped_dgrad_nn_small_ragged(b_block):
+    """dX_e = dY_e W_e, W_e stored [K x N]; dY ROW with stochastic rounding."""
+    dev = device()
+    counts = [0, 5, 300, 1, 256, 0, 77, 513]
+    G, N, K = len(counts), 96, 192
+    off = _offsets(counts)
+    T = int(off[-1])
+    dy = synth.laplace((T, K), 1e-3, 61)
+    w = synth.normal((G, K, N), 0.02, 62) * (1 + np.arange(G) % 3).astype(np.float32)[:, None, None]
+    qa = nv.quantize_1d(synth.to_bf16(dy).to(dev), "row", "sr", nv.Philox(63))
+    qb = nv.quantize_2d(synth.to_bf16(w).to(dev)) if b_block == "2d" else _stack_col(list(w), dev)
+    off_d = torch.from_numpy(off).to(dev)
+    c = nv.grouped_gemm_nn(qa, qb, off_d, out_dtype=torch.float32)
+    cb = nv.grouped_gemm_nn(qa, qb, off_d, out_dtype=torch.bfloat16)
+    assert torch.equal(cb.view(torch.int16), c.to(torch.bfloat16).view(torch.int16))
+    A = to_np(qa)
+    for e in range(G):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        Ae = dict(codes=A["codes"][r0:r1], scales=A["scales"][r0:r1], block="row", g=A["g"])
+        Be = dict(codes=qb.codes[e].cpu().numpy(), scales=qb.scales[e].cpu().numpy(),
+                  block=b_block, g=float(qb.global_dec[e].item()))
+        R, D = O.gemm_full("N", "N", r1 - r0, N, K, Ae, Be)
+        err = O.gemm_rel_err(c[r0:r1].cpu().numpy(), R, D)
+        assert err <= TOL, f"group {e}: {err:.3e}"
+
+
+def _wgrad_case(counts, M, N, seed, dev, mask=0x3C5A):
+    """Per-group token segments padded with zero rows to multiples of 16."""
+    counts = np.asarray(counts, dtype=np.int64)
+    padded = (counts + 15) // 16 * 16
+    off = _offsets(padded)
+    total = int(off[-1])
+    dy = np.zeros((total, M), dtype=np.float32)
+    x = np.zeros((total, N), dtype=np.float32)
+    rng = np.random.default_rng(seed)
+    for e, c in enumerate(counts):
+        k0 = int(off[e])
+        dy[k0:k0 + c] = rng.laplace(0.0, 1e-3, (c, M)).astype(np.float32)
+        x[k0:k0 + c] = rng.standard_normal((c, N)).astype(np.float32)
+    qa = nv.quantize_1d(synth.to_bf16(dy).to(dev), "col", "sr", nv.Philox(seed), mask)
+    qb = nv.quantize_1d(synth.to_bf16(x).to(dev), "col", "rne", None, mask)
+    return qa, qb, off
+
+
+def _check_wgrad_group(qa, qb, off, c, e, M, N, rows=None):
+    k0, k1 = int(off[e]), int(off[e + 1])
+    got = c[e].cpu().numpy()
+    if k1 == k0:
+        assert not got.any(), f"empty group {e} must give zeros"
+        return
+    A, B = to_np(qa), to_np(qb)
+    Ae = dict(codes=A["codes"][k0:k1], scales=A["scales"][k0 // 16:k1 // 16], block="col", g=A["g"])
+    Be = dict(codes=B["codes"][k0:k1], scales=B["scales"][k0 // 16:k1 // 16], block="col", g=B["g"])
+    if rows is None:
+        R, D = O.gemm_full("T", "N", M, N, k1 - k0, Ae, Be)
+        err = O.gemm_rel_err(got, R, D)
+    else:
+        ii = np.repeat(np.asarray(rows, dtype=np.int64), N)
+        jj = np.tile(np.arange(N, dtype=np.int64), len(rows))
+        R, D = O.gemm_entries("T", "N", M, N, k1 - k0, Ae, Be, ii, jj)
+        err = O.gemm_rel_err(got[ii, jj], R, D)
+    assert err <= TOL, f"group {e}: {err:.3e}"
+
+
+def test_grouped_wgrad_tn_small_ragged():
+    """dW_e = dY_e^T X_e over each group's own tokens: empty groups, one-block
+    groups, and token counts that leave a partial last stage of 64."""
+    dev = device()
+    counts = [0, 5, 40, 1, 130, 0, 77, 64, 200, 16]
+    M, N = 96, 288
+    qa, qb, off = _wgrad_case(counts, M, N, 71, dev)
+    c = nv.grouped_gemm_tn(qa, qb, torch.from_numpy(off).to(dev), len(counts))
+    for e in range(len(counts)):
+        _check_wgrad_group(qa, qb, off, c, e, M, N)
+
+
+def test_grouped_wgrad_tn_matches_dense_per_group():
+    """Each group's result equals the dense TN GEMM on that group's rows when
+    the group's token count is a multiple of 64 (bit for bit: same sums in
+    the same order)."""
+    dev = device()
+    counts = [128, 0, 64, 320]
+    M, N = 256, 512
+    qa, qb, off = _wgrad_case(counts, M, N, 72, dev)
+    c = nv.grouped_gemm_tn(qa, qb, torch.from_numpy(off).to(dev), len(counts))
+    for e in range(len(counts)):
+        k0, k1 = int(off[e]), int(off[e + 1])
+        if k1 == k0:
+            assert not c[e].any()
+            continue
+        sa = nv.QTensor(qa.codes[k0:k1], qa.scales[k0 // 16:k1 // 16], qa.global_dec, qa.amax,
+                        k1 - k0, M, "col")
+        sb = nv.QTensor(qb.codes[k0:k1], qb.scales[k0 // 16:k1 // 16], qb.global_dec, qb.amax,
+                        k1 - k0, N, "col")
+        d = nv.gemm("T", "N", sa, sb, out_dtype=torch.float32)
+        assert torch.equal(d.view(torch.int32), c[e].view(torch.int32)), f"group {e}"
+
+
+def test_full_grouped_super_backward_sampled():
+    """Routed-expert backward at the Super shapes (512 experts, 8192 tokens
+    top-22, Zipf 1.1 routing; hidden 2688, latent 1024): grouped dgrad
+    dX = dY W (bf16 out) and grouped wgrad dW_e = dY_e^T X_e (fp32 out),
+    sampled rows of the largest, smallest and a middle expert."""
+    dev = device()
+    counts, tok, _ = synth.zipf_routing(8192, 512, 22, 1.1, 9)
+    H, L = 2688, 1024
+    # dgrad: dY gathered [T x H] ROW SR, W_e stored [H x L] 2D (the fprop's W_e^T layout)
+    off = _offsets(counts)
+    T = int(off[-1])
+    dy = synth.laplace_device((T, H), 1e-3, 81, dev)
+    w = synth.normal_device((512, H, L), 0.02, 82, dev)
+    qa = nv.quantize_1d(dy, "row", "sr", nv.Philox(83))
+    qw = nv.quantize_2d(w)
+    del w
+    off_d = torch.from_numpy(off).to(dev)
+    dx = nv.grouped_gemm_nn(qa, qw, off_d, out_dtype=torch.float32)
+    A = to_np(qa)
+    order = np.argsort(counts)
+    picks = [int(order[-1]), int(order[0]), int(order[256])]
+    for e in picks:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.linspace(0, r1 - r0 - 1, 6).astype(np.int64))
+        Ae = dict(codes=A["codes"][r0:r1], scales=A["scales"][r0:r1], block="row", g=A["g"])
+        Be = dict(codes=qw.codes[e].cpu().numpy(), scales=qw.scales[e].cpu().numpy(),
+                  block="2d", g=float(qw.global_dec[e].item()))
+        ii = np.repeat(rows, L)
+        jj = np.tile(np.arange(L, dtype=np.int64), len(rows))
+        R, D = O.gemm_entries("N", "N", r1 - r0, L, H, Ae, Be, ii, jj)
+        err = O.gemm_rel_err(dx[r0 + ii, jj].cpu().numpy(), R, D)
+        assert err <= TOL, f"dgrad expert {e}: {err:.3e}"
+    del dx, qa, qw, dy
+    torch.cuda.empty_cache()
+    # wgrad: per-expert token segments padded to 16; dY and X COL with the transform
+    padded = (counts + 15) // 16 * 16
+    koff = _offsets(padded)
+    KT = int(koff[-1])
+    rows_idx = np.concatenate([np.arange(int(koff[e]), int(koff[e]) + int(counts[e]))
+                               for e in range(512)])
+    dyp = torch.zeros((KT, H), dtype=torch.bfloat16, device=dev)
+    xp = torch.zeros((KT, L), dtype=torch.bfloat16, device=dev)
+    ridx = torch.from_numpy(rows_idx).to(dev)
+    dyp[ridx] = synth.laplace_device((T, H), 1e-3, 84, dev)
+    xp[ridx] = synth.normal_device((T, L), 1.0, 85, dev)
+    mask = synth.rht_mask(6)
+    qa = nv.quantize_1d(dyp, "col", "sr", nv.Philox(86), mask)
+    qb = nv.quantize_1d(xp, "col", "rne", None, mask)
+    del dyp, xp
+    dw = nv.grouped_gemm_tn(qa, qb, torch.from_numpy(koff).to(dev), 512)
+    for e in picks:
+        _check_wgrad_group(qa, qb, koff, dw, e, H, L, rows=[0, 1000, 2687])
