@@ -127,3 +127,24 @@ def test_grouped_validation(lib):
     assert f(4, FAKE, 100, 60, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -2
     wide = _Operand(0x100000, 0x200000, 0x300000, 1 << 21, 128, 2, 0)
     assert f(4, FAKE, 100, 1 << 21, 128, C.byref(A), C.byref(wide), FAKE, 0, None) == -2
+
+
+def test_grouped_backward_validation(lib):
+    from nvfp4_block_scaled_07_amd._binding import _Operand
+    nn, tn = lib.nvfp4_grouped_gemm_nn, lib.nvfp4_grouped_gemm_tn
+    A = _Operand(0x100000, 0x200000, 0x300000, 100, 128, 0, 0)          # dY [100 x 128] ROW
+    W = _Operand(0x100000, 0x200000, 0x300000, 128, 64, 2, 0)           # W_e [K=128 x N=64] 2D
+    assert nn(4, None, 100, 64, 128, C.byref(A), C.byref(W), FAKE, 0, None) == -1
+    assert nn(4, FAKE, 100, 48, 128, C.byref(A), C.byref(W), FAKE, 0, None) == -2  # N % 32
+    assert nn(5000, FAKE, 100, 64, 128, C.byref(A), C.byref(W), FAKE, 0, None) == -2
+    rowW = _Operand(0x100000, 0x200000, 0x300000, 128, 64, 0, 0)        # ROW blocks along N: wrong
+    assert nn(4, FAKE, 100, 64, 128, C.byref(A), C.byref(rowW), FAKE, 0, None) == -4
+    dY = _Operand(0x100000, 0x200000, 0x300000, 160, 96, 1, 0)          # [tokens=160 x M=96] COL
+    X = _Operand(0x100000, 0x200000, 0x300000, 160, 64, 1, 0)           # [tokens=160 x N=64] COL
+    assert tn(4, None, 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == -1
+    assert tn(4, FAKE, 160, 80, 64, C.byref(dY), C.byref(X), FAKE, None) == -2   # M % 32
+    assert tn(4, FAKE, 150, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == -2   # total_k % 16
+    rowX = _Operand(0x100000, 0x200000, 0x300000, 160, 64, 0, 0)        # ROW blocks: not along tokens
+    assert tn(4, FAKE, 160, 96, 64, C.byref(dY), C.byref(rowX), FAKE, None) == -4
+    assert tn(4, C.c_void_p(0x100004), 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == -3
+    assert tn(0, FAKE, 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == 0     # no groups: no-op
