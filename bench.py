@@ -331,6 +331,69 @@ def row_grouped(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688, 
                                          2.0 * total * hidden * latent, "flops")}
 
 
+def row_grouped_bwd(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688,
+                    route_seed=9, name="grouped_bwd_super"):
+    """Routed-expert backward: dY of the experts' up projection (gathered
+    rows, [tokens x hidden]) quantized once for both GEMMs (ROW+SR for
+    dgrad, COL+RHT+SR for wgrad, each expert's rows padded to 16), X (the
+    gathered latent inputs) COL+RHT; grouped dgrad dX = dY W_e (W_e the
+    fprop's 2D codes, stored [hidden x latent]) and grouped wgrad dW_e =
+    dY_e^T X_e over each expert's own tokens (fp32)."""
+    import numpy as np
+    counts, _, _ = synth.zipf_routing(8192, 512, 22, 1.1, route_seed)
+    padded = (counts + 15) // 16 * 16
+    koff = np.zeros(513, dtype=np.int64)
+    koff[1:] = np.cumsum(padded)
+    KT = int(koff[-1])
+    rows = np.concatenate([np.arange(int(koff[e]), int(koff[e]) + int(counts[e]))
+                           for e in range(512)])
+    ridx = torch.from_numpy(rows).to(dev)
+    T = len(rows)
+    mask = synth.rht_mask(6)
+    dy = torch.zeros((KT, hidden), dtype=torch.bfloat16, device=dev)
+    dy[ridx] = synth.laplace_device((T, hidden), 1e-3, 91, dev, zero_frac=0.07)
+    x = torch.zeros((KT, latent), dtype=torch.bfloat16, device=dev)
+    x[ridx] = synth.normal_device((T, latent), 1.0, 92, dev)
+    w = synth.normal_device((512, hidden, latent), 0.02, 93, dev)
+    qw = nv.quantize_2d(w)
+    del w
+    qr, qc, z = nv.quantize_dual(dy, nv.Philox(94), nv.Philox(95), mask)
+    qx = nv.quantize_1d(x, "col", "rne", None, mask)
+    koff_d = torch.from_numpy(koff).to(dev)
+    dx = torch.empty((KT, latent), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((512, hidden, latent), dtype=torch.float32, device=dev)
+    g = torch.empty(2, dtype=torch.float32, device=dev)
+    a = torch.empty(2, dtype=torch.float32, device=dev)
+    rr, rc = nv.Philox(94), nv.Philox(95)
+    timer = Timer(torch)
+
+    def step(i):
+        rr.offset = rc.offset = i
+        timer.run("quantize_dual_dy", lambda: nv.nvfp4_quantize_dual(
+            dy, rr, rc, mask, a, False, qr.codes, qr.scales, g[0:1], qc.codes, qc.scales, g[1:2],
+            z))
+        timer.run("quantize_col_rht_x", lambda: nv.nvfp4_quantize_1d(
+            x, nv.NVFP4_BLOCK_COL, nv.NVFP4_RNE, None, mask, qx.amax, False, qx.codes, qx.scales,
+            qx.global_dec))
+        # dgrad over the padded rows (the pad rows of dY are zero: their dX rows are 0)
+        timer.run("grouped_dgrad_nn", lambda: nv.nvfp4_grouped_gemm_nn(
+            512, koff_d, KT, latent, hidden, qr.operand(), qw.operand(), dx, nv.NVFP4_BF16))
+        timer.run("grouped_wgrad_tn", lambda: nv.nvfp4_grouped_gemm_tn(
+            512, koff_d, KT, hidden, latent, qc.operand(), qx.operand(), dw))
+
+    ms, _ = timed(torch, timer, step, steps, warmup)
+    flops = 2.0 * KT * hidden * latent
+    return {"workload": f"{name}: 8192 tokens top-22 of 512 experts (Zipf 1.1), expert rows "
+                        f"padded to 16 ({KT} rows); dY [rows x {hidden}], X [rows x {latent}]",
+            "ms_per_step": round(ms, 4),
+            "quantize_dual_dy": kernel_entry(timer.avg_ms("quantize_dual_dy"),
+                                             KT * hidden * (2 + 2 * (0.5 + 1.0 / 16)), "bytes"),
+            "quantize_col_rht_x": kernel_entry(timer.avg_ms("quantize_col_rht_x"),
+                                               q1d_bytes(KT, latent), "bytes"),
+            "grouped_dgrad_nn": kernel_entry(timer.avg_ms("grouped_dgrad_nn"), flops, "flops"),
+            "grouped_wgrad_tn": kernel_entry(timer.avg_ms("grouped_wgrad_tn"), flops, "flops")}
+
+
 def row_ultra(nv, synth, torch, dev, steps, warmup):
     M = N = K = 8192
     xs = [synth.normal_device((M, K), 1.0, 11 + i, dev) for i in range(2)]
@@ -376,7 +439,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,ultra,grouped_ultra,all")
+    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel for scaling "
@@ -436,7 +499,7 @@ def main():
     }
     extra = [r.strip() for r in args.rows.split(",") if r.strip()]
     if "all" in extra:
-        extra = ["wgrad", "dy_dual", "grouped", "ultra", "grouped_ultra"]
+        extra = ["wgrad", "dy_dual", "grouped", "grouped_bwd", "ultra", "grouped_ultra"]
     rows = {}
     del xs, ws
     torch.cuda.empty_cache()
@@ -448,6 +511,8 @@ def main():
             rows[r] = row_dy_dual(nv, synth, torch, dev, max(5, args.steps // 5), 2)
         elif r == "grouped":
             rows[r] = row_grouped(nv, synth, torch, dev, max(5, args.steps // 5), 2)
+        elif r == "grouped_bwd":
+            rows[r] = row_grouped_bwd(nv, synth, torch, dev, max(3, args.steps // 10), 1)
         elif r == "grouped_ultra":
             rows[r] = row_grouped(nv, synth, torch, dev, max(3, args.steps // 10), 1, latent=2048,
                                   hidden=5120, route_seed=16, name="grouped_ultra")
