@@ -57,6 +57,10 @@ def lib():
         L.oracle_amax.argtypes = [vp, C.c_int, i64, i64, i64, C.c_int, i32, vp]
         L.oracle_rht16.restype = C.c_int
         L.oracle_rht16.argtypes = [vp, C.c_int, i64, i64, C.c_int, u32, vp]
+        L.oracle_sr_fp16_one.restype = C.c_uint16
+        L.oracle_sr_fp16_one.argtypes = [C.c_float, u32]
+        L.oracle_sr_fp16.restype = None
+        L.oracle_sr_fp16.argtypes = [vp, i64, u64, u64, u32, vp]
         L.oracle_dequantize.restype = C.c_int
         L.oracle_dequantize.argtypes = [vp, vp, C.c_float, i64, i64, C.c_int, vp]
         L.oracle_gemm_entries.restype = C.c_int
@@ -187,6 +191,20 @@ def quantize(x, block, rounding=RNE, seed=0, offset=0, rounds=5, rht_mask=-1,
     if x.ndim == 2:
         return dict(codes=codes, scales=scales, amax=amax_out[0], g=g[0])
     return dict(codes=codes, scales=scales, amax=amax_out, g=g)
+
+
+def sr_fp16_one(x, u16):
+    """fp16 bits of x rounded stochastically with the 16-bit value u16."""
+    return int(lib().oracle_sr_fp16_one(float(np.float32(x)), int(u16)))
+
+
+def sr_fp16(x, seed, offset=0, rounds=5):
+    """fp32 array -> fp16 bit patterns (uint16), stochastic rounding with the
+    Philox stream (seed, offset, rounds): the SSM-state cache recipe."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    y = np.zeros(x.shape, dtype=np.uint16)
+    lib().oracle_sr_fp16(_ptr(x), x.size, int(seed), int(offset), int(rounds), _ptr(y))
+    return y
 
 
 def zero_codes(codes):

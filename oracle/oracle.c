@@ -532,3 +532,47 @@ int oracle_gemm_full(char opA, char opB, int64_t M, int64_t N, int64_t K,
   }
   return 0;
 }
+
+/* ========================================================================
+ * fp32 -> fp16 stochastic rounding (SSM-state cache)
+ * ======================================================================== */
+static double fp16_values[0x7C00]; /* fp16 0x0000 .. 0x7BFF: ascending */
+static int fp16_ready = 0;
+
+static const double* fp16_table(void) {
+  if (!fp16_ready) {
+    for (int h = 0; h < 0x7C00; h++) {
+      int e = h >> 10, m = h & 0x3FF;
+      /* subnormal m * 2^-24; normal (1024 + m) * 2^(e - 25) */
+      fp16_values[h] = e == 0 ? ldexp((double)m, -24) : ldexp(1024.0 + m, e - 25);
+    }
+    fp16_ready = 1;
+  }
+  return fp16_values;
+}
+
+uint16_t oracle_sr_fp16_one(float x, uint32_t u16) {
+  const uint16_t sign = signbit(x) ? 0x8000 : 0;
+  if (isnan(x)) return (uint16_t)(sign | 0x7E00);
+  const double a = fabs((double)x);
+  if (a >= 65504.0) return (uint16_t)(sign | 0x7BFF);
+  const double* V = fp16_table();
+  int lo = 0, hi = 0x7BFE; /* the largest index with V[index] <= a */
+  while (lo < hi) {
+    int mid = (lo + hi + 1) / 2;
+    if (V[mid] <= a) lo = mid; else hi = mid - 1;
+  }
+  const double frac = (a - V[lo]) / (V[lo + 1] - V[lo]);
+  const int up = (double)u16 < frac * 65536.0;
+  return (uint16_t)(sign | (lo + up));
+}
+
+void oracle_sr_fp16(const float* x, int64_t n, uint64_t seed, uint64_t offset,
+                    uint32_t rounds, uint16_t* y) {
+  fp16_table();
+  for (int64_t i = 0; i < n; i++) {
+    /* call i/8 is call 2*(i/16) + (i%16)/8 of block i/16, slot i%8 */
+    const uint32_t u = oracle_sr_bits(seed, offset, rounds, (uint64_t)(i >> 4), (int)(i & 15));
+    y[i] = oracle_sr_fp16_one(x[i], u);
+  }
+}

@@ -136,6 +136,19 @@ int oracle_gemm_full(char opA, char opB, int64_t M, int64_t N, int64_t K,
                      const uint8_t* b_codes, const uint8_t* b_scales,
                      int b_block, float gB, double* R, double* D);
 
+/* fp32 -> fp16 with stochastic rounding, the SSM-state cache recipe (Super
+ * report summary, section 4.3: FP16 with Philox<5> stochastic rounding, no
+ * block scales).  lo = the largest finite fp16 <= |x| (found in a table of
+ * every finite fp16 value), hi = the next one; the magnitude rounds up to hi
+ * iff u < 65536 * (|x| - lo) / (hi - lo), evaluated in fp64 (exact).
+ * Readings: |x| >= 65504 (infinities included) saturates to 65504; NaN gives
+ * 0x7E00 with x's sign; the sign bit is kept (so -0 stays -0).
+ * Element i draws the 16-bit slot i % 8 of Philox call i / 8 (the same
+ * word/half order as the block quantizers).  Returns the fp16 bit pattern. */
+uint16_t oracle_sr_fp16_one(float x, uint32_t u16);
+void oracle_sr_fp16(const float* x, int64_t n, uint64_t seed, uint64_t offset,
+                    uint32_t rounds, uint16_t* y);
+
 #ifdef __cplusplus
 }
 #endif
