@@ -394,6 +394,29 @@ def row_grouped_bwd(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=26
             "grouped_wgrad_tn": kernel_entry(timer.avg_ms("grouped_wgrad_tn"), flops, "flops")}
 
 
+def row_ssm_sr(nv, synth, torch, dev, steps, warmup):
+    """An SSM-state cache written back in fp16 with Philox<5> stochastic
+    rounding: a decode batch's states, 64 x 128 x 64 x 128 fp32 (256 MiB),
+    three rotating sets so that each call reads from HBM."""
+    shape = (64, 128, 64, 128)
+    n = 64 * 128 * 64 * 128
+    xs = [synth.normal_device(shape, 1.0, 120 + i, dev, dtype=torch.float32) for i in range(3)]
+    y = torch.empty(shape, dtype=torch.float16, device=dev)
+    rng = nv.Philox(5)
+    timer = Timer(torch)
+
+    def step(i):
+        rng.offset = i
+        x = xs[i % 3]
+        timer.run("sr_fp16", lambda: nv.nvfp4_sr_fp16(x, rng, y))
+
+    ms, _ = timed(torch, timer, step, steps, warmup)
+    return {"workload": "ssm_sr: SSM states fp32 [64x128x64x128] -> fp16, Philox<5> stochastic "
+                        "rounding",
+            "ms_per_step": round(ms, 4),
+            "sr_fp16": kernel_entry(timer.avg_ms("sr_fp16"), n * 6.0, "bytes")}
+
+
 def row_ultra(nv, synth, torch, dev, steps, warmup):
     M = N = K = 8192
     xs = [synth.normal_device((M, K), 1.0, 11 + i, dev) for i in range(2)]
@@ -439,7 +462,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,all")
+    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,ssm_sr,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel for scaling "
@@ -499,7 +522,7 @@ def main():
     }
     extra = [r.strip() for r in args.rows.split(",") if r.strip()]
     if "all" in extra:
-        extra = ["wgrad", "dy_dual", "grouped", "grouped_bwd", "ultra", "grouped_ultra"]
+        extra = ["wgrad", "dy_dual", "grouped", "grouped_bwd", "ultra", "grouped_ultra", "ssm_sr"]
     rows = {}
     del xs, ws
     torch.cuda.empty_cache()
@@ -513,6 +536,8 @@ def main():
             rows[r] = row_grouped(nv, synth, torch, dev, max(5, args.steps // 5), 2)
         elif r == "grouped_bwd":
             rows[r] = row_grouped_bwd(nv, synth, torch, dev, max(3, args.steps // 10), 1)
+        elif r == "ssm_sr":
+            rows[r] = row_ssm_sr(nv, synth, torch, dev, max(10, args.steps // 2), 2)
         elif r == "grouped_ultra":
             rows[r] = row_grouped(nv, synth, torch, dev, max(3, args.steps // 10), 1, latent=2048,
                                   hidden=5120, route_seed=16, name="grouped_ultra")

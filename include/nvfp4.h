@@ -286,6 +286,23 @@ int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t 
                               int64_t M, int64_t N, const nvfp4_operand* A,
                               const nvfp4_operand* B, float* C, void* stream);
 
+/*
+ * fp32 -> fp16 with stochastic rounding, for an SSM (Mamba) state cache
+ * (Super report summary, section 4.3: an fp16 cache rounded to nearest even
+ * drifts through the recurrence; the recipe is fp16 with Philox<5>
+ * stochastic rounding and no block scales).  With lo the largest fp16 <=
+ * |x| and hi the next one, the magnitude rounds up iff
+ * u < 65536 (|x| - lo) / (hi - lo), u the element's 16-bit slot: element i
+ * uses slot i % 8 (word (i % 8) / 2, low half for even i) of Philox call
+ * i / 8, counter (i / 8, offset), key seed.  |x| >= 65504 (and +-inf)
+ * saturates to +-65504, NaN gives NaN (0x7E00 with x's sign), the sign is
+ * kept (so -0 stays -0).
+ *   x  device fp32 [n];  y  device fp16 bit patterns [n] out.
+ * Shapes: any n >= 0 (n == 0 is a no-op).  Alignment: x and y 16 bytes.
+ */
+int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16_t* y,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -78,6 +78,8 @@ def load():
     L.nvfp4_grouped_gemm.restype = i32
     L.nvfp4_grouped_gemm.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
                                      C.POINTER(_Operand), vp, i32, vp]
+    L.nvfp4_sr_fp16.restype = i32
+    L.nvfp4_sr_fp16.argtypes = [vp, i64, C.POINTER(_Philox), vp, vp]
     L.nvfp4_grouped_gemm_nn.restype = i32
     L.nvfp4_grouped_gemm_nn.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
                                         C.POINTER(_Operand), vp, i32, vp]
@@ -225,6 +227,12 @@ def nvfp4_grouped_gemm_tn(groups, k_offsets, total_k, M, N, A_operand, B_operand
     _check("nvfp4_grouped_gemm_tn", st)
 
 
+def nvfp4_sr_fp16(x, rng, y, stream=None):
+    st = load().nvfp4_sr_fp16(_p(x), x.numel(), C.byref(_Philox(rng.seed, rng.offset, rng.rounds, 0)),
+                              _p(y), _stream(stream))
+    _check("nvfp4_sr_fp16", st)
+
+
 # ---- allocating convenience wrappers ------------------------------------------------------
 def _scale_shape(block, rows, cols):
     if block == "row":
@@ -345,3 +353,10 @@ def grouped_gemm_tn(A: QTensor, B: QTensor, k_offsets, groups, out=None, stream=
         out = torch.empty((groups, M, N), dtype=torch.float32, device=A.codes.device)
     nvfp4_grouped_gemm_tn(groups, k_offsets, total, M, N, A.operand(), B.operand(), out, stream)
     return out
+
+
+def sr_fp16(x, rng: Philox, stream=None):
+    """fp32 tensor -> fp16 tensor of the same shape, stochastic rounding."""
+    y = torch.empty(x.shape, dtype=torch.float16, device=x.device)
+    nvfp4_sr_fp16(x, rng, y, stream)
+    return y

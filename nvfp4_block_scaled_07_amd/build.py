@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnvfp4.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "ssm_state.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

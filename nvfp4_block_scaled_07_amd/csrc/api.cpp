@@ -309,4 +309,16 @@ int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t 
   return device_status(nvfp4::launch_grouped_wgrad(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16_t* y,
+                      void* stream) {
+  if (n < 0) return NVFP4_ERR_SHAPE;
+  if (!rng) return NVFP4_ERR_NULL;
+  if (rng->rounds < 1 || rng->rounds > 16) return NVFP4_ERR_UNSUPPORTED;
+  if (n == 0) return NVFP4_OK;  // empty: pointers may be NULL
+  if (!x || !y) return NVFP4_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
+  return device_status(nvfp4::launch_sr_fp16(x, n, rng->seed, rng->offset, rng->rounds, y,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

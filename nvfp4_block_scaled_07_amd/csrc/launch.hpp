@@ -105,6 +105,8 @@ hipError_t launch_rht16(const void* x, bool x_fp32, int64_t rows, int64_t cols, 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gdec,
                              int64_t rows, int64_t cols, int block, float* y, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_sr_fp16(const float* x, int64_t n, uint64_t seed, uint64_t offset,
+                          uint32_t rounds, uint16_t* y, hipStream_t st);
 hipError_t launch_grouped_gemm(const GroupedArgs& a, hipStream_t st);
 hipError_t launch_grouped_wgrad(const WgradArgs& a, hipStream_t st);
 

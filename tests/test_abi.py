@@ -148,3 +148,15 @@ def test_grouped_backward_validation(lib):
     assert tn(4, FAKE, 160, 96, 64, C.byref(dY), C.byref(rowX), FAKE, None) == -4
     assert tn(4, C.c_void_p(0x100004), 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == -3
     assert tn(0, FAKE, 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == 0     # no groups: no-op
+
+
+def test_sr_fp16_validation(lib):
+    from nvfp4_block_scaled_07_amd._binding import _Philox
+    f = lib.nvfp4_sr_fp16
+    r = C.byref(_Philox(1, 0, 5, 0))
+    assert f(FAKE, -1, r, FAKE, None) == -2
+    assert f(FAKE, 64, None, FAKE, None) == -1
+    assert f(FAKE, 64, C.byref(_Philox(1, 0, 17, 0)), FAKE, None) == -5
+    assert f(None, 64, r, FAKE, None) == -1
+    assert f(C.c_void_p(0x100008), 64, r, FAKE, None) == -3   # x needs 16-byte alignment
+    assert f(FAKE, 0, r, None, None) == 0                     # empty: nothing launched
