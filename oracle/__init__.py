@@ -57,6 +57,8 @@ def lib():
         L.oracle_amax.argtypes = [vp, C.c_int, i64, i64, i64, C.c_int, i32, vp]
         L.oracle_rht16.restype = C.c_int
         L.oracle_rht16.argtypes = [vp, C.c_int, i64, i64, C.c_int, u32, vp]
+        L.oracle_quantize_mse.restype = C.c_int
+        L.oracle_quantize_mse.argtypes = [vp, C.c_int, i64, i64, vp, vp, vp, vp, vp]
         L.oracle_sr_fp16_one.restype = C.c_uint16
         L.oracle_sr_fp16_one.argtypes = [C.c_float, u32]
         L.oracle_sr_fp16.restype = None
@@ -191,6 +193,21 @@ def quantize(x, block, rounding=RNE, seed=0, offset=0, rounds=5, rht_mask=-1,
     if x.ndim == 2:
         return dict(codes=codes, scales=scales, amax=amax_out[0], g=g[0])
     return dict(codes=codes, scales=scales, amax=amax_out, g=g)
+
+
+def quantize_mse(x, amax=None):
+    """PTQ weight quantization: ROW blocks, RNE, MSE-calibrated block scales
+    (see oracle_quantize_mse).  Returns dict(codes, scales, amax, g)."""
+    x, is_bf16, batch, rows, cols = _as_input(x)
+    assert batch == 1 and x.ndim == 2
+    codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    scales = np.zeros((rows, cols // 16), dtype=np.uint8)
+    a_out = np.zeros(1, dtype=np.float32)
+    g = np.zeros(1, dtype=np.float32)
+    a_in = None if amax is None else np.array([amax], dtype=np.float32)
+    _check(lib().oracle_quantize_mse(_ptr(x), is_bf16, rows, cols, _ptr(a_in), _ptr(codes),
+                                     _ptr(scales), _ptr(a_out), _ptr(g)), "quantize_mse")
+    return dict(codes=codes, scales=scales, amax=a_out[0], g=g[0])
 
 
 def sr_fp16_one(x, u16):

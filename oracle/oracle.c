@@ -576,3 +576,69 @@ void oracle_sr_fp16(const float* x, int64_t n, uint64_t seed, uint64_t offset,
     y[i] = oracle_sr_fp16_one(x[i], u);
   }
 }
+
+/* ========================================================================
+ * PTQ: MSE-calibrated block scales (ROW blocks, RNE)
+ * ======================================================================== */
+static double mse_candidate(const float* xb, uint8_t e, float S, float g, uint8_t* q) {
+  const float d = oracle_e4m3_decode(e);
+  float rb = 0.0f;
+  if (d != 0.0f) {
+    rb = S / d;
+    if (isinf(rb)) rb = FLT_MAX;
+  }
+  double half[2] = {0.0, 0.0};
+  for (int i = 0; i < 16; i++) {
+    q[i] = oracle_e2m1_encode_rne(xb[i] * rb);
+    const float xh = (oracle_e2m1_decode(q[i]) * d) * g;
+    const double err = (double)xb[i] - (double)xh;
+    half[i >> 3] += err * err;
+  }
+  return half[0] + half[1];
+}
+
+int oracle_quantize_mse(const void* x, int x_is_bf16, int64_t rows, int64_t cols,
+                        const float* amax_in, uint8_t* codes, uint8_t* scales,
+                        float* amax_out, float* g_out) {
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return -2;
+  float A = 0.0f;
+  if (amax_in) {
+    A = *amax_in;
+  } else {
+    for (int64_t i = 0; i < rows * cols; i++) {
+      float a = fabsf(load_elem(x, x_is_bf16, i));
+      if (a > A) A = a;
+    }
+  }
+  float S, k, g;
+  oracle_global_scales(A, &S, &k, &g);
+  *amax_out = A;
+  *g_out = g;
+  for (int64_t r = 0; r < rows; r++)
+    for (int64_t c0 = 0; c0 < cols; c0 += 16) {
+      float xb[16];
+      float a = 0.0f;
+      for (int i = 0; i < 16; i++) {
+        xb[i] = load_elem(x, x_is_bf16, r * cols + c0 + i);
+        if (fabsf(xb[i]) > a) a = fabsf(xb[i]);
+      }
+      const int e0 = oracle_e4m3_encode_rne_sat(a * k);
+      uint8_t best_q[16], q[16];
+      int best = e0;
+      double best_err = mse_candidate(xb, (uint8_t)e0, S, g, best_q);
+      for (int t = 1; t <= 16; t++) {
+        const int e = t == 1 ? e0 + 1 : e0 - (t - 1);
+        if (e < 0 || e > 126) continue;
+        const double err = mse_candidate(xb, (uint8_t)e, S, g, q);
+        if (err < best_err) {
+          best_err = err;
+          best = e;
+          memcpy(best_q, q, 16);
+        }
+      }
+      scales[r * (cols / 16) + c0 / 16] = (uint8_t)best;
+      for (int i = 0; i < 16; i += 2)
+        codes[(r * cols + c0 + i) / 2] = (uint8_t)(best_q[i] | (best_q[i + 1] << 4));
+    }
+  return 0;
+}

@@ -136,6 +136,24 @@ int oracle_gemm_full(char opA, char opB, int64_t M, int64_t N, int64_t K,
                      const uint8_t* b_codes, const uint8_t* b_scales,
                      int b_block, float gB, double* R, double* D);
 
+/* PTQ weight quantization with MSE-calibrated block scales (Super report
+ * summary, section 4.2: NVFP4 PTQ picks each weight block's scale by
+ * minimizing the weight's MSE instead of taking the max-based one).
+ * ROW blocks (1x16 along cols), RNE elements, per-tensor S, k, g from amax
+ * (computed, or amax_in when non-NULL) exactly as the max-based quantizer.
+ * For each block the candidate E4M3 scale codes are, in this order: the
+ * max-based code e0 = E4M3(RN32(a k)), then e0 + 1, e0 - 1, e0 - 2, ...,
+ * e0 - 15 (those within 0 .. 126).  A candidate e encodes the block as the
+ * max-based quantizer would with scale e (r = RN32(S / val(e)), y = RN32(x
+ * r), RNE) and its error is, in fp64, (sum_{i<8} (x_i - xh_i)^2) +
+ * (sum_{i>=8} (x_i - xh_i)^2), each sum in index order, with xh_i =
+ * RN32(RN32(val(code_i) val(e)) g) the dequantized value.  A candidate
+ * replaces the current choice only if its error is strictly smaller.
+ * Outputs as oracle_quantize (codes, scales [rows x cols/16], amax, g). */
+int oracle_quantize_mse(const void* x, int x_is_bf16, int64_t rows, int64_t cols,
+                        const float* amax_in, uint8_t* codes, uint8_t* scales,
+                        float* amax_out, float* g_out);
+
 /* fp32 -> fp16 with stochastic rounding, the SSM-state cache recipe (Super
  * report summary, section 4.3: FP16 with Philox<5> stochastic rounding, no
  * block scales).  lo = the largest finite fp16 <= |x| (found in a table of
