@@ -175,6 +175,27 @@ int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_
                             uint64_t* zero_codes, void* stream);
 
 /*
+ * Post-training weight quantization with MSE-calibrated block scales (Super
+ * report summary, section 4.2, NVFP4 PTQ: each weight block's scale is chosen
+ * to minimize the weight's MSE rather than from the block max; activations
+ * keep the dynamic max-based nvfp4_quantize_1d).  ROW blocks (1x16 along
+ * cols, i.e. along K of a weight stored [N x K]), RNE elements, per-tensor
+ * scales as nvfp4_quantize_1d.  Per block, the candidate E4M3 codes are the
+ * max-based one e0, then e0 + 1, e0 - 1, ..., e0 - 15 (within 0 .. 126); each
+ * encodes the block as nvfp4_quantize_1d would with that scale, and its error
+ * is the fp64 sum of (x - dequantized x)^2, as (elements 0..7) + (8..15), each
+ * sum in index order; a candidate replaces the choice only if strictly
+ * better.  The result is a ROW operand for nvfp4_gemm (e.g. B of an NT GEMM).
+ *   w [rows x cols] NVFP4_BF16 or NVFP4_FP32; amax as nvfp4_quantize_1d;
+ *   codes [rows x cols/2], scales [rows x cols/16], global_dec out.
+ * Shapes: cols % 32 == 0; rows == 0 is a no-op.  Alignment as
+ * nvfp4_quantize_1d.
+ */
+int32_t nvfp4_quantize_mse(const void* w, int32_t w_dtype, int64_t rows, int64_t cols,
+                           float* amax, int32_t amax_is_input, uint8_t* codes, uint8_t* scales,
+                           float* global_dec, void* stream);
+
+/*
  * 2D (16x16) block quantization of weights (Super summary, Infra table: 2D
  * block scaling for weights; the 16x16 size is the reading).  Round to
  * nearest even, no transform.  A batch of `batch` independent slices

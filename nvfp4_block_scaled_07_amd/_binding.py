@@ -66,6 +66,8 @@ def load():
     L.nvfp4_quantize_dual.restype = i32
     L.nvfp4_quantize_dual.argtypes = [vp, i32, i64, i64, C.POINTER(_Philox), C.POINTER(_Philox),
                                        i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize_mse.restype = i32
+    L.nvfp4_quantize_mse.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp]
     L.nvfp4_quantize_2d.restype = i32
     L.nvfp4_quantize_2d.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, vp]
     L.nvfp4_rht16.restype = i32
@@ -176,6 +178,14 @@ def nvfp4_quantize_dual(x, rng_row, rng_col, rht_sign_mask, amax, amax_is_input,
     _check("nvfp4_quantize_dual", st)
 
 
+def nvfp4_quantize_mse(w, amax, amax_is_input, codes, scales, global_dec, stream=None):
+    rows, cols = w.shape
+    st = load().nvfp4_quantize_mse(_p(w), _dtype_code(w), rows, cols, _p(amax),
+                                   int(bool(amax_is_input)), _p(codes), _p(scales),
+                                   _p(global_dec), _stream(stream))
+    _check("nvfp4_quantize_mse", st)
+
+
 def nvfp4_quantize_2d(w, amax, amax_is_input, codes, scales, global_dec, stream=None):
     if w.dim() == 2:
         batch, (rows, cols) = 1, w.shape
@@ -276,6 +286,20 @@ def quantize_dual(x, rng_row: Philox, rng_col: Philox, rht_sign_mask=-1, amax=No
                         g[1:2], z, stream)
     return (QTensor(rc, rs, g[0:1], a[0:1], rows, cols, "row"),
             QTensor(cc, cs, g[1:2], a[1:2], rows, cols, "col"), z)
+
+
+def quantize_mse(w, amax=None, stream=None):
+    """PTQ weight quantization: ROW blocks with MSE-calibrated scales."""
+    rows, cols = w.shape
+    dev = w.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    given = amax is not None
+    a = (amax.reshape(1).to(torch.float32).clone() if given
+         else torch.empty(1, dtype=torch.float32, device=dev))
+    nvfp4_quantize_mse(w, a, given, codes, scales, g, stream)
+    return QTensor(codes, scales, g, a, rows, cols, "row")
 
 
 def quantize_2d(w, amax=None, stream=None):

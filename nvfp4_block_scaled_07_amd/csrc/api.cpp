@@ -185,6 +185,21 @@ int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_
   return device_status(nvfp4::launch_quantize_dual(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t nvfp4_quantize_mse(const void* w, int32_t w_dtype, int64_t rows, int64_t cols,
+                           float* amax, int32_t amax_is_input, uint8_t* codes, uint8_t* scales,
+                           float* global_dec, void* stream) {
+  if (!valid_dtype(w_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return NVFP4_OK;  // empty: pointers may be NULL
+  if (!w || !amax || !codes || !scales || !global_dec) return NVFP4_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
+      !aligned(global_dec, 4))
+    return NVFP4_ERR_ALIGN;
+  return device_status(nvfp4::launch_quantize_mse(w, w_dtype == NVFP4_FP32, rows, cols, amax,
+                                                  amax_is_input != 0, codes, scales, global_dec,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int32_t nvfp4_quantize_2d(const void* w, int32_t w_dtype, int64_t batch, int64_t rows,
                           int64_t cols, float* amax, int32_t amax_is_input, uint8_t* codes,
                           uint8_t* scales, float* global_dec, void* stream) {

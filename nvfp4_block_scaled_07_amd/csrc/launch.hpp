@@ -100,6 +100,9 @@ struct WgradArgs {
 hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st);
 hipError_t launch_quantize_2d(const Quant2dArgs& a, hipStream_t st);
 hipError_t launch_quantize_dual(const QuantDualArgs& a, hipStream_t st);
+hipError_t launch_quantize_mse(const void* x, bool x_fp32, int64_t rows, int64_t cols,
+                               float* amax, bool amax_is_input, uint8_t* codes, uint8_t* scales,
+                               float* gdec, hipStream_t st);
 hipError_t launch_rht16(const void* x, bool x_fp32, int64_t rows, int64_t cols, int axis,
                         uint32_t mask, float* y, hipStream_t st);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* gdec,

@@ -160,3 +160,12 @@ def test_sr_fp16_validation(lib):
     assert f(None, 64, r, FAKE, None) == -1
     assert f(C.c_void_p(0x100008), 64, r, FAKE, None) == -3   # x needs 16-byte alignment
     assert f(FAKE, 0, r, None, None) == 0                     # empty: nothing launched
+
+
+def test_quantize_mse_validation(lib):
+    f = lib.nvfp4_quantize_mse
+    assert f(FAKE, 0, 64, 80, FAKE, 0, FAKE, FAKE, FAKE, None) == -2   # cols % 32
+    assert f(FAKE, 3, 64, 64, FAKE, 0, FAKE, FAKE, FAKE, None) == -5   # dtype
+    assert f(None, 0, 64, 64, FAKE, 0, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 0, 64, 64, FAKE, 0, C.c_void_p(0x100008), FAKE, FAKE, None) == -3
+    assert f(FAKE, 0, 0, 64, None, 0, None, None, None, None) == 0

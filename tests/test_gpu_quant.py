@@ -295,3 +295,59 @@ def test_full_wgrad_super_dy_dual():
         assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales), name
     n = dy.size
     print(f"dY zero-code fraction: ROW {zeros[0] / n:.4f}, COL+RHT {zeros[1] / n:.4f}")
+
+
+# ---- PTQ weights: MSE-calibrated block scales ---------------------------------------------------
+@pytest.mark.parametrize("shape", [(16, 32), (48, 96), (1000, 64), (64, 2080)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_mse_small(shape, dtype):
+    dev = device()
+    x = make_input("normal", shape, seed=shape[0] + shape[1]) * np.float32(0.02)
+    x[0, :16] = 0.0                                    # a zero block
+    x[min(1, shape[0] - 1), 16:32] = [6.0] * 15 + [7.2]  # a block the MSE choice moves
+    t, xo = device_input(x, dtype, dev)
+    q = nv.quantize_mse(t)
+    got = to_np(q)
+    ref = O.quantize_mse(xo)
+    assert_same(got["amax"][0], ref["amax"], "amax")
+    assert_same(np.float32(got["g"]), ref["g"], "g")
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+
+
+@pytest.mark.parametrize("kind", ["wide", "tiny", "zeros", "laplace_zeros"])
+def test_quantize_mse_distributions(kind):
+    dev = device()
+    x = make_input(kind, (64, 256), seed=7)
+    t, xo = device_input(x, "bf16", dev)
+    q = nv.quantize_mse(t, amax=None)
+    got = to_np(q)
+    ref = O.quantize_mse(xo)
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+
+
+def test_quantize_mse_amax_input():
+    dev = device()
+    x = make_input("normal", (64, 128), seed=8)
+    t, xo = device_input(x, "bf16", dev)
+    q = nv.quantize_mse(t, amax=torch.tensor([9.0], device=dev))
+    got = to_np(q)
+    ref = O.quantize_mse(xo, amax=9.0)
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+
+
+def test_full_ptq_weight():
+    """A Super-width weight [6144 x 6144] N(0, 0.02): every block against the
+    oracle."""
+    dev = device()
+    w = synth.normal((6144, 6144), 0.02, 2)
+    t, xo = device_input(w, "bf16", dev)
+    q = nv.quantize_mse(t)
+    got = to_np(q)
+    ref = O.quantize_mse(xo)
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+    moved = (got["scales"] != O.quantize(xo, "row")["scales"]).mean()
+    print(f"blocks whose scale the MSE choice moved: {moved:.3f}")
