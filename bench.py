@@ -12,8 +12,9 @@ the stream the library launches on (torch's current stream), which gives the
 per-kernel averages used for the roofline fractions.
 
 `--rows` adds further rows of the hot path (wgrad with RHT + stochastic
-rounding, routed-expert grouped GEMM, Ultra-width fprop/dgrad), each timed the
-same way and reported under "rows".
+rounding, routed-expert grouped GEMM, Ultra-width fprop/dgrad, the SSM-state
+fp16 rounding, the post-training-quantized decode path), each timed the same
+way (the decode path from HIP graph replays) and reported under "rows".
 
 Prints one JSON line.
 """
@@ -417,6 +418,98 @@ def row_ssm_sr(nv, synth, torch, dev, steps, warmup):
             "sr_fp16": kernel_entry(timer.avg_ms("sr_fp16"), n * 6.0, "bytes")}
 
 
+def row_ptq_decode(nv, synth, torch, dev, steps, warmup, layers=16, hidden=6144, batches=(1, 32)):
+    """Post-training-quantized decode: Super-width weights W_l [6144 x 6144]
+    N(0, 0.02) quantized offline with MSE-calibrated block scales, then per
+    decode step and layer the activations X_l [M x 6144] quantized with
+    dynamic max-based ROW scales and Y_l = X_l W_l^T (W4A4, small-M kernel).
+    Sixteen layers (340 MB of weight codes, more than the 256 MB last-level
+    cache) so every GEMM streams its weight from HBM.  Each step is replayed
+    from a HIP graph (the kernels take microseconds, less than a Python
+    launch); every replay is checked bit for bit against the eager result."""
+    N = K = hidden
+    ws = []
+    timer = Timer(torch)
+    for l in range(layers):
+        w = synth.normal_device((N, K), 0.02, 300 + l, dev)
+        qw = nv.quantize_mse(w)
+        timer.run("quantize_mse_w", lambda w=w, qw=qw: nv.nvfp4_quantize_mse(
+            w, qw.amax, False, qw.codes, qw.scales, qw.global_dec))
+        ws.append(qw)
+        del w
+    torch.cuda.synchronize()
+    timer.collect()
+    out = {"workload": f"ptq_decode: {layers} layers W [{N}x{K}] MSE-scaled 1x16 NVFP4, "
+                       f"X [M x {K}] max-scaled 1x16, Y = X W^T bf16 (NT, small-M kernel)",
+           "layers": layers,
+           "quantize_mse_w": kernel_entry(timer.avg_ms("quantize_mse_w"), N * K * 2.0 + N * K / 2
+                                          + N * K / 16, "bytes")}
+    w_bytes = N * K / 2 + N * K / 16
+    for M in batches:
+        xs = [synth.normal_device((M, K), 1.0, 400 + l, dev) for l in range(layers)]
+        qxs = [nv.quantize_1d(x, "row") for x in xs]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+
+        def quant(l):
+            q = qxs[l]
+            nv.nvfp4_quantize_1d(xs[l], nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, q.amax, False,
+                                 q.codes, q.scales, q.global_dec)
+
+        def gemm(l):
+            nv.nvfp4_gemm("N", "T", M, N, K, qxs[l].operand(), ws[l].operand(), ys[l],
+                          nv.NVFP4_BF16)
+
+        def step():
+            for l in range(layers):
+                quant(l)
+                gemm(l)
+
+        def gemms():
+            for l in range(layers):
+                gemm(l)
+
+        step()
+        torch.cuda.synchronize()
+        ref = [y.clone() for y in ys]
+        graphs = {}
+        for name, fn in (("step", step), ("gemms", gemms)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs[name] = g
+        match = True
+        res = {}
+        for name, g in graphs.items():
+            for _ in range(warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / steps
+            for l in range(layers):
+                match = match and torch.equal(ys[l].view(torch.int16), ref[l].view(torch.int16))
+            for y in ys:
+                y.zero_()
+            torch.cuda.synchronize()
+        gemm_ms = res["gemms"] / layers
+        gemm_bytes = w_bytes + M * K / 2 + M * K / 16 + M * N * 2
+        out[f"M{M}"] = {
+            "ms_per_step": round(res["step"], 4),
+            "tokens_per_s": round(M / (res["step"] * 1e-3), 1),
+            "gemm": {**kernel_entry(gemm_ms, gemm_bytes, "bytes"),
+                     "TFLOP/s": round(2.0 * M * N * K / (gemm_ms * 1e-3) / 1e12, 2)},
+            "quantize_x_ms_per_layer": round((res["step"] - res["gemms"]) / layers, 5),
+            "graph_replays_match_eager": bool(match),
+        }
+        del xs, qxs, ys, ref, graphs
+    return out
+
+
 def row_ultra(nv, synth, torch, dev, steps, warmup):
     M = N = K = 8192
     xs = [synth.normal_device((M, K), 1.0, 11 + i, dev) for i in range(2)]
@@ -462,7 +555,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,ssm_sr,all")
+    ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,ssm_sr,ptq_decode,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel for scaling "
@@ -522,7 +615,8 @@ def main():
     }
     extra = [r.strip() for r in args.rows.split(",") if r.strip()]
     if "all" in extra:
-        extra = ["wgrad", "dy_dual", "grouped", "grouped_bwd", "ultra", "grouped_ultra", "ssm_sr"]
+        extra = ["wgrad", "dy_dual", "grouped", "grouped_bwd", "ultra", "grouped_ultra", "ssm_sr",
+                 "ptq_decode"]
     rows = {}
     del xs, ws
     torch.cuda.empty_cache()
@@ -538,6 +632,8 @@ def main():
             rows[r] = row_grouped_bwd(nv, synth, torch, dev, max(3, args.steps // 10), 1)
         elif r == "ssm_sr":
             rows[r] = row_ssm_sr(nv, synth, torch, dev, max(10, args.steps // 2), 2)
+        elif r == "ptq_decode":
+            rows[r] = row_ptq_decode(nv, synth, torch, dev, max(20, args.steps), 3)
         elif r == "grouped_ultra":
             rows[r] = row_grouped(nv, synth, torch, dev, max(3, args.steps // 10), 1, latent=2048,
                                   hidden=5120, route_seed=16, name="grouped_ultra")

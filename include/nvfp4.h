@@ -98,7 +98,10 @@ typedef struct {
 } nvfp4_philox;
 
 /* A quantized operand: device pointers to its codes, its scale bytes and its
- * fp32 decode scale g, with the stored shape [rows x cols] and block kind. */
+ * fp32 decode scale g, with the stored shape [rows x cols] and block kind.
+ * As a GEMM operand (kernels address it with 32-bit offsets): cols < 2^24
+ * when K is its contiguous dimension, rows * cols < 2^32 when K is its row
+ * dimension (else NVFP4_ERR_SHAPE). */
 typedef struct {
   const uint8_t* codes;
   const uint8_t* scales;
@@ -246,6 +249,10 @@ int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream);
  * or 2D operand has rows % 16 == 0; N % 8 == 0 and N < 2^21 (else
  * NVFP4_ERR_SHAPE).  M == 0 or N == 0 is a no-op.  Alignment: codes 16
  * bytes, scales 4, C 16 bytes.
+ * NT with M <= 64 (decode-like shapes) runs a split-K kernel: K is divided
+ * among the waves of a workgroup and their partial sums are added in a fixed
+ * order, so C is deterministic but rounds differently from the product of a
+ * larger M (within the same error bound).
  */
 int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nvfp4_operand* A,
                    const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream);

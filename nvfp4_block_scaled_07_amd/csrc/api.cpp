@@ -36,6 +36,11 @@ int32_t check_operand(const nvfp4_operand* q, const Expect& e) {
   if (q->cols % 32 != 0) return NVFP4_ERR_SHAPE;  // contiguous dim: 16-byte code rows
   if ((q->block == NVFP4_BLOCK_COL || q->block == NVFP4_BLOCK_2D) && q->rows % 16 != 0)
     return NVFP4_ERR_SHAPE;
+  // The kernels address operands through 32-bit buffer offsets: 256 rows of a
+  // K-major operand, or all of an MN-major one, must span fewer than 2^31
+  // code bytes.
+  if (e.kmajor ? q->cols >= (int64_t(1) << 24) : q->rows * (q->cols / 2) >= (int64_t(1) << 31))
+    return NVFP4_ERR_SHAPE;
   if (!aligned(q->codes, 16) || !aligned(q->scales, 4) || !aligned(q->global_dec, 4))
     return NVFP4_ERR_ALIGN;
   return NVFP4_OK;

@@ -1020,6 +1020,303 @@ __global__ __launch_bounds__(C::NT) void grouped_wgrad_kernel(WgradArgs a) {
   }
 }
 
+// ---- small M (decode-like shapes): NT with M <= 64 ---------------------------------------------
+// With a few rows of activations the weight codes dominate the traffic and a
+// 256-row tile would leave most of the chip idle (N / 256 workgroups).  A
+// workgroup here takes 32 columns of C (all M <= 64 rows of A) with NWV
+// waves; wave w takes the w-th share of the K range in chunks of 256 k.  A
+// chunk is loaded with whole 128-byte row segments per group of 8 lanes (B:
+// 32 rows of W; A: the 8 * NA8 rows of A rounded up from M), so each load
+// instruction touches 8 cache lines, with NB chunks in flight in registers;
+// the wave then writes the chunk into its own LDS slot and reads back the
+// fragments of the tiled kernel -- lane l: row l%32 and, per 64-k group, the
+// 32 k at 32 * (l/32) with their two scale bytes -- decodes them the same
+// way and multiplies with the same MFMA, into two accumulator sets (even and
+// odd 16-k steps) so that consecutive MFMAs do not wait on each other.
+// Partial sums are added in a fixed order (odd set onto even, then waves in
+// order through LDS), so results are deterministic; they round like 2 * NWV
+// partial sums, not like the tiled kernel's one sequential sum, within the
+// same error bound.
+//
+// Slot layout (bytes): B codes [32 rows][128], B scales [32 rows][16],
+// A scales [64 rows][16] (only the first 8 * NA8 rows are read), then A
+// codes [8 * NA8 rows][128] or, for M <= 16, A decoded to fp16 (below).  In
+// a code row, 16-byte unit u (k = 32u .. 32u+31 of the chunk) sits at
+// position u ^ ((row >> 1) & 7): the 16 lanes of one 16-byte LDS access (16
+// consecutive rows and one unit on reads, 2 rows and 8 units on writes) fall
+// in 16 distinct slots of a 256-byte bank window.
+constexpr int kSkChunkK = 256;          // k per chunk (4 groups of 64)
+constexpr int kSkOob = INT32_MIN;       // buffer offset past every range: loads return 0
+
+__device__ __forceinline__ int sk_swz(int row) { return (row >> 1) & 7; }
+
+template <int NA8>
+struct SkLayout {
+  // A16: with at most 16 rows, A is decoded once per chunk into an fp16
+  // image [8 * NA8 rows][256 k] (8-k unit U of row r at U ^ (r & 15)), so
+  // its decode scales with M instead of the 32 fragment rows.
+  static constexpr bool A16 = NA8 <= 2;
+  static constexpr int kBC = 0, kBS = 4096, kAS = 4608, kAC = kAS + 64 * 16;
+  static constexpr int kSlot = kAC + NA8 * (A16 ? 4096 : 1024);
+  static constexpr int MT = NA8 > 4 ? 2 : 1;
+};
+
+template <int NA8>
+struct SkChunk {
+  uint4 bc[4];  // B codes: rows 8i + l/8, unit l%8
+  uint2 bs;     // B scales: row l/2, bytes 8 (l%2) .. +8
+  uint4 ac[NA8];
+  uint4 as;     // A scales: row l (lanes from 8 NA8 on are never read)
+};
+
+// Per-lane sources of one wave's chunks (offsets from the buffer bases).
+// Rows past an operand's edge re-read its last valid row (in bounds); they
+// only reach outputs that are not stored.  Past the end of a row, a chunk's
+// loads read the next row or, past the operand, zeros; those k are never
+// multiplied.
+template <int NA8>
+struct SkSrc {
+  __amdgpu_buffer_rsrc_t bcr, bsr, acr, asr;
+  uint32_t boff[4], bsoff, aoff[NA8], asoff;
+
+  __device__ __forceinline__ void load(SkChunk<NA8>& d, int64_t c, bool valid) const {
+    const int cb = valid ? (int)(c * (kSkChunkK / 2)) : kSkOob;
+    const int sb = valid ? (int)(c * (kSkChunkK / 16)) : kSkOob;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      d.bc[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(bcr, boff[i], cb, 0));
+    d.bs = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(bsr, bsoff, sb, 0));
+#pragma unroll
+    for (int i = 0; i < NA8; i++)
+      d.ac[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(acr, aoff[i], cb, 0));
+    d.as = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(asr, asoff, sb, 0));
+  }
+};
+
+template <int NA8>
+__device__ __forceinline__ void sk_put(uint8_t* lds, const SkChunk<NA8>& d, int lane) {
+  using L = SkLayout<NA8>;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int row = 8 * i + lane / 8;
+    *reinterpret_cast<uint4*>(lds + L::kBC + 128 * row + 16 * ((lane % 8) ^ sk_swz(row))) = d.bc[i];
+  }
+  *reinterpret_cast<uint2*>(lds + L::kBS + 8 * lane) = d.bs;
+  *reinterpret_cast<uint4*>(lds + L::kAS + 16 * lane) = d.as;
+  if constexpr (L::A16) {
+    // Lane l holds unit l%8 (k = 32 (l%8) .. +32) of A row 8i + l/8: decode
+    // it with that row's two scale bytes (just written above) into the image.
+#pragma unroll
+    for (int i = 0; i < NA8; i++) {
+      const int row = 8 * i + lane / 8, u = lane % 8;
+      const half2 sc = scale_pair(*reinterpret_cast<const uint16_t*>(lds + L::kAS + 16 * row + 2 * u));
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *reinterpret_cast<half8*>(lds + L::kAC + 512 * row + 16 * ((4 * u + j) ^ (row & 15))) =
+            decode8(pick(d.ac[i], j), splat(sc, j >= 2));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NA8; i++) {
+      const int row = 8 * i + lane / 8;
+      *reinterpret_cast<uint4*>(lds + L::kAC + 128 * row + 16 * ((lane % 8) ^ sk_swz(row))) = d.ac[i];
+    }
+  }
+}
+
+template <int NA8, int NWV, int NB>
+__global__ __launch_bounds__(NWV * 64) void gemm_skinny_kernel(GemmArgs a) {
+  using L = SkLayout<NA8>;
+  constexpr int MT = L::MT, SLOT = L::kSlot;
+  static_assert(NB >= 1 && NB <= 4, "chunks in flight");
+  static_assert(SLOT >= MT * 4096, "the reduction reuses the slots");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NWV * SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int64_t M = a.M, N = a.N, K = a.K, kc = K / 2, ks = K / 16;
+  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const int64_t G = K / 64, CN = (K + kSkChunkK - 1) / kSkChunkK;
+  const int64_t c0 = wave * CN / NWV, c1 = (wave + 1) * CN / NWV;
+  uint8_t* const slot = lds + wave * SLOT;
+
+  const bool b2d = a.B.block == kBlock2d, a2d = a.A.block == kBlock2d;
+  const int64_t nlim = N - n0 < 32 ? N - n0 : 32;
+  SkSrc<NA8> src;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int64_t row = 8 * i + lane / 8;
+    src.boff[i] = (uint32_t)((row < nlim ? row : nlim - 1) * kc + 16 * (lane % 8));
+  }
+  const int64_t bsbase = b2d ? (n0 / 16) * ks : n0 * ks;
+  {
+    const int64_t row = lane / 2;
+    const int64_t r = n0 + (row < nlim ? row : nlim - 1);
+    src.bsoff = (uint32_t)((b2d ? (r / 16) * ks : r * ks) - bsbase + 8 * (lane % 2));
+  }
+#pragma unroll
+  for (int i = 0; i < NA8; i++) {
+    const int64_t row = 8 * i + lane / 8;
+    src.aoff[i] = (uint32_t)((row < M ? row : M - 1) * kc + 16 * (lane % 8));
+  }
+  {
+    const int64_t r = lane < M ? lane : M - 1;
+    src.asoff = lane < 8 * NA8 ? (uint32_t)(a2d ? (r / 16) * ks : r * ks) : (uint32_t)kSkOob;
+  }
+  const int64_t b_end = b2d ? ((n0 + nlim + 15) / 16) * ks : (n0 + nlim) * ks;
+  src.bcr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.B.codes + n0 * kc), 0,
+                                              (int)(nlim * kc), kBufferFlags);
+  src.bsr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.B.scales + bsbase), 0,
+                                              (int)(b_end - bsbase), kBufferFlags);
+  src.acr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.A.codes), 0,
+                                              (int)(M * kc), kBufferFlags);
+  src.asr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.A.scales), 0, (int)(a2d ? ((M + 15) / 16) * ks : M * ks),
+      kBufferFlags);
+
+  // LDS rows this lane reads: B row lrow, A row min(32 s + lrow, M - 1).
+  int arow[MT];
+#pragma unroll
+  for (int s = 0; s < MT; s++) arow[s] = 32 * s + lrow < M ? 32 * s + lrow : (int)M - 1;
+
+  f32x16 acc[2][MT];
+#pragma unroll
+  for (int p = 0; p < 2; p++)
+#pragma unroll
+    for (int s = 0; s < MT; s++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[p][s][r] = 0.0f;
+
+  // One chunk from the wave's slot.  All of the chunk's fragments are read
+  // up front, so the LDS latency is paid once per chunk rather than once per
+  // group.
+  auto compute = [&](int64_t c) {
+    const uint4 bsv = *reinterpret_cast<const uint4*>(slot + L::kBS + 16 * lrow);
+    uint4 bq[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      bq[u] = *reinterpret_cast<const uint4*>(slot + L::kBC + 128 * lrow +
+                                              16 * ((2 * u + lhalf) ^ sk_swz(lrow)));
+    // A group past K (the last chunk of a K that is not a multiple of 256)
+    // is multiplied with zero scales: its finite codes then add exact zeros.
+    const int64_t gleft = G - 4 * c;
+    if constexpr (L::A16) {
+      // 8-k unit 8u + 4h + st of A row arow: the k of B's dword st.
+      const int ra = arow[0];
+      half8 af[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+#pragma unroll
+        for (int st = 0; st < 4; st++)
+          af[u][st] = *reinterpret_cast<const half8*>(
+              slot + L::kAC + 512 * ra + 16 * ((8 * u + 4 * lhalf + st) ^ (ra & 15)));
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const uint32_t live = u < gleft ? 0xFFFFFFFFu : 0u;
+        const half2 bsc = scale_pair((pick(bsv, u) & live) >> (16 * lhalf));
+#pragma unroll
+        for (int st = 0; st < 4; st++)
+          acc[st & 1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              af[u][st], decode8(pick(bq[u], st), splat(bsc, st >= 2)), acc[st & 1][0], 0, 0, 0);
+      }
+    } else {
+      uint4 asv[MT], aq[4][MT];
+#pragma unroll
+      for (int s = 0; s < MT; s++)
+        asv[s] = *reinterpret_cast<const uint4*>(slot + L::kAS + 16 * arow[s]);
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+#pragma unroll
+        for (int s = 0; s < MT; s++)
+          aq[u][s] = *reinterpret_cast<const uint4*>(slot + L::kAC + 128 * arow[s] +
+                                                     16 * ((2 * u + lhalf) ^ sk_swz(arow[s])));
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const uint32_t live = u < gleft ? 0xFFFFFFFFu : 0u;
+        const half2 bsc = scale_pair((pick(bsv, u) & live) >> (16 * lhalf));
+        half2 asc[MT];
+#pragma unroll
+        for (int s = 0; s < MT; s++) asc[s] = scale_pair(pick(asv[s], u) >> (16 * lhalf));
+#pragma unroll
+        for (int st = 0; st < 4; st++) {
+          const half8 bf = decode8(pick(bq[u], st), splat(bsc, st >= 2));
+#pragma unroll
+          for (int s = 0; s < MT; s++)
+            acc[st & 1][s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                decode8(pick(aq[u][s], st), splat(asc[s], st >= 2)), bf, acc[st & 1][s], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Chunk c + j sits in buf[j % NB].  Every step issues its refill (out of
+  // range, so without traffic, past the wave's share) and the scheduling
+  // fences keep each chunk's loads together and in order: all paths then
+  // carry the same load sequence, and the wait before a chunk's LDS write
+  // leaves the NB - 1 later chunks in flight.
+  SkChunk<NA8> buf[NB];
+#pragma unroll
+  for (int j = 0; j < NB; j++) {
+    src.load(buf[j], c0 + j, c0 + j < c1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t c = c0; c < c1; c += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+      const bool live = c + j < c1;  // wave-uniform
+      if (live) sk_put<NA8>(slot, buf[j], lane);
+      __builtin_amdgcn_sched_barrier(0);
+      src.load(buf[j], c + j + NB, c + j + NB < c1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (live) compute(c + j);
+    }
+  }
+
+  // Reduction through the (now idle) slots.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds);  // [NWV][MT][16][64]
+#pragma unroll
+  for (int s = 0; s < MT; s++)
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      red[((wave * MT + s) * 16 + r) * 64 + lane] = acc[0][s][r] + acc[1][s][r];
+  __syncthreads();
+  // Wave w adds and stores accumulator entries r with r % NWV == w (per sub-tile).
+  const float gscale = *a.A.gdec * *a.B.gdec;
+  const int64_t col = n0 + lrow;
+#pragma unroll
+  for (int s = 0; s < MT; s++) {
+    for (int r = wave; r < 16; r += NWV) {
+      float v = red[(s * 16 + r) * 64 + lane];
+      for (int w = 1; w < NWV; w++) v = v + red[((w * MT + s) * 16 + r) * 64 + lane];
+      const int64_t row = 32 * s + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+      if (row < M && col < N) {
+        const float o = v * gscale;
+        if (a.c_bf16) {
+          const __bf16 b = (__bf16)o;
+          static_cast<uint16_t*>(a.C)[row * N + col] = __builtin_bit_cast(uint16_t, b);
+        } else {
+          static_cast<float*>(a.C)[row * N + col] = o;
+        }
+      }
+    }
+  }
+}
+
+template <int NA8, int NWV, int NB>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+  const int64_t grid = (a.N + 31) / 32;
+  gemm_skinny_kernel<NA8, NWV, NB><<<(unsigned)grid, NWV * 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_m(const GemmArgs& a, hipStream_t st) {
+  if (a.M <= 8) return launch_skinny<1, 8, 2>(a, st);
+  if (a.M <= 16) return launch_skinny<2, 8, 2>(a, st);
+  if (a.M <= 32) return launch_skinny<4, 8, 2>(a, st);
+  return launch_skinny<8, 8, 2>(a, st);
+}
+
 template <class C, bool AK, bool BKM>
 hipError_t launch_dense(const GemmArgs& a, hipStream_t st) {
   const int64_t ntm = (a.M + C::BM - 1) / C::BM, ntn = (a.N + C::BN - 1) / C::BN;
@@ -1078,6 +1375,8 @@ hipError_t launch_grouped(const GroupedArgs& a, int cus, hipStream_t st) {
 // is the same sum in the same order whatever the choice.
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  if (a.a_kmajor && a.b_kmajor && a.M <= 64)  // decode-like NT: small-M kernel
+    return launch_small_m(a, st);
   int cus = 256;
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;

@@ -329,6 +329,88 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
   }
 }
 
+// ---- small tensors: ROW quantization in one workgroup --------------------------------------------
+// A decode step quantizes activations of a few rows per layer; three launches
+// (clear, tensor amax, encode) would cost more than the data.  One workgroup
+// takes the tensor amax (max of |x|: exact, whatever the order), publishes it
+// through LDS and then encodes exactly as quant_row_kernel does (same block
+// code, reciprocal table and rounding), so the outputs are bit-identical.
+// Each thread takes kSmallUnroll chunks (all its loads in flight at once):
+// the launch takes at most kSmallChunks chunks.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallUnroll = 8;         // chunks in flight per thread
+constexpr int64_t kSmallChunks = kSmallThreads * kSmallUnroll;  // 8-element chunks (64 Ki elements)
+
+template <typename T, bool kSR>
+__global__ __launch_bounds__(kSmallThreads) void quant_row_small_kernel(
+    const T* __restrict__ x, int64_t chunks, float* __restrict__ amax, bool amax_is_input,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
+    uint64_t seed, uint64_t offset, uint32_t rounds) {
+  __shared__ float rtab[128];
+  __shared__ float red[kSmallThreads / 64];
+  const int tid = threadIdx.x;
+  float a;
+  if (amax_is_input) {
+    a = *amax;
+  } else {
+    float m = 0.0f;
+    float v[kSmallUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kSmallUnroll; u++) {  // all loads first (past the end: zeros)
+      const int64_t i = tid + (int64_t)u * kSmallThreads;
+      if (i < chunks) {
+        In<T>::load8(x + i * 8, v[u]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; t++) v[u][t] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSmallUnroll; u++) m = fmaxf(m, max8(v[u]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    a = red[0];
+#pragma unroll
+    for (int w = 1; w < kSmallThreads / 64; w++) a = fmaxf(a, red[w]);
+    if (tid == 0) *amax = a;
+  }
+  const TensorScales ts = tensor_scales(a);
+  if (tid == 0) *gdec = ts.g;
+  build_recip_table(rtab, ts.S);
+  // The stride is even and chunks is even: the two lanes of a block are
+  // active together, so the pair exchange always finds its partner.
+  float v[kSmallUnroll][8];
+#pragma unroll
+  for (int u = 0; u < kSmallUnroll; u++) {
+    const int64_t i = tid + (int64_t)u * kSmallThreads;
+    if (i < chunks) In<T>::load8(x + i * 8, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kSmallUnroll; u++) {
+    const int64_t i = tid + (int64_t)u * kSmallThreads;
+    if (i >= chunks) break;
+    const float mm = max8(v[u]);
+    const float bm = fmaxf(mm, xor1(mm));
+    const uint32_t e = block_code(bm, ts.k);
+    const float r = rtab[e];
+    float y[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) y[t] = v[u][t] * r;
+    uint32_t packed = 0;
+    if (kSR) {
+      Philox4 p = sr_call((uint64_t)i, seed, offset, rounds);
+#pragma unroll
+      for (int t = 0; t < 8; t++) packed |= e2m1_sr(y[t], sr_slot(p, t)) << (4 * t);
+    } else {
+      packed = pack8_rne(y);
+    }
+    codes[i] = packed;
+    if (!(i & 1)) scales[i >> 1] = (uint8_t)e;
+  }
+}
+
 // ---- PTQ weights: ROW blocks with MSE-calibrated scales ----------------------------------------
 // As the ROW quantizer (lane: 8 elements, lanes 2t and 2t+1: one block), but
 // each block's E4M3 scale is the candidate with the smallest squared error
@@ -777,6 +859,17 @@ int amax_grid(int64_t units, int unroll, int64_t cap = 512) {
 template <typename T>
 hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
+  if (a.axis == kBlockRow && !a.rht && a.rows * a.cols / 8 <= kSmallChunks) {
+    const int64_t chunks = a.rows * a.cols / 8;
+    uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
+    if (a.sr)
+      quant_row_small_kernel<T, true><<<1, kSmallThreads, 0, st>>>(
+          x, chunks, a.amax, a.amax_is_input, cd, a.scales, a.gdec, a.seed, a.offset, a.rounds);
+    else
+      quant_row_small_kernel<T, false><<<1, kSmallThreads, 0, st>>>(
+          x, chunks, a.amax, a.amax_is_input, cd, a.scales, a.gdec, 0, 0, 0);
+    return hipGetLastError();
+  }
   if (!a.amax_is_input) {
     fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 1);
     if (a.axis == kBlockCol && a.rht) {

@@ -115,6 +115,19 @@ def test_gemm_validation(lib):
     # N < 2^21: a tile's output rows must span fewer than 2^31 bytes
     wide = _Operand(0x100000, 0x200000, 0x300000, 1 << 21, 128, 2, 0)
     assert g(b"N", b"T", 64, 1 << 21, 128, C.byref(A), C.byref(wide), FAKE, 0, None) == -2
+    # 32-bit buffer offsets: K < 2^24 for a K-major operand, rows * cols < 2^32
+    # for an MN-major one
+    K = 1 << 24
+    ak = _Operand(0x100000, 0x200000, 0x300000, 64, K, 0, 0)
+    bk = _Operand(0x100000, 0x200000, 0x300000, 64, K, 2, 0)
+    assert g(b"N", b"T", 64, 64, K, C.byref(ak), C.byref(bk), FAKE, 0, None) == -2
+    bn = _Operand(0x100000, 0x200000, 0x300000, 1 << 16, 1 << 16, 2, 0)  # [K x N], 2^32 elements
+    an = _Operand(0x100000, 0x200000, 0x300000, 64, 1 << 16, 0, 0)
+    assert g(b"N", b"N", 64, 1 << 16, 1 << 16, C.byref(an), C.byref(bn), FAKE, 0, None) == -2
+    bn_ok = _Operand(0x100000, 0x200000, 0x300000, 1 << 16, (1 << 16) - 32, 2, 0)
+    an0 = _Operand(0x100000, 0x200000, 0x300000, 0, 1 << 16, 0, 0)
+    assert g(b"N", b"N", 0, (1 << 16) - 32, 1 << 16, C.byref(an0), C.byref(bn_ok), FAKE, 0,
+             None) == 0  # just under the limit; M == 0 returns before any device call
 
 
 def test_grouped_validation(lib):

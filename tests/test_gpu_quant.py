@@ -63,6 +63,20 @@ def test_quantize_1d_distributions(kind, axis, rounding):
     _check_1d(x, "fp32", axis, rounding, -1, seed=77)
 
 
+@pytest.mark.parametrize("rows", [1, 5, 64, 66, 130])
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_1d_row_launch_paths(rows, rounding, dtype):
+    """ROW quantization of tensors up to 64 Ki elements runs in one workgroup
+    (tensor amax and encode in one launch), larger ones in the multi-
+    workgroup kernels: rows of 1024 columns on both sides of the boundary
+    (64 rows = 65536 elements) match the oracle bit for bit, computed amax
+    and supplied amax alike."""
+    x = make_input("normal", (rows, 1024), seed=500 + rows)
+    _check_1d(x, dtype, "row", rounding, -1, seed=rows)
+    _check_1d(x, dtype, "row", rounding, -1, seed=rows, amax=3.25)
+
+
 def test_quantize_1d_philox_rounds_and_offsets():
     x = make_input("normal", (32, 128), seed=3)
     for rounds in (1, 5, 10, 16):
