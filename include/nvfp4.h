@@ -72,6 +72,11 @@ extern "C" {
 /* Element types of unquantized tensors. */
 #define NVFP4_BF16 0
 #define NVFP4_FP32 1
+/* GEMM output only: fp32 C that the product is added to, C = RN32(C +
+ * result) (gradient accumulation into an fp32 main-grad buffer; Ultra report
+ * section 2.7 traces a divergence to local gradient accumulation in bf16
+ * instead of fp32). */
+#define NVFP4_FP32_ACCUMULATE 2
 
 /* Rounding of elements onto the E2M1 grid. */
 #define NVFP4_RNE 0 /* nearest, ties to the even code (activations, weights) */
@@ -243,7 +248,9 @@ int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream);
  * 6 significant bits, range 2^-10 .. 2688); products are summed by MFMA with
  * fp32 accumulation (the pages trace a divergence to bf16 accumulation,
  * Ultra report section 2.7); epilogue C = RN32(acc * RN32(gA * gB)), then
- * bf16 (RNE) or fp32 per c_dtype.
+ * bf16 (RNE) or fp32 per c_dtype; with NVFP4_FP32_ACCUMULATE, C (fp32) is
+ * read and C = RN32(C + that fp32 result) is written.  The grouped GEMMs
+ * take the same c_dtype values.
  * Shapes: K % 64 == 0 and K > 0 (one pipeline stage is 64 k); M, N >= 0;
  * the contiguous dimension of a stored operand is a multiple of 32 and a COL
  * or 2D operand has rows % 16 == 0; N % 8 == 0 and N < 2^21 (else
@@ -313,6 +320,18 @@ int32_t nvfp4_grouped_gemm_nn(int64_t groups, const int64_t* row_offsets, int64_
 int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t total_k,
                               int64_t M, int64_t N, const nvfp4_operand* A,
                               const nvfp4_operand* B, float* C, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_tn accumulating into fp32 main-grad buffers (Ultra
+ * report section 2.7: local gradient accumulation must stay fp32): for every
+ * group e, C[e] = RN32(C[e] + P_e) with P_e the product nvfp4_grouped_gemm_tn
+ * writes (a group with no tokens adds +0).  Same arguments, shapes and
+ * errors; C is read and written.
+ */
+int32_t nvfp4_grouped_gemm_tn_accumulate(int64_t groups, const int64_t* k_offsets,
+                                         int64_t total_k, int64_t M, int64_t N,
+                                         const nvfp4_operand* A, const nvfp4_operand* B,
+                                         float* C, void* stream);
 
 /*
  * fp32 -> fp16 with stochastic rounding, for an SSM (Mamba) state cache

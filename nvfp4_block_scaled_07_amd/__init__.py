@@ -10,14 +10,14 @@ call them.  Nothing here computes a value of the method; if the library is
 missing, every call raises.
 """
 from ._binding import (  # noqa: F401
-    NVFP4_BF16, NVFP4_FP32, NVFP4_RNE, NVFP4_SR, NVFP4_BLOCK_ROW, NVFP4_BLOCK_COL, NVFP4_BLOCK_2D,
-    NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_LAYOUT,
+    NVFP4_BF16, NVFP4_FP32, NVFP4_FP32_ACCUMULATE, NVFP4_RNE, NVFP4_SR,
+    NVFP4_BLOCK_ROW, NVFP4_BLOCK_COL, NVFP4_BLOCK_2D, NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_LAYOUT,
     NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_DEVICE,
     NVFP4Error, Philox, QTensor, library_path, load,
-    nvfp4_abi_version, nvfp4_status_string, nvfp4_quantize_1d, nvfp4_quantize_dual, nvfp4_quantize_mse,
-    nvfp4_quantize_2d, nvfp4_rht16,
+    nvfp4_abi_version, nvfp4_status_string, nvfp4_quantize_1d, nvfp4_quantize_dual,
+    nvfp4_quantize_mse, nvfp4_quantize_2d, nvfp4_rht16,
     nvfp4_dequantize, nvfp4_gemm, nvfp4_grouped_gemm, nvfp4_grouped_gemm_nn, nvfp4_grouped_gemm_tn,
-    nvfp4_sr_fp16,
+    nvfp4_grouped_gemm_tn_accumulate, nvfp4_sr_fp16,
     quantize_1d, quantize_dual, quantize_mse, quantize_2d, rht16, dequantize, gemm, grouped_gemm,
     grouped_gemm_nn, grouped_gemm_tn, sr_fp16,
 )

@@ -11,7 +11,7 @@ from typing import Optional
 
 import torch
 
-NVFP4_BF16, NVFP4_FP32 = 0, 1
+NVFP4_BF16, NVFP4_FP32, NVFP4_FP32_ACCUMULATE = 0, 1, 2
 NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_BLOCK_ROW, NVFP4_BLOCK_COL, NVFP4_BLOCK_2D = 0, 1, 2
 NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN = 0, -1, -2, -3
@@ -88,6 +88,9 @@ def load():
     L.nvfp4_grouped_gemm_tn.restype = i32
     L.nvfp4_grouped_gemm_tn.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
                                         C.POINTER(_Operand), vp, vp]
+    L.nvfp4_grouped_gemm_tn_accumulate.restype = i32
+    L.nvfp4_grouped_gemm_tn_accumulate.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
+                                                   C.POINTER(_Operand), vp, vp]
     _lib = L
     return L
 
@@ -237,6 +240,14 @@ def nvfp4_grouped_gemm_tn(groups, k_offsets, total_k, M, N, A_operand, B_operand
     _check("nvfp4_grouped_gemm_tn", st)
 
 
+def nvfp4_grouped_gemm_tn_accumulate(groups, k_offsets, total_k, M, N, A_operand, B_operand,
+                                     C_inout, stream=None):
+    st = load().nvfp4_grouped_gemm_tn_accumulate(groups, _p(k_offsets), total_k, M, N,
+                                                 C.byref(A_operand), C.byref(B_operand),
+                                                 _p(C_inout), _stream(stream))
+    _check("nvfp4_grouped_gemm_tn_accumulate", st)
+
+
 def nvfp4_sr_fp16(x, rng, y, stream=None):
     st = load().nvfp4_sr_fp16(_p(x), x.numel(), C.byref(_Philox(rng.seed, rng.offset, rng.rounds, 0)),
                               _p(y), _stream(stream))
@@ -330,14 +341,21 @@ def dequantize(q: QTensor, index=None, stream=None):
     return y
 
 
-def gemm(opA, opB, A: QTensor, B: QTensor, out_dtype=torch.bfloat16, out=None, stream=None):
-    """C = op(A) op(B) * gA * gB with row-major op letters (see nvfp4.h)."""
+def gemm(opA, opB, A: QTensor, B: QTensor, out_dtype=torch.bfloat16, out=None, stream=None,
+         accumulate=False):
+    """C = op(A) op(B) * gA * gB with row-major op letters (see nvfp4.h);
+    accumulate=True adds the product to the fp32 tensor `out`."""
     M = A.rows if opA == "N" else A.cols
     K = A.cols if opA == "N" else A.rows
     N = B.rows if opB == "T" else B.cols
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=A.codes.device)
-    cd = NVFP4_BF16 if out.dtype == torch.bfloat16 else NVFP4_FP32
+    if accumulate:
+        if out is None or out.dtype != torch.float32:
+            raise ValueError("accumulate needs an fp32 `out`")
+        cd = NVFP4_FP32_ACCUMULATE
+    else:
+        if out is None:
+            out = torch.empty((M, N), dtype=out_dtype, device=A.codes.device)
+        cd = NVFP4_BF16 if out.dtype == torch.bfloat16 else NVFP4_FP32
     nvfp4_gemm(opA, opB, M, N, K, A.operand(), B.operand(), out, cd, stream)
     return out
 
@@ -369,10 +387,18 @@ def grouped_gemm_nn(A: QTensor, B: QTensor, row_offsets, out_dtype=torch.bfloat1
     return out
 
 
-def grouped_gemm_tn(A: QTensor, B: QTensor, k_offsets, groups, out=None, stream=None):
-    """Per group e: C[e] = A[k_e:k_e+1]^T B[k_e:k_e+1], fp32 [groups, M, N]."""
+def grouped_gemm_tn(A: QTensor, B: QTensor, k_offsets, groups, out=None, stream=None,
+                    accumulate=False):
+    """Per group e: C[e] = A[k_e:k_e+1]^T B[k_e:k_e+1], fp32 [groups, M, N];
+    accumulate=True adds it to `out` instead."""
     total, M = A.rows, A.cols
     N = B.cols
+    if accumulate:
+        if out is None:
+            raise ValueError("accumulate needs `out`")
+        nvfp4_grouped_gemm_tn_accumulate(groups, k_offsets, total, M, N, A.operand(),
+                                         B.operand(), out, stream)
+        return out
     if out is None:
         out = torch.empty((groups, M, N), dtype=torch.float32, device=A.codes.device)
     nvfp4_grouped_gemm_tn(groups, k_offsets, total, M, N, A.operand(), B.operand(), out, stream)

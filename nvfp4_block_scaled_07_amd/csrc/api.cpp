@@ -20,6 +20,9 @@ int32_t device_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_
 
 bool valid_dtype(int32_t t) { return t == NVFP4_BF16 || t == NVFP4_FP32; }
 
+// GEMM outputs may also accumulate into an fp32 C.
+bool valid_out(int32_t t) { return valid_dtype(t) || t == NVFP4_FP32_ACCUMULATE; }
+
 // The stored shape an operand must have, and the block kinds that tile K.
 struct Expect {
   int64_t rows, cols;
@@ -59,7 +62,7 @@ constexpr int64_t kMaxN = int64_t(1) << 21;
 int32_t grouped_gemm(bool b_kmajor, int64_t groups, const int64_t* row_offsets,
                      int64_t total_rows, int64_t N, int64_t K, const nvfp4_operand* A,
                      const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream) {
-  if (!valid_dtype(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (!valid_out(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
   if (groups < 0 || total_rows < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
   if (groups > 4096) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0 || N % 16 != 0 || K == 0 || N >= kMaxN) return NVFP4_ERR_SHAPE;
@@ -83,6 +86,7 @@ int32_t grouped_gemm(bool b_kmajor, int64_t groups, const int64_t* row_offsets,
   a.b_kmajor = b_kmajor;
   a.C = C;
   a.c_bf16 = c_dtype == NVFP4_BF16;
+  a.c_acc = c_dtype == NVFP4_FP32_ACCUMULATE;
   return device_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -264,7 +268,7 @@ int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nv
                    const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream) {
   if ((opA != 'N' && opA != 'T') || (opB != 'N' && opB != 'T')) return NVFP4_ERR_LAYOUT;
   if (opA == 'T' && opB == 'T') return NVFP4_ERR_UNSUPPORTED;
-  if (!valid_dtype(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
+  if (!valid_out(c_dtype)) return NVFP4_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0) return NVFP4_ERR_SHAPE;
   if (K % 64 != 0) return NVFP4_ERR_SHAPE;
   if (!A || !B || !C) return NVFP4_ERR_NULL;
@@ -289,6 +293,7 @@ int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nv
   a.B = dev(B);
   a.C = C;
   a.c_bf16 = c_dtype == NVFP4_BF16;
+  a.c_acc = c_dtype == NVFP4_FP32_ACCUMULATE;
   return device_status(nvfp4::launch_gemm(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -304,9 +309,11 @@ int32_t nvfp4_grouped_gemm_nn(int64_t groups, const int64_t* row_offsets, int64_
   return grouped_gemm(false, groups, row_offsets, total_rows, N, K, A, B, C, c_dtype, stream);
 }
 
-int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t total_k,
-                              int64_t M, int64_t N, const nvfp4_operand* A,
-                              const nvfp4_operand* B, float* C, void* stream) {
+namespace {
+
+int32_t grouped_tn(bool accumulate, int64_t groups, const int64_t* k_offsets, int64_t total_k,
+                   int64_t M, int64_t N, const nvfp4_operand* A, const nvfp4_operand* B, float* C,
+                   void* stream) {
   if (groups < 0 || total_k < 0 || M < 0 || N < 0) return NVFP4_ERR_SHAPE;
   if (groups > 4096) return NVFP4_ERR_SHAPE;
   if (M % 32 != 0 || N % 32 != 0 || total_k % 16 != 0 || N >= kMaxN) return NVFP4_ERR_SHAPE;
@@ -326,7 +333,23 @@ int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t 
   a.A = dev(A);
   a.B = dev(B);
   a.C = C;
+  a.c_acc = accumulate;
   return device_status(nvfp4::launch_grouped_wgrad(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int32_t nvfp4_grouped_gemm_tn(int64_t groups, const int64_t* k_offsets, int64_t total_k,
+                              int64_t M, int64_t N, const nvfp4_operand* A,
+                              const nvfp4_operand* B, float* C, void* stream) {
+  return grouped_tn(false, groups, k_offsets, total_k, M, N, A, B, C, stream);
+}
+
+int32_t nvfp4_grouped_gemm_tn_accumulate(int64_t groups, const int64_t* k_offsets,
+                                         int64_t total_k, int64_t M, int64_t N,
+                                         const nvfp4_operand* A, const nvfp4_operand* B,
+                                         float* C, void* stream) {
+  return grouped_tn(true, groups, k_offsets, total_k, M, N, A, B, C, stream);
 }
 
 int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16_t* y,

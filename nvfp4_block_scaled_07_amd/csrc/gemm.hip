@@ -492,7 +492,7 @@ struct TileDesc {
 // when there is always exactly one (its store then follows the loop).
 template <class C, bool AK, bool BKM, class Src>
 __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K, bool c_bf16,
-                                           int64_t ldc, const TileLds& L) {
+                                           bool c_acc, int64_t ldc, const TileLds& L) {
   constexpr int H = C::H, TM = C::TM, TN = C::TN;
   const int64_t NJ = src.count();
   if (NJ <= 0) return;
@@ -681,11 +681,25 @@ __device__ __forceinline__ void gemm_tiles(const Src& src, int64_t N, int64_t K,
         } else {
           const uint32_t loff = (uint32_t)(rl0 * ldc32 + col) * 4u;
           const bool cok = col < N;
+          // Accumulating output: C = RN32(C + RN32(acc * g)).  The loads take
+          // the stores' offsets (past the range: 0, never stored), all issued
+          // before the first add.
+          float prev[16];
+          if (c_acc) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int dr = 8 * (r >> 2) + (r & 3);
+              const bool ok = cok && rl0 + dr < rows_left;
+              prev[r] = __uint_as_float(
+                  __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? loff : kDrop, dr * ldc32 * 4, 0));
+            }
+          }
 #pragma unroll
           for (int r = 0; r < 16; r++) {
             const int dr = 8 * (r >> 2) + (r & 3);
             const bool ok = cok && rl0 + dr < rows_left;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r] * t.gscale), rs,
+            const float v = acc[i][j][r] * t.gscale;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c_acc ? prev[r] + v : v), rs,
                                                   ok ? loff : kDrop, dr * ldc32 * 4, 0);
           }
         }
@@ -863,7 +877,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   src.t.n0 = tn * C::BN;
   src.t.gscale = *a.A.gdec * *a.B.gdec;
   src.t.C = a.C;
-  gemm_tiles<C, AK, BKM>(src, a.N, a.K, a.c_bf16, a.N, lds);
+  gemm_tiles<C, AK, BKM>(src, a.N, a.K, a.c_bf16, a.c_acc, a.N, lds);
 }
 
 constexpr int kMaxGroups = 4096;  // the ABI's limit on groups
@@ -977,11 +991,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_kernel(GroupedArgs a) {
   const int32_t total = prefix[G];
   GroupedTiles<C> src{&a, prefix, ntn, total};
   if (a.K >= 2 * C::BK) {
-    gemm_tiles<C, true, BKM>(src, a.N, a.K, a.c_bf16, a.N, lds);
+    gemm_tiles<C, true, BKM>(src, a.N, a.K, a.c_bf16, a.c_acc, a.N, lds);
   } else {  // one stage per tile: no pipeline across tiles
     for (int64_t j = 0; j < src.count(); j++) {
       DenseTile one{src.get(j)};
-      gemm_tiles<C, true, BKM>(one, a.N, a.K, a.c_bf16, a.N, lds);
+      gemm_tiles<C, true, BKM>(one, a.N, a.K, a.c_bf16, a.c_acc, a.N, lds);
       __syncthreads();
     }
   }
@@ -1015,7 +1029,7 @@ __global__ __launch_bounds__(C::NT) void grouped_wgrad_kernel(WgradArgs a) {
     one.t.n0 = (r / mt) * C::BN;
     one.t.gscale = gscale;
     one.t.C = a.C + e * M * N;
-    gemm_tiles<C, false, false>(one, N, k1 - k0, false, N, lds);
+    gemm_tiles<C, false, false>(one, N, k1 - k0, false, a.c_acc, N, lds);
     __syncthreads();  // the next tile reuses the LDS buffers
   }
 }
@@ -1296,7 +1310,8 @@ __global__ __launch_bounds__(NWV * 64) void gemm_skinny_kernel(GemmArgs a) {
           const __bf16 b = (__bf16)o;
           static_cast<uint16_t*>(a.C)[row * N + col] = __builtin_bit_cast(uint16_t, b);
         } else {
-          static_cast<float*>(a.C)[row * N + col] = o;
+          float* c = static_cast<float*>(a.C) + row * N + col;
+          *c = a.c_acc ? *c + o : o;
         }
       }
     }

@@ -74,6 +74,7 @@ struct GemmArgs {
   DevOperand A, B;
   void* C;
   bool c_bf16;
+  bool c_acc;  // fp32 C is added to: C = RN32(C + result)
 };
 
 struct GroupedArgs {
@@ -85,6 +86,7 @@ struct GroupedArgs {
   bool b_kmajor;  // NT (fprop) when true, NN (dgrad) when false
   void* C;
   bool c_bf16;
+  bool c_acc;
 };
 
 // Grouped wgrad: C[e] [M x N] fp32 = A[k_e : k_{e+1}]^T B[k_e : k_{e+1}].
@@ -95,6 +97,7 @@ struct WgradArgs {
   DevOperand A;  // [total_k x M] COL (or 2D)
   DevOperand B;  // [total_k x N] COL (or 2D)
   float* C;      // [groups x M x N]
+  bool c_acc;    // C[e] += the product instead of C[e] = it
 };
 
 hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st);

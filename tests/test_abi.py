@@ -106,6 +106,8 @@ def test_gemm_validation(lib):
     g = lib.nvfp4_gemm
     assert g(b"T", b"T", 64, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -5
     assert g(b"X", b"T", 64, 64, 128, C.byref(A), C.byref(B), FAKE, 0, None) == -4
+    assert g(b"N", b"T", 64, 64, 128, C.byref(A), C.byref(B), FAKE, 3, None) == -5  # c_dtype
+    assert g(b"N", b"T", 64, 64, 96, C.byref(A), C.byref(B), FAKE, 2, None) == -2   # accumulate
     assert g(b"N", b"T", 64, 64, 96, C.byref(A), C.byref(B), FAKE, 0, None) == -2   # K % 64
     assert g(b"N", b"T", 64, 64, 128, C.byref(A), C.byref(B), None, 0, None) == -1
     bad = _Operand(0x100000, 0x200000, 0x300000, 64, 128, 1, 0)  # COL blocks on a K-major A
@@ -161,6 +163,11 @@ def test_grouped_backward_validation(lib):
     assert tn(4, FAKE, 160, 96, 64, C.byref(dY), C.byref(rowX), FAKE, None) == -4
     assert tn(4, C.c_void_p(0x100004), 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == -3
     assert tn(0, FAKE, 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == 0     # no groups: no-op
+    acc = lib.nvfp4_grouped_gemm_tn_accumulate  # same checks, C read and written
+    assert acc(4, None, 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == -1
+    assert acc(4, FAKE, 160, 80, 64, C.byref(dY), C.byref(X), FAKE, None) == -2
+    assert acc(4, FAKE, 160, 96, 64, C.byref(dY), C.byref(rowX), FAKE, None) == -4
+    assert acc(0, FAKE, 160, 96, 64, C.byref(dY), C.byref(X), FAKE, None) == 0
 
 
 def test_sr_fp16_validation(lib):

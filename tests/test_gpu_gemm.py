@@ -234,3 +234,25 @@ def test_gemm_deterministic_long_k(layout):
         assert torch.equal(c1, c2)
         check_bf16_is_rne_of_fp32(nv.gemm(layout[0], layout[1], qa, qb,
                                           out_dtype=torch.bfloat16), c1)
+
+
+@pytest.mark.parametrize("layout,M,N,K", [("TN", 288, 544, 256), ("NN", 200, 96, 192),
+                                          ("NT", 300, 272, 320), ("NT", 40, 96, 512)])
+def test_gemm_accumulate_into_fp32(layout, M, N, K):
+    """NVFP4_FP32_ACCUMULATE: C = RN32(C + P) with P the product the plain
+    fp32 call writes, bit for bit (tiled kernels with partial tiles, and the
+    small-M kernel); P itself meets the oracle bar."""
+    dev = device()
+    qa, qb = _operands(layout, M, N, K, seed=M + 2 * N + K, sr=layout != "NT",
+                       mask=0x2D4B if layout == "TN" else -1)
+    p = nv.gemm(layout[0], layout[1], qa, qb, out_dtype=torch.float32)
+    c0 = torch.from_numpy(make_input("normal", (M, N), 77)).to(dev)
+    c0[0, :8] = 0.0
+    c = c0.clone()
+    nv.gemm(layout[0], layout[1], qa, qb, out=c, accumulate=True)
+    assert torch.equal(c.view(torch.int32), (c0 + p).view(torch.int32))
+    nv.gemm(layout[0], layout[1], qa, qb, out=c, accumulate=True)
+    assert torch.equal(c.view(torch.int32), ((c0 + p) + p).view(torch.int32))
+    A, B = to_np(qa), to_np(qb)
+    R, D = O.gemm_full(layout[0], layout[1], M, N, K, A, B)
+    assert O.gemm_rel_err(p.cpu().numpy(), R, D) <= TOL

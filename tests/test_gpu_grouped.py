@@ -250,6 +250,40 @@ def test_grouped_wgrad_tn_small_ragged():
         _check_wgrad_group(qa, qb, off, c, e, M, N)
 
 
+def test_grouped_fprop_accumulate_into_fp32():
+    """The grouped fprop's NVFP4_FP32_ACCUMULATE output: C = RN32(C + P), bit
+    for bit against the plain fp32 call (partial 128- and 256-row tiles)."""
+    counts = [40, 0, 300, 7]
+    N, K = 272, 192
+    qa, qb, off, p = _grouped_case(counts, N, K, seed=13, out=torch.float32)
+    dev = p.device
+    c0 = torch.randn(p.shape, generator=torch.Generator(device=dev).manual_seed(3), device=dev)
+    c = c0.clone()
+    nv.nvfp4_grouped_gemm(len(counts), torch.from_numpy(off).to(dev), int(sum(counts)), N, K,
+                          qa.operand(), qb.operand(), c, nv.NVFP4_FP32_ACCUMULATE)
+    assert torch.equal(c.view(torch.int32), (c0 + p).view(torch.int32))
+
+
+def test_grouped_wgrad_tn_accumulate():
+    """Accumulating into fp32 main-grad buffers: C[e] = RN32(C[e] + P_e), bit
+    for bit against the plain call's P_e, twice in a row; a group with no
+    tokens adds +0."""
+    dev = device()
+    counts = [0, 5, 40, 130, 0, 77]
+    M, N = 96, 288
+    qa, qb, off = _wgrad_case(counts, M, N, 72, dev)
+    offs = torch.from_numpy(off).to(dev)
+    p = nv.grouped_gemm_tn(qa, qb, offs, len(counts))
+    c0 = torch.randn((len(counts), M, N), generator=torch.Generator(device=dev).manual_seed(5),
+                     device=dev)
+    c = c0.clone()
+    nv.grouped_gemm_tn(qa, qb, offs, len(counts), out=c, accumulate=True)
+    assert torch.equal(c.view(torch.int32), (c0 + p).view(torch.int32))
+    nv.grouped_gemm_tn(qa, qb, offs, len(counts), out=c, accumulate=True)
+    assert torch.equal(c.view(torch.int32), ((c0 + p) + p).view(torch.int32))
+    assert torch.equal(p[0], torch.zeros_like(p[0]))
+
+
 def test_grouped_wgrad_tn_matches_dense_per_group():
     """Each group's result equals the dense TN GEMM on that group's rows when
     the group's token count is a multiple of 64 (bit for bit: same sums in
