@@ -195,6 +195,26 @@ def quantize(x, block, rounding=RNE, seed=0, offset=0, rounds=5, rht_mask=-1,
     return dict(codes=codes, scales=scales, amax=amax_out, g=g)
 
 
+def gather_rows(x, row_index):
+    """The tensor a gathering quantizer quantizes: row r is x[row_index[r]],
+    or a row of zeros when row_index[r] lies outside [0, len(x)) -- the MoE
+    token dispatch, with the padding that rounds each expert's rows up to a
+    multiple of 16 (Super report summary, sections 2.1-2.2).  Works on fp32
+    arrays and on bf16 bit patterns (uint16; zero bits are +0.0)."""
+    x = np.asarray(x)
+    idx = np.asarray(row_index, dtype=np.int64)
+    out = np.zeros((idx.shape[0],) + x.shape[1:], dtype=x.dtype)
+    ok = (idx >= 0) & (idx < x.shape[0])
+    out[ok] = x[idx[ok]]
+    return out
+
+
+def quantize_gather(x, row_index, block, **kw):
+    """quantize() of gather_rows(x, row_index): the gathered tensor's own
+    amax, scales and Philox block ids (by gathered position)."""
+    return quantize(gather_rows(x, row_index), block, **kw)
+
+
 def quantize_mse(x, amax=None):
     """PTQ weight quantization: ROW blocks, RNE, MSE-calibrated block scales
     (see oracle_quantize_mse).  Returns dict(codes, scales, amax, g)."""
