@@ -299,11 +299,17 @@ def row_dy_dual(nv, synth, torch, dev, steps, warmup):
 
 def row_grouped(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688, route_seed=9,
                 name="grouped_super"):
+    """Routed-expert fprop: token-major X [8192 x latent] dispatched to 22 of
+    512 experts and quantized in the same pass (row-index gather, ROW RNE),
+    the experts' weights 16x16, then the grouped GEMM.  The gather done
+    apart (torch index_select, then the plain quantizer) is timed beside it
+    for comparison."""
     counts, tok, offsets = synth.zipf_routing(8192, 512, 22, 1.1, route_seed)
     x = synth.normal_device((8192, latent), 1.0, 8, dev)
-    a = x[torch.from_numpy(tok).to(dev)].contiguous()
+    idx = torch.from_numpy(tok).to(dev)
+    a = x[idx].contiguous()
     w = synth.normal_device((512, hidden, latent), 0.02, 10, dev)
-    qa = nv.quantize_1d(a, "row")
+    qa = nv.quantize_1d(x, "row", row_index=idx)
     qw = nv.quantize_2d(w)
     off = torch.from_numpy(offsets).to(dev)
     total = int(offsets[-1])
@@ -311,21 +317,34 @@ def row_grouped(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688, 
     timer = Timer(torch)
 
     def step(i):
-        timer.run("quantize_1d", lambda: nv.nvfp4_quantize_1d(
-            a, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qa.amax, False, qa.codes, qa.scales,
-            qa.global_dec))
+        timer.run("quantize_1d_gather", lambda: nv.nvfp4_quantize_1d(
+            x, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qa.amax, False, qa.codes, qa.scales,
+            qa.global_dec, row_index=idx))
         timer.run("quantize_2d_experts", lambda: nv.nvfp4_quantize_2d(
             w, qw.amax, False, qw.codes, qw.scales, qw.global_dec))
         timer.run("grouped_gemm", lambda: nv.nvfp4_grouped_gemm(
             512, off, total, hidden, latent, qa.operand(), qw.operand(), y, nv.NVFP4_BF16))
 
     ms, _ = timed(torch, timer, step, steps, warmup)
+    ref = Timer(torch)
+    qb = nv.quantize_1d(a, "row")
+
+    def apart(i):
+        ref.run("gather_index_select", lambda: torch.index_select(x, 0, idx, out=a))
+        ref.run("quantize_1d", lambda: nv.nvfp4_quantize_1d(
+            a, nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qb.amax, False, qb.codes, qb.scales,
+            qb.global_dec))
+
+    timed(torch, ref, apart, steps, warmup)
     return {"workload": f"{name}: 8192 tokens top-22 of 512 experts (Zipf 1.1), "
                         f"{latent} -> {hidden}",
             "ms_per_step": round(ms, 4), "max_vio": round(synth.max_vio(counts, 22), 3),
             "rows_per_expert_min_max": [int(counts.min()), int(counts.max())],
-            "quantize_1d": kernel_entry(timer.avg_ms("quantize_1d"), q1d_bytes(total, latent),
-                                        "bytes"),
+            "quantize_1d_gather": kernel_entry(timer.avg_ms("quantize_1d_gather"),
+                                               q1d_bytes(total, latent), "bytes"),
+            "gather_then_quantize_ms": {
+                "index_select": round(ref.avg_ms("gather_index_select"), 5),
+                "quantize_1d": round(ref.avg_ms("quantize_1d"), 5)},
             "quantize_2d_experts": kernel_entry(timer.avg_ms("quantize_2d_experts"),
                                                 q2d_bytes(512 * hidden, latent), "bytes"),
             "grouped_gemm": kernel_entry(timer.avg_ms("grouped_gemm"),
@@ -334,32 +353,37 @@ def row_grouped(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688, 
 
 def row_grouped_bwd(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=2688,
                     route_seed=9, name="grouped_bwd_super"):
-    """Routed-expert backward: dY of the experts' up projection (gathered
-    rows, [tokens x hidden]) quantized once for both GEMMs (ROW+SR for
-    dgrad, COL+RHT+SR for wgrad, each expert's rows padded to 16), X (the
-    gathered latent inputs) COL+RHT; grouped dgrad dX = dY W_e (W_e the
-    fprop's 2D codes, stored [hidden x latent]) and grouped wgrad dW_e =
-    dY_e^T X_e over each expert's own tokens (fp32)."""
+    """Routed-expert backward of the experts' up projection.  dY arrives in
+    expert order ([rows x hidden], unpadded) and is quantized once for both
+    GEMMs (ROW+SR for dgrad, COL+RHT+SR for wgrad) with each expert's rows
+    padded to 16 by the row-index gather; X is gathered from the token-major
+    latent activations and quantized COL+RHT in the same pass.  Then grouped
+    dgrad dX = dY W_e (W_e the fprop's 2D codes, stored [hidden x latent])
+    and grouped wgrad dW_e = dY_e^T X_e over each expert's own tokens
+    (fp32)."""
     import numpy as np
-    counts, _, _ = synth.zipf_routing(8192, 512, 22, 1.1, route_seed)
+    counts, tok, offsets = synth.zipf_routing(8192, 512, 22, 1.1, route_seed)
     padded = (counts + 15) // 16 * 16
     koff = np.zeros(513, dtype=np.int64)
     koff[1:] = np.cumsum(padded)
     KT = int(koff[-1])
-    rows = np.concatenate([np.arange(int(koff[e]), int(koff[e]) + int(counts[e]))
-                           for e in range(512)])
-    ridx = torch.from_numpy(rows).to(dev)
-    T = len(rows)
+    T = int(offsets[-1])
+    idx_dy = np.full(KT, -1, dtype=np.int64)   # padded row -> row of the unpadded dY
+    idx_x = np.full(KT, -1, dtype=np.int64)    # padded row -> token
+    for e in range(512):
+        n = int(counts[e])
+        idx_dy[koff[e]:koff[e] + n] = np.arange(offsets[e], offsets[e] + n)
+        idx_x[koff[e]:koff[e] + n] = tok[offsets[e]:offsets[e] + n]
+    idx_dy = torch.from_numpy(idx_dy).to(dev)
+    idx_x = torch.from_numpy(idx_x).to(dev)
     mask = synth.rht_mask(6)
-    dy = torch.zeros((KT, hidden), dtype=torch.bfloat16, device=dev)
-    dy[ridx] = synth.laplace_device((T, hidden), 1e-3, 91, dev, zero_frac=0.07)
-    x = torch.zeros((KT, latent), dtype=torch.bfloat16, device=dev)
-    x[ridx] = synth.normal_device((T, latent), 1.0, 92, dev)
+    dy = synth.laplace_device((T, hidden), 1e-3, 91, dev, zero_frac=0.07)
+    x = synth.normal_device((8192, latent), 1.0, 92, dev)
     w = synth.normal_device((512, hidden, latent), 0.02, 93, dev)
     qw = nv.quantize_2d(w)
     del w
-    qr, qc, z = nv.quantize_dual(dy, nv.Philox(94), nv.Philox(95), mask)
-    qx = nv.quantize_1d(x, "col", "rne", None, mask)
+    qr, qc, z = nv.quantize_dual(dy, nv.Philox(94), nv.Philox(95), mask, row_index=idx_dy)
+    qx = nv.quantize_1d(x, "col", "rne", None, mask, row_index=idx_x)
     koff_d = torch.from_numpy(koff).to(dev)
     dx = torch.empty((KT, latent), dtype=torch.bfloat16, device=dev)
     dw = torch.empty((512, hidden, latent), dtype=torch.float32, device=dev)
@@ -372,10 +396,10 @@ def row_grouped_bwd(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=26
         rr.offset = rc.offset = i
         timer.run("quantize_dual_dy", lambda: nv.nvfp4_quantize_dual(
             dy, rr, rc, mask, a, False, qr.codes, qr.scales, g[0:1], qc.codes, qc.scales, g[1:2],
-            z))
+            z, row_index=idx_dy))
         timer.run("quantize_col_rht_x", lambda: nv.nvfp4_quantize_1d(
             x, nv.NVFP4_BLOCK_COL, nv.NVFP4_RNE, None, mask, qx.amax, False, qx.codes, qx.scales,
-            qx.global_dec))
+            qx.global_dec, row_index=idx_x))
         # dgrad over the padded rows (the pad rows of dY are zero: their dX rows are 0)
         timer.run("grouped_dgrad_nn", lambda: nv.nvfp4_grouped_gemm_nn(
             512, koff_d, KT, latent, hidden, qr.operand(), qw.operand(), dx, nv.NVFP4_BF16))
@@ -385,12 +409,15 @@ def row_grouped_bwd(nv, synth, torch, dev, steps, warmup, latent=1024, hidden=26
     ms, _ = timed(torch, timer, step, steps, warmup)
     flops = 2.0 * KT * hidden * latent
     return {"workload": f"{name}: 8192 tokens top-22 of 512 experts (Zipf 1.1), expert rows "
-                        f"padded to 16 ({KT} rows); dY [rows x {hidden}], X [rows x {latent}]",
+                        f"padded to 16 by the gather ({KT} rows); dY [{T} x {hidden}] in expert "
+                        f"order, X [8192 x {latent}] token-major",
             "ms_per_step": round(ms, 4),
             "quantize_dual_dy": kernel_entry(timer.avg_ms("quantize_dual_dy"),
-                                             KT * hidden * (2 + 2 * (0.5 + 1.0 / 16)), "bytes"),
+                                             T * hidden * 2 + KT * hidden * 2 * (0.5 + 1.0 / 16),
+                                             "bytes"),
             "quantize_col_rht_x": kernel_entry(timer.avg_ms("quantize_col_rht_x"),
-                                               q1d_bytes(KT, latent), "bytes"),
+                                               T * latent * 2 + KT * latent * (0.5 + 1.0 / 16),
+                                               "bytes"),
             "grouped_dgrad_nn": kernel_entry(timer.avg_ms("grouped_dgrad_nn"), flops, "flops"),
             "grouped_wgrad_tn": kernel_entry(timer.avg_ms("grouped_wgrad_tn"), flops, "flops")}
 

@@ -183,6 +183,37 @@ int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_
                             uint64_t* zero_codes, void* stream);
 
 /*
+ * Quantization fused with the MoE token dispatch (Super report summary,
+ * section 2.1: LatentMoE routes each token to 22 of 512 experts; section 2.2:
+ * the routed-expert GEMMs run in NVFP4).  The tensor quantized is
+ *   G [rows x cols], row r of G = row row_index[r] of x [src_rows x cols],
+ * and an index outside [0, src_rows) makes row r a row of zeros (the padding
+ * that keeps each expert's rows a multiple of 16 for COL blocks).  The result
+ * (codes, scales, amax, g, and for the dual form the zero counts) is bit for
+ * bit that of nvfp4_quantize_1d / nvfp4_quantize_dual on G materialized, so
+ * the gathered bf16/fp32 copy of the activations is never written.
+ *   row_index  device int64 [rows], 8-byte aligned, read only.
+ *   src_rows   >= 1; x is [src_rows x cols] as in the plain call.
+ * Other arguments, shapes and errors as the plain calls, plus: src_rows < 1
+ * or rows * cols / 8 >= 2^32 -> NVFP4_ERR_SHAPE; a NULL row_index with a
+ * non-empty G -> NVFP4_ERR_NULL.
+ */
+int32_t nvfp4_quantize_1d_gather(const void* x, int32_t x_dtype, int64_t src_rows,
+                                 const int64_t* row_index, int64_t rows, int64_t cols,
+                                 int32_t axis, int32_t rounding, const nvfp4_philox* rng,
+                                 int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                                 uint8_t* codes, uint8_t* scales, float* global_dec,
+                                 void* stream);
+int32_t nvfp4_quantize_dual_gather(const void* x, int32_t x_dtype, int64_t src_rows,
+                                   const int64_t* row_index, int64_t rows, int64_t cols,
+                                   const nvfp4_philox* rng_row, const nvfp4_philox* rng_col,
+                                   int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                                   uint8_t* row_codes, uint8_t* row_scales,
+                                   float* row_global_dec, uint8_t* col_codes,
+                                   uint8_t* col_scales, float* col_global_dec,
+                                   uint64_t* zero_codes, void* stream);
+
+/*
  * Post-training weight quantization with MSE-calibrated block scales (Super
  * report summary, section 4.2, NVFP4 PTQ: each weight block's scale is chosen
  * to minimize the weight's MSE rather than from the block max; activations

@@ -66,6 +66,13 @@ def load():
     L.nvfp4_quantize_dual.restype = i32
     L.nvfp4_quantize_dual.argtypes = [vp, i32, i64, i64, C.POINTER(_Philox), C.POINTER(_Philox),
                                        i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.nvfp4_quantize_1d_gather.restype = i32
+    L.nvfp4_quantize_1d_gather.argtypes = [vp, i32, i64, vp, i64, i64, i32, i32,
+                                           C.POINTER(_Philox), i32, vp, i32, vp, vp, vp, vp]
+    L.nvfp4_quantize_dual_gather.restype = i32
+    L.nvfp4_quantize_dual_gather.argtypes = [vp, i32, i64, vp, i64, i64, C.POINTER(_Philox),
+                                             C.POINTER(_Philox), i32, vp, i32, vp, vp, vp, vp,
+                                             vp, vp, vp, vp]
     L.nvfp4_quantize_mse.restype = i32
     L.nvfp4_quantize_mse.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, vp]
     L.nvfp4_quantize_2d.restype = i32
@@ -158,27 +165,41 @@ def nvfp4_status_string(status):
 
 
 def nvfp4_quantize_1d(x, axis, rounding, rng, rht_sign_mask, amax, amax_is_input, codes, scales,
-                      global_dec, stream=None):
-    rows, cols = x.shape
+                      global_dec, stream=None, row_index=None):
+    """row_index (device int64): quantize the rows x[row_index] (indices
+    outside [0, len(x)) give zero rows) through nvfp4_quantize_1d_gather."""
+    src_rows, cols = x.shape
     ph = None if rng is None else C.byref(_Philox(rng.seed, rng.offset, rng.rounds, 0))
-    st = load().nvfp4_quantize_1d(_p(x), _dtype_code(x), rows, cols, int(axis), int(rounding), ph,
-                                  int(rht_sign_mask), _p(amax), int(bool(amax_is_input)),
-                                  _p(codes), _p(scales), _p(global_dec), _stream(stream))
-    _check("nvfp4_quantize_1d", st)
+    if row_index is None:
+        st = load().nvfp4_quantize_1d(_p(x), _dtype_code(x), src_rows, cols, int(axis),
+                                      int(rounding), ph, int(rht_sign_mask), _p(amax),
+                                      int(bool(amax_is_input)), _p(codes), _p(scales),
+                                      _p(global_dec), _stream(stream))
+        _check("nvfp4_quantize_1d", st)
+        return
+    st = load().nvfp4_quantize_1d_gather(_p(x), _dtype_code(x), src_rows, _p(row_index),
+                                         row_index.numel(), cols, int(axis), int(rounding), ph,
+                                         int(rht_sign_mask), _p(amax), int(bool(amax_is_input)),
+                                         _p(codes), _p(scales), _p(global_dec), _stream(stream))
+    _check("nvfp4_quantize_1d_gather", st)
 
 
 def nvfp4_quantize_dual(x, rng_row, rng_col, rht_sign_mask, amax, amax_is_input, row_codes,
                         row_scales, row_global_dec, col_codes, col_scales, col_global_dec,
-                        zero_codes, stream=None):
-    rows, cols = x.shape
+                        zero_codes, stream=None, row_index=None):
+    src_rows, cols = x.shape
     pr = C.byref(_Philox(rng_row.seed, rng_row.offset, rng_row.rounds, 0))
     pc = C.byref(_Philox(rng_col.seed, rng_col.offset, rng_col.rounds, 0))
-    st = load().nvfp4_quantize_dual(_p(x), _dtype_code(x), rows, cols, pr, pc, int(rht_sign_mask),
-                                    _p(amax), int(bool(amax_is_input)), _p(row_codes),
-                                    _p(row_scales), _p(row_global_dec), _p(col_codes),
-                                    _p(col_scales), _p(col_global_dec), _p(zero_codes),
-                                    _stream(stream))
-    _check("nvfp4_quantize_dual", st)
+    tail = (int(rht_sign_mask), _p(amax), int(bool(amax_is_input)), _p(row_codes),
+            _p(row_scales), _p(row_global_dec), _p(col_codes), _p(col_scales),
+            _p(col_global_dec), _p(zero_codes), _stream(stream))
+    if row_index is None:
+        st = load().nvfp4_quantize_dual(_p(x), _dtype_code(x), src_rows, cols, pr, pc, *tail)
+        _check("nvfp4_quantize_dual", st)
+        return
+    st = load().nvfp4_quantize_dual_gather(_p(x), _dtype_code(x), src_rows, _p(row_index),
+                                           row_index.numel(), cols, pr, pc, *tail)
+    _check("nvfp4_quantize_dual_gather", st)
 
 
 def nvfp4_quantize_mse(w, amax, amax_is_input, codes, scales, global_dec, stream=None):
@@ -264,8 +285,12 @@ def _scale_shape(block, rows, cols):
 
 
 def quantize_1d(x, axis="row", rounding="rne", rng: Optional[Philox] = None, rht_sign_mask=-1,
-                amax=None, stream=None):
+                amax=None, stream=None, row_index=None):
+    """row_index: quantize x[row_index] (out-of-range indices: zero rows)
+    without materializing the gathered rows."""
     rows, cols = x.shape
+    if row_index is not None:
+        rows = row_index.numel()
     dev = x.device
     codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty(_scale_shape(axis, rows, cols), dtype=torch.uint8, device=dev)
@@ -274,15 +299,19 @@ def quantize_1d(x, axis="row", rounding="rne", rng: Optional[Philox] = None, rht
     a = (amax.reshape(1).to(torch.float32).clone() if given
          else torch.empty(1, dtype=torch.float32, device=dev))
     rnd = NVFP4_SR if rounding == "sr" else NVFP4_RNE
-    nvfp4_quantize_1d(x, _BLOCKS[axis], rnd, rng, rht_sign_mask, a, given, codes, scales, g, stream)
+    nvfp4_quantize_1d(x, _BLOCKS[axis], rnd, rng, rht_sign_mask, a, given, codes, scales, g, stream,
+                      row_index)
     return QTensor(codes, scales, g, a, rows, cols, axis)
 
 
 def quantize_dual(x, rng_row: Philox, rng_col: Philox, rht_sign_mask=-1, amax=None,
-                  count_zeros=True, stream=None):
-    """ROW (dgrad) and COL (wgrad) quantization of one gradient from one read.
-    Returns (row QTensor, col QTensor, zero-code counts int64[2] or None)."""
+                  count_zeros=True, stream=None, row_index=None):
+    """ROW (dgrad) and COL (wgrad) quantization of one gradient from one read
+    (of x[row_index] when given).  Returns (row QTensor, col QTensor,
+    zero-code counts int64[2] or None)."""
     rows, cols = x.shape
+    if row_index is not None:
+        rows = row_index.numel()
     dev = x.device
     rc = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
     rs = torch.empty(_scale_shape("row", rows, cols), dtype=torch.uint8, device=dev)
@@ -294,7 +323,7 @@ def quantize_dual(x, rng_row: Philox, rng_col: Philox, rht_sign_mask=-1, amax=No
          else torch.empty(2, dtype=torch.float32, device=dev))
     z = torch.empty(2, dtype=torch.int64, device=dev) if count_zeros else None
     nvfp4_quantize_dual(x, rng_row, rng_col, rht_sign_mask, a, given, rc, rs, g[0:1], cc, cs,
-                        g[1:2], z, stream)
+                        g[1:2], z, stream, row_index)
     return (QTensor(rc, rs, g[0:1], a[0:1], rows, cols, "row"),
             QTensor(cc, cs, g[1:2], a[1:2], rows, cols, "col"), z)
 

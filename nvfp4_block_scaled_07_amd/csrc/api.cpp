@@ -110,10 +110,25 @@ const char* nvfp4_status_string(int32_t s) {
   }
 }
 
-int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
-                          int32_t axis, int32_t rounding, const nvfp4_philox* rng,
-                          int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
-                          uint8_t* codes, uint8_t* scales, float* global_dec, void* stream) {
+namespace {
+
+// Gathering (row_index != null): row r of the quantized tensor is row
+// row_index[r] of x's src_rows rows.  The flat chunk index of a ROW kernel is
+// split into (row, chunk) with 32-bit arithmetic, hence rows * cols / 8 < 2^32.
+int32_t gather_check(const void* x, int64_t src_rows, const int64_t* row_index, int64_t rows,
+                     int64_t cols) {
+  if (src_rows < 1) return NVFP4_ERR_SHAPE;
+  if (rows * (cols / 8) >= (int64_t(1) << 32)) return NVFP4_ERR_SHAPE;
+  if (rows > 0 && cols > 0 && (!row_index || !x)) return NVFP4_ERR_NULL;
+  if (!aligned(row_index, 8)) return NVFP4_ERR_ALIGN;
+  return NVFP4_OK;
+}
+
+int32_t quantize_1d(const void* x, int32_t x_dtype, const int64_t* row_index, int64_t src_rows,
+                    int64_t rows, int64_t cols, int32_t axis, int32_t rounding,
+                    const nvfp4_philox* rng, int32_t rht_sign_mask, float* amax,
+                    int32_t amax_is_input, uint8_t* codes, uint8_t* scales, float* global_dec,
+                    void* stream) {
   if (!valid_dtype(x_dtype)) return NVFP4_ERR_UNSUPPORTED;
   if (axis != NVFP4_BLOCK_ROW && axis != NVFP4_BLOCK_COL) return NVFP4_ERR_LAYOUT;
   if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_UNSUPPORTED;
@@ -146,15 +161,42 @@ int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t 
   a.codes = codes;
   a.scales = scales;
   a.gdec = global_dec;
+  a.ridx = row_index;
+  a.src_rows = src_rows;
   return device_status(nvfp4::launch_quantize_1d(a, static_cast<hipStream_t>(stream)));
 }
 
-int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
-                            const nvfp4_philox* rng_row, const nvfp4_philox* rng_col,
-                            int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
-                            uint8_t* row_codes, uint8_t* row_scales, float* row_global_dec,
-                            uint8_t* col_codes, uint8_t* col_scales, float* col_global_dec,
-                            uint64_t* zero_codes, void* stream) {
+}  // namespace
+
+int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                          int32_t axis, int32_t rounding, const nvfp4_philox* rng,
+                          int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                          uint8_t* codes, uint8_t* scales, float* global_dec, void* stream) {
+  return quantize_1d(x, x_dtype, nullptr, 0, rows, cols, axis, rounding, rng, rht_sign_mask, amax,
+                     amax_is_input, codes, scales, global_dec, stream);
+}
+
+int32_t nvfp4_quantize_1d_gather(const void* x, int32_t x_dtype, int64_t src_rows,
+                                 const int64_t* row_index, int64_t rows, int64_t cols,
+                                 int32_t axis, int32_t rounding, const nvfp4_philox* rng,
+                                 int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                                 uint8_t* codes, uint8_t* scales, float* global_dec,
+                                 void* stream) {
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  const int32_t g = gather_check(x, src_rows, row_index, rows, cols);
+  if (g != NVFP4_OK) return g;
+  return quantize_1d(x, x_dtype, row_index, src_rows, rows, cols, axis, rounding, rng,
+                     rht_sign_mask, amax, amax_is_input, codes, scales, global_dec, stream);
+}
+
+namespace {
+
+int32_t quantize_dual(const void* x, int32_t x_dtype, const int64_t* row_index, int64_t src_rows,
+                      int64_t rows, int64_t cols, const nvfp4_philox* rng_row,
+                      const nvfp4_philox* rng_col, int32_t rht_sign_mask, float* amax,
+                      int32_t amax_is_input, uint8_t* row_codes, uint8_t* row_scales,
+                      float* row_global_dec, uint8_t* col_codes, uint8_t* col_scales,
+                      float* col_global_dec, uint64_t* zero_codes, void* stream) {
   if (!valid_dtype(x_dtype)) return NVFP4_ERR_UNSUPPORTED;
   if (rht_sign_mask < -1 || rht_sign_mask > 0xFFFF) return NVFP4_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 32 != 0) return NVFP4_ERR_SHAPE;
@@ -191,7 +233,38 @@ int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_
   a.col_scales = col_scales;
   a.col_gdec = col_global_dec;
   a.zeros = reinterpret_cast<unsigned long long*>(zero_codes);
+  a.ridx = row_index;
+  a.src_rows = src_rows;
   return device_status(nvfp4::launch_quantize_dual(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int32_t nvfp4_quantize_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                            const nvfp4_philox* rng_row, const nvfp4_philox* rng_col,
+                            int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                            uint8_t* row_codes, uint8_t* row_scales, float* row_global_dec,
+                            uint8_t* col_codes, uint8_t* col_scales, float* col_global_dec,
+                            uint64_t* zero_codes, void* stream) {
+  return quantize_dual(x, x_dtype, nullptr, 0, rows, cols, rng_row, rng_col, rht_sign_mask, amax,
+                       amax_is_input, row_codes, row_scales, row_global_dec, col_codes,
+                       col_scales, col_global_dec, zero_codes, stream);
+}
+
+int32_t nvfp4_quantize_dual_gather(const void* x, int32_t x_dtype, int64_t src_rows,
+                                   const int64_t* row_index, int64_t rows, int64_t cols,
+                                   const nvfp4_philox* rng_row, const nvfp4_philox* rng_col,
+                                   int32_t rht_sign_mask, float* amax, int32_t amax_is_input,
+                                   uint8_t* row_codes, uint8_t* row_scales,
+                                   float* row_global_dec, uint8_t* col_codes,
+                                   uint8_t* col_scales, float* col_global_dec,
+                                   uint64_t* zero_codes, void* stream) {
+  if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+  const int32_t g = gather_check(x, src_rows, row_index, rows, cols);
+  if (g != NVFP4_OK) return g;
+  return quantize_dual(x, x_dtype, row_index, src_rows, rows, cols, rng_row, rng_col,
+                       rht_sign_mask, amax, amax_is_input, row_codes, row_scales, row_global_dec,
+                       col_codes, col_scales, col_global_dec, zero_codes, stream);
 }
 
 int32_t nvfp4_quantize_mse(const void* w, int32_t w_dtype, int64_t rows, int64_t cols,

@@ -25,6 +25,8 @@ struct QuantArgs {
   uint8_t* codes;
   uint8_t* scales;
   float* gdec;
+  const int64_t* ridx;  // null, or row r of the input is row ridx[r] of x (MoE gather)
+  int64_t src_rows;     // rows of x when gathering; other indices read as zero rows
 };
 
 // Both 1D quantizations of one gradient tensor from one read: ROW blocks with
@@ -46,6 +48,8 @@ struct QuantDualArgs {
   uint8_t *col_codes, *col_scales;
   float* col_gdec;
   unsigned long long* zeros;  // [2] or null
+  const int64_t* ridx;        // as QuantArgs
+  int64_t src_rows;
 };
 
 struct Quant2dArgs {

@@ -186,12 +186,55 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
 // contiguous across the wave) before reducing them.
 constexpr int kAmaxUnroll = 4;
 
+// ---- input rows, optionally gathered (the MoE dispatch) ---------------------------------------
+// Row r of the tensor being quantized is row r of x or, gathering, row idx[r]
+// of x (src_rows rows); an index outside [0, src_rows) reads as a row of
+// zeros, which is how per-expert padding rows are expressed.
+template <bool kGather>
+struct RowSrc {
+  const int64_t* idx = nullptr;
+  int64_t src_rows = 0;
+  // Source row of row r, or -1 for a row of zeros.
+  __device__ __forceinline__ int64_t at(int64_t r) const {
+    if constexpr (!kGather) {
+      return r;
+    } else {
+      const int64_t s = idx[r];
+      return s >= 0 && s < src_rows ? s : -1;
+    }
+  }
+  // Element offset of flat chunk i (8 elements, cpr chunks per row) and
+  // whether it is read (false: zeros).  Gathering needs i < 2^32.
+  __device__ __forceinline__ int64_t chunk(int64_t i, uint32_t cpr, bool& ok) const {
+    if constexpr (!kGather) {
+      ok = true;
+      return i * 8;
+    } else {
+      const uint32_t r = (uint32_t)i / cpr, c = (uint32_t)i - r * cpr;
+      const int64_t sr = at(r);
+      ok = sr >= 0;
+      return ((ok ? sr : 0) * cpr + c) * 8;
+    }
+  }
+};
+
+// p always points at readable data (a zero row reads source row 0, which
+// exists: src_rows >= 1), so the load needs no branch; !ok selects zeros.
+template <typename T>
+__device__ __forceinline__ void load8_or_zero(const T* p, bool ok, float v[8]) {
+  In<T>::load8(p, v);
+#pragma unroll
+  for (int t = 0; t < 8; t++) v[t] = ok ? v[t] : 0.0f;
+}
+
 // amax2 (nullable): a second target that receives the same maximum.
-template <typename T, bool kRHT>
+template <typename T, bool kRHT, bool kGather = false>
 __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __restrict__ x,
                                                                  int64_t chunks, uint32_t mask,
                                                                  float* __restrict__ amax,
-                                                                 float* __restrict__ amax2) {
+                                                                 float* __restrict__ amax2,
+                                                                 RowSrc<kGather> rs = {},
+                                                                 uint32_t cpr = 1) {
   const T* xs = x + (int64_t)blockIdx.y * chunks * 8;
   float m = 0.0f;
   constexpr int U = (In<T>::kBf16 && !kRHT) ? kAmaxUnroll : 2;
@@ -203,7 +246,10 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
 #pragma unroll
       for (int u = 0; u < U; u++) {
         int64_t i = base + (int64_t)u * NT;
-        q[u] = i < chunks ? *reinterpret_cast<const uint4*>(xs + i * 8) : make_uint4(0, 0, 0, 0);
+        bool ok;
+        const int64_t off = rs.chunk(i < chunks ? i : 0, cpr, ok);
+        q[u] = i < chunks ? *reinterpret_cast<const uint4*>(xs + off) : make_uint4(0, 0, 0, 0);
+        if (!ok) q[u] = make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < U; u++) m = fmaxf(m, max8_bf16_bits(q[u]));
@@ -214,7 +260,9 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
         int64_t i = base + (int64_t)u * NT;
         // Past the end: zeros (a duplicated chunk would not change a plain
         // max, but its transform, paired with its partner, could).
-        In<T>::load8(xs + (i < chunks ? i : chunks - 1) * 8, v[u]);
+        bool ok;
+        const int64_t off = rs.chunk(i < chunks ? i : chunks - 1, cpr, ok);
+        load8_or_zero(xs + off, ok, v[u]);
         if (i >= chunks)
 #pragma unroll
           for (int q = 0; q < 8; q++) v[u][q] = 0.0f;
@@ -237,12 +285,13 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
 // 256-thread workgroups: each lane holds a 16 x 8 tile and its transform,
 // too many registers for the large amax workgroups.  kPlain: also the max of
 // |x| itself (into amax_plain), from the same loads.
-template <typename T, bool kPlain>
+template <typename T, bool kPlain, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restrict__ x,
                                                                 int64_t rows, int64_t cols,
                                                                 uint32_t mask,
                                                                 float* __restrict__ amax,
-                                                                float* __restrict__ amax_plain) {
+                                                                float* __restrict__ amax_plain,
+                                                                RowSrc<kGather> rs = {}) {
   const int64_t cg = cols / 8;
   const int64_t units = (rows / 16) * cg;
   float m = 0.0f, mp = 0.0f;
@@ -251,7 +300,10 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
     int64_t g = u / cg, c0 = (u % cg) * 8;
     float v[16][8];
 #pragma unroll
-    for (int r = 0; r < 16; r++) In<T>::load8(x + (g * 16 + r) * cols + c0, v[r]);
+    for (int r = 0; r < 16; r++) {
+      const int64_t sr = rs.at(g * 16 + r);
+      load8_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0, v[r]);
+    }
     if (kPlain)
 #pragma unroll
       for (int r = 0; r < 16; r++) mp = fmaxf(mp, max8(v[r]));
@@ -276,11 +328,12 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
 // its Philox counter is 2 * block + (i & 1) = i.
 constexpr int kRowUnroll = 4;
 
-template <typename T, bool kSR, bool kRHT>
+template <typename T, bool kSR, bool kRHT, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(
     const T* __restrict__ x, int64_t chunks, const float* __restrict__ amax,
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
-    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
+    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds, RowSrc<kGather> rs = {},
+    uint32_t cpr = 1) {
   __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
@@ -292,7 +345,9 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
   for (int u = 0; u < kRowUnroll; u++) {
     int64_t i = base + (int64_t)u * kThreads;
     int64_t ic = i < chunks ? i : chunks - 1;  // chunks is even: pairs agree
-    In<T>::load8(x + ic * 8, v[u]);
+    bool ok;
+    const int64_t off = rs.chunk(ic, cpr, ok);
+    load8_or_zero(x + off, ok, v[u]);
   }
   build_recip_table(rtab, ts.S);
 #pragma unroll
@@ -341,11 +396,11 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallUnroll = 8;         // chunks in flight per thread
 constexpr int64_t kSmallChunks = kSmallThreads * kSmallUnroll;  // 8-element chunks (64 Ki elements)
 
-template <typename T, bool kSR>
+template <typename T, bool kSR, bool kGather = false>
 __global__ __launch_bounds__(kSmallThreads) void quant_row_small_kernel(
     const T* __restrict__ x, int64_t chunks, float* __restrict__ amax, bool amax_is_input,
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
-    uint64_t seed, uint64_t offset, uint32_t rounds) {
+    uint64_t seed, uint64_t offset, uint32_t rounds, RowSrc<kGather> rs = {}, uint32_t cpr = 1) {
   __shared__ float rtab[128];
   __shared__ float red[kSmallThreads / 64];
   const int tid = threadIdx.x;
@@ -358,8 +413,10 @@ __global__ __launch_bounds__(kSmallThreads) void quant_row_small_kernel(
 #pragma unroll
     for (int u = 0; u < kSmallUnroll; u++) {  // all loads first (past the end: zeros)
       const int64_t i = tid + (int64_t)u * kSmallThreads;
+      bool ok = false;
+      const int64_t off = i < chunks ? rs.chunk(i, cpr, ok) : 0;
       if (i < chunks) {
-        In<T>::load8(x + i * 8, v[u]);
+        load8_or_zero(x + off, ok, v[u]);
       } else {
 #pragma unroll
         for (int t = 0; t < 8; t++) v[u][t] = 0.0f;
@@ -385,7 +442,11 @@ __global__ __launch_bounds__(kSmallThreads) void quant_row_small_kernel(
 #pragma unroll
   for (int u = 0; u < kSmallUnroll; u++) {
     const int64_t i = tid + (int64_t)u * kSmallThreads;
-    if (i < chunks) In<T>::load8(x + i * 8, v[u]);
+    if (i < chunks) {
+      bool ok;
+      const int64_t off = rs.chunk(i, cpr, ok);
+      load8_or_zero(x + off, ok, v[u]);
+    }
   }
 #pragma unroll
   for (int u = 0; u < kSmallUnroll; u++) {
@@ -520,6 +581,11 @@ template <>
 struct RawRow<uint16_t> {  // 8 bf16 = 4 words; column pair p is word p
   uint4 q;
   __device__ __forceinline__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_or_zero(const uint16_t* p, bool ok) {  // p readable
+    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+    q = make_uint4(t.x & m, t.y & m, t.z & m, t.w & m);
+  }
   __device__ __forceinline__ void pair(int p, float& a, float& b) const {
     const uint32_t w = p == 0 ? q.x : p == 1 ? q.y : p == 2 ? q.z : q.w;
     a = __uint_as_float(w << 16);
@@ -537,6 +603,12 @@ struct RawRow<float> {  // named words (no array, so selects stay in registers)
   __device__ __forceinline__ void load(const float* p) {
     lo = reinterpret_cast<const uint4*>(p)[0];
     hi = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_or_zero(const float* p, bool ok) {  // p readable
+    load(p);
+    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+    lo = make_uint4(lo.x & m, lo.y & m, lo.z & m, lo.w & m);
+    hi = make_uint4(hi.x & m, hi.y & m, hi.z & m, hi.w & m);
   }
   __device__ __forceinline__ void pair(int p, float& a, float& b) const {
     const uint32_t wa = p == 0 ? lo.x : p == 1 ? lo.z : p == 2 ? hi.x : hi.z;
@@ -598,11 +670,11 @@ __device__ __forceinline__ void col_encode(const RawRow<T> (&raw)[16], int64_t r
   }
 }
 
-template <typename T, bool kSR, bool kRHT>
+template <typename T, bool kSR, bool kRHT, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
-    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds) {
+    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds, RowSrc<kGather> rs = {}) {
   __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
@@ -613,7 +685,10 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
   const int64_t g = uc / cg, c0 = (uc % cg) * 8;
   RawRow<T> raw[16];
 #pragma unroll
-  for (int r = 0; r < 16; r++) raw[r].load(x + (g * 16 + r) * cols + c0);
+  for (int r = 0; r < 16; r++) {
+    const int64_t sr = rs.at(g * 16 + r);
+    raw[r].load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
+  }
   build_recip_table(rtab, ts.S);
   if (u >= units) return;
   uint32_t out[16], sc[2];
@@ -645,14 +720,14 @@ __device__ __forceinline__ uint32_t zero_nibbles(uint32_t w) {
 // zeros (nullable): the zero-magnitude codes of each output, summed per
 // workgroup and added with one atomic each (an atomic per wave on the same
 // two addresses serializes in L2 and doubled the kernel's time).
-template <typename T, bool kRHT>
+template <typename T, bool kRHT, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
     uint32_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
     float* __restrict__ row_gdec, uint8_t* __restrict__ col_codes,
     uint8_t* __restrict__ col_scales, float* __restrict__ col_gdec, uint32_t mask,
     uint64_t seed_r, uint64_t offset_r, uint32_t rounds_r, uint64_t seed_c, uint64_t offset_c,
-    uint32_t rounds_c, unsigned long long* __restrict__ zeros) {
+    uint32_t rounds_c, unsigned long long* __restrict__ zeros, RowSrc<kGather> rs = {}) {
   __shared__ float rtab_r[128], rtab_c[128];
   const TensorScales tr = tensor_scales(amax[0]), tc = tensor_scales(amax[1]);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -667,7 +742,10 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
   const int64_t g = uc / cg, c0 = (uc % cg) * 8;
   RawRow<T> raw[16];
 #pragma unroll
-  for (int r = 0; r < 16; r++) raw[r].load(x + (g * 16 + r) * cols + c0);
+  for (int r = 0; r < 16; r++) {
+    const int64_t sr = rs.at(g * 16 + r);
+    raw[r].load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
+  }
   for (int e = threadIdx.x; e < 128; e += blockDim.x) {
     const float d = e4m3_decode((uint32_t)e);
     rtab_r[e] = block_recip(tr.S, d);
@@ -694,7 +772,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
 #pragma unroll 1
   for (int r = 0; r < 16; r++) {
     RawRow<T> rr;  // this row's segment again (just loaded: a cache hit)
-    rr.load(x + (g * 16 + r) * cols + c0);
+    const int64_t sr = rs.at(g * 16 + r);
+    rr.load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
     float v[8];
     rr.all(v);
     const float m = max8(v);
@@ -856,48 +935,55 @@ int amax_grid(int64_t units, int unroll, int64_t cap = 512) {
   return (int)(g < cap ? (g > 0 ? g : 1) : cap);
 }
 
-template <typename T>
+template <typename T, bool G>
 hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
+  RowSrc<G> rs;
+  if constexpr (G) {
+    rs.idx = a.ridx;
+    rs.src_rows = a.src_rows;
+  }
+  const uint32_t cpr = (uint32_t)(a.cols / 8);
   if (a.axis == kBlockRow && !a.rht && a.rows * a.cols / 8 <= kSmallChunks) {
     const int64_t chunks = a.rows * a.cols / 8;
     uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
     if (a.sr)
-      quant_row_small_kernel<T, true><<<1, kSmallThreads, 0, st>>>(
-          x, chunks, a.amax, a.amax_is_input, cd, a.scales, a.gdec, a.seed, a.offset, a.rounds);
+      quant_row_small_kernel<T, true, G><<<1, kSmallThreads, 0, st>>>(
+          x, chunks, a.amax, a.amax_is_input, cd, a.scales, a.gdec, a.seed, a.offset, a.rounds,
+          rs, cpr);
     else
-      quant_row_small_kernel<T, false><<<1, kSmallThreads, 0, st>>>(
-          x, chunks, a.amax, a.amax_is_input, cd, a.scales, a.gdec, 0, 0, 0);
+      quant_row_small_kernel<T, false, G><<<1, kSmallThreads, 0, st>>>(
+          x, chunks, a.amax, a.amax_is_input, cd, a.scales, a.gdec, 0, 0, 0, rs, cpr);
     return hipGetLastError();
   }
   if (!a.amax_is_input) {
     fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 1);
     if (a.axis == kBlockCol && a.rht) {
       int64_t units = (a.rows / 16) * (a.cols / 8);
-      amax_col_rht_kernel<T, false><<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024),
-                                      kThreads, 0, st>>>(x, a.rows, a.cols, a.mask, a.amax,
-                                                         nullptr);
+      amax_col_rht_kernel<T, false, G>
+          <<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads, 0, st>>>(
+              x, a.rows, a.cols, a.mask, a.amax, nullptr, rs);
     } else {
       int64_t chunks = a.rows * a.cols / 8;
       // ROW with the transform needs the pair exchange; COL amax without the
       // transform is the plain max.
       const int u = (!a.x_fp32 && !(a.rht && a.axis == kBlockRow)) ? kAmaxUnroll : 2;
       if (a.rht && a.axis == kBlockRow)
-        amax_flat_kernel<T, true><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-            x, chunks, a.mask, a.amax, nullptr);
+        amax_flat_kernel<T, true, G><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
+            x, chunks, a.mask, a.amax, nullptr, rs, cpr);
       else
-        amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-            x, chunks, 0, a.amax, nullptr);
+        amax_flat_kernel<T, false, G><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
+            x, chunks, 0, a.amax, nullptr, rs, cpr);
     }
   }
   if (a.axis == kBlockRow) {
     int64_t chunks = a.rows * a.cols / 8;
     int grid = (int)cdiv(chunks, (int64_t)kThreads * kRowUnroll);
     uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
-#define NVFP4_ROW(SR, RHT)                                                                   \
-  quant_row_kernel<T, SR, RHT><<<grid, kThreads, 0, st>>>(x, chunks, a.amax, cd, a.scales,   \
-                                                          a.gdec, a.mask, a.seed, a.offset, \
-                                                          a.rounds)
+#define NVFP4_ROW(SR, RHT)                                                                     \
+  quant_row_kernel<T, SR, RHT, G><<<grid, kThreads, 0, st>>>(x, chunks, a.amax, cd, a.scales, \
+                                                             a.gdec, a.mask, a.seed, a.offset, \
+                                                             a.rounds, rs, cpr)
     if (a.sr && a.rht) NVFP4_ROW(true, true);
     else if (a.sr) NVFP4_ROW(true, false);
     else if (a.rht) NVFP4_ROW(false, true);
@@ -906,10 +992,10 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
   } else {
     int64_t units = (a.rows / 16) * (a.cols / 8);
     int grid = (int)cdiv(units, kThreads);
-#define NVFP4_COL(SR, RHT)                                                                     \
-  quant_col_kernel<T, SR, RHT><<<grid, kThreads, 0, st>>>(x, a.rows, a.cols, a.amax, a.codes, \
-                                                          a.scales, a.gdec, a.mask, a.seed,   \
-                                                          a.offset, a.rounds)
+#define NVFP4_COL(SR, RHT)                                                                        \
+  quant_col_kernel<T, SR, RHT, G><<<grid, kThreads, 0, st>>>(x, a.rows, a.cols, a.amax, a.codes, \
+                                                             a.scales, a.gdec, a.mask, a.seed,   \
+                                                             a.offset, a.rounds, rs)
     if (a.sr && a.rht) NVFP4_COL(true, true);
     else if (a.sr) NVFP4_COL(true, false);
     else if (a.rht) NVFP4_COL(false, true);
@@ -953,31 +1039,36 @@ hipError_t launch_rht16_t(const void* xv, int64_t rows, int64_t cols, int axis, 
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool G>
 hipError_t launch_quantize_dual_t(const QuantDualArgs& a, hipStream_t st) {
   const T* x = static_cast<const T*>(a.x);
+  RowSrc<G> rs;
+  if constexpr (G) {
+    rs.idx = a.ridx;
+    rs.src_rows = a.src_rows;
+  }
   const int64_t units = (a.rows / 16) * (a.cols / 8);
   if (!a.amax_is_input) {
     fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 2);
     if (a.rht) {  // transform max for COL, plain max for ROW, one read
-      amax_col_rht_kernel<T, true><<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024),
-                                     kThreads, 0, st>>>(x, a.rows, a.cols, a.mask, a.amax + 1,
-                                                        a.amax);
+      amax_col_rht_kernel<T, true, G>
+          <<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads, 0, st>>>(
+              x, a.rows, a.cols, a.mask, a.amax + 1, a.amax, rs);
     } else {  // the same plain max for both
       const int64_t chunks = a.rows * a.cols / 8;
       const int u = a.x_fp32 ? 2 : kAmaxUnroll;
-      amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-          x, chunks, 0, a.amax, a.amax + 1);
+      amax_flat_kernel<T, false, G><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
+          x, chunks, 0, a.amax, a.amax + 1, rs, (uint32_t)(a.cols / 8));
     }
   }
   if (a.zeros) fill_zero_kernel<<<1, 64, 0, st>>>(reinterpret_cast<float*>(a.zeros), 4);
   const int grid = (int)cdiv(units, kThreads);
   uint32_t* rc = reinterpret_cast<uint32_t*>(a.row_codes);
 #define NVFP4_DUAL(RHT)                                                                       \
-  quant_dual_kernel<T, RHT><<<grid, kThreads, 0, st>>>(                                       \
+  quant_dual_kernel<T, RHT, G><<<grid, kThreads, 0, st>>>(                                    \
       x, a.rows, a.cols, a.amax, rc, a.row_scales, a.row_gdec, a.col_codes, a.col_scales,     \
       a.col_gdec, a.mask, a.seed_r, a.offset_r, a.rounds_r, a.seed_c, a.offset_c, a.rounds_c, \
-      a.zeros)
+      a.zeros, rs)
   if (a.rht) NVFP4_DUAL(true);
   else NVFP4_DUAL(false);
 #undef NVFP4_DUAL
@@ -1015,11 +1106,19 @@ hipError_t launch_quantize_mse(const void* x, bool x_fp32, int64_t rows, int64_t
 }
 
 hipError_t launch_quantize_dual(const QuantDualArgs& a, hipStream_t st) {
-  return a.x_fp32 ? launch_quantize_dual_t<float>(a, st) : launch_quantize_dual_t<uint16_t>(a, st);
+  if (a.ridx)
+    return a.x_fp32 ? launch_quantize_dual_t<float, true>(a, st)
+                    : launch_quantize_dual_t<uint16_t, true>(a, st);
+  return a.x_fp32 ? launch_quantize_dual_t<float, false>(a, st)
+                  : launch_quantize_dual_t<uint16_t, false>(a, st);
 }
 
 hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st) {
-  return a.x_fp32 ? launch_quantize_1d_t<float>(a, st) : launch_quantize_1d_t<uint16_t>(a, st);
+  if (a.ridx)
+    return a.x_fp32 ? launch_quantize_1d_t<float, true>(a, st)
+                    : launch_quantize_1d_t<uint16_t, true>(a, st);
+  return a.x_fp32 ? launch_quantize_1d_t<float, false>(a, st)
+                  : launch_quantize_1d_t<uint16_t, false>(a, st);
 }
 
 hipError_t launch_quantize_2d(const Quant2dArgs& a, hipStream_t st) {

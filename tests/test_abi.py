@@ -99,6 +99,36 @@ def test_quantize_dual_validation(lib):
     assert f(P, 7, 64, 128, r, r, -1, P, 0, P, P, P, P, P, P, None, None) == -5  # dtype
 
 
+def test_quantize_gather_validation(lib):
+    """The gathering quantizers: the plain calls' checks plus src_rows >= 1,
+    a row index for a non-empty G (8-byte aligned) and rows * cols / 8 <
+    2^32."""
+    q, d = lib.nvfp4_quantize_1d_gather, lib.nvfp4_quantize_dual_gather
+
+    def q1(src_rows=10, idx=FAKE, rows=32, cols=64, axis=0):
+        return q(FAKE, 0, src_rows, idx, rows, cols, axis, 0, None, -1, FAKE, 0, FAKE, FAKE,
+                 FAKE, None)
+
+    assert q1(src_rows=0) == -2
+    assert q1(idx=None) == -1
+    assert q1(idx=C.c_void_p(0x100004)) == -3
+    assert q1(rows=1 << 26, cols=1 << 10) == -2        # rows * cols / 8 = 2^33
+    assert q1(cols=48) == -2                           # cols % 32
+    assert q1(rows=40, axis=1) == -2                   # COL: rows % 16
+    assert q1(rows=0, idx=None) == 0                   # empty G: no-op
+    from nvfp4_block_scaled_07_amd._binding import _Philox
+    r = _Philox(1, 0, 5, 0)
+
+    def q2(src_rows=10, idx=FAKE, rows=32, cols=64):
+        return d(FAKE, 0, src_rows, idx, rows, cols, C.byref(r), C.byref(r), -1, FAKE, 0, FAKE,
+                 FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+
+    assert q2(src_rows=0) == -2
+    assert q2(idx=None) == -1
+    assert q2(rows=40) == -2                           # rows % 16
+    assert q2(rows=0, idx=None) == 0
+
+
 def test_gemm_validation(lib):
     from nvfp4_block_scaled_07_amd._binding import _Operand
     A = _Operand(0x100000, 0x200000, 0x300000, 64, 128, 0, 0)
