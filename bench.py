@@ -589,8 +589,8 @@ def main():
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; the hot path has no "
-                                   "multi-GPU mode (see DESIGN.md for how it would shard)",
+        print(json.dumps({"error": "libnvfp4 runs on one GPU: the hot path has no "
+                                   "multi-GPU mode, so only --gpus 1 is measured",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

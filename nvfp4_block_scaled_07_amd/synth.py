@@ -82,7 +82,7 @@ def max_vio(counts, topk):
     return float(counts.max() / counts.mean())
 
 
-# Workload definitions (seeds and distributions as stated in the design doc).
+# Workload definitions: shapes, seeds and value distributions of each workload.
 WORKLOADS = {
     "tiny": dict(x=(256, 512), a=(256, 256), b=(256, 256)),
     "fprop_super": dict(M=8192, N=6144, K=6144, x_std=1.0, w_std=0.02,
