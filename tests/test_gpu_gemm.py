@@ -256,3 +256,37 @@ def test_gemm_accumulate_into_fp32(layout, M, N, K):
     A, B = to_np(qa), to_np(qb)
     R, D = O.gemm_full(layout[0], layout[1], M, N, K, A, B)
     assert O.gemm_rel_err(p.cpu().numpy(), R, D) <= TOL
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 256, 1 << 17), (300, 256, 1 << 16)])
+def test_gemm_long_k(M, N, K):
+    """Long contractions (small-M and tiled kernels): 2^16 and 2^17 k, far
+    past one tile's buffer range, sampled against the oracle."""
+    dev = device()
+    a = make_input("normal", (M, K), 61)
+    b = (make_input("normal", (N, K), 62) * np.float32(0.02)).astype(np.float32)
+    qa = nv.quantize_1d(device_input(a, "bf16", dev)[0], "row")
+    qb = nv.quantize_2d(device_input(b, "bf16", dev)[0])
+    c = nv.gemm("N", "T", qa, qb, out_dtype=torch.float32)
+    _sampled_check("NT", qa, qb, M, N, K, c, n_random=512)
+
+
+@pytest.mark.parametrize("M", [1, 33, 130])
+def test_gemm_widest_n(M):
+    """N = 2^21 - 32, the widest output the ABI accepts (31-bit store offsets
+    within a tile, 65535 small-M workgroups), sampled against the oracle
+    including the last columns."""
+    dev = device()
+    N, K = (1 << 21) - 32, 64
+    a = make_input("normal", (M, K), 63)
+    qa = nv.quantize_1d(device_input(a, "fp32", dev)[0], "row")
+    qb = nv.quantize_1d(synth.normal_device((N, K), 0.02, 64, dev, dtype=torch.float32), "row")
+    c = nv.gemm("N", "T", qa, qb, out_dtype=torch.bfloat16)
+    c32 = nv.gemm("N", "T", qa, qb, out_dtype=torch.float32)
+    check_bf16_is_rne_of_fp32(c, c32)
+    rng = np.random.default_rng(M)
+    ii = np.concatenate([rng.integers(0, M, 2048), np.full(64, M - 1)])
+    jj = np.concatenate([rng.integers(0, N, 2048), np.arange(N - 64, N)])
+    R, D = O.gemm_entries("N", "T", M, N, K, to_np(qa), to_np(qb), ii, jj)
+    err = O.gemm_rel_err(c32[ii, jj].cpu().numpy(), R, D)
+    assert err <= TOL, f"sampled max |C-R|/D = {err:.3e}"
