@@ -287,10 +287,11 @@ int32_t nvfp4_dequantize(const nvfp4_operand* q, float* y, void* stream);
  * or 2D operand has rows % 16 == 0; N % 8 == 0 and N < 2^21 (else
  * NVFP4_ERR_SHAPE).  M == 0 or N == 0 is a no-op.  Alignment: codes 16
  * bytes, scales 4, C 16 bytes.
- * NT with M <= 64 (decode-like shapes) runs a split-K kernel: K is divided
- * among the waves of a workgroup and their partial sums are added in a fixed
- * order, so C is deterministic but rounds differently from the product of a
- * larger M (within the same error bound).
+ * NT with M <= 64 (decode-like shapes), or M <= 512 when 256 x 256 tiles
+ * would leave CUs idle, runs a split-K kernel: K is divided among the waves
+ * of a workgroup and their partial sums are added in a fixed order, so C is
+ * deterministic but rounds differently from the tiled kernel's product
+ * (within the same error bound).
  */
 int32_t nvfp4_gemm(char opA, char opB, int64_t M, int64_t N, int64_t K, const nvfp4_operand* A,
                    const nvfp4_operand* B, void* C, int32_t c_dtype, void* stream);

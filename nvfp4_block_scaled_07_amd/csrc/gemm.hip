@@ -1034,7 +1034,7 @@ __global__ __launch_bounds__(C::NT) void grouped_wgrad_kernel(WgradArgs a) {
   }
 }
 
-// ---- small M (decode-like shapes): NT with M <= 64 ---------------------------------------------
+// ---- small M (decode-like shapes): NT with M <= 64 per row block ----------------------------------
 // With a few rows of activations the weight codes dominate the traffic and a
 // 256-row tile would leave most of the chip idle (N / 256 workgroups).  A
 // workgroup here takes 32 columns of C (all M <= 64 rows of A) with NWV
@@ -1148,7 +1148,10 @@ __global__ __launch_bounds__(NWV * 64) void gemm_skinny_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int64_t M = a.M, N = a.N, K = a.K, kc = K / 2, ks = K / 16;
+  // Row block blockIdx.y: rows m0 .. m0 + 63 of A and C (all row blocks of
+  // a column tile read the same weight columns, which the caches share).
+  const int64_t m0 = (int64_t)blockIdx.y * 64;
+  const int64_t M = a.M - m0 < 64 ? a.M - m0 : 64, N = a.N, K = a.K, kc = K / 2, ks = K / 16;
   const int64_t n0 = (int64_t)blockIdx.x * 32;
   const int64_t G = K / 64, CN = (K + kSkChunkK - 1) / kSkChunkK;
   const int64_t c0 = wave * CN / NWV, c1 = (wave + 1) * CN / NWV;
@@ -1182,10 +1185,11 @@ __global__ __launch_bounds__(NWV * 64) void gemm_skinny_kernel(GemmArgs a) {
                                               (int)(nlim * kc), kBufferFlags);
   src.bsr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.B.scales + bsbase), 0,
                                               (int)(b_end - bsbase), kBufferFlags);
-  src.acr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.A.codes), 0,
+  src.acr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.A.codes + m0 * kc), 0,
                                               (int)(M * kc), kBufferFlags);
   src.asr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.A.scales), 0, (int)(a2d ? ((M + 15) / 16) * ks : M * ks),
+      const_cast<uint8_t*>(a.A.scales + (a2d ? m0 / 16 : m0) * ks), 0,
+      (int)(a2d ? ((M + 15) / 16) * ks : M * ks),
       kBufferFlags);
 
   // LDS rows this lane reads: B row lrow, A row min(32 s + lrow, M - 1).
@@ -1308,9 +1312,9 @@ __global__ __launch_bounds__(NWV * 64) void gemm_skinny_kernel(GemmArgs a) {
         const float o = v * gscale;
         if (a.c_bf16) {
           const __bf16 b = (__bf16)o;
-          static_cast<uint16_t*>(a.C)[row * N + col] = __builtin_bit_cast(uint16_t, b);
+          static_cast<uint16_t*>(a.C)[(m0 + row) * N + col] = __builtin_bit_cast(uint16_t, b);
         } else {
-          float* c = static_cast<float*>(a.C) + row * N + col;
+          float* c = static_cast<float*>(a.C) + (m0 + row) * N + col;
           *c = a.c_acc ? *c + o : o;
         }
       }
@@ -1321,10 +1325,12 @@ __global__ __launch_bounds__(NWV * 64) void gemm_skinny_kernel(GemmArgs a) {
 template <int NA8, int NWV, int NB>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
   const int64_t grid = (a.N + 31) / 32;
-  gemm_skinny_kernel<NA8, NWV, NB><<<(unsigned)grid, NWV * 64, 0, st>>>(a);
+  const dim3 g3((unsigned)grid, (unsigned)((a.M + 63) / 64));  // column tiles x 64-row blocks
+  gemm_skinny_kernel<NA8, NWV, NB><<<g3, NWV * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
+// Rows beyond 64 run as row blocks of 64 (blockIdx.y).
 hipError_t launch_small_m(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 8) return launch_skinny<1, 8, 2>(a, st);
   if (a.M <= 16) return launch_skinny<2, 8, 2>(a, st);
@@ -1388,13 +1394,20 @@ hipError_t launch_grouped(const GroupedArgs& a, int cus, hipStream_t st) {
 // rate per output, so take the one whose last round of workgroups leaves
 // the fewest CUs idle (cost = rounds of tiles times tile area).  Every output
 // is the same sum in the same order whatever the choice.
+//
+// NT with few rows takes the small-M kernel: always up to 64 rows, and up to
+// 512 when 256 x 256 tiles would leave CUs without a tile (at N = K = 6144:
+// 27 us instead of 105 us at M = 128, 74 us instead of 106 us at M = 512; the
+// two meet near M = 768).
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (a.a_kmajor && a.b_kmajor && a.M <= 64)  // decode-like NT: small-M kernel
-    return launch_small_m(a, st);
+  const bool nt = a.a_kmajor && a.b_kmajor;
+  if (nt && a.M <= 64) return launch_small_m(a, st);
   int cus = 256;
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
+  if (nt && a.M <= 512 && ((a.M + 255) / 256) * ((a.N + 255) / 256) < cus)
+    return launch_small_m(a, st);
   if (a.K % 128 == 0) return launch_depth<128>(a, cus, st);
   return launch_depth<64>(a, cus, st);
 }

@@ -58,6 +58,37 @@ def test_small_m_k_splits(K):
     _check(qa, qb, M, N, K, nv.gemm("N", "T", qa, qb, out_dtype=torch.float32))
 
 
+@pytest.mark.parametrize("M", [65, 100, 128, 200, 300, 512])
+@pytest.mark.parametrize("b_block", ["row", "2d"])
+def test_small_m_row_blocks(M, b_block):
+    """Beyond 64 rows (with few 256 x 256 tiles) the small-M kernel takes row
+    blocks of 64: ragged last blocks, both weight block kinds, bf16 output
+    the RNE of the fp32 one."""
+    N, K = 160, 384
+    dev = device()
+    a = make_input("normal", (M, K), 70 + M)
+    b = (make_input("normal", (N, K), 71 + M) * np.float32(0.02)).astype(np.float32)
+    qa = nv.quantize_1d(device_input(a, "bf16", dev)[0], "row")
+    tb = device_input(b, "bf16", dev)[0]
+    qb = nv.quantize_2d(tb) if b_block == "2d" else nv.quantize_1d(tb, "row")
+    c = nv.gemm("N", "T", qa, qb, out_dtype=torch.float32)
+    _check(qa, qb, M, N, K, c)
+    _bf16_is_rne(nv.gemm("N", "T", qa, qb, out_dtype=torch.bfloat16), c)
+    c0 = torch.ones_like(c)
+    nv.gemm("N", "T", qa, qb, out=c0, accumulate=True)
+    assert torch.equal(c0.view(torch.int32), (torch.ones_like(c) + c).view(torch.int32))
+
+
+def test_small_m_row_blocks_2d_activations():
+    M, N, K = 208, 96, 256
+    dev = device()
+    a = make_input("normal", (M, K), 9)
+    b = (make_input("normal", (N, K), 10) * np.float32(0.02)).astype(np.float32)
+    qa = nv.quantize_2d(device_input(a, "fp32", dev)[0])
+    qb = nv.quantize_1d(device_input(b, "fp32", dev)[0], "row")
+    _check(qa, qb, M, N, K, nv.gemm("N", "T", qa, qb, out_dtype=torch.float32))
+
+
 def test_small_m_2d_activation_operand():
     """A 16x16-block A operand (rows % 16 == 0) on the small-M path."""
     M, N, K = 48, 160, 256
@@ -92,8 +123,8 @@ def test_small_m_exact_special_case():
 
 def test_small_m_deterministic_and_matches_tiled_within_bound():
     """Repeated calls give the same bits; rows computed by the small-M kernel
-    agree with the same rows of a 256-row product (tiled kernel) to the bar."""
-    M, N, K = 256, 512, 2048
+    agree with the same rows of a 1024-row product (tiled kernel) to the bar."""
+    M, N, K = 1024, 512, 2048
     dev = device()
     a = make_input("normal", (M, K), 12)
     b = (make_input("normal", (N, K), 13) * np.float32(0.02)).astype(np.float32)

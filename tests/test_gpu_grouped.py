@@ -77,17 +77,17 @@ def test_grouped_small_ragged(b_block, out):
 
 
 def test_grouped_matches_dense_per_group():
-    """Groups of more than 64 rows give exactly the dense GEMM's bits (the same
-    sum in the same order); a dense call with at most 64 rows takes the
-    split-K small-M kernel, which rounds differently, so those groups are
-    held to the oracle bar instead."""
-    counts = [40, 0, 260, 7, 90]
+    """Groups of more than 512 rows give exactly the dense GEMM's bits (the
+    same sum in the same order); a dense NT call with fewer rows (and few
+    tiles) takes the split-K small-M kernel, which rounds differently, so
+    those groups are held to the oracle bar instead."""
+    counts = [40, 0, 600, 7, 90]
     N, K = 272, 192
     qa, qb, off, c = _grouped_case(counts, N, K, seed=9, out=torch.float32)
     for e, n in enumerate(counts):
         if n == 0:
             continue
-        if n <= 64:
+        if n <= 512:
             _check_group(qa, qb, off, c, e, N, K)
             continue
         r0 = int(off[e])
@@ -99,18 +99,18 @@ def test_grouped_matches_dense_per_group():
         assert torch.equal(d, c[r0:r0 + n])
 
 
-@pytest.mark.parametrize("counts,K", [([40, 0, 260, 7, 100], 192),  # few rows per group: 128-row tiles
+@pytest.mark.parametrize("counts,K", [([40, 0, 600, 7, 100], 192),  # few rows per group: 128-row tiles
                                       ([600, 1100, 0, 700], 256)])  # many: 256-row tiles
 def test_grouped_tile_shapes_match_dense(counts, K):
-    """Both grouped tile shapes give each group of more than 64 rows exactly
-    the dense GEMM's bits (smaller dense calls take the small-M kernel)."""
+    """Both grouped tile shapes give each group of more than 512 rows exactly
+    the dense GEMM's bits (smaller dense NT calls take the small-M kernel)."""
     N = 272
     qa, qb, off, c = _grouped_case(counts, N, K, seed=11, out=torch.float32)
     for e, n in enumerate(counts):
         if n == 0:
             continue
         _check_group(qa, qb, off, c, e, N, K)
-        if n <= 64:
+        if n <= 512:
             continue
         r0 = int(off[e])
         sub = nv.QTensor(qa.codes[r0:r0 + n], qa.scales[r0:r0 + n], qa.global_dec, qa.amax, n, K,
