@@ -1369,7 +1369,12 @@ hipError_t launch_depth(const GemmArgs& a, int cus, hipStream_t st) {
     const int64_t tiles = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
     return ((tiles + cus - 1) / cus) * bm * bn;
   };
-  if (cost(192, 256) < cost(256, 256)) return launch_layout<Cfg<192, 256, 2, 4, BK>>(a, st);
+  const int64_t c256 = cost(256, 256), c192 = cost(192, 256);
+  if (a.a_kmajor && cost(128, 256) * 5 < (c192 < c256 ? c192 : c256) * 4) {
+    if (a.b_kmajor) return launch_dense<Cfg<128, 256, 1, 8, BK>, true, true>(a, st);
+    return launch_dense<Cfg<128, 256, 1, 8, BK>, true, false>(a, st);
+  }
+  if (c192 < c256) return launch_layout<Cfg<192, 256, 2, 4, BK>>(a, st);
   return launch_layout<Cfg<256, 256, 2, 4, BK>>(a, st);
 }
 
@@ -1390,10 +1395,14 @@ hipError_t launch_grouped(const GroupedArgs& a, int cus, hipStream_t st) {
 }  // namespace
 
 // Stage depth: 128 k when K allows (longer row segments per transfer and
-// half the barriers), else 64.  Tile: both tile shapes run at about the same
-// rate per output, so take the one whose last round of workgroups leaves
-// the fewest CUs idle (cost = rounds of tiles times tile area).  Every output
-// is the same sum in the same order whatever the choice.
+// half the barriers), else 64.  Tile: the 256- and 192-row shapes run at
+// about the same rate per output, so take the one whose last round of
+// workgroups leaves the fewest CUs idle (cost = rounds of tiles times tile
+// area).  With A K-major (NT, NN) a 128-row tile also competes, at a 5/4
+// cost for its lower rate per output: it wins where bigger tiles leave CUs
+// idle (N = K = 6144: 81 us instead of 108 us at M = 640 .. 1024) and ties
+// from M = 1536 on.  Every output is the same sum in the same order whatever
+// the choice.
 //
 // NT with few rows takes the small-M kernel: always up to 64 rows, and up to
 // 512 when 256 x 256 tiles would leave CUs without a tile (at N = K = 6144:

@@ -194,15 +194,18 @@ def test_gemm_large_tiles_full(layout):
 
 @pytest.mark.parametrize("layout", ["NT", "NN"])
 def test_gemm_tile_shape_does_not_change_bits(layout):
-    """C for A's first 768 rows (192-row tiles) equals those rows of the
-    4096 x 4096 product (256-row tiles) bit for bit: each output is the same
-    sum in the same order whatever the tile shape."""
+    """C for A's first 768 rows (128-row tiles on 256 CUs) and first 3072
+    rows (192-row tiles) equals those rows of the 4096 x 4096 product
+    (256-row tiles) bit for bit: each output is the same sum in the same
+    order whatever the tile shape."""
     M, N, K = 4096, 4096, 256
     qa, qb = _operands(layout, M, N, K, seed=23, sr=layout != "NT")
     full = nv.gemm(layout[0], layout[1], qa, qb, out_dtype=torch.float32)
-    sub = nv.QTensor(qa.codes[:768], qa.scales[:768], qa.global_dec, qa.amax, 768, K, "row")
-    part = nv.gemm(layout[0], layout[1], sub, qb, out_dtype=torch.float32)
-    assert torch.equal(part, full[:768])
+    for rows in (768, 3072):
+        sub = nv.QTensor(qa.codes[:rows], qa.scales[:rows], qa.global_dec, qa.amax, rows, K,
+                         "row")
+        part = nv.gemm(layout[0], layout[1], sub, qb, out_dtype=torch.float32)
+        assert torch.equal(part, full[:rows]), rows
 
 
 def test_full_ultra_wgrad():
