@@ -7,9 +7,10 @@ One step = the fprop of one Super-width linear layer from bf16 inputs:
   Y = X W^T with the NVFP4 GEMM (NT), bf16 out.
 Inputs are resident in HBM before timing starts; four input sets rotate so
 that the 256 MB Infinity Cache cannot serve a step's inputs from the step
-before.  Every kernel launch in the timed region is bracketed by HIP events on
-the stream the library launches on (torch's current stream), which gives the
-per-kernel averages used for the roofline fractions.
+before.  In the timed region one HIP event is recorded before every library
+call, on the stream the library launches on (torch's current stream); a
+call's time runs to the next event, which gives the per-kernel averages used
+for the roofline fractions.
 
 `--rows` adds further rows of the hot path (wgrad with RHT + stochastic
 rounding, routed-expert grouped GEMM, Ultra-width fprop/dgrad, the SSM-state
