@@ -16,6 +16,8 @@ for the roofline fractions.
 rounding, routed-expert grouped GEMM, Ultra-width fprop/dgrad, the SSM-state
 fp16 rounding, the post-training-quantized decode path), each timed the same
 way (the decode path from HIP graph replays) and reported under "rows".
+Without --rows the Ultra-width fprop/dgrad row is reported.  "context" holds
+hipBLASLt's plain bf16/fp16 GEMM rate at the fprop shape (not a target).
 
 Prints one JSON line.
 """
@@ -175,57 +177,75 @@ def gemm_traffic():
 
 
 # ---- CPU baseline: the oracle on a bounded sample of the same step ---------------------------
-def cpu_baseline(torch, synth, xs, ws, M, N, K, budget_s=(3.0, 3.0, 12.0)):
-    """Times the oracle on growing slices of the fprop step until each part
-    has run for about its share of `budget_s` seconds, then scales each part
-    to the full step."""
+def cpu_baseline(torch, synth, xs, ws, M, N, K, q_rows=1024, g_rows=64):
+    """The oracle on fixed slices of the fprop step: ROW quantization of
+    q_rows rows of X and 16x16 quantization of q_rows rows of W (one core
+    each, amax given: those blocks only see their own rows), and the fp64
+    GEMM reference of g_rows full rows of Y (g_rows x N outputs over all of K,
+    OpenMP over all host cores).  Each part is timed and scaled to the full
+    step by its share of rows."""
     import numpy as np
 
     import oracle as O
     threads = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    xb_all = synth.bf16_bits(xs[0].cpu())
+    xb = synth.bf16_bits(xs[0][:q_rows].cpu())
     wb_all = synth.bf16_bits(ws[0].cpu())
     amax_x = float(xs[0].float().abs().max())
     amax_w = float(ws[0].float().abs().max())
 
-    def run_chunks(fn, total, chunk, budget):
-        done, spent = 0, 0.0
-        while done < total and spent < budget:
-            hi = min(done + chunk, total)
-            t0 = time.perf_counter()
-            fn(done, hi)
-            spent += time.perf_counter() - t0
-            done = hi
-        return done, spent
-
-    # ROW and 16x16 blocks only see their own rows once the amax is given.
-    rows_x, t_qx = run_chunks(lambda a, b: O.quantize(xb_all[a:b], "row", amax=amax_x), M, 256,
-                              budget_s[0])
-    rows_w, t_qw = run_chunks(lambda a, b: O.quantize(wb_all[a:b], "2d", amax=amax_w), N, 256,
-                              budget_s[1])
-    qa = O.quantize(xb_all[:256], "row", amax=amax_x)
-    qw_full = O.quantize(wb_all, "2d", amax=amax_w)
+    t0 = time.perf_counter()
+    qa = O.quantize(xb, "row", amax=amax_x)
+    t_qx = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.quantize(wb_all[:q_rows], "2d", amax=amax_w)
+    t_qw = time.perf_counter() - t0
+    qw_full = O.quantize(wb_all, "2d", amax=amax_w)  # the GEMM's B (not timed)
     A = dict(codes=qa["codes"], scales=qa["scales"], block="row", g=qa["g"])
     B = dict(codes=qw_full["codes"], scales=qw_full["scales"], block="2d", g=qw_full["g"])
-
-    def gemm_rows(a, b):
-        ii = np.repeat(np.arange(a, b) % 256, N)
-        jj = np.tile(np.arange(N), b - a)
-        O.gemm_entries("N", "T", 256, N, K, A, B, ii, jj)
-
-    rows_g, t_g = run_chunks(gemm_rows, M, 8, budget_s[2])
-    est = t_qx * (M / rows_x) + t_qw * (N / rows_w) + t_g * (M / rows_g)
+    ii = np.repeat(np.arange(g_rows), N)
+    jj = np.tile(np.arange(N), g_rows)
+    t0 = time.perf_counter()
+    O.gemm_entries("N", "T", q_rows, N, K, A, B, ii, jj)
+    t_g = time.perf_counter() - t0
+    est = t_qx * (M / q_rows) + t_qw * (N / q_rows) + t_g * (M / g_rows)
     flops = 2.0 * M * N * K
     return {
         "value": round(flops / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle quantize of {rows_x} of {M} rows of X and {rows_w} of {N} rows of W "
-                   f"(1 core each), fp64 GEMM reference of {rows_g} of {M} rows of Y "
-                   f"({threads} OpenMP threads); each part scaled to the full step"),
+        "sample": (f"oracle ROW quantize of {q_rows} of {M} rows of X and 16x16 quantize of "
+                   f"{q_rows} of {N} rows of W (1 core each), fp64 GEMM reference of {g_rows} "
+                   f"full rows of Y ({g_rows} x {N} outputs, K = {K}; {threads} OpenMP "
+                   f"threads); each part scaled to the full step by rows"),
         "est_step_s": round(est, 2),
         "sample_seconds": round(t_qx + t_qw + t_g, 2),
+        "parts_s": {"quantize_x": round(t_qx, 3), "quantize_w": round(t_qw, 3),
+                    "gemm_rows": round(t_g, 3)},
     }
+
+
+def hipblaslt_context(torch, dev, M, N, K, reps=20):
+    """Context only: torch.matmul (hipBLASLt) bf16 and fp16 at the same shape
+    (plain GEMMs, no decode), TFLOP/s."""
+    out = {}
+    for name, dt in (("bf16", torch.bfloat16), ("fp16", torch.float16)):
+        a = torch.randn((M, K), device=dev, dtype=dt)
+        b = torch.randn((N, K), device=dev, dtype=dt)
+        c = torch.empty((M, N), device=dev, dtype=dt)
+        for _ in range(3):
+            torch.matmul(a, b.t(), out=c)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b.t(), out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"hipblaslt_{name}_tflops"] = round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    return out
 
 
 # ---- further rows ------------------------------------------------------------------------------
@@ -597,6 +617,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,ssm_sr,ptq_decode,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the hipBLASLt context GEMMs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -654,6 +676,8 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
     extra = [r.strip() for r in args.rows.split(",") if r.strip()]
+    if not args.rows:  # the default run also reports the Ultra-width GEMMs
+        extra = ["ultra"]
     if "all" in extra:
         extra = ["wgrad", "dy_dual", "grouped", "grouped_bwd", "ultra", "grouped_ultra", "ssm_sr",
                  "ptq_decode"]
@@ -682,11 +706,22 @@ def main():
         torch.cuda.empty_cache()
     if rows:
         out["rows"] = rows
+    if not args.no_context:
+        log("context: hipBLASLt plain GEMMs at the fprop shape")
+        out["context"] = hipblaslt_context(torch, dev, M, N, K)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")
         xs1 = [synth.normal_device((M, K), 1.0, 1, dev)]
         ws1 = [synth.normal_device((N, K), 0.02, 2, dev)]
         out["cpu_baseline"] = cpu_baseline(torch, synth, xs1, ws1, M, N, K)
+        del xs1, ws1
+    # Leave nothing queued or allocated on the device before the interpreter
+    # exits (the exit handlers of the HIP runtime, of libnvfp4's code-object
+    # registration and of a profiler's tool then find an idle device).
+    del qx, qw, y, timer
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

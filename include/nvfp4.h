@@ -105,8 +105,9 @@ typedef struct {
 /* A quantized operand: device pointers to its codes, its scale bytes and its
  * fp32 decode scale g, with the stored shape [rows x cols] and block kind.
  * As a GEMM operand (kernels address it with 32-bit offsets): cols < 2^24
- * when K is its contiguous dimension, rows * cols < 2^32 when K is its row
- * dimension (else NVFP4_ERR_SHAPE). */
+ * when K is its contiguous dimension (any number of rows: each tile's loads
+ * cover at most 256 rows), rows * cols < 2^32 when K is its row dimension
+ * (else NVFP4_ERR_SHAPE). */
 typedef struct {
   const uint8_t* codes;
   const uint8_t* scales;
@@ -219,12 +220,13 @@ int32_t nvfp4_quantize_dual_gather(const void* x, int32_t x_dtype, int64_t src_r
  * to minimize the weight's MSE rather than from the block max; activations
  * keep the dynamic max-based nvfp4_quantize_1d).  ROW blocks (1x16 along
  * cols, i.e. along K of a weight stored [N x K]), RNE elements, per-tensor
- * scales as nvfp4_quantize_1d.  Per block, the candidate E4M3 codes are the
- * max-based one e0, then e0 + 1, e0 - 1, ..., e0 - 15 (within 0 .. 126); each
- * encodes the block as nvfp4_quantize_1d would with that scale, and its error
- * is the fp64 sum of (x - dequantized x)^2, as (elements 0..7) + (8..15), each
- * sum in index order; a candidate replaces the choice only if strictly
- * better.  The result is a ROW operand for nvfp4_gemm (e.g. B of an NT GEMM).
+ * scales as nvfp4_quantize_1d.  Each block's E4M3 scale is the one, of all
+ * 127 finite codes, whose encoding of the block (as nvfp4_quantize_1d would
+ * encode it with that scale) has the smallest error, the fp64 sum in index
+ * order of (x - dequantized x)^2; on a tie the max-based code is kept if it
+ * is a minimum, else the smallest code wins.  The search runs on the
+ * device, offline (once per weight).
+ * The result is a ROW operand for nvfp4_gemm (e.g. B of an NT GEMM).
  *   w [rows x cols] NVFP4_BF16 or NVFP4_FP32; amax as nvfp4_quantize_1d;
  *   codes [rows x cols/2], scales [rows x cols/16], global_dec out.
  * Shapes: cols % 32 == 0; rows == 0 is a no-op.  Alignment as

@@ -154,9 +154,12 @@ struct DmaK {
       const int64_t mn = mn0 + row < mn_lim ? mn0 + row : mn_lim - 1;
       coff[q] = (uint32_t)((mn - mn0) * kc + 16 * unit);
     }
+    // The buffer ranges cover the tile's own rows (at most ROWS of them), so
+    // they fit 31 bits whatever the operand's size (K < 2^24).
+    const int64_t rows_t = mn_lim - mn0 < ROWS ? mn_lim - mn0 : ROWS;
     const bool two_d = op.block == kBlock2d;
     const int64_t sbase = two_d ? (mn0 / 16) * ks : mn0 * ks;
-    const int64_t slim = two_d ? ((mn_lim + 15) / 16) * ks : mn_lim * ks;
+    const int64_t slim = two_d ? ((mn0 + rows_t + 15) / 16) * ks : (mn0 + rows_t) * ks;
 #pragma unroll
     for (int q = 0; q < Plan::SPW; q++) {
       // Row SB bytes = SB/4 lanes of 4 bytes (the stage's k-blocks).
@@ -167,7 +170,7 @@ struct DmaK {
       soff[q] = (uint32_t)((two_d ? (mn / 16) * ks : mn * ks) - sbase + 4 * part);
     }
     crsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.codes + mn0 * kc), 0,
-                                              (int)((mn_lim - mn0) * kc), kBufferFlags);
+                                              (int)(rows_t * kc), kBufferFlags);
     srsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.scales + sbase), 0,
                                               (int)(slim - sbase), kBufferFlags);
   }

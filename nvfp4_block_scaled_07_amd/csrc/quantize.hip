@@ -473,49 +473,42 @@ __global__ __launch_bounds__(kSmallThreads) void quant_row_small_kernel(
 }
 
 // ---- PTQ weights: ROW blocks with MSE-calibrated scales ----------------------------------------
-// As the ROW quantizer (lane: 8 elements, lanes 2t and 2t+1: one block), but
-// each block's E4M3 scale is the candidate with the smallest squared error
-// of the dequantized block: the max-based code e0 first, then e0 + 1, e0 - 1,
-// ..., e0 - 15 (within 0 .. 126), a candidate winning only when strictly
-// better.  A lane sums its 8 squared errors in fp64 in index order; the pair
-// adds its two halves (even lane's first), so both lanes hold the same error
-// and make the same choice.  xh = RN32(RN32(val(code) d) g), the value the
-// dequantizer gives.  The pair's two lanes agree on every branch here (the
-// candidate list depends only on e0, the pair's), so the exchanges always
-// find their partner active.
-__device__ __forceinline__ double xor1_d(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, 0xB1, 0xF, 0xF, true);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), 0xB1, 0xF, 0xF, true);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
+// One lane per 16-element block.  Each block's E4M3 scale is the code, of all
+// 127 finite ones, whose encoding of the block has the smallest squared
+// error: the max-based code e0 is tried first, then codes 0 .. 126 in order,
+// each replacing the choice only when strictly better (so a tie keeps e0 if
+// it is a minimum, else the smallest code).  A code e encodes the block as
+// the ROW quantizer would with that scale (r from the reciprocal table,
+// y = RN32(x r), hardware RNE), decodes it as the dequantizer does
+// (v_cvt_scalef32_pk_f16_fp4, exact, then RN32(RN32(val d) g)), and sums the
+// 16 terms (x - xh)^2 in fp64 in index order.  Offline work (once per
+// weight), so the 127 candidates are all evaluated.
 
-// Squared error (this lane's 8 elements) of the block quantized with scale
-// code e; packed receives the 8 codes.
-__device__ __forceinline__ double mse_half(const float v[8], uint32_t e, const float* rtab,
-                                           float g, uint32_t& packed) {
+// Squared error of the block v encoded with scale code e; packed receives
+// its 16 codes (element 2j in the low nibble of byte j).
+__device__ __forceinline__ double mse_block(const float v[16], const double vd[16], uint32_t e,
+                                            const float* rtab, float g, uint2& packed) {
   const float d = e4m3_decode(e);
   const float r = rtab[e];
-  float y[8];
+  float y[16];
 #pragma unroll
-  for (int t = 0; t < 8; t++) y[t] = v[t] * r;
-  packed = pack8_rne(y);
+  for (int t = 0; t < 16; t++) y[t] = v[t] * r;
+  packed.x = pack8_rne(y);
+  packed.y = pack8_rne(y + 8);
   double acc = 0.0;
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    // codes 2q, 2q+1 (byte q) -> exact E2M1 values, by the fp16 conversion
-    // (the one the GEMM decode uses), then exactly to fp32
+  for (int q = 0; q < 8; q++) {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t w = q < 4 ? packed.x : packed.y;
     f16x2 h2;
-    switch (q) {
-      case 0: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 0); break;
-      case 1: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 1); break;
-      case 2: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2); break;
-      default: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 3); break;
+    switch (q & 3) {
+      case 0: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0); break;
+      case 1: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1); break;
+      case 2: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2); break;
+      default: h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3); break;
     }
-    const float val[2] = {(float)h2[0], (float)h2[1]};
-    const float xh0 = (val[0] * d) * g, xh1 = (val[1] * d) * g;
-    const double e0 = (double)v[2 * q] - (double)xh0, e1 = (double)v[2 * q + 1] - (double)xh1;
+    const float xh0 = ((float)h2[0] * d) * g, xh1 = ((float)h2[1] * d) * g;
+    const double e0 = vd[2 * q] - (double)xh0, e1 = vd[2 * q + 1] - (double)xh1;
     acc = acc + e0 * e0;
     acc = acc + e1 * e1;
   }
@@ -524,48 +517,37 @@ __device__ __forceinline__ double mse_half(const float v[8], uint32_t e, const f
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void quant_mse_row_kernel(
-    const T* __restrict__ x, int64_t chunks, const float* __restrict__ amax,
-    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec) {
+    const T* __restrict__ x, int64_t blocks, const float* __restrict__ amax,
+    uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec) {
   __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
-  const int64_t base = (int64_t)blockIdx.x * kThreads * 4 + threadIdx.x;
-  float v[4][8];
-#pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const int64_t i = base + (int64_t)u * kThreads;
-    In<T>::load8(x + (i < chunks ? i : chunks - 1) * 8, v[u]);  // chunks is even: pairs agree
-  }
+  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t bc = b < blocks ? b : blocks - 1;
+  float v[16];
+  In<T>::load8(x + bc * 16, v);
+  In<T>::load8(x + bc * 16 + 8, v + 8);
   build_recip_table(rtab, ts.S);
+  if (b >= blocks) return;
+  double vd[16];
+#pragma unroll
+  for (int t = 0; t < 16; t++) vd[t] = (double)v[t];
+  const uint32_t e0 = block_code(fmaxf(max8(v), max8(v + 8)), ts.k);
+  uint2 best_q, q;
+  double best_err = mse_block(v, vd, e0, rtab, ts.g, best_q);
+  uint32_t best = e0;
 #pragma unroll 1
-  for (int u = 0; u < 4; u++) {
-    const int64_t i = base + (int64_t)u * kThreads;
-    const float m = max8(v[u]);
-    const int e0 = (int)block_code(fmaxf(m, xor1(m)), ts.k);
-    uint32_t best_q, q;
-    double h = mse_half(v[u], (uint32_t)e0, rtab, ts.g, best_q);
-    const bool odd = i & 1;
-    // The pair's total: both lanes exchange halves outside any branch (a lane
-    // shut off by a branch would be read as 0) and add them; the addition is
-    // commutative, so both lanes get half0 + half1 exactly.
-    double best_err = h + xor1_d(h);
-    int best = e0;
-#pragma unroll 1
-    for (int t = 1; t <= 16; t++) {
-      const int e = t == 1 ? e0 + 1 : e0 - (t - 1);
-      if (e < 0 || e > 126) continue;  // the pair agrees (e0 is the pair's)
-      h = mse_half(v[u], (uint32_t)e, rtab, ts.g, q);
-      const double err = h + xor1_d(h);
-      if (err < best_err) {
-        best_err = err;
-        best = e;
-        best_q = q;
-      }
+  for (uint32_t e = 0; e <= 126; e++) {
+    if (e == e0) continue;
+    const double err = mse_block(v, vd, e, rtab, ts.g, q);
+    if (err < best_err) {
+      best_err = err;
+      best = e;
+      best_q = q;
     }
-    if (i >= chunks) continue;
-    codes[i] = best_q;
-    if (!odd) scales[i >> 1] = (uint8_t)best;
   }
+  codes[b] = best_q;
+  scales[b] = (uint8_t)best;
 }
 
 // ---- COL quantizer (lane: 8 cols x 16 rows = 8 blocks) ---------------------------------------
@@ -1087,9 +1069,10 @@ hipError_t launch_quantize_mse_t(const void* xv, int64_t rows, int64_t cols, boo
     amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
         x, chunks, 0, amax, nullptr);
   }
-  const int grid = (int)cdiv(chunks, (int64_t)kThreads * 4);
-  quant_mse_row_kernel<T><<<grid, kThreads, 0, st>>>(x, chunks, amax,
-                                                     reinterpret_cast<uint32_t*>(codes), scales,
+  const int64_t blocks = rows * cols / 16;
+  const int grid = (int)cdiv(blocks, (int64_t)kThreads);
+  quant_mse_row_kernel<T><<<grid, kThreads, 0, st>>>(x, blocks, amax,
+                                                     reinterpret_cast<uint2*>(codes), scales,
                                                      gdec);
   return hipGetLastError();
 }

@@ -42,6 +42,10 @@ def lib():
         L.oracle_e4m3_decode.argtypes = [u8]
         L.oracle_e4m3_encode_rne_sat.restype = u8
         L.oracle_e4m3_encode_rne_sat.argtypes = [C.c_float]
+        L.oracle_e2m1_encode_rne_n.restype = None
+        L.oracle_e2m1_encode_rne_n.argtypes = [vp, i64, vp]
+        L.oracle_e4m3_encode_rne_sat_n.restype = None
+        L.oracle_e4m3_encode_rne_sat_n.argtypes = [vp, i64, vp]
         L.oracle_philox4x32.restype = None
         L.oracle_philox4x32.argtypes = [vp, vp, u32, vp]
         L.oracle_sr_bits.restype = u32
@@ -110,6 +114,23 @@ def e4m3_decode(e):
 
 def e4m3_encode(s):
     return lib().oracle_e4m3_encode_rne_sat(float(s))
+
+
+def e2m1_encode_rne_array(y):
+    """oracle_e2m1_encode_rne on every element of a float32 array (uint8
+    codes: sign bit 8, magnitude index 0..7)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().oracle_e2m1_encode_rne_n(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_array(s):
+    """oracle_e4m3_encode_rne_sat on every element of a float32 array."""
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    out = np.empty(s.shape, dtype=np.uint8)
+    lib().oracle_e4m3_encode_rne_sat_n(_ptr(s), s.size, _ptr(out))
+    return out
 
 
 def philox4x32(ctr, key, rounds):

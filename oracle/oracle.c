@@ -118,6 +118,19 @@ uint8_t oracle_e4m3_encode_rne_sat(float s) {
   return (uint8_t)best;
 }
 
+/* The two encoders above applied to arrays (threads split the elements;
+ * each element is the scalar encoder's result). */
+void oracle_e2m1_encode_rne_n(const float* y, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_e2m1_encode_rne(y[i]);
+}
+
+void oracle_e4m3_encode_rne_sat_n(const float* s, int64_t n, uint8_t* out) {
+  (void)e4m3_values(); /* fill the value table before the threads */
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3_encode_rne_sat(s[i]);
+}
+
 /* ========================================================================
  * Philox4x32-R (Salmon, Moraes, Dror, Shaw: "Parallel random numbers: as
  * easy as 1, 2, 3", SC 2011).  The pages use Philox with five rounds for
@@ -580,6 +593,11 @@ void oracle_sr_fp16(const float* x, int64_t n, uint64_t seed, uint64_t offset,
 /* ========================================================================
  * PTQ: MSE-calibrated block scales (ROW blocks, RNE)
  * ======================================================================== */
+/* Squared error of block xb encoded with scale code e, as the max-based
+ * quantizer would encode it with that scale: r = RN32(S / val(e)) (0 for a
+ * zero scale), y = RN32(x r), RNE code, then the dequantized value
+ * xh = RN32(RN32(val(code) val(e)) g).  The 16 terms (x - xh)^2 are summed
+ * in fp64 in index order, one running sum. */
 static double mse_candidate(const float* xb, uint8_t e, float S, float g, uint8_t* q) {
   const float d = oracle_e4m3_decode(e);
   float rb = 0.0f;
@@ -587,14 +605,14 @@ static double mse_candidate(const float* xb, uint8_t e, float S, float g, uint8_
     rb = S / d;
     if (isinf(rb)) rb = FLT_MAX;
   }
-  double half[2] = {0.0, 0.0};
+  double sum = 0.0;
   for (int i = 0; i < 16; i++) {
     q[i] = oracle_e2m1_encode_rne(xb[i] * rb);
     const float xh = (oracle_e2m1_decode(q[i]) * d) * g;
     const double err = (double)xb[i] - (double)xh;
-    half[i >> 3] += err * err;
+    sum += err * err;
   }
-  return half[0] + half[1];
+  return sum;
 }
 
 int oracle_quantize_mse(const void* x, int x_is_bf16, int64_t rows, int64_t cols,
@@ -614,6 +632,9 @@ int oracle_quantize_mse(const void* x, int x_is_bf16, int64_t rows, int64_t cols
   oracle_global_scales(A, &S, &k, &g);
   *amax_out = A;
   *g_out = g;
+  (void)oracle_e4m3_encode_rne_sat(0.0f); /* fill the value table before the threads */
+  /* Blocks are independent: threads split the rows. */
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t c0 = 0; c0 < cols; c0 += 16) {
       float xb[16];
@@ -622,13 +643,16 @@ int oracle_quantize_mse(const void* x, int x_is_bf16, int64_t rows, int64_t cols
         xb[i] = load_elem(x, x_is_bf16, r * cols + c0 + i);
         if (fabsf(xb[i]) > a) a = fabsf(xb[i]);
       }
+      /* Start from the max-based scale; then every finite E4M3 code in
+       * ascending order, replacing the choice only when strictly better.  So
+       * the result is the argmin over all 127 codes; on a tie the max-based
+       * code is kept if it is among the minima, else the smallest code. */
       const int e0 = oracle_e4m3_encode_rne_sat(a * k);
       uint8_t best_q[16], q[16];
       int best = e0;
       double best_err = mse_candidate(xb, (uint8_t)e0, S, g, best_q);
-      for (int t = 1; t <= 16; t++) {
-        const int e = t == 1 ? e0 + 1 : e0 - (t - 1);
-        if (e < 0 || e > 126) continue;
+      for (int e = 0; e <= 126; e++) {
+        if (e == e0) continue;
         const double err = mse_candidate(xb, (uint8_t)e, S, g, q);
         if (err < best_err) {
           best_err = err;

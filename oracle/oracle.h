@@ -50,6 +50,9 @@ uint8_t oracle_e2m1_encode_rne(float y);           /* nearest, ties to even */
 uint8_t oracle_e2m1_encode_sr(float y, uint32_t u16);
 float   oracle_e4m3_decode(uint8_t e);             /* byte -> value (NaN for 0x7F/0xFF) */
 uint8_t oracle_e4m3_encode_rne_sat(float s);       /* s >= 0 finite -> byte */
+/* Element-wise over arrays of n values (for exhaustive sweeps). */
+void oracle_e2m1_encode_rne_n(const float* y, int64_t n, uint8_t* out);
+void oracle_e4m3_encode_rne_sat_n(const float* s, int64_t n, uint8_t* out);
 
 /* ---- Philox4x32 ---------------------------------------------------------- */
 void oracle_philox4x32(const uint32_t ctr[4], const uint32_t key[2],
@@ -141,14 +144,14 @@ int oracle_gemm_full(char opA, char opB, int64_t M, int64_t N, int64_t K,
  * minimizing the weight's MSE instead of taking the max-based one).
  * ROW blocks (1x16 along cols), RNE elements, per-tensor S, k, g from amax
  * (computed, or amax_in when non-NULL) exactly as the max-based quantizer.
- * For each block the candidate E4M3 scale codes are, in this order: the
- * max-based code e0 = E4M3(RN32(a k)), then e0 + 1, e0 - 1, e0 - 2, ...,
- * e0 - 15 (those within 0 .. 126).  A candidate e encodes the block as the
- * max-based quantizer would with scale e (r = RN32(S / val(e)), y = RN32(x
- * r), RNE) and its error is, in fp64, (sum_{i<8} (x_i - xh_i)^2) +
- * (sum_{i>=8} (x_i - xh_i)^2), each sum in index order, with xh_i =
- * RN32(RN32(val(code_i) val(e)) g) the dequantized value.  A candidate
- * replaces the current choice only if its error is strictly smaller.
+ * Each block's E4M3 scale code is the one, of all 127 finite codes
+ * 0 .. 126, whose encoding of the block has the smallest squared error.  A
+ * code e encodes the block as the max-based quantizer would with scale e
+ * (r = RN32(S / val(e)), y = RN32(x r), RNE) and its error is the fp64 sum,
+ * in index order, of (x_i - xh_i)^2 with xh_i = RN32(RN32(val(code_i)
+ * val(e)) g) the dequantized value.  Ties: the max-based code e0 =
+ * E4M3(RN32(a k)) if it reaches the minimum, else the smallest code that
+ * does.
  * Outputs as oracle_quantize (codes, scales [rows x cols/16], amax, g). */
 int oracle_quantize_mse(const void* x, int x_is_bf16, int64_t rows, int64_t cols,
                         const float* amax_in, uint8_t* codes, uint8_t* scales,

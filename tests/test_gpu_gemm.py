@@ -127,16 +127,28 @@ def test_gemm_exact_special_case(layout):
     assert np.array_equal(c.astype(np.float64), exact)
 
 
-def _sampled_check(layout, qa, qb, M, N, K, c, n_random=4096, seed=0):
+def _pick(n, k, rng):
+    """k distinct indices of range(n) including the first and the last (all of
+    them when n <= k), sorted."""
+    if n <= k:
+        return np.arange(n, dtype=np.int64)
+    mid = rng.choice(np.arange(1, n - 1), k - 2, replace=False)
+    return np.sort(np.concatenate([[0, n - 1], mid]).astype(np.int64))
+
+
+def _sampled_check(layout, qa, qb, M, N, K, c, n_rows=64, n_cols=64, n_random=4096, seed=0):
+    """Full rows (n_rows, the first and last included), full columns (n_cols,
+    likewise) and n_random random outputs against the oracle."""
     rng = np.random.default_rng(seed)
-    rows = [0, M - 1]
-    cols = [0, N - 1]
-    ii = [np.full(N, r) for r in rows] + [np.arange(M) for _ in cols] + [rng.integers(0, M, n_random)]
-    jj = [np.arange(N) for _ in rows] + [np.full(M, cc) for cc in cols] + [rng.integers(0, N, n_random)]
+    rows = _pick(M, n_rows, rng)
+    cols = _pick(N, n_cols, rng)
+    ii = [np.repeat(rows, N), np.tile(np.arange(M), len(cols)), rng.integers(0, M, n_random)]
+    jj = [np.tile(np.arange(N), len(rows)), np.repeat(cols, M), rng.integers(0, N, n_random)]
     ii = np.concatenate(ii); jj = np.concatenate(jj)
     A, B = to_np(qa), to_np(qb)
     R, D = O.gemm_entries(layout[0], layout[1], M, N, K, A, B, ii, jj)
-    got = c[ii, jj].float().cpu().numpy()
+    got = c[torch.from_numpy(ii).to(c.device), torch.from_numpy(jj).to(c.device)]
+    got = got.float().cpu().numpy()
     err = O.gemm_rel_err(got, R, D)
     assert err <= TOL, f"{layout} {M}x{N}x{K}: sampled max |C-R|/D = {err:.3e}"
     return err
@@ -180,6 +192,90 @@ def test_full_ultra_dgrad():
     c = nv.gemm("N", "N", qa, qb, out_dtype=torch.float32)
     check_bf16_is_rne_of_fp32(nv.gemm("N", "N", qa, qb, out_dtype=torch.bfloat16), c)
     _sampled_check("NN", qa, qb, M, N, K, c)
+
+
+def test_full_ultra_fprop():
+    """Ultra-width fprop: X bf16 [8192 x 8192] N(0,1) 1x16 RNE, W [8192 x
+    8192] N(0, 0.015) 16x16, Y = X W^T (NT); bf16 out, the RNE of the fp32
+    result, which is sampled against the oracle."""
+    w = synth.WORKLOADS["ultra"]
+    dev = device()
+    M, N, K = w["M"], w["N"], w["K"]
+    x = synth.to_bf16(synth.normal((M, K), 1.0, w["x_seed"])).to(dev)
+    wt = synth.to_bf16(synth.normal((N, K), w["w_std"], w["w_seed"])).to(dev)
+    qa = nv.quantize_1d(x, "row")
+    qb = nv.quantize_2d(wt)
+    del x, wt
+    c = nv.gemm("N", "T", qa, qb, out_dtype=torch.float32)
+    check_bf16_is_rne_of_fp32(nv.gemm("N", "T", qa, qb, out_dtype=torch.bfloat16), c)
+    _sampled_check("NT", qa, qb, M, N, K, c, seed=1)
+
+
+def test_gemm_kmajor_operand_past_4gib():
+    """A K-major A with 2^20 + 256 rows of K = 8192 (4 GiB of codes): each
+    tile's buffer range covers its own rows, so tiles far into the operand,
+    and the last one, read their codes (a range running to the operand's end
+    would wrap 32 bits and read zeros).  A's codes and scales are drawn
+    directly; rows are checked against the oracle on those rows alone (row i
+    of an NT product only depends on row i of A)."""
+    dev = device()
+    M, N, K = (1 << 20) + 256, 64, 8192
+    g = torch.Generator(device=dev).manual_seed(41)
+    codes = torch.randint(0, 256, (M, K // 2), generator=g, device=dev, dtype=torch.uint8)
+    scales = torch.randint(0x30, 0x48, (M, K // 16), generator=g, device=dev,
+                           dtype=torch.uint8)
+    one = torch.ones(1, device=dev)
+    qa = nv.QTensor(codes, scales, one, one, M, K, "row")
+    qb = nv.quantize_2d(synth.normal_device((N, K), 0.02, 42, dev))
+    c = nv.gemm("N", "T", qa, qb, out_dtype=torch.float32)
+    rows = np.array([0, 1, 255, 256, 4097, (1 << 19) + 3, 1 << 20, M - 2, M - 1], dtype=np.int64)
+    ridx = torch.from_numpy(rows).to(dev)
+    A = dict(codes=codes[ridx].cpu().numpy(), scales=scales[ridx].cpu().numpy(), block="row",
+             g=1.0)
+    ii = np.repeat(np.arange(len(rows), dtype=np.int64), N)
+    jj = np.tile(np.arange(N, dtype=np.int64), len(rows))
+    R, D = O.gemm_entries("N", "T", len(rows), N, K, A, to_np(qb), ii, jj)
+    got = c[ridx].cpu().numpy().reshape(-1)
+    err = O.gemm_rel_err(got, R, D)
+    assert err <= TOL, f"max |C-R|/D = {err:.3e}"
+
+
+SENTINEL = 0x7FC0DEAD  # a NaN pattern no kernel writes
+
+
+def _guarded(shape, dtype, dev, pad=1024):
+    """A tensor of `shape` inside a larger buffer whose other bytes hold a
+    sentinel pattern: (view, buffer, pad in elements)."""
+    n = int(np.prod(shape))
+    esz = torch.empty(0, dtype=dtype).element_size()
+    words = (n * esz + 3) // 4 + 2 * pad
+    buf = torch.full((words,), SENTINEL, dtype=torch.int32, device=dev)
+    view = buf[pad:].view(torch.uint8)[:n * esz].view(dtype).view(shape)
+    return view, buf, pad, (n * esz + 3) // 4
+
+
+def _intact(buf, pad, used):
+    b = buf.cpu().numpy()
+    return bool(np.all(b[:pad] == SENTINEL) and np.all(b[pad + used:] == SENTINEL))
+
+
+@pytest.mark.parametrize("layout,M,N,K", [("NT", 300, 272, 320), ("NN", 200, 96, 192),
+                                          ("TN", 288, 544, 128), ("NT", 40, 96, 512),
+                                          ("NT", 4096, 4096, 128)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_output_canaries(layout, M, N, K, out):
+    """The GEMMs write nothing outside C: sentinel words before and after the
+    output (partial tiles, small-M kernel, full tiles) are untouched."""
+    dev = device()
+    qa, qb = _operands(layout, M, N, K, seed=M + N, sr=layout != "NT",
+                       mask=0x3C5A if layout == "TN" else -1)
+    c, buf, pad, used = _guarded((M, N), out, dev)
+    nv.gemm(layout[0], layout[1], qa, qb, out=c)
+    torch.cuda.synchronize()
+    assert _intact(buf, pad, used)
+    want = nv.gemm(layout[0], layout[1], qa, qb, out_dtype=out)
+    assert torch.equal(c.view(torch.int16 if out == torch.bfloat16 else torch.int32),
+                       want.view(torch.int16 if out == torch.bfloat16 else torch.int32))
 
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])

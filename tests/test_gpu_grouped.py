@@ -42,8 +42,8 @@ def _grouped_case(counts, N, K, seed, b_block="2d", out=torch.bfloat16):
     return qa, qb, offsets, c
 
 
-def _check_group(qa, qb, offsets, c, e, N, K, rows=None):
-    A = to_np(qa)
+def _check_group(qa, qb, offsets, c, e, N, K, rows=None, A=None):
+    A = to_np(qa) if A is None else A
     Bc = qb.codes[e].cpu().numpy()
     Bs = qb.scales[e].cpu().numpy()
     gB = float(qb.global_dec[e].item())
@@ -149,10 +149,52 @@ def test_full_grouped_super_sampled():
     cb = nv.grouped_gemm(qa, qb, off_d, out_dtype=torch.bfloat16)
     assert torch.equal(cb.view(torch.int16), c.to(torch.bfloat16).view(torch.int16))
     torch.cuda.synchronize()
-    big, small = int(np.argmax(counts)), int(np.argmin(counts))
-    for e in sorted({0, 1, big, small, 257, 511}):
+    A = to_np(qa)
+    for e in _spread_experts(counts, 16):
         n = int(counts[e])
-        _check_group(qa, qb, offsets, c, e, w["hidden"], w["latent"], rows=[0, n // 2, n - 1])
+        _check_group(qa, qb, offsets, c, e, w["hidden"], w["latent"], rows=[0, n // 2, n - 1],
+                     A=A)
+
+
+def _spread_experts(counts, k):
+    """k experts spread over the range of row counts: the largest, the
+    smallest non-empty one, and k - 2 between them by rank, plus experts 0
+    and the last."""
+    order = [int(e) for e in np.argsort(counts, kind="stable") if counts[e] > 0]
+    picks = {order[-1], order[0], 0, len(counts) - 1}
+    for t in np.linspace(0, len(order) - 1, k).astype(int):
+        picks.add(order[t])
+    return sorted(e for e in picks if counts[e] > 0)
+
+
+def test_full_grouped_ultra_sampled():
+    """Ultra's routed experts: 8192 tokens x top-22 of 512 experts (Zipf 1.1
+    routing, seed 16), latent 2048 -> expert hidden 5120, W_e N(0, 0.015);
+    full rows (first, middle, last) of at least 16 experts against the
+    oracle, and bf16 output equal to the RNE of the fp32 result."""
+    w = synth.WORKLOADS["ultra"]
+    dev = device()
+    E, L, H = 512, w["glat"], w["ghidden"]
+    counts, tok, offsets = synth.zipf_routing(8192, E, 22, 1.1, w["groute_seed"])
+    x = synth.to_bf16(synth.normal((8192, L), 1.0, w["gx_seed"])).to(dev)
+    a = x[torch.from_numpy(tok).to(dev)]
+    W = synth.normal_device((E, H, L), w["w_std"], w["gw_seed"], dev)
+    qa = nv.quantize_1d(a, "row")
+    qb = nv.quantize_2d(W)
+    del W, a
+    torch.cuda.empty_cache()
+    off_d = torch.from_numpy(offsets).to(dev)
+    c = nv.grouped_gemm(qa, qb, off_d, out_dtype=torch.float32)
+    cb = nv.grouped_gemm(qa, qb, off_d, out_dtype=torch.bfloat16)
+    assert torch.equal(cb.view(torch.int16), c.to(torch.bfloat16).view(torch.int16))
+    del cb
+    torch.cuda.synchronize()
+    picks = _spread_experts(counts, 16)
+    assert len(picks) >= 16
+    A = to_np(qa)
+    for e in picks:
+        n = int(counts[e])
+        _check_group(qa, qb, offsets, c, e, H, L, rows=[0, n // 2, n - 1], A=A)
 
 
 # ---- routed-expert backward: grouped dgrad (NN) and grouped wgrad (TN) -------------------------
@@ -218,13 +260,13 @@ def _wgrad_case(counts, M, N, seed, dev, mask=0x3C5A):
     return qa, qb, off
 
 
-def _check_wgrad_group(qa, qb, off, c, e, M, N, rows=None):
+def _check_wgrad_group(qa, qb, off, c, e, M, N, rows=None, AB=None):
     k0, k1 = int(off[e]), int(off[e + 1])
     got = c[e].cpu().numpy()
     if k1 == k0:
         assert not got.any(), f"empty group {e} must give zeros"
         return
-    A, B = to_np(qa), to_np(qb)
+    A, B = (to_np(qa), to_np(qb)) if AB is None else AB
     Ae = dict(codes=A["codes"][k0:k1], scales=A["scales"][k0 // 16:k1 // 16], block="col", g=A["g"])
     Be = dict(codes=B["codes"][k0:k1], scales=B["scales"][k0 // 16:k1 // 16], block="col", g=B["g"])
     if rows is None:
@@ -310,7 +352,7 @@ def test_full_grouped_super_backward_sampled():
     """Routed-expert backward at the Super shapes (512 experts, 8192 tokens
     top-22, Zipf 1.1 routing; hidden 2688, latent 1024): grouped dgrad
     dX = dY W (bf16 out) and grouped wgrad dW_e = dY_e^T X_e (fp32 out),
-    sampled rows of the largest, smallest and a middle expert."""
+    sampled rows of at least 16 experts spread over the row counts."""
     dev = device()
     counts, tok, _ = synth.zipf_routing(8192, 512, 22, 1.1, 9)
     H, L = 2688, 1024
@@ -325,8 +367,8 @@ def test_full_grouped_super_backward_sampled():
     off_d = torch.from_numpy(off).to(dev)
     dx = nv.grouped_gemm_nn(qa, qw, off_d, out_dtype=torch.float32)
     A = to_np(qa)
-    order = np.argsort(counts)
-    picks = [int(order[-1]), int(order[0]), int(order[256])]
+    picks = _spread_experts(counts, 16)
+    assert len(picks) >= 16
     for e in picks:
         r0, r1 = int(off[e]), int(off[e + 1])
         rows = np.unique(np.linspace(0, r1 - r0 - 1, 6).astype(np.int64))
@@ -356,5 +398,6 @@ def test_full_grouped_super_backward_sampled():
     qb = nv.quantize_1d(xp, "col", "rne", None, mask)
     del dyp, xp
     dw = nv.grouped_gemm_tn(qa, qb, torch.from_numpy(koff).to(dev), 512)
+    AB = (to_np(qa), to_np(qb))
     for e in picks:
-        _check_wgrad_group(qa, qb, koff, dw, e, H, L, rows=[0, 1000, 2687])
+        _check_wgrad_group(qa, qb, koff, dw, e, H, L, rows=[0, 1000, 2687], AB=AB)

@@ -96,3 +96,46 @@ def test_layout_errors():
         O.gemm_entries("T", "T", 32, 16, 16, A, A, [0], [0])
     with pytest.raises(ValueError):  # ROW blocks cannot serve a K-by-rows operand
         O.gemm_entries("T", "N", 32, 32, 16, A, A, [0], [0])
+
+
+# ---- the parity metric itself ------------------------------------------------------------------
+def test_rel_err_hand_cases():
+    """max |C - R| / D on hand-made values: exact agreement is 0, a known
+    relative offset is recovered, D = 0 demands C = 0, and the maximum over
+    entries is what is reported."""
+    R = np.array([1.0, -2.0, 0.5, 0.0])
+    D = np.array([3.0, 2.0, 8.0, 0.0])
+    assert O.gemm_rel_err(R.copy(), R, D) == 0.0
+    e = O.gemm_rel_err(R + 2e-3 * D, R, D)
+    assert abs(e - 2e-3) < 1e-15
+    bad = R.copy()
+    bad[3] = 1e-30  # the D = 0 entry must be exactly 0
+    assert O.gemm_rel_err(bad, R, D) == np.inf
+    one = R.copy()
+    one[2] += 0.5 * D[2]  # one entry off by half its D
+    assert O.gemm_rel_err(one, R, D) == 0.5
+    assert O.gemm_rel_err(np.zeros(0), np.zeros(0), np.zeros(0)) == 0.0
+
+
+def test_rel_err_flags_a_dropped_block():
+    """A product computed independently (numpy fp32 matmul of the decoded
+    operands) passes the 1e-3 bar; the same product missing one 16-k block of
+    the contraction, or with one operand's block scale off by one code, fails
+    it."""
+    rng = np.random.default_rng(22)
+    M, N, K = 32, 48, 256
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A = _q(a, "row"); B = _q(b, "2d")
+    R, D = O.gemm_full("N", "T", M, N, K, A, B)
+    Ad = _decode(A, M, K).astype(np.float32)
+    Bd = _decode(B, N, K).astype(np.float32)
+    g = np.float32(A["g"]) * np.float32(B["g"])
+    good = (Ad @ Bd.T) * g
+    assert O.gemm_rel_err(good, R, D) <= 1e-3
+    dropped = (Ad[:, 16:] @ Bd[:, 16:].T) * g
+    assert O.gemm_rel_err(dropped, R, D) > 1e-3
+    A2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in A.items()}
+    A2["scales"][5, 3] = A2["scales"][5, 3] + 1
+    off = (_decode(A2, M, K).astype(np.float32) @ Bd.T) * g
+    assert O.gemm_rel_err(off, R, D) > 1e-3

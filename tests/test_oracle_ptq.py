@@ -2,12 +2,17 @@
 (Super report summary 4.2: each weight block's scale minimizes the weight's
 MSE instead of being max-based).
 
-Checked against: a worked example computed by hand; blocks for which the
-max-based scale is already exact (they keep it); all-zero blocks; the
-candidate window; an independent brute force over every candidate scale on
-random blocks (numpy nearest-value search with ties to the even code, not
-the oracle's encoder); and never being worse than the max-based quantizer,
-measured with the oracle's dequantizer."""
+Reading pinned here: the scale is the argmin of the block's squared error
+over all 127 finite E4M3 codes (the error summed in fp64 in index order);
+ties keep the max-based code when it is among the minima, else the smallest
+code.  Checked against: worked examples computed by hand (one of them has its
+best scale five codes above the max-based one, so a search window around the
+max-based code is not enough, and one has a tie); blocks for which the
+max-based scale is already exact (they keep it); all-zero blocks; an
+independent brute force over every code on random and adversarial blocks
+(numpy nearest-value search with ties to the even code, not the oracle's
+encoder); and never being worse than the max-based quantizer, measured with
+the oracle's dequantizer."""
 import numpy as np
 import pytest
 
@@ -16,27 +21,41 @@ import oracle as O
 E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
-def _unpack(codes):
-    return np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(codes.shape[0], -1)
-
-
-def test_worked_example():
+def test_worked_example_tie():
     """Tensor amax 2688 gives S = 1, k = 1/6, g = 1.  Block [6.0 x 15, 7.2]:
     max-based s = 7.2/6 = 1.2 -> E4M3 1.25 (0x3A); 6.0 * 0.8 = 4.8 -> 4 ->
     5.0 (error 1.0, fifteen times), 7.2 * 0.8 = 5.76 -> 6 -> 7.5 (0.09):
-    15.09.  Scale 1.0 (0x38): 6.0 -> 6 exactly, 7.2 saturates to 6 (1.44):
-    1.44.  Scale 1.125 (0x39): 6.0 * 0.888.. -> 6 -> 6.75 (0.5625 x 15) plus
-    7.2 -> 6.75 (0.2025): 8.64.  Smaller scales saturate 6.0 as well.  So the
-    choice is 0x38 with every code 6 (0x7)."""
+    15.09.  Scale 2.0 (0x40): 6.0 -> 3 exactly, 7.2 -> 3.6 -> 4 -> 8.0
+    (0.64): 0.64.  Scale 4.0 (0x48): 6.0 -> 1.5 exactly, 7.2 -> 1.8 -> 2 ->
+    8.0: also 0.64.  Every scale that keeps 6.0 exact leaves 7.2 at 6.0 or
+    8.0 (1.44 or 0.64), and one that does not costs at least fifteen errors
+    of 6.0.  The tie between 0x40 and 0x48 goes to the smaller code (the
+    max-based 0x3A is not a minimum)."""
     x = np.zeros((1, 32), dtype=np.float32)
     x[0, 0] = 2688.0
     x[0, 16:31] = 6.0
     x[0, 31] = 7.2
     q = O.quantize_mse(x)
     assert q["g"] == np.float32(1.0)
-    assert q["scales"][0, 1] == 0x38
-    assert np.all(q["codes"][0, 8:] == 0x77)
+    assert q["scales"][0, 1] == 0x40
+    assert np.all(q["codes"][0, 8:15] == 0x55) and q["codes"][0, 15] == 0x65
     assert O.quantize(x, "row")["scales"][0, 1] == 0x3A  # the max-based choice
+
+
+def test_worked_example_far_above_max_based():
+    """S = 1, g = 1.  A block of sixteen 6.375: max-based s = 1.0625, a tie
+    between E4M3 1.0 and 1.125 that goes to the even code, 1.0 (0x38);
+    6.375 saturates to 6 (error 0.375^2 x 16 = 2.25).  Scale 1.625 (0x3D,
+    five codes up): 6.375 / 1.625 = 3.923 -> 4 -> 6.5 (0.125^2 x 16 = 0.25),
+    the minimum: no scale represents 6.375 exactly (6.375 = 51/8 would need
+    an E4M3 value 51/8/v for a grid value v)."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0] = 2688.0
+    x[0, 16:] = 6.375
+    q = O.quantize_mse(x)
+    assert O.quantize(x, "row")["scales"][0, 1] == 0x38
+    assert q["scales"][0, 1] == 0x3D
+    assert np.all(q["codes"][0, 8:] == 0x66)
 
 
 def test_exact_blocks_keep_the_max_based_scale():
@@ -64,43 +83,83 @@ def test_zero_blocks():
 
 
 def _encode_rne(y):
-    """Nearest E2M1 value (ties to the even code), by search over the grid."""
-    m = abs(float(y))
-    dist = np.abs(E2M1 - m)
-    best = np.flatnonzero(dist == dist.min())
-    i = int(best[0]) if len(best) == 1 else int(best[0] if best[0] % 2 == 0 else best[1])
-    return (8 if np.signbit(y) else 0) | i
+    """Nearest E2M1 magnitude index for each fp32 y (ties to the even index,
+    |y| >= 6 saturating), by a search over the grid; the sign bit as code 8."""
+    m = np.abs(y.astype(np.float64))
+    best = np.zeros(m.shape, dtype=np.int64)
+    best_d = np.abs(m - E2M1[0])
+    for i in range(1, 8):
+        d = np.abs(m - E2M1[i])
+        take = (d < best_d) | ((d == best_d) & (i % 2 == 0))
+        best = np.where(take, i, best)
+        best_d = np.where(take, d, best_d)
+    best = np.where(m >= 6.0, 7, best)
+    return best | np.where(np.signbit(y), 8, 0)
 
 
-def _block_err(xb, e, S, g):
-    d = np.float32(O.e4m3_decode(e))
-    r = np.float32(0.0) if d == 0 else np.float32(min(np.float32(S) / d, np.finfo(np.float32).max))
-    h = [0.0, 0.0]
-    for i, xi in enumerate(xb):
-        c = _encode_rne(np.float32(xi * r))
-        v = E2M1[c & 7] * (-1.0 if c & 8 else 1.0)
-        xh = np.float32(np.float32(np.float32(v) * d) * np.float32(g))
-        h[i // 8] += (float(xi) - float(xh)) ** 2
-    return h[0] + h[1]
+def _all_code_errors(xb, S, g):
+    """Squared error of block xb (16 fp32) for every E4M3 code 0..126."""
+    S, g = np.float32(S), np.float32(g)
+    d = np.array([O.e4m3_decode(e) for e in range(127)], dtype=np.float32)
+    with np.errstate(over="ignore", divide="ignore"):
+        r = np.where(d == 0, np.float32(0), S / np.where(d == 0, np.float32(1), d))
+    r = np.minimum(r, np.finfo(np.float32).max).astype(np.float32)
+    y = (xb[None, :] * r[:, None]).astype(np.float32)  # RN32 products
+    c = _encode_rne(y)
+    val = (E2M1[c & 7] * np.where(c & 8, -1.0, 1.0)).astype(np.float32)
+    xh = ((val * d[:, None]).astype(np.float32) * g).astype(np.float32)
+    err = xb.astype(np.float64)[None, :] - xh.astype(np.float64)
+    total = np.zeros(127)
+    for i in range(16):  # index order, one running sum
+        total = total + err[:, i] * err[:, i]
+    return total, c
 
 
-def test_brute_force_over_the_window():
+def _check_blocks(x):
+    q, m = O.quantize_mse(x), O.quantize(x, "row")
+    S = np.float32(2688.0) / np.float32(q["amax"]) if q["amax"] != 0 else np.float32(1.0)
+    rows, cols = x.shape
+    codes = np.stack([q["codes"] & 0xF, q["codes"] >> 4], axis=-1).reshape(rows, cols)
+    for r in range(rows):
+        for b in range(cols // 16):
+            xb = x[r, 16 * b:16 * b + 16]
+            errs, c = _all_code_errors(xb, S, q["g"])
+            e0 = int(m["scales"][r, b])
+            want = e0 if errs[e0] == errs.min() else int(np.flatnonzero(errs == errs.min())[0])
+            assert int(q["scales"][r, b]) == want, (r, b)
+            assert np.array_equal(codes[r, 16 * b:16 * b + 16], c[want]), (r, b)
+
+
+def test_brute_force_all_codes_random():
     rng = np.random.default_rng(11)
     x = (rng.standard_normal((6, 64)) * np.exp(rng.standard_normal((6, 64)))).astype(np.float32)
-    q, m = O.quantize_mse(x), O.quantize(x, "row")
-    S = np.float32(2688.0) / np.float32(q["amax"])
-    for r in range(6):
-        for b in range(4):
-            xb = x[r, 16 * b:16 * b + 16]
-            e0 = int(m["scales"][r, b])
-            cands = [e for e in [e0, e0 + 1] + [e0 - t for t in range(1, 16)] if 0 <= e <= 126]
-            errs = {e: _block_err(xb, e, S, q["g"]) for e in cands}
-            chosen = int(q["scales"][r, b])
-            assert chosen in errs
-            assert errs[chosen] <= min(errs.values()) * (1 + 1e-12)
-            # the first candidate (in order) reaching the minimum
-            first = next(e for e in cands if errs[e] <= min(errs.values()) * (1 + 1e-12))
-            assert chosen == first
+    _check_blocks(x)
+
+
+def test_brute_force_all_codes_adversarial():
+    """Constant blocks at values between scale steps, blocks with one large
+    outlier, grid-valued blocks off the max-based scale, midpoints of the
+    E2M1 grid, and tiny blocks whose scales are E4M3 subnormals."""
+    rng = np.random.default_rng(12)
+    x = np.zeros((8, 64), dtype=np.float32)
+    x[0, 0] = 2688.0  # S = 1, g = 1 for the whole tensor
+    x[0, 16:32] = 6.375
+    x[0, 32:48] = np.float32(6.0 * 1.1875)
+    x[0, 48:64] = np.linspace(-5.0, 5.0, 16)
+    for b in range(4):  # one outlier among small values
+        x[1, 16 * b:16 * b + 16] = rng.standard_normal(16) * 0.1
+        x[1, 16 * b + b] = 40.0 * (b + 1)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+    for b in range(4):  # E2M1 midpoints times an E4M3 value
+        d = O.e4m3_decode(0x30 + 5 * b)
+        x[2, 16 * b:16 * b + 16] = rng.choice(mids, 16) * d
+        x[3, 16 * b:16 * b + 16] = rng.choice(E2M1, 16) * O.e4m3_decode(0x28 + 7 * b)
+    for b in range(4):  # scales near the bottom of E4M3 (subnormal codes)
+        x[4, 16 * b:16 * b + 16] = rng.standard_normal(16) * (2.0 ** (-12 - 2 * b))
+    x[5] = rng.laplace(0.0, 1.0, 64) * np.where(rng.random(64) < 0.3, 0.0, 1.0)
+    x[6] = np.repeat(np.array([3.0, -3.0, 0.0, 1e-30], dtype=np.float32), 16)
+    x[7] = rng.standard_normal(64) * 1e3
+    _check_blocks(x)
 
 
 @pytest.mark.parametrize("seed", [1, 2])
