@@ -678,6 +678,8 @@ def main():
     extra = [r.strip() for r in args.rows.split(",") if r.strip()]
     if not args.rows:  # the default run also reports the Ultra-width GEMMs
         extra = ["ultra"]
+    if "none" in extra:
+        extra = []
     if "all" in extra:
         extra = ["wgrad", "dy_dual", "grouped", "grouped_bwd", "ultra", "grouped_ultra", "ssm_sr",
                  "ptq_decode"]

@@ -384,6 +384,22 @@ int32_t nvfp4_grouped_gemm_tn_accumulate(int64_t groups, const int64_t* k_offset
 int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16_t* y,
                       void* stream);
 
+/*
+ * Tuning of the single-pass quantizers (a performance setting: results are
+ * the same either way).  A bf16 tensor that fits in the registers of one
+ * workgroup per CU (ROW blocks with RNE and no transform; one 16x16-blocked
+ * matrix) is quantized in one launch that reads it once: its workgroups
+ * meet at a grid barrier to combine the tensor amax.  They wait there at
+ * most wait_us microseconds (default 2000); a workgroup that gives up, which
+ * only happens when other kernels hold CUs (e.g. on concurrent streams),
+ * reads the whole tensor to take the amax itself, so the results are
+ * unchanged but slower.  wait_us < 0 turns the single-pass kernels off
+ * (every call then takes the two-pass path: amax, then encode).  Applies to
+ * calls made after it, process-wide.  Returns the previous setting (-1 when
+ * off).
+ */
+int32_t nvfp4_set_single_pass_wait(int32_t wait_us);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ from ._binding import (  # noqa: F401
     nvfp4_abi_version, nvfp4_status_string, nvfp4_quantize_1d, nvfp4_quantize_dual,
     nvfp4_quantize_mse, nvfp4_quantize_2d, nvfp4_rht16,
     nvfp4_dequantize, nvfp4_gemm, nvfp4_grouped_gemm, nvfp4_grouped_gemm_nn, nvfp4_grouped_gemm_tn,
-    nvfp4_grouped_gemm_tn_accumulate, nvfp4_sr_fp16,
+    nvfp4_grouped_gemm_tn_accumulate, nvfp4_sr_fp16, nvfp4_set_single_pass_wait,
     quantize_1d, quantize_dual, quantize_mse, quantize_2d, rht16, dequantize, gemm, grouped_gemm,
     grouped_gemm_nn, grouped_gemm_tn, sr_fp16,
 )

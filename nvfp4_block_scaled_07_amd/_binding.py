@@ -98,6 +98,8 @@ def load():
     L.nvfp4_grouped_gemm_tn_accumulate.restype = i32
     L.nvfp4_grouped_gemm_tn_accumulate.argtypes = [i64, vp, i64, i64, i64, C.POINTER(_Operand),
                                                    C.POINTER(_Operand), vp, vp]
+    L.nvfp4_set_single_pass_wait.restype = i32
+    L.nvfp4_set_single_pass_wait.argtypes = [i32]
     _lib = L
     return L
 
@@ -153,6 +155,12 @@ class QTensor:
 
 
 # ---- one-to-one mirrors of the C entry points ------------------------------------------
+def nvfp4_set_single_pass_wait(wait_us):
+    """Grid-barrier wait of the single-pass quantizers in microseconds (< 0:
+    single-pass kernels off); returns the previous setting."""
+    return load().nvfp4_set_single_pass_wait(int(wait_us))
+
+
 def nvfp4_abi_version():
     return load().nvfp4_abi_version()
 

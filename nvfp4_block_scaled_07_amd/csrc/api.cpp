@@ -438,4 +438,8 @@ int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16
                                              static_cast<hipStream_t>(stream)));
 }
 
+int32_t nvfp4_set_single_pass_wait(int32_t wait_us) {
+  return nvfp4::set_single_pass_wait_us(wait_us);
+}
+
 }  // extern "C"

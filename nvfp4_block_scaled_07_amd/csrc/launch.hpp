@@ -105,6 +105,9 @@ struct WgradArgs {
 };
 
 hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st);
+// Sets the single-pass kernels' barrier wait (microseconds; negative: do not
+// use them) and returns the previous setting.
+int set_single_pass_wait_us(int us);
 hipError_t launch_quantize_2d(const Quant2dArgs& a, hipStream_t st);
 hipError_t launch_quantize_dual(const QuantDualArgs& a, hipStream_t st);
 hipError_t launch_quantize_mse(const void* x, bool x_fp32, int64_t rows, int64_t cols,

@@ -31,6 +31,9 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstddef>
+#include <type_traits>
 
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
@@ -139,38 +142,166 @@ __device__ __forceinline__ uint32_t pack8_rne(const float y[8]) {
   return w;
 }
 
-// ---- workgroup max -> atomicMax ---------------------------------------------------------
+// ---- workgroup max -> tensor amax --------------------------------------------------------
 // Same-address atomics serialize in L2 (several ns each), so the amax passes
 // run few, large workgroups (kAmaxThreads) and one atomic per workgroup.
 constexpr int kAmaxThreads = 1024;
 
-// m0 -> out0 and, when out1 is given, m1 -> out1 (one reduction pass).
-__device__ __forceinline__ void block_max_to(float m0, float* out0, float m1 = 0.0f,
-                                             float* out1 = nullptr) {
+// Per-call scratch of the amax passes.  A pass combines its workgroups'
+// maxima in a slot of this array instead of in the caller's output, which
+// would need an extra launch to clear it first: each workgroup raises the
+// maxima (atomicMax on the fp32 bits: non-negative floats order like
+// integers, so the result does not depend on the order) and counts itself
+// in; the last one to arrive copies the maxima to the caller's outputs and
+// clears the slot for its next use.  The zero-code counts of the dual
+// quantizer are gathered the same way.  The host hands slots out round
+// robin (next_slot), so calls in flight at the same time on different
+// streams use different slots unless more than kSlots of them overlap.  The
+// array starts zeroed when the code object loads and every completed use
+// leaves it zeroed.
+//
+// Same-address atomics serialize (about 20-25 ns each here), so a slot is
+// two-level: workgroup b counts in at group line b % 8 (the XCD it runs on),
+// and the last of each group carries the group's maxima and counts up to the
+// top line.  A line sees at most a few dozen atomics.  Single-pass kernels
+// also wait on go lines (one per group, written once by the last arrival),
+// which keeps their polling off the lines that take the atomics.
+struct alignas(128) Line {
+  // bits0 and arrive share one 8-byte word: a go line holds the maximum and
+  // its flag there, read together in one load.
+  unsigned int bits0;           // running maximum
+  unsigned int arrive;          // workgroups counted in (go line: 1 = go)
+  unsigned int bits1;           // second running maximum
+  unsigned int depart;          // workgroups done (single-pass kernels)
+  unsigned int done;            // workgroups that added their zero-code counts
+  unsigned int pad;
+  unsigned long long zeros[2];  // zero-code counts (dual quantizer)
+};
+static_assert(offsetof(Line, arrive) == offsetof(Line, bits0) + 4, "flag above the maximum");
+constexpr int kGroups = 8;
+struct Slot {
+  Line group[kGroups];
+  Line top;
+  Line go[kGroups];
+};
+constexpr int kSlots = 256;
+__device__ Slot g_slots[kSlots];
+
+constexpr int kAgent = __HIP_MEMORY_SCOPE_AGENT;
+
+// All slot accesses are relaxed device-scope atomics, which are coherent
+// across the XCDs on their own; acquire/release orderings would also write
+// back and invalidate the XCD's L2 on every access, which slowed the passes
+// by tens of microseconds.  Where one atomic must be performed before the
+// next one is issued (a maximum before the arrival that announces it), the
+// first returns its old value and the wave waits for it (done()).
+__device__ __forceinline__ void done(unsigned int v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void done(unsigned long long v) { asm volatile("" ::"v"(v)); }
+
+__device__ __forceinline__ unsigned int ld(const unsigned int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, kAgent);
+}
+__device__ __forceinline__ void st(unsigned int* p, unsigned int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, kAgent);
+}
+
+__device__ __forceinline__ void raise_max(unsigned int* p, unsigned int v) {
+  // Most workgroups find the maximum already at least theirs: a relaxed load
+  // first skips their atomic, which removes most of the contention.
+  if (ld(p) < v) done(__hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, kAgent));
+}
+
+// Counter fields of a line.
+enum Field { kArrive, kDepart, kDone };
+__device__ __forceinline__ unsigned int* field(Line& l, Field f) {
+  return f == kArrive ? &l.arrive : f == kDepart ? &l.depart : &l.done;
+}
+
+// Counts workgroup blockIdx.x (of `count`) in on field f: at its group
+// line, then, for the last of the group, at the top line.  Before counting
+// in at a level, the maxima (nmax of them) and zero-code counts (when zc)
+// are added there: a workgroup's own values at its group line, a group's
+// totals at the top line.  Returns true in the one workgroup that completes
+// the count; the top line then holds the totals.  Thread 0 only.
+__device__ __forceinline__ bool count_in(Slot& s, Field f, unsigned int count, int nmax,
+                                         const unsigned int* mx, bool zc,
+                                         const unsigned long long* z) {
+  const unsigned int g = blockIdx.x % kGroups;
+  const unsigned int ng = (count - g + kGroups - 1) / kGroups;  // workgroups of group g
+  Line& L = s.group[g];
+  if (nmax > 0) raise_max(&L.bits0, mx[0]);
+  if (nmax > 1) raise_max(&L.bits1, mx[1]);
+  if (zc)
+    for (int k = 0; k < 2; k++)
+      if (z[k]) done(__hip_atomic_fetch_add(&L.zeros[k], z[k], __ATOMIC_RELAXED, kAgent));
+  if (__hip_atomic_fetch_add(field(L, f), 1u, __ATOMIC_RELAXED, kAgent) != ng - 1) return false;
+  Line& T = s.top;
+  if (nmax > 0) raise_max(&T.bits0, ld(&L.bits0));
+  if (nmax > 1) raise_max(&T.bits1, ld(&L.bits1));
+  if (zc)
+    for (int k = 0; k < 2; k++) {
+      const unsigned long long v = __hip_atomic_load(&L.zeros[k], __ATOMIC_RELAXED, kAgent);
+      if (v) done(__hip_atomic_fetch_add(&T.zeros[k], v, __ATOMIC_RELAXED, kAgent));
+    }
+  const unsigned int groups = count < kGroups ? count : kGroups;
+  return __hip_atomic_fetch_add(field(T, f), 1u, __ATOMIC_RELAXED, kAgent) == groups - 1;
+}
+
+// Zeroes every line of a slot (by the workgroup that completed its use).
+__device__ __forceinline__ void slot_clear(Slot& s) {
+  Line* l = &s.group[0];
+  for (int i = 0; i < 2 * kGroups + 1; i++) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(&l[i].bits0), 0ull,
+                       __ATOMIC_RELAXED, kAgent);
+    st(&l[i].bits1, 0u);
+    st(&l[i].depart, 0u);
+    st(&l[i].done, 0u);
+    __hip_atomic_store(&l[i].zeros[0], 0ull, __ATOMIC_RELAXED, kAgent);
+    __hip_atomic_store(&l[i].zeros[1], 0ull, __ATOMIC_RELAXED, kAgent);
+  }
+}
+
+// Maxima of m0 and m1 over the workgroup, valid in thread 0.
+__device__ __forceinline__ void block_max2(float& m0, float& m1) {
   __shared__ float red[2][kAmaxThreads / 64];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     m0 = fmaxf(m0, __shfl_xor(m0, o));
     m1 = fmaxf(m1, __shfl_xor(m1, o));
   }
-  int w = threadIdx.x >> 6;
+  const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     red[0][w] = m0;
     red[1][w] = m1;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int k = 0; k < (out1 ? 2 : 1); k++) {
-      float r = red[k][0];
-      for (int i = 1; i < (int)(blockDim.x >> 6); i++) r = fmaxf(r, red[k][i]);
-      // Thousands of workgroups target one address: skip the atomic when the
-      // value already there is at least ours (it only grows, and the max of
-      // the atomics performed is the same), which removes most of the
-      // contention.
-      unsigned int* p = reinterpret_cast<unsigned int*>(k ? out1 : out0);
-      if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < __float_as_uint(r))
-        atomicMax(p, __float_as_uint(r));
+    for (int i = 1; i < (int)(blockDim.x >> 6); i++) {
+      m0 = fmaxf(m0, red[0][i]);
+      m1 = fmaxf(m1, red[1][i]);
     }
+  }
+}
+
+// m0 -> out0 and, when out1 is given, m1 -> out1.  slot < 0: atomicMax
+// straight into the outputs (cleared beforehand by the caller; used for
+// batched slices).  slot >= 0: through g_slots[slot], `count` workgroups in
+// all, with no clearing needed.
+__device__ __forceinline__ void block_max_to(float m0, float* out0, float m1, float* out1,
+                                             int slot, unsigned int count) {
+  block_max2(m0, m1);
+  if (threadIdx.x != 0) return;
+  if (slot < 0) {
+    raise_max(reinterpret_cast<unsigned int*>(out0), __float_as_uint(m0));
+    if (out1) raise_max(reinterpret_cast<unsigned int*>(out1), __float_as_uint(m1));
+    return;
+  }
+  Slot& s = g_slots[slot];
+  const unsigned int mx[2] = {__float_as_uint(m0), __float_as_uint(m1)};
+  if (count_in(s, kArrive, count, out1 ? 2 : 1, mx, false, nullptr)) {
+    *out0 = __uint_as_float(ld(&s.top.bits0));
+    if (out1) *out1 = __uint_as_float(ld(&s.top.bits1));
+    slot_clear(s);
   }
 }
 
@@ -233,6 +364,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
                                                                  int64_t chunks, uint32_t mask,
                                                                  float* __restrict__ amax,
                                                                  float* __restrict__ amax2,
+                                                                 int slot,
                                                                  RowSrc<kGather> rs = {},
                                                                  uint32_t cpr = 1) {
   const T* xs = x + (int64_t)blockIdx.y * chunks * 8;
@@ -278,7 +410,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
       }
     }
   }
-  block_max_to(m, amax + blockIdx.y, m, amax2);
+  block_max_to(m, amax + blockIdx.y, m, amax2, slot, gridDim.x);
 }
 
 // ---- amax of COL blocks with the transform (lane: 8 cols x 16 rows) ---------------------
@@ -291,6 +423,7 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
                                                                 uint32_t mask,
                                                                 float* __restrict__ amax,
                                                                 float* __restrict__ amax_plain,
+                                                                int slot,
                                                                 RowSrc<kGather> rs = {}) {
   const int64_t cg = cols / 8;
   const int64_t units = (rows / 16) * cg;
@@ -317,10 +450,7 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
       for (int r = 0; r < 16; r++) m = fmaxf(m, __builtin_fabsf(col[r]));
     }
   }
-  if (kPlain)
-    block_max_to(m, amax, mp, amax_plain);
-  else
-    block_max_to(m, amax);
+  block_max_to(m, amax, mp, kPlain ? amax_plain : nullptr, slot, gridDim.x);
 }
 
 // ---- ROW quantizer ---------------------------------------------------------------------------
@@ -709,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     float* __restrict__ row_gdec, uint8_t* __restrict__ col_codes,
     uint8_t* __restrict__ col_scales, float* __restrict__ col_gdec, uint32_t mask,
     uint64_t seed_r, uint64_t offset_r, uint32_t rounds_r, uint64_t seed_c, uint64_t offset_c,
-    uint32_t rounds_c, unsigned long long* __restrict__ zeros, RowSrc<kGather> rs = {}) {
+    uint32_t rounds_c, unsigned long long* __restrict__ zeros, int slot, RowSrc<kGather> rs = {}) {
   __shared__ float rtab_r[128], rtab_c[128];
   const TensorScales tr = tensor_scales(amax[0]), tc = tensor_scales(amax[1]);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -784,11 +914,19 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
       wz[1][threadIdx.x >> 6] = zc;
     }
     __syncthreads();
-    if (threadIdx.x < 2) {
-      unsigned long long t = 0;
+    if (threadIdx.x == 0) {  // through the slot: the last workgroup writes the totals
+      Slot& sl = g_slots[slot];
+      unsigned long long t[2] = {0, 0};
 #pragma unroll
-      for (int w = 0; w < kThreads / 64; w++) t += wz[threadIdx.x][w];
-      if (t) atomicAdd(zeros + threadIdx.x, t);
+      for (int k = 0; k < 2; k++)
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; w++) t[k] += wz[k][w];
+      if (count_in(sl, kDone, gridDim.x, 0, nullptr, true, t)) {
+#pragma unroll
+        for (int k = 0; k < 2; k++)
+          zeros[k] = __hip_atomic_load(&sl.top.zeros[k], __ATOMIC_RELAXED, kAgent);
+        slot_clear(sl);
+      }
     }
   }
 }
@@ -830,6 +968,237 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
     *reinterpret_cast<uint32_t*>(cs + (g * 16 + r) * (cols / 2) + c0 / 2) = pack8_rne(y);
   }
   if (((uc % cg) & 1) == 0) ss[g * (cols / 16) + c0 / 16] = (uint8_t)e;
+}
+
+// ---- single-pass quantizers (tensor amax and encode in one launch) -------------------------
+// A bf16 tensor that fits in the registers of one workgroup per CU is read
+// once: every thread loads its share and keeps it, the workgroups combine
+// their maxima through a grid barrier, then every thread encodes what it
+// holds, exactly as the two-pass kernels do (same block codes, reciprocal
+// table and rounding), so the outputs are bit-identical.  The grid is one
+// workgroup per CU, and a workgroup fills a CU's registers (kSpThreads
+// threads, up to 256 VGPRs each), so on an otherwise idle device all of them
+// are resident at once.  When they are not (another kernel holds CUs, e.g.
+// from a concurrent stream), the barrier's wait is bounded by wait_ticks of
+// the 100 MHz real-time counter: a workgroup that gives up takes the tensor
+// maximum by reading the whole tensor itself, which is slow but gives the
+// same value, so the results stay exact and no wait can last.
+constexpr int kSpThreads = 512;
+constexpr int kSpRowHold = 48;   // 16-byte chunks (8 bf16) held per thread: 192 VGPRs
+constexpr int kSp2dHold = 3;     // 16 x 8 bf16 units held per thread: 192 VGPRs
+
+// Max of |x| over n16 16-byte chunks of bf16 by the whole workgroup (the
+// fallback of a workgroup that gave up waiting at the grid barrier).
+__device__ __noinline__ float own_tensor_max(const uint16_t* x, int64_t n16) {
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x)
+    m = fmaxf(m, max8_bf16_bits(*reinterpret_cast<const uint4*>(x + i * 8)));
+  float m1 = 0.0f;
+  block_max2(m, m1);
+  return m;  // valid in thread 0
+}
+
+// Tensor amax from every workgroup's max m (all threads call it; the result
+// is returned to all).  x, n16: the tensor, for the fallback.  The workgroup
+// that completes the count writes the maximum and a go flag to every group's
+// go line; the others poll their group's go line (one 8-byte load gives flag
+// and maximum).
+__device__ __forceinline__ float grid_amax(float m, int slot, const uint16_t* x, int64_t n16,
+                                           uint64_t wait_ticks) {
+  __shared__ float bcast;
+  __shared__ int late;
+  float m1 = 0.0f;
+  block_max2(m, m1);
+  if (threadIdx.x == 0) {
+    Slot& s = g_slots[slot];
+    const unsigned int count = gridDim.x;
+    const unsigned int mx[1] = {__float_as_uint(m)};
+    bool ok = true;
+    unsigned long long word;
+    if (count_in(s, kArrive, count, 1, mx, false, nullptr)) {
+      word = (1ull << 32) | ld(&s.top.bits0);
+      const unsigned int groups = count < kGroups ? count : kGroups;
+      for (unsigned int k = 0; k < groups; k++)
+        __hip_atomic_store(reinterpret_cast<unsigned long long*>(&s.go[k].bits0), word,
+                           __ATOMIC_RELAXED, kAgent);
+    } else {
+      // Bounded by the real-time counter and, independently of it, by a poll
+      // count (s_sleep 2 between polls: at least 0.05 us each).
+      unsigned long long* go =
+          reinterpret_cast<unsigned long long*>(&s.go[blockIdx.x % kGroups].bits0);
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      const uint64_t max_polls = wait_ticks * 20 + 1;
+      uint64_t polls = 0;
+      for (;;) {
+        word = __hip_atomic_load(go, __ATOMIC_RELAXED, kAgent);
+        if (word >> 32) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks || ++polls > max_polls) {
+          ok = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    bcast = __uint_as_float((unsigned int)word);
+    late = ok ? 0 : 1;
+  }
+  __syncthreads();
+  if (late) {  // workgroup-uniform
+    const float a = own_tensor_max(x, n16);
+    if (threadIdx.x == 0) bcast = a;
+    __syncthreads();
+  }
+  return bcast;
+}
+
+// End of a single-pass kernel (thread 0 of every workgroup): the last
+// workgroup writes the caller's amax and g and clears the slot.  Every
+// workgroup has arrived by then, so the top line holds the final maximum.
+__device__ __forceinline__ void grid_finish(int slot, float* amax_out, float* gdec) {
+  if (threadIdx.x != 0) return;
+  Slot& s = g_slots[slot];
+  if (count_in(s, kDepart, gridDim.x, 0, nullptr, false, nullptr)) {
+    const float a = __uint_as_float(ld(&s.top.bits0));
+    *amax_out = a;
+    *gdec = tensor_scales(a).g;
+    slot_clear(s);
+  }
+}
+
+// ROW blocks.  Thread t of the grid (P threads) holds chunks t + j P, j <
+// kSpRowHold (consecutive lanes: consecutive 16-byte chunks; lanes 2t and
+// 2t+1 hold the two halves of a block, as in quant_row_kernel).  Loads and
+// stores go through buffer resources sized to the tensor: the per-lane part
+// of an offset is the thread's, the per-round part (j P) a wave-uniform
+// scalar, so no per-round address stays live in vector registers; chunks
+// past the end read zeros and their stores are dropped by the range check.
+// The tensor is at most a few hundred MB here (it fits in the registers), so
+// 32-bit byte offsets suffice.
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
+constexpr uint32_t kDropOff = 0x80000000u;  // past every range: the store is dropped
+
+template <bool kSR, bool kRHT>
+__global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
+    const uint16_t* __restrict__ x, int64_t chunks, int slot, float* __restrict__ amax_out,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
+    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds, uint64_t wait_ticks) {
+  __shared__ float rtab[128];
+  const uint32_t P = gridDim.x * kSpThreads;
+  const uint32_t wg0 = blockIdx.x * kSpThreads;  // first chunk of the workgroup, round 0
+  const uint32_t tid = threadIdx.x;
+  const int odd = (int)(tid & 1);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), 0, (int)(chunks * 16), kBufFlags);
+  uint4 q[kSpRowHold];
+#pragma unroll
+  for (int j = 0; j < kSpRowHold; j++)
+    q[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         xr, tid * 16, (int)((wg0 + j * P) * 16), 0));
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSpRowHold; j++) {
+    if (kRHT) {  // the amax is taken after the transform (chunks past the end are zeros)
+      float v[8];
+      RawRow<uint16_t>{q[j]}.all(v);
+      rht_signs_and_low_stages(v, mask, odd * 8);
+      rht_pair_stage8(v, odd);
+      m = fmaxf(m, max8(v));
+    } else {
+      m = fmaxf(m, max8_bf16_bits(q[j]));
+    }
+  }
+  // (with the transform the fallback's plain max would not be the amax: the
+  // transform is only used where the launch never takes this kernel)
+  const float A = grid_amax(m, slot, x, chunks, wait_ticks);
+  const TensorScales ts = tensor_scales(A);
+  build_recip_table(rtab, ts.S);
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc(codes, 0, (int)(chunks * 4), kBufFlags);
+  const __amdgpu_buffer_rsrc_t sr =
+      __builtin_amdgcn_make_buffer_rsrc(scales, 0, (int)(chunks / 2), kBufFlags);
+  const uint32_t s_off = odd ? kDropOff : tid / 2;  // even lanes store the block's scale
+#pragma unroll
+  for (int j = 0; j < kSpRowHold; j++) {
+    const uint32_t base = wg0 + j * P;  // wave-uniform
+    float v[8];
+    RawRow<uint16_t>{q[j]}.all(v);
+    if (kRHT) {
+      rht_signs_and_low_stages(v, mask, odd * 8);
+      rht_pair_stage8(v, odd);
+    }
+    const float mm = max8(v);
+    const uint32_t e = block_code(fmaxf(mm, xor1(mm)), ts.k);
+    const float r = rtab[e];
+    float y[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) y[u] = v[u] * r;
+    uint32_t packed = 0;
+    if (kSR) {
+      const Philox4 p = sr_call((uint64_t)(base + tid), seed, offset, rounds);
+#pragma unroll
+      for (int u = 0; u < 8; u++) packed |= e2m1_sr(y[u], sr_slot(p, u)) << (4 * u);
+    } else {
+      packed = pack8_rne(y);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(packed, cr, tid * 4, (int)(base * 4), 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e, sr, s_off, (int)(base / 2), 0);
+  }
+  grid_finish(slot, amax_out, gdec);
+}
+
+// 16x16 blocks of one bf16 matrix.  Thread t of the grid holds units t + j P
+// (16 rows x 8 columns, as in quant_2d_kernel; lanes 2t and 2t+1 hold the two
+// halves of a block).
+__global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
+    const uint16_t* __restrict__ w, int64_t rows, int64_t cols, int slot,
+    float* __restrict__ amax_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ gdec, uint64_t wait_ticks) {
+  __shared__ float rtab[128];
+  const int64_t P = (int64_t)gridDim.x * kSpThreads;
+  const int64_t t0 = (int64_t)blockIdx.x * kSpThreads + threadIdx.x;
+  const int64_t cg = cols / 8;  // a multiple of 4: pairs never straddle rows
+  const int64_t units = (rows / 16) * cg;
+  uint4 q[kSp2dHold][16];
+#pragma unroll
+  for (int j = 0; j < kSp2dHold; j++) {
+    const int64_t u = t0 + j * P;
+    const int64_t uc = u < units ? u : 0;
+    const int64_t g = uc / cg, c0 = (uc % cg) * 8;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      q[j][r] = u < units ? *reinterpret_cast<const uint4*>(w + (g * 16 + r) * cols + c0)
+                          : make_uint4(0, 0, 0, 0);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kSp2dHold; j++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) m = fmaxf(m, max8_bf16_bits(q[j][r]));
+  const float A = grid_amax(m, slot, w, rows * cols / 8, wait_ticks);
+  const TensorScales ts = tensor_scales(A);
+  build_recip_table(rtab, ts.S);
+#pragma unroll
+  for (int j = 0; j < kSp2dHold; j++) {
+    const int64_t u = t0 + j * P;
+    if (u >= units) break;  // units and P are even: the lanes of a pair agree
+    const int64_t g = u / cg, c0 = (u % cg) * 8;
+    float bm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, max8_bf16_bits(q[j][r]));
+    bm = fmaxf(bm, xor1(bm));
+    const uint32_t e = block_code(bm, ts.k);
+    const float rcp = rtab[e];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      float v[8], y[8];
+      RawRow<uint16_t>{q[j][r]}.all(v);
+#pragma unroll
+      for (int k = 0; k < 8; k++) y[k] = v[k] * rcp;
+      *reinterpret_cast<uint32_t*>(codes + (g * 16 + r) * (cols / 2) + c0 / 2) = pack8_rne(y);
+    }
+    if (((u % cg) & 1) == 0) scales[g * (cols / 16) + c0 / 16] = (uint8_t)e;
+  }
+  grid_finish(slot, amax_out, gdec);
 }
 
 // ---- standalone transform ------------------------------------------------------------------
@@ -910,6 +1279,32 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint32_t* __res
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The next scratch slot (round robin over kSlots).
+// How long a single-pass kernel's workgroups wait at the grid barrier before
+// each takes the tensor maximum on its own, in microseconds; negative: the
+// single-pass kernels are not used.
+std::atomic<int> g_single_pass_wait_us{2000};
+
+int next_slot() {
+  static std::atomic<unsigned int> counter{0};
+  return (int)(counter.fetch_add(1u, std::memory_order_relaxed) % kSlots);
+}
+
+// Compute units of the current device (the single-pass grid: one workgroup
+// per CU), cached per device.
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Workgroups of an amax pass: one per kAmaxThreads * unroll units, capped
 // near the CU count (the kernels loop over the rest) to keep the atomics few.
 int amax_grid(int64_t units, int unroll, int64_t cap = 512) {
@@ -938,13 +1333,29 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
           x, chunks, a.amax, a.amax_is_input, cd, a.scales, a.gdec, 0, 0, 0, rs, cpr);
     return hipGetLastError();
   }
+  if constexpr (!G && !std::is_same<T, float>::value) {
+    // Single pass when the tensor fits in the grid's registers.
+    const int64_t chunks = a.rows * a.cols / 8;
+    const int cus = device_cu_count();
+    // (RNE without the transform: with stochastic rounding or the transform
+    // the compiler does not keep the held chunks in registers.)
+    const int wait_us = g_single_pass_wait_us.load(std::memory_order_relaxed);
+    if (a.axis == kBlockRow && !a.sr && !a.rht && !a.amax_is_input && cus > 0 && wait_us >= 0 &&
+        chunks <= (int64_t)cus * kSpThreads * kSpRowHold) {
+      quant_row_1pass_kernel<false, false><<<cus, kSpThreads, 0, st>>>(
+          reinterpret_cast<const uint16_t*>(x), chunks, next_slot(), a.amax,
+          reinterpret_cast<uint32_t*>(a.codes), a.scales, a.gdec, 0, 0, 0, 0,
+          (uint64_t)wait_us * 100u);
+      return hipGetLastError();
+    }
+  }
   if (!a.amax_is_input) {
-    fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 1);
+    const int slot = next_slot();
     if (a.axis == kBlockCol && a.rht) {
       int64_t units = (a.rows / 16) * (a.cols / 8);
       amax_col_rht_kernel<T, false, G>
           <<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads, 0, st>>>(
-              x, a.rows, a.cols, a.mask, a.amax, nullptr, rs);
+              x, a.rows, a.cols, a.mask, a.amax, nullptr, slot, rs);
     } else {
       int64_t chunks = a.rows * a.cols / 8;
       // ROW with the transform needs the pair exchange; COL amax without the
@@ -952,10 +1363,10 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
       const int u = (!a.x_fp32 && !(a.rht && a.axis == kBlockRow)) ? kAmaxUnroll : 2;
       if (a.rht && a.axis == kBlockRow)
         amax_flat_kernel<T, true, G><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-            x, chunks, a.mask, a.amax, nullptr, rs, cpr);
+            x, chunks, a.mask, a.amax, nullptr, slot, rs, cpr);
       else
         amax_flat_kernel<T, false, G><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-            x, chunks, 0, a.amax, nullptr, rs, cpr);
+            x, chunks, 0, a.amax, nullptr, slot, rs, cpr);
     }
   }
   if (a.axis == kBlockRow) {
@@ -990,14 +1401,32 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
 template <typename T>
 hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
   const T* w = static_cast<const T*>(a.w);
+  if constexpr (!std::is_same<T, float>::value) {
+    // Single pass when one matrix fits in the grid's registers.
+    const int64_t units = (a.rows / 16) * (a.cols / 8);
+    const int cus = device_cu_count();
+    const int wait_us = g_single_pass_wait_us.load(std::memory_order_relaxed);
+    if (a.batch == 1 && !a.amax_is_input && cus > 0 && wait_us >= 0 &&
+        units <= (int64_t)cus * kSpThreads * kSp2dHold) {
+      quant_2d_1pass_kernel<<<cus, kSpThreads, 0, st>>>(
+          reinterpret_cast<const uint16_t*>(w), a.rows, a.cols, next_slot(), a.amax, a.codes,
+          a.scales, a.gdec, (uint64_t)wait_us * 100u);
+      return hipGetLastError();
+    }
+  }
   if (!a.amax_is_input) {
-    fill_zero_kernel<<<(unsigned)cdiv(a.batch, 256), 256, 0, st>>>(a.amax, a.batch);
     int64_t chunks = a.rows * a.cols / 8;
     const int u = a.w_fp32 ? 2 : kAmaxUnroll;
-    // about 512 workgroups in all, at least one per slice
-    const int64_t per = a.batch >= 512 ? 1 : 512 / a.batch;
-    dim3 grid((unsigned)amax_grid(chunks, u, per), (unsigned)a.batch);
-    amax_flat_kernel<T, false><<<grid, kAmaxThreads, 0, st>>>(w, chunks, 0, a.amax, nullptr);
+    if (a.batch == 1) {
+      amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
+          w, chunks, 0, a.amax, nullptr, next_slot());
+    } else {  // one maximum per slice: straight into the cleared outputs
+      fill_zero_kernel<<<(unsigned)cdiv(a.batch, 256), 256, 0, st>>>(a.amax, a.batch);
+      // about 512 workgroups in all, at least one per slice
+      const int64_t per = a.batch >= 512 ? 1 : 512 / a.batch;
+      dim3 grid((unsigned)amax_grid(chunks, u, per), (unsigned)a.batch);
+      amax_flat_kernel<T, false><<<grid, kAmaxThreads, 0, st>>>(w, chunks, 0, a.amax, nullptr, -1);
+    }
   }
   int64_t units = (a.rows / 16) * (a.cols / 8);
   dim3 grid((unsigned)cdiv(units, kThreads), (unsigned)a.batch);
@@ -1030,27 +1459,26 @@ hipError_t launch_quantize_dual_t(const QuantDualArgs& a, hipStream_t st) {
     rs.src_rows = a.src_rows;
   }
   const int64_t units = (a.rows / 16) * (a.cols / 8);
+  const int slot = next_slot();
   if (!a.amax_is_input) {
-    fill_zero_kernel<<<1, 64, 0, st>>>(a.amax, 2);
     if (a.rht) {  // transform max for COL, plain max for ROW, one read
       amax_col_rht_kernel<T, true, G>
           <<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads, 0, st>>>(
-              x, a.rows, a.cols, a.mask, a.amax + 1, a.amax, rs);
+              x, a.rows, a.cols, a.mask, a.amax + 1, a.amax, slot, rs);
     } else {  // the same plain max for both
       const int64_t chunks = a.rows * a.cols / 8;
       const int u = a.x_fp32 ? 2 : kAmaxUnroll;
       amax_flat_kernel<T, false, G><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-          x, chunks, 0, a.amax, a.amax + 1, rs, (uint32_t)(a.cols / 8));
+          x, chunks, 0, a.amax, a.amax + 1, slot, rs, (uint32_t)(a.cols / 8));
     }
   }
-  if (a.zeros) fill_zero_kernel<<<1, 64, 0, st>>>(reinterpret_cast<float*>(a.zeros), 4);
   const int grid = (int)cdiv(units, kThreads);
   uint32_t* rc = reinterpret_cast<uint32_t*>(a.row_codes);
 #define NVFP4_DUAL(RHT)                                                                       \
   quant_dual_kernel<T, RHT, G><<<grid, kThreads, 0, st>>>(                                    \
       x, a.rows, a.cols, a.amax, rc, a.row_scales, a.row_gdec, a.col_codes, a.col_scales,     \
       a.col_gdec, a.mask, a.seed_r, a.offset_r, a.rounds_r, a.seed_c, a.offset_c, a.rounds_c, \
-      a.zeros, rs)
+      a.zeros, slot, rs)
   if (a.rht) NVFP4_DUAL(true);
   else NVFP4_DUAL(false);
 #undef NVFP4_DUAL
@@ -1064,10 +1492,9 @@ hipError_t launch_quantize_mse_t(const void* xv, int64_t rows, int64_t cols, boo
   const T* x = static_cast<const T*>(xv);
   const int64_t chunks = rows * cols / 8;
   if (!amax_is_input) {
-    fill_zero_kernel<<<1, 64, 0, st>>>(amax, 1);
     const int u = x_fp32 ? 2 : kAmaxUnroll;
     amax_flat_kernel<T, false><<<dim3(amax_grid(chunks, u), 1), kAmaxThreads, 0, st>>>(
-        x, chunks, 0, amax, nullptr);
+        x, chunks, 0, amax, nullptr, next_slot());
   }
   const int64_t blocks = rows * cols / 16;
   const int grid = (int)cdiv(blocks, (int64_t)kThreads);
@@ -1078,6 +1505,10 @@ hipError_t launch_quantize_mse_t(const void* xv, int64_t rows, int64_t cols, boo
 }
 
 }  // namespace
+
+int set_single_pass_wait_us(int us) {
+  return g_single_pass_wait_us.exchange(us < 0 ? -1 : us, std::memory_order_relaxed);
+}
 
 hipError_t launch_quantize_mse(const void* x, bool x_fp32, int64_t rows, int64_t cols,
                                float* amax, bool amax_is_input, uint8_t* codes, uint8_t* scales,

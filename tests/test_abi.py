@@ -219,3 +219,12 @@ def test_quantize_mse_validation(lib):
     assert f(None, 0, 64, 64, FAKE, 0, FAKE, FAKE, FAKE, None) == -1
     assert f(FAKE, 0, 64, 64, FAKE, 0, C.c_void_p(0x100008), FAKE, FAKE, None) == -3
     assert f(FAKE, 0, 0, 64, None, 0, None, None, None, None) == 0
+
+
+def test_single_pass_wait_setting(lib):
+    """The single-pass tuning knob is host state only: it returns the previous
+    setting, and any negative value reads back as -1 (off)."""
+    prev = lib.nvfp4_set_single_pass_wait(123)
+    assert lib.nvfp4_set_single_pass_wait(-7) == 123
+    assert lib.nvfp4_set_single_pass_wait(0) == -1
+    assert lib.nvfp4_set_single_pass_wait(prev) == 0

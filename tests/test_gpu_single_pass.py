@@ -1,0 +1,176 @@
+"""GPU parity of the single-pass quantizers and of the per-call scratch slots
+that replace a cleared amax output.
+
+* Single pass (bf16 ROW RNE without transform, one bf16 16x16-blocked
+  matrix): bit-exact against the oracle on both sides of the size limit (the
+  largest tensor the grid's registers hold, and one row group more, which
+  takes the two-pass path), equal to the two-pass path, and exact when the
+  grid barrier's wait is forced to give up (every late workgroup takes the
+  tensor maximum by itself) and when two streams run single-pass calls at
+  the same time.
+* Slots: hundreds of calls in a row, more than the slots, with tensor maxima
+  going up and down (a slot left dirty would hand a stale, larger maximum to
+  a later call), and repeated dual quantizations whose zero-code counts must
+  not accumulate across calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_block_scaled_07_amd as nv
+import oracle as O
+from nvfp4_block_scaled_07_amd import synth
+from _gpu import assert_same, device, make_input, to_np
+
+pytestmark = pytest.mark.gpu
+
+THREADS, ROW_HOLD, UNITS_HOLD = 512, 48, 3  # the single-pass kernels' capacity per CU
+
+
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _bf16(x, dev):
+    t = synth.to_bf16(x)
+    return t.to(dev), synth.bf16_bits(t)
+
+
+def _check(q, ref):
+    got = to_np(q)
+    assert_same(got["amax"][0], ref["amax"], "amax")
+    assert_same(np.float32(got["g"]), ref["g"], "g")
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+
+
+def _same(a, b):
+    for f in ("codes", "scales", "global_dec", "amax"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+@pytest.mark.parametrize("extra_rows", [0, 16])
+def test_row_single_pass_size_limit(extra_rows):
+    """Rows of 4096: the largest ROW tensor held in registers (single pass)
+    and 16 rows more (two passes), both against the oracle."""
+    dev = device()
+    rows = _cus() * THREADS * ROW_HOLD * 8 // 4096 + extra_rows
+    x = make_input("normal", (rows, 4096), seed=600 + extra_rows)
+    t, xo = _bf16(x, dev)
+    _check(nv.quantize_1d(t, "row"), O.quantize(xo, "row"))
+
+
+@pytest.mark.parametrize("extra_rows", [0, 16])
+def test_2d_single_pass_size_limit(extra_rows):
+    dev = device()
+    rows = 16 * _cus() * THREADS * UNITS_HOLD // (4096 // 8) + extra_rows
+    x = make_input("normal", (rows, 4096), seed=610 + extra_rows) * np.float32(0.02)
+    t, xo = _bf16(x, dev)
+    _check(nv.quantize_2d(t), O.quantize(xo, "2d"))
+
+
+@pytest.mark.parametrize("shape", [(66, 1024), (2000, 6144), (4096, 4160), (1024, 32)])
+def test_single_pass_equals_two_pass(shape):
+    """The same bits with the single-pass kernels turned off (tensors of
+    several sizes, ragged against the grid)."""
+    dev = device()
+    x = make_input("laplace_zeros", shape, seed=shape[0])
+    t, xo = _bf16(x, dev)
+    w = t[: shape[0] // 16 * 16]
+    one_r, one_w = nv.quantize_1d(t, "row"), nv.quantize_2d(w)
+    prev = nv.nvfp4_set_single_pass_wait(-1)
+    try:
+        two_r, two_w = nv.quantize_1d(t, "row"), nv.quantize_2d(w)
+    finally:
+        nv.nvfp4_set_single_pass_wait(prev)
+    _same(one_r, two_r)
+    _same(one_w, two_w)
+    _check(one_r, O.quantize(xo, "row"))
+
+
+def test_single_pass_barrier_gives_up():
+    """With no wait at the grid barrier, workgroups that find it incomplete
+    read the whole tensor for the maximum: the results are still exact."""
+    dev = device()
+    x = make_input("normal", (2000, 6144), seed=620)
+    t, xo = _bf16(x, dev)
+    w = t[:1984]
+    prev = nv.nvfp4_set_single_pass_wait(0)
+    try:
+        qr, qw = nv.quantize_1d(t, "row"), nv.quantize_2d(w)
+        torch.cuda.synchronize()
+    finally:
+        nv.nvfp4_set_single_pass_wait(prev)
+    _check(qr, O.quantize(xo, "row"))
+    _check(qw, O.quantize(xo[:1984], "2d"))
+
+
+def test_single_pass_on_two_streams():
+    """Single-pass calls issued on two streams at once (each may find CUs
+    held by the other's workgroups) give the single-stream results."""
+    dev = device()
+    xs = [_bf16(make_input("normal", (2048, 6144), seed=630 + i) * np.float32(1 + i), dev)[0]
+          for i in range(2)]
+    ref = [nv.quantize_1d(x, "row") for x in xs] + [nv.quantize_2d(x) for x in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    out = []
+    for rep in range(4):
+        for i, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                out.append((i, nv.quantize_1d(xs[i], "row", stream=s),
+                            nv.quantize_2d(xs[i], stream=s)))
+    torch.cuda.synchronize()
+    for i, qr, qw in out:
+        _same(qr, ref[i])
+        _same(qw, ref[2 + i])
+
+
+def test_slots_reused_and_cleared():
+    """600 end-to-end calls (more than the slots), single-pass and two-pass,
+    ROW, 2D and COL, with the tensor maximum scaled by powers of two up and
+    down between calls: every call's amax is its own tensor's (exact: a
+    power-of-two scale scales the maximum exactly)."""
+    dev = device()
+    base = [make_input("normal", (66, 1024), seed=640),           # ROW single pass (bf16)
+            make_input("normal", (256, 1024), seed=641)]          # two-pass (fp32)
+    amax0 = [float(O.amax(synth.bf16_bits(synth.to_bf16(base[0])), "row")),
+             float(O.amax(base[1], "row"))]
+    t_bf = synth.to_bf16(base[0]).to(dev)
+    t_32 = torch.from_numpy(base[1]).to(dev)
+    for i in range(600):
+        k = (i * 7) % 11 - 5                   # scale 2^k, k in -5 .. 5
+        f = float(2.0 ** k)
+        kind = i % 4
+        if kind == 0:
+            q, want = nv.quantize_1d(t_bf * f, "row"), amax0[0] * f
+        elif kind == 1:
+            q, want = nv.quantize_1d(t_32 * f, "row"), amax0[1] * f
+        elif kind == 2:
+            q, want = nv.quantize_2d(t_bf[:64] * f), None
+        else:
+            q, want = nv.quantize_1d(t_32 * f, "col"), amax0[1] * f
+        got = float(q.amax.item())
+        if want is not None:
+            assert got == np.float32(want), (i, got, want)
+        else:
+            want2d = float(O.amax(synth.bf16_bits(synth.to_bf16(base[0][:64])), "row")) * f
+            assert got == np.float32(want2d), (i, got, want2d)
+
+
+def test_dual_zero_counts_do_not_accumulate():
+    """The dual quantizer's zero-code counts go through the call's slot: the
+    same input gives the same counts call after call, equal to the oracle's
+    count of its codes."""
+    dev = device()
+    x = make_input("laplace_zeros", (512, 1024), seed=650)
+    t, xo = _bf16(x, dev)
+    mask = 0x5A3C
+    counts = []
+    for rep in range(5):
+        qr, qc, z = nv.quantize_dual(t, nv.Philox(11), nv.Philox(12), mask)
+        counts.append(z.cpu().tolist())
+    assert all(c == counts[0] for c in counts)
+    rr = O.quantize(xo, "row", rounding=O.SR, seed=11)
+    rc = O.quantize(xo, "col", rounding=O.SR, seed=12, rht_mask=mask)
+    assert counts[0] == [O.zero_codes(rr["codes"]), O.zero_codes(rc["codes"])]
