@@ -77,27 +77,35 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
 }
 
 // Stochastic rounding: lo = largest grid value <= |y|, round up iff
-// u16 < 65536 * (|y| - lo) / step, |y| >= 6 saturating.  Computed without
-// branches (both candidates, then selects):
-//  * [1, 6) from the fp32 bits F of |y|: lo's code is (F >> 22) - 252
-//    (exponent and the top mantissa bit) and 65536 * (|y| - lo) / step is the
-//    22 lower mantissa bits over 64;
-//    Above 6 the same formula gives a code of at least 7 (F >> 22 is at most
-//    511), so the saturation is a min;
-//  * [0, 1), where the grid step is 0.5: with t = 2|y| (exact), lo's code is
-//    [t >= 1] and the fraction is t - [t >= 1] (exact), scaled by 65536
-//    (exact) and compared with u16 as floats.
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16) {
-  const uint32_t bits = __float_as_uint(y);
-  const uint32_t F = bits & 0x7FFFFFFFu;
-  const uint32_t hi = ((F >> 22) - 252u) + ((u16 << 6) < (F & 0x3FFFFFu) ? 1u : 0u);
-  const float t = __uint_as_float(F) * 2.0f;
-  const bool t1 = t >= 1.0f;
-  const float frac = t1 ? t - 1.0f : t;
-  const uint32_t lo = (t1 ? 1u : 0u) + ((float)u16 < frac * 65536.0f ? 1u : 0u);
-  const uint32_t code = F >= 0x3F800000u ? __builtin_elementwise_min(hi, 7u) : lo;
-  return code | ((bits >> 28) & 8u);
+// u16 < 65536 * (|y| - lo) / step, |y| >= 6 saturating.  sr_value returns
+// the chosen grid value (sign of y), which the hardware conversion (round to
+// nearest) then encodes exactly.
+//
+// Worked on B = bits(|y| * 2^-126).  That scaling moves E2M1's boundary
+// between its subnormal and normal values (1.0) onto fp32's (2^-126), so for
+// every |y| the bits of B from 22 up hold lo's code and the 22 bits below
+// hold (|y| - lo) / step as a binary fraction.  For |y| >= 1 the multiply is
+// exact (only the exponent moves); for |y| < 1, B is |y| * 2^23 in fixed
+// point, rounded to nearest by the multiply and raised by one where that
+// rounding went down (B * 2^126 < |y|, exact test), so B is the ceiling, which
+// is what the comparison with a multiple of 64 needs.  The rule's test
+// u16 * 64 < (B & 0x3FFFFF) holds exactly when adding
+// a = (65535 - u16) * 64 + 63 carries into bit 22, so bits 22 and up of B + a
+// hold the chosen code; capped at code 7 (6.0) and scaled back by 2^126
+// (exact), they are the chosen value.
+__device__ __forceinline__ float sr_value(float y, uint32_t a) {
+  const float m = __builtin_fabsf(y);
+  const float ms = m * 0x1p-126f;
+  const uint32_t below = ms * 0x1p126f < m ? 1u : 0u;
+  uint32_t s = (__float_as_uint(ms) + a + below) & 0xFFC00000u;
+  s = __builtin_elementwise_min(s, 7u << 22);
+  return __uint_as_float(s | (__float_as_uint(y) & 0x80000000u)) * 0x1p126f;
 }
+
+// The addend a of 16-bit slot 2q (low half of Philox word w) and of slot
+// 2q + 1 (high half).
+__device__ __forceinline__ uint32_t sr_addend_lo(uint32_t w) { return ((~w & 0xFFFFu) << 6) | 63u; }
+__device__ __forceinline__ uint32_t sr_addend_hi(uint32_t w) { return ((~w >> 16) << 6) | 63u; }
 
 // ---- Philox4x32 ----------------------------------------------------------------------
 struct Philox4 {
@@ -141,6 +149,16 @@ __device__ __forceinline__ Philox4 sr_call(uint64_t n, uint64_t seed, uint64_t o
 __device__ __forceinline__ uint32_t sr_slot(const Philox4& p, int t) {
   uint32_t w = (t >> 1) == 0 ? p.x : (t >> 1) == 1 ? p.y : (t >> 1) == 2 ? p.z : p.w;
   return (t & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// y[t] -> its stochastically rounded grid value, slot t of the call p.
+__device__ __forceinline__ void sr_values8(float y[8], const Philox4& p) {
+  const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    y[2 * q] = sr_value(y[2 * q], sr_addend_lo(w[q]));
+    y[2 * q + 1] = sr_value(y[2 * q + 1], sr_addend_hi(w[q]));
+  }
 }
 
 // ---- 16-point Hadamard butterflies -----------------------------------------------

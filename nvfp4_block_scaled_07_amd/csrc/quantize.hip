@@ -501,14 +501,8 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
     float y[8];
 #pragma unroll
     for (int t = 0; t < 8; t++) y[t] = v[u][t] * r;
-    uint32_t packed = 0;
-    if (kSR) {
-      Philox4 p = sr_call((uint64_t)i, seed, offset, rounds);
-#pragma unroll
-      for (int t = 0; t < 8; t++) packed |= e2m1_sr(y[t], sr_slot(p, t)) << (4 * t);
-    } else {
-      packed = pack8_rne(y);
-    }
+    if (kSR) sr_values8(y, sr_call((uint64_t)i, seed, offset, rounds));
+    const uint32_t packed = pack8_rne(y);
     codes[i] = packed;
     if (!odd) scales[i >> 1] = (uint8_t)e;
   }
@@ -589,14 +583,8 @@ __global__ __launch_bounds__(kSmallThreads) void quant_row_small_kernel(
     float y[8];
 #pragma unroll
     for (int t = 0; t < 8; t++) y[t] = v[u][t] * r;
-    uint32_t packed = 0;
-    if (kSR) {
-      Philox4 p = sr_call((uint64_t)i, seed, offset, rounds);
-#pragma unroll
-      for (int t = 0; t < 8; t++) packed |= e2m1_sr(y[t], sr_slot(p, t)) << (4 * t);
-    } else {
-      packed = pack8_rne(y);
-    }
+    if (kSR) sr_values8(y, sr_call((uint64_t)i, seed, offset, rounds));
+    const uint32_t packed = pack8_rne(y);
     codes[i] = packed;
     if (!(i & 1)) scales[i >> 1] = (uint8_t)e;
   }
@@ -762,23 +750,17 @@ __device__ __forceinline__ void col_encode(const RawRow<T> (&raw)[16], int64_t r
       sc[cp >> 1] |= e << (8 * (c & 3));
 #pragma unroll
       for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp;
-      if (kSR) {
+      if (kSR) {  // rows 0..7 take call 2 * block, rows 8..15 call 2 * block + 1
         const uint64_t blk = (uint64_t)(c0 + c) * (uint64_t)(rows / 16) + (uint64_t)g;
-        const Philox4 p0 = sr_call(2 * blk, seed, offset, rounds);
-        const Philox4 p1 = sr_call(2 * blk + 1, seed, offset, rounds);
-#pragma unroll
-        for (int r = 0; r < 8; r++) out[r] |= e2m1_sr(col[h][r], sr_slot(p0, r)) << (4 * c);
-#pragma unroll
-        for (int r = 0; r < 8; r++)
-          out[r + 8] |= e2m1_sr(col[h][r + 8], sr_slot(p1, r)) << (4 * c);
+        sr_values8(col[h], sr_call(2 * blk, seed, offset, rounds));
+        sr_values8(col[h] + 8, sr_call(2 * blk + 1, seed, offset, rounds));
       }
     }
-    if (!kSR) {
+    // RNE, or (after stochastic rounding) the exact conversion of grid values.
 #pragma unroll
-      for (int r = 0; r < 16; r++)
-        out[r] |= __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0)
-                  << (8 * cp);
-    }
+    for (int r = 0; r < 16; r++)
+      out[r] |= __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0)
+                << (8 * cp);
   }
 }
 
@@ -892,10 +874,10 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(
     const uint32_t e = block_code(fmaxf(m, xor1(m)), tr.k);
     const float rc = rtab_r[e];
     const int64_t chunk = (g * 16 + r) * cg + c0 / 8;
-    const Philox4 p = sr_call((uint64_t)chunk, seed_r, offset_r, rounds_r);
-    uint32_t packed = 0;
 #pragma unroll
-    for (int t = 0; t < 8; t++) packed |= e2m1_sr(v[t] * rc, sr_slot(p, t)) << (4 * t);
+    for (int t = 0; t < 8; t++) v[t] = v[t] * rc;
+    sr_values8(v, sr_call((uint64_t)chunk, seed_r, offset_r, rounds_r));
+    const uint32_t packed = pack8_rne(v);
     if (active) {
       row_codes[chunk] = packed;
       if (even) row_scales[(g * 16 + r) * (cols / 16) + c0 / 16] = (uint8_t)e;
@@ -1132,14 +1114,8 @@ __global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
     float y[8];
 #pragma unroll
     for (int u = 0; u < 8; u++) y[u] = v[u] * r;
-    uint32_t packed = 0;
-    if (kSR) {
-      const Philox4 p = sr_call((uint64_t)(base + tid), seed, offset, rounds);
-#pragma unroll
-      for (int u = 0; u < 8; u++) packed |= e2m1_sr(y[u], sr_slot(p, u)) << (4 * u);
-    } else {
-      packed = pack8_rne(y);
-    }
+    if (kSR) sr_values8(y, sr_call((uint64_t)(base + tid), seed, offset, rounds));
+    const uint32_t packed = pack8_rne(y);
     __builtin_amdgcn_raw_buffer_store_b32(packed, cr, tid * 4, (int)(base * 4), 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e, sr, s_off, (int)(base / 2), 0);
   }
