@@ -32,7 +32,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <cstddef>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -134,7 +133,7 @@ __device__ __forceinline__ uint32_t block_code(float a, float k) {
 
 // 8 values (already multiplied by the block reciprocal) -> 8 RNE codes.
 __device__ __forceinline__ uint32_t pack8_rne(const float y[8]) {
-  uint32_t w = 0;
+  uint32_t w = __float_as_uint(y[0]);  // any start value: the four conversions write every byte
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
@@ -163,26 +162,18 @@ constexpr int kAmaxThreads = 1024;
 // Same-address atomics serialize (about 20-25 ns each here), so a slot is
 // two-level: workgroup b counts in at group line b % 8 (the XCD it runs on),
 // and the last of each group carries the group's maxima and counts up to the
-// top line.  A line sees at most a few dozen atomics.  Single-pass kernels
-// also wait on go lines (one per group, written once by the last arrival),
-// which keeps their polling off the lines that take the atomics.
+// top line.  A line sees at most a few dozen atomics.
 struct alignas(128) Line {
-  // bits0 and arrive share one 8-byte word: a go line holds the maximum and
-  // its flag there, read together in one load.
   unsigned int bits0;           // running maximum
-  unsigned int arrive;          // workgroups counted in (go line: 1 = go)
+  unsigned int arrive;          // workgroups counted in
   unsigned int bits1;           // second running maximum
-  unsigned int depart;          // workgroups done (single-pass kernels)
   unsigned int done;            // workgroups that added their zero-code counts
-  unsigned int pad;
   unsigned long long zeros[2];  // zero-code counts (dual quantizer)
 };
-static_assert(offsetof(Line, arrive) == offsetof(Line, bits0) + 4, "flag above the maximum");
 constexpr int kGroups = 8;
 struct Slot {
   Line group[kGroups];
   Line top;
-  Line go[kGroups];
 };
 constexpr int kSlots = 256;
 __device__ Slot g_slots[kSlots];
@@ -212,9 +203,9 @@ __device__ __forceinline__ void raise_max(unsigned int* p, unsigned int v) {
 }
 
 // Counter fields of a line.
-enum Field { kArrive, kDepart, kDone };
+enum Field { kArrive, kDone };
 __device__ __forceinline__ unsigned int* field(Line& l, Field f) {
-  return f == kArrive ? &l.arrive : f == kDepart ? &l.depart : &l.done;
+  return f == kArrive ? &l.arrive : &l.done;
 }
 
 // Counts workgroup blockIdx.x (of `count`) in on field f: at its group
@@ -250,11 +241,10 @@ __device__ __forceinline__ bool count_in(Slot& s, Field f, unsigned int count, i
 // Zeroes every line of a slot (by the workgroup that completed its use).
 __device__ __forceinline__ void slot_clear(Slot& s) {
   Line* l = &s.group[0];
-  for (int i = 0; i < 2 * kGroups + 1; i++) {
-    __hip_atomic_store(reinterpret_cast<unsigned long long*>(&l[i].bits0), 0ull,
-                       __ATOMIC_RELAXED, kAgent);
+  for (int i = 0; i < kGroups + 1; i++) {
+    st(&l[i].bits0, 0u);
+    st(&l[i].arrive, 0u);
     st(&l[i].bits1, 0u);
-    st(&l[i].depart, 0u);
     st(&l[i].done, 0u);
     __hip_atomic_store(&l[i].zeros[0], 0ull, __ATOMIC_RELAXED, kAgent);
     __hip_atomic_store(&l[i].zeros[1], 0ull, __ATOMIC_RELAXED, kAgent);
@@ -980,49 +970,71 @@ __device__ __noinline__ float own_tensor_max(const uint16_t* x, int64_t n16) {
   return m;  // valid in thread 0
 }
 
+// The grid barrier is a board: one 8-byte entry per workgroup, holding
+// (epoch << 32) | the workgroup's maximum (fp32 bits), written with a single
+// store; every workgroup then reads all the entries until each carries the
+// call's epoch, and takes the largest maximum.  No read-modify-write atomics
+// (same-address atomics serialize) and nothing to clear: the host gives each
+// call a board (round robin over kSlots) and an epoch that no earlier use of
+// that board had, so entries left by earlier calls never match.  Relaxed
+// device-scope loads and stores are coherent across the XCDs on their own.
+constexpr int kBoardMax = 256;  // workgroups (one per CU) a board holds
+__device__ unsigned long long g_board[kSlots][kBoardMax];
+
 // Tensor amax from every workgroup's max m (all threads call it; the result
-// is returned to all).  x, n16: the tensor, for the fallback.  The workgroup
-// that completes the count writes the maximum and a go flag to every group's
-// go line; the others poll their group's go line (one 8-byte load gives flag
-// and maximum).
-__device__ __forceinline__ float grid_amax(float m, int slot, const uint16_t* x, int64_t n16,
-                                           uint64_t wait_ticks) {
+// is returned to all).  Wave 0 polls the board, bounded by wait_ticks of the
+// real-time counter and, independently of it, by a poll count (s_sleep 2
+// between polls: at least 0.05 us each).  x, n16: the tensor, for the
+// fallback of a workgroup that gives up.
+__device__ __forceinline__ float grid_amax(float m, int slot, uint32_t epoch, const uint16_t* x,
+                                           int64_t n16, uint64_t wait_ticks) {
   __shared__ float bcast;
   __shared__ int late;
   float m1 = 0.0f;
   block_max2(m, m1);
-  if (threadIdx.x == 0) {
-    Slot& s = g_slots[slot];
-    const unsigned int count = gridDim.x;
-    const unsigned int mx[1] = {__float_as_uint(m)};
+  unsigned long long* board = g_board[slot];
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&board[blockIdx.x], ((unsigned long long)epoch << 32) | __float_as_uint(m),
+                       __ATOMIC_RELAXED, kAgent);
+  if (threadIdx.x < 64) {
+    const unsigned int n = gridDim.x;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t max_polls = wait_ticks * 20 + 1;
+    uint64_t polls = 0;
+    unsigned int mx;
     bool ok = true;
-    unsigned long long word;
-    if (count_in(s, kArrive, count, 1, mx, false, nullptr)) {
-      word = (1ull << 32) | ld(&s.top.bits0);
-      const unsigned int groups = count < kGroups ? count : kGroups;
-      for (unsigned int k = 0; k < groups; k++)
-        __hip_atomic_store(reinterpret_cast<unsigned long long*>(&s.go[k].bits0), word,
-                           __ATOMIC_RELAXED, kAgent);
-    } else {
-      // Bounded by the real-time counter and, independently of it, by a poll
-      // count (s_sleep 2 between polls: at least 0.05 us each).
-      unsigned long long* go =
-          reinterpret_cast<unsigned long long*>(&s.go[blockIdx.x % kGroups].bits0);
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      const uint64_t max_polls = wait_ticks * 20 + 1;
-      uint64_t polls = 0;
-      for (;;) {
-        word = __hip_atomic_load(go, __ATOMIC_RELAXED, kAgent);
-        if (word >> 32) break;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks || ++polls > max_polls) {
-          ok = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+    for (;;) {
+      // All of a lane's loads in flight at once (indices past the grid
+      // re-read the last entry).
+      unsigned long long e[kBoardMax / 64];
+#pragma unroll
+      for (int j = 0; j < kBoardMax / 64; j++) {
+        const unsigned int k = threadIdx.x + 64u * j;
+        e[j] = __hip_atomic_load(&board[k < n ? k : n - 1], __ATOMIC_RELAXED, kAgent);
       }
+      bool ready = true;
+      mx = 0;
+#pragma unroll
+      for (int j = 0; j < kBoardMax / 64; j++) {
+        ready = ready && (unsigned int)(e[j] >> 32) == epoch;
+        mx = mx > (unsigned int)e[j] ? mx : (unsigned int)e[j];
+      }
+      if (__all(ready)) break;  // wave-uniform
+      if (__builtin_amdgcn_s_memrealtime() - t0 > wait_ticks || ++polls > max_polls) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
     }
-    bcast = __uint_as_float((unsigned int)word);
-    late = ok ? 0 : 1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned int other = (unsigned int)__shfl_xor((int)mx, o);
+      mx = mx > other ? mx : other;
+    }
+    if (threadIdx.x == 0) {
+      bcast = __uint_as_float(mx);
+      late = ok ? 0 : 1;
+    }
   }
   __syncthreads();
   if (late) {  // workgroup-uniform
@@ -1033,17 +1045,12 @@ __device__ __forceinline__ float grid_amax(float m, int slot, const uint16_t* x,
   return bcast;
 }
 
-// End of a single-pass kernel (thread 0 of every workgroup): the last
-// workgroup writes the caller's amax and g and clears the slot.  Every
-// workgroup has arrived by then, so the top line holds the final maximum.
-__device__ __forceinline__ void grid_finish(int slot, float* amax_out, float* gdec) {
-  if (threadIdx.x != 0) return;
-  Slot& s = g_slots[slot];
-  if (count_in(s, kDepart, gridDim.x, 0, nullptr, false, nullptr)) {
-    const float a = __uint_as_float(ld(&s.top.bits0));
-    *amax_out = a;
-    *gdec = tensor_scales(a).g;
-    slot_clear(s);
+// The caller's amax and g, from workgroup 0 (every workgroup holds the same
+// tensor maximum).
+__device__ __forceinline__ void grid_outputs(float A, float* amax_out, float* gdec) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *amax_out = A;
+    *gdec = tensor_scales(A).g;
   }
 }
 
@@ -1059,12 +1066,17 @@ __device__ __forceinline__ void grid_finish(int slot, float* amax_out, float* gd
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
 constexpr uint32_t kDropOff = 0x80000000u;  // past every range: the store is dropped
 
-template <bool kSR, bool kRHT>
+// Block maxima are taken before the barrier (while the last workgroups are
+// still loading) and kept in LDS as bf16 bits (a block's maximum is one of
+// its bf16 values), two rounds per word; each thread reads back only its own
+// words.
 __global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
-    const uint16_t* __restrict__ x, int64_t chunks, int slot, float* __restrict__ amax_out,
-    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
-    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds, uint64_t wait_ticks) {
+    const uint16_t* __restrict__ x, int64_t chunks, int slot, uint32_t epoch,
+    float* __restrict__ amax_out, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ gdec, uint64_t wait_ticks) {
+  static_assert(kSpRowHold % 2 == 0, "rounds pair up in the LDS words");
   __shared__ float rtab[128];
+  __shared__ uint32_t bmax[kSpRowHold / 2][kSpThreads];
   const uint32_t P = gridDim.x * kSpThreads;
   const uint32_t wg0 = blockIdx.x * kSpThreads;  // first chunk of the workgroup, round 0
   const uint32_t tid = threadIdx.x;
@@ -1076,22 +1088,16 @@ __global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
   for (int j = 0; j < kSpRowHold; j++)
     q[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                          xr, tid * 16, (int)((wg0 + j * P) * 16), 0));
-  float m = 0.0f;
+  float m = 0.0f;  // chunks past the end are zeros
 #pragma unroll
-  for (int j = 0; j < kSpRowHold; j++) {
-    if (kRHT) {  // the amax is taken after the transform (chunks past the end are zeros)
-      float v[8];
-      RawRow<uint16_t>{q[j]}.all(v);
-      rht_signs_and_low_stages(v, mask, odd * 8);
-      rht_pair_stage8(v, odd);
-      m = fmaxf(m, max8(v));
-    } else {
-      m = fmaxf(m, max8_bf16_bits(q[j]));
-    }
+  for (int j = 0; j < kSpRowHold; j += 2) {
+    const float c0 = max8_bf16_bits(q[j]), c1 = max8_bf16_bits(q[j + 1]);
+    const float b0 = fmaxf(c0, xor1(c0)), b1 = fmaxf(c1, xor1(c1));
+    bmax[j / 2][tid] = (__float_as_uint(b0) >> 16) | (__float_as_uint(b1) & 0xFFFF0000u);
+    m = fmaxf(m, fmaxf(b0, b1));
   }
-  // (with the transform the fallback's plain max would not be the amax: the
-  // transform is only used where the launch never takes this kernel)
-  const float A = grid_amax(m, slot, x, chunks, wait_ticks);
+  const float A = grid_amax(m, slot, epoch, x, chunks, wait_ticks);
+  grid_outputs(A, amax_out, gdec);
   const TensorScales ts = tensor_scales(A);
   build_recip_table(rtab, ts.S);
   const __amdgpu_buffer_rsrc_t cr =
@@ -1102,31 +1108,24 @@ __global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
 #pragma unroll
   for (int j = 0; j < kSpRowHold; j++) {
     const uint32_t base = wg0 + j * P;  // wave-uniform
-    float v[8];
-    RawRow<uint16_t>{q[j]}.all(v);
-    if (kRHT) {
-      rht_signs_and_low_stages(v, mask, odd * 8);
-      rht_pair_stage8(v, odd);
-    }
-    const float mm = max8(v);
-    const uint32_t e = block_code(fmaxf(mm, xor1(mm)), ts.k);
+    const uint32_t bw = bmax[j / 2][tid];
+    const float bm = __uint_as_float((j & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
+    const uint32_t e = block_code(bm, ts.k);
     const float r = rtab[e];
-    float y[8];
+    float v[8], y[8];
+    RawRow<uint16_t>{q[j]}.all(v);
 #pragma unroll
     for (int u = 0; u < 8; u++) y[u] = v[u] * r;
-    if (kSR) sr_values8(y, sr_call((uint64_t)(base + tid), seed, offset, rounds));
-    const uint32_t packed = pack8_rne(y);
-    __builtin_amdgcn_raw_buffer_store_b32(packed, cr, tid * 4, (int)(base * 4), 0);
+    __builtin_amdgcn_raw_buffer_store_b32(pack8_rne(y), cr, tid * 4, (int)(base * 4), 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e, sr, s_off, (int)(base / 2), 0);
   }
-  grid_finish(slot, amax_out, gdec);
 }
 
 // 16x16 blocks of one bf16 matrix.  Thread t of the grid holds units t + j P
 // (16 rows x 8 columns, as in quant_2d_kernel; lanes 2t and 2t+1 hold the two
 // halves of a block).
 __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
-    const uint16_t* __restrict__ w, int64_t rows, int64_t cols, int slot,
+    const uint16_t* __restrict__ w, int64_t rows, int64_t cols, int slot, uint32_t epoch,
     float* __restrict__ amax_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ gdec, uint64_t wait_ticks) {
   __shared__ float rtab[128];
@@ -1145,12 +1144,21 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
       q[j][r] = u < units ? *reinterpret_cast<const uint4*>(w + (g * 16 + r) * cols + c0)
                           : make_uint4(0, 0, 0, 0);
   }
+  // Block maxima before the barrier, kept in LDS (each thread reads back
+  // only its own entries).
+  __shared__ float bmax[kSp2dHold][kSpThreads];
   float m = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kSp2dHold; j++)
+  for (int j = 0; j < kSp2dHold; j++) {
+    float bm = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; r++) m = fmaxf(m, max8_bf16_bits(q[j][r]));
-  const float A = grid_amax(m, slot, w, rows * cols / 8, wait_ticks);
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, max8_bf16_bits(q[j][r]));
+    bm = fmaxf(bm, xor1(bm));
+    bmax[j][threadIdx.x] = bm;
+    m = fmaxf(m, bm);
+  }
+  const float A = grid_amax(m, slot, epoch, w, rows * cols / 8, wait_ticks);
+  grid_outputs(A, amax_out, gdec);
   const TensorScales ts = tensor_scales(A);
   build_recip_table(rtab, ts.S);
 #pragma unroll
@@ -1158,11 +1166,7 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
     const int64_t u = t0 + j * P;
     if (u >= units) break;  // units and P are even: the lanes of a pair agree
     const int64_t g = u / cg, c0 = (u % cg) * 8;
-    float bm = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; r++) bm = fmaxf(bm, max8_bf16_bits(q[j][r]));
-    bm = fmaxf(bm, xor1(bm));
-    const uint32_t e = block_code(bm, ts.k);
+    const uint32_t e = block_code(bmax[j][threadIdx.x], ts.k);
     const float rcp = rtab[e];
 #pragma unroll
     for (int r = 0; r < 16; r++) {
@@ -1174,7 +1178,6 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
     }
     if (((u % cg) & 1) == 0) scales[g * (cols / 16) + c0 / 16] = (uint8_t)e;
   }
-  grid_finish(slot, amax_out, gdec);
 }
 
 // ---- standalone transform ------------------------------------------------------------------
@@ -1266,6 +1269,19 @@ int next_slot() {
   return (int)(counter.fetch_add(1u, std::memory_order_relaxed) % kSlots);
 }
 
+// The next board of the single-pass kernels (round robin over kSlots) and
+// its epoch: 1 + the number of earlier uses of that board, so never 0 (the
+// value of an unused entry) and never a value an earlier call left there.
+struct Board {
+  int slot;
+  uint32_t epoch;
+};
+Board next_board() {
+  static std::atomic<unsigned long long> counter{0};
+  const unsigned long long c = counter.fetch_add(1u, std::memory_order_relaxed);
+  return Board{(int)(c % kSlots), (uint32_t)((c / kSlots) % 0xFFFFFFFFull) + 1u};
+}
+
 // Compute units of the current device (the single-pass grid: one workgroup
 // per CU), cached per device.
 int device_cu_count() {
@@ -1316,12 +1332,12 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     // (RNE without the transform: with stochastic rounding or the transform
     // the compiler does not keep the held chunks in registers.)
     const int wait_us = g_single_pass_wait_us.load(std::memory_order_relaxed);
-    if (a.axis == kBlockRow && !a.sr && !a.rht && !a.amax_is_input && cus > 0 && wait_us >= 0 &&
-        chunks <= (int64_t)cus * kSpThreads * kSpRowHold) {
-      quant_row_1pass_kernel<false, false><<<cus, kSpThreads, 0, st>>>(
-          reinterpret_cast<const uint16_t*>(x), chunks, next_slot(), a.amax,
-          reinterpret_cast<uint32_t*>(a.codes), a.scales, a.gdec, 0, 0, 0, 0,
-          (uint64_t)wait_us * 100u);
+    if (a.axis == kBlockRow && !a.sr && !a.rht && !a.amax_is_input && cus > 0 &&
+        cus <= kBoardMax && wait_us >= 0 && chunks <= (int64_t)cus * kSpThreads * kSpRowHold) {
+      const Board b = next_board();
+      quant_row_1pass_kernel<<<cus, kSpThreads, 0, st>>>(
+          reinterpret_cast<const uint16_t*>(x), chunks, b.slot, b.epoch, a.amax,
+          reinterpret_cast<uint32_t*>(a.codes), a.scales, a.gdec, (uint64_t)wait_us * 100u);
       return hipGetLastError();
     }
   }
@@ -1382,10 +1398,11 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
     const int64_t units = (a.rows / 16) * (a.cols / 8);
     const int cus = device_cu_count();
     const int wait_us = g_single_pass_wait_us.load(std::memory_order_relaxed);
-    if (a.batch == 1 && !a.amax_is_input && cus > 0 && wait_us >= 0 &&
+    if (a.batch == 1 && !a.amax_is_input && cus > 0 && cus <= kBoardMax && wait_us >= 0 &&
         units <= (int64_t)cus * kSpThreads * kSp2dHold) {
+      const Board b = next_board();
       quant_2d_1pass_kernel<<<cus, kSpThreads, 0, st>>>(
-          reinterpret_cast<const uint16_t*>(w), a.rows, a.cols, next_slot(), a.amax, a.codes,
+          reinterpret_cast<const uint16_t*>(w), a.rows, a.cols, b.slot, b.epoch, a.amax, a.codes,
           a.scales, a.gdec, (uint64_t)wait_us * 100u);
       return hipGetLastError();
     }
