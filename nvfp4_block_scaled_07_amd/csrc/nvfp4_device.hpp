@@ -179,6 +179,21 @@ __device__ __forceinline__ void rht_signs_and_low_stages(float v[8], uint32_t ma
   }
 }
 
+// The butterflies of the transform alone (strides 1, 2, 4, then 8), without
+// the sign flips and the final * 1/4.
+__device__ __forceinline__ void hadamard16_unscaled(float v[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      if (i & h) continue;
+      float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+}
+
 // Full 16-point transform of one in-register block (stride 8 last, * 1/4).
 __device__ __forceinline__ void rht16_inreg(float v[16], uint32_t mask) {
   rht_signs_and_low_stages(v, mask, 0);

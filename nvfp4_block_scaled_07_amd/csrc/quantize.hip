@@ -403,10 +403,83 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
   block_max_to(m, amax + blockIdx.y, m, amax2, slot, gridDim.x);
 }
 
+// ---- a lane's 16 x 8 tile, kept as loaded ------------------------------------------------------
+// The COL kernels hold 16 rows of 8 columns per lane as raw input words and
+// work them one column pair at a time.
+template <typename T>
+struct RawRow;
+
+template <>
+struct RawRow<uint16_t> {  // 8 bf16 = 4 words; column pair p is word p
+  uint4 q;
+  __device__ __forceinline__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void load_or_zero(const uint16_t* p, bool ok) {  // p readable
+    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+    q = make_uint4(t.x & m, t.y & m, t.z & m, t.w & m);
+  }
+  __device__ __forceinline__ void pair(int p, float& a, float& b) const {
+    const uint32_t w = p == 0 ? q.x : p == 1 ? q.y : p == 2 ? q.z : q.w;
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ void all(float v[8]) const {
+#pragma unroll
+    for (int p = 0; p < 4; p++) pair(p, v[2 * p], v[2 * p + 1]);
+  }
+  // Negates every element when neg (one XOR per two elements).
+  __device__ __forceinline__ void flip(bool neg) {
+    const uint32_t m = neg ? 0x80008000u : 0u;
+    q = make_uint4(q.x ^ m, q.y ^ m, q.z ^ m, q.w ^ m);
+  }
+  __device__ __forceinline__ float absmax() const { return max8_bf16_bits(q); }
+};
+
+template <>
+struct RawRow<float> {  // named words (no array, so selects stay in registers)
+  uint4 lo, hi;         // elements 0..3, 4..7
+  __device__ __forceinline__ void load(const float* p) {
+    lo = reinterpret_cast<const uint4*>(p)[0];
+    hi = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_or_zero(const float* p, bool ok) {  // p readable
+    load(p);
+    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+    lo = make_uint4(lo.x & m, lo.y & m, lo.z & m, lo.w & m);
+    hi = make_uint4(hi.x & m, hi.y & m, hi.z & m, hi.w & m);
+  }
+  __device__ __forceinline__ void pair(int p, float& a, float& b) const {
+    const uint32_t wa = p == 0 ? lo.x : p == 1 ? lo.z : p == 2 ? hi.x : hi.z;
+    const uint32_t wb = p == 0 ? lo.y : p == 1 ? lo.w : p == 2 ? hi.y : hi.w;
+    a = __uint_as_float(wa);
+    b = __uint_as_float(wb);
+  }
+  __device__ __forceinline__ void all(float v[8]) const {
+#pragma unroll
+    for (int p = 0; p < 4; p++) pair(p, v[2 * p], v[2 * p + 1]);
+  }
+  __device__ __forceinline__ void flip(bool neg) {
+    const uint32_t m = neg ? 0x80000000u : 0u;
+    lo = make_uint4(lo.x ^ m, lo.y ^ m, lo.z ^ m, lo.w ^ m);
+    hi = make_uint4(hi.x ^ m, hi.y ^ m, hi.z ^ m, hi.w ^ m);
+  }
+  __device__ __forceinline__ float absmax() const {
+    float v[8];
+    all(v);
+    return max8(v);
+  }
+};
+
+
 // ---- amax of COL blocks with the transform (lane: 8 cols x 16 rows) ---------------------
-// 256-thread workgroups: each lane holds a 16 x 8 tile and its transform,
-// too many registers for the large amax workgroups.  kPlain: also the max of
-// |x| itself (into amax_plain), from the same loads.
+// 256-thread workgroups, one 16 x 8 tile per lane at a time, kept as raw
+// words; the compiler issues the next tile's loads before transforming the
+// current one, so the grid is sized to two workgroups per CU (what fits in
+// the registers) and each lane takes several tiles.  kPlain:
+// also the max of |x| itself (into amax_plain), from the same loads.  The
+// transform's sign flips are applied to the raw words (exact negations), and
+// its final * 1/4 to the maximum instead of to every element: rounding is
+// monotone, so max |RN32(c / 4)| = RN32(max |c| / 4).
 template <typename T, bool kPlain, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restrict__ x,
                                                                 int64_t rows, int64_t cols,
@@ -420,27 +493,32 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
   float m = 0.0f, mp = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
-    int64_t g = u / cg, c0 = (u % cg) * 8;
-    float v[16][8];
+    const int64_t g = u / cg, c0 = (u % cg) * 8;
+    RawRow<T> raw[16];
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const int64_t sr = rs.at(g * 16 + r);
-      load8_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0, v[r]);
+      raw[r].load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
     }
     if (kPlain)
 #pragma unroll
-      for (int r = 0; r < 16; r++) mp = fmaxf(mp, max8(v[r]));
+      for (int r = 0; r < 16; r++) mp = fmaxf(mp, raw[r].absmax());
 #pragma unroll
-    for (int c = 0; c < 8; c++) {
-      float col[16];
+    for (int r = 0; r < 16; r++) raw[r].flip((mask >> r) & 1u);
 #pragma unroll
-      for (int r = 0; r < 16; r++) col[r] = v[r][c];
-      rht16_inreg(col, mask);
+    for (int cp = 0; cp < 4; cp++) {
+      float col[2][16];
 #pragma unroll
-      for (int r = 0; r < 16; r++) m = fmaxf(m, __builtin_fabsf(col[r]));
+      for (int r = 0; r < 16; r++) raw[r].pair(cp, col[0][r], col[1][r]);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        hadamard16_unscaled(col[h]);
+#pragma unroll
+        for (int r = 0; r < 16; r++) m = fmaxf(m, __builtin_fabsf(col[h][r]));
+      }
     }
   }
-  block_max_to(m, amax, mp, kPlain ? amax_plain : nullptr, slot, gridDim.x);
+  block_max_to(m * 0.25f, amax, mp, kPlain ? amax_plain : nullptr, slot, gridDim.x);
 }
 
 // ---- ROW quantizer ---------------------------------------------------------------------------
@@ -659,63 +737,15 @@ __global__ __launch_bounds__(kThreads) void quant_mse_row_kernel(
 }
 
 // ---- COL quantizer (lane: 8 cols x 16 rows = 8 blocks) ---------------------------------------
-// The 16 rows stay as loaded (raw input words) and are worked one column pair
-// at a time (the loop is kept rolled so that only one pair's transform and
-// random bits are live): with stochastic rounding an unrolled lane would hold
-// all 8 blocks' Philox output and its occupancy would drop to one wave per
-// SIMD.
-template <typename T>
-struct RawRow;
-
-template <>
-struct RawRow<uint16_t> {  // 8 bf16 = 4 words; column pair p is word p
-  uint4 q;
-  __device__ __forceinline__ void load(const uint16_t* p) { q = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ void load_or_zero(const uint16_t* p, bool ok) {  // p readable
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
-    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-    q = make_uint4(t.x & m, t.y & m, t.z & m, t.w & m);
-  }
-  __device__ __forceinline__ void pair(int p, float& a, float& b) const {
-    const uint32_t w = p == 0 ? q.x : p == 1 ? q.y : p == 2 ? q.z : q.w;
-    a = __uint_as_float(w << 16);
-    b = __uint_as_float(w & 0xFFFF0000u);
-  }
-  __device__ __forceinline__ void all(float v[8]) const {
-#pragma unroll
-    for (int p = 0; p < 4; p++) pair(p, v[2 * p], v[2 * p + 1]);
-  }
-};
-
-template <>
-struct RawRow<float> {  // named words (no array, so selects stay in registers)
-  uint4 lo, hi;         // elements 0..3, 4..7
-  __device__ __forceinline__ void load(const float* p) {
-    lo = reinterpret_cast<const uint4*>(p)[0];
-    hi = reinterpret_cast<const uint4*>(p)[1];
-  }
-  __device__ __forceinline__ void load_or_zero(const float* p, bool ok) {  // p readable
-    load(p);
-    const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-    lo = make_uint4(lo.x & m, lo.y & m, lo.z & m, lo.w & m);
-    hi = make_uint4(hi.x & m, hi.y & m, hi.z & m, hi.w & m);
-  }
-  __device__ __forceinline__ void pair(int p, float& a, float& b) const {
-    const uint32_t wa = p == 0 ? lo.x : p == 1 ? lo.z : p == 2 ? hi.x : hi.z;
-    const uint32_t wb = p == 0 ? lo.y : p == 1 ? lo.w : p == 2 ? hi.y : hi.w;
-    a = __uint_as_float(wa);
-    b = __uint_as_float(wb);
-  }
-  __device__ __forceinline__ void all(float v[8]) const {
-#pragma unroll
-    for (int p = 0; p < 4; p++) pair(p, v[2 * p], v[2 * p + 1]);
-  }
-};
-
 // COL encode of one lane's 8 columns x 16 rows (8 blocks), from its raw
-// rows: out[r] gets the 8 codes of row r, sc[0..1] the 8 scale bytes.
+// rows: out[r] gets the 8 codes of row r, sc[0..1] the 8 scale bytes.  With
+// the transform, its sign flips are applied to raw (in place: exact
+// negations of whole rows).  The loop over column pairs is kept rolled, so
+// that only one pair's transform and random bits are live: unrolled, the
+// lane holds more of them and its occupancy drops from three waves per SIMD
+// to two.
 template <typename T, bool kSR, bool kRHT>
-__device__ __forceinline__ void col_encode(const RawRow<T> (&raw)[16], int64_t rows, int64_t g,
+__device__ __forceinline__ void col_encode(RawRow<T> (&raw)[16], int64_t rows, int64_t g,
                                            int64_t c0, const TensorScales& ts,
                                            const float* rtab, uint32_t mask, uint64_t seed,
                                            uint64_t offset, uint32_t rounds, uint32_t (&out)[16],
@@ -723,6 +753,9 @@ __device__ __forceinline__ void col_encode(const RawRow<T> (&raw)[16], int64_t r
 #pragma unroll
   for (int r = 0; r < 16; r++) out[r] = 0;
   sc[0] = sc[1] = 0;
+  if (kRHT)
+#pragma unroll
+    for (int r = 0; r < 16; r++) raw[r].flip((mask >> r) & 1u);
 #pragma unroll 1
   for (int cp = 0; cp < 4; cp++) {  // column pairs (c, c+1) share one code byte per row
     float col[2][16];
@@ -731,7 +764,11 @@ __device__ __forceinline__ void col_encode(const RawRow<T> (&raw)[16], int64_t r
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const int c = 2 * cp + h;
-      if (kRHT) rht16_inreg(col[h], mask);
+      if (kRHT) {
+        hadamard16_unscaled(col[h]);
+#pragma unroll
+        for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * 0.25f;
+      }
       float bm = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[h][r]));
@@ -1297,6 +1334,16 @@ int device_cu_count() {
   return n;
 }
 
+// Workgroups of the COL amax pass with the transform: one per kThreads
+// tiles, at most two per CU (the kernel's occupancy), so that every lane
+// takes the same number of tiles, give or take one.
+unsigned col_amax_grid(int64_t units) {
+  const int64_t cus = device_cu_count();
+  const int64_t cap = cus > 0 ? 2 * cus : 512;
+  const int64_t g = cdiv(units, kThreads);
+  return (unsigned)(g < cap ? (g > 0 ? g : 1) : cap);
+}
+
 // Workgroups of an amax pass: one per kAmaxThreads * unroll units, capped
 // near the CU count (the kernels loop over the rest) to keep the atomics few.
 int amax_grid(int64_t units, int unroll, int64_t cap = 512) {
@@ -1346,7 +1393,7 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     if (a.axis == kBlockCol && a.rht) {
       int64_t units = (a.rows / 16) * (a.cols / 8);
       amax_col_rht_kernel<T, false, G>
-          <<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads, 0, st>>>(
+          <<<col_amax_grid(units), kThreads, 0, st>>>(
               x, a.rows, a.cols, a.mask, a.amax, nullptr, slot, rs);
     } else {
       int64_t chunks = a.rows * a.cols / 8;
@@ -1456,7 +1503,7 @@ hipError_t launch_quantize_dual_t(const QuantDualArgs& a, hipStream_t st) {
   if (!a.amax_is_input) {
     if (a.rht) {  // transform max for COL, plain max for ROW, one read
       amax_col_rht_kernel<T, true, G>
-          <<<(unsigned)std::min<int64_t>(cdiv(units, kThreads), 1024), kThreads, 0, st>>>(
+          <<<col_amax_grid(units), kThreads, 0, st>>>(
               x, a.rows, a.cols, a.mask, a.amax + 1, a.amax, slot, rs);
     } else {  // the same plain max for both
       const int64_t chunks = a.rows * a.cols / 8;
