@@ -980,11 +980,13 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
 }
 
 // ---- single-pass quantizers (tensor amax and encode in one launch) -------------------------
-// A bf16 tensor that fits in the registers of one workgroup per CU is read
-// once: every thread loads its share and keeps it, the workgroups combine
+// A bf16 tensor is read once as far as the registers of one workgroup per CU
+// hold it: every thread loads its share and keeps it, the workgroups combine
 // their maxima through a grid barrier, then every thread encodes what it
 // holds, exactly as the two-pass kernels do (same block codes, reciprocal
-// table and rounding), so the outputs are bit-identical.  The grid is one
+// table, rounding and Philox calls), so the outputs are bit-identical.  What
+// does not fit is read twice, once for the maximum before the barrier and
+// once to be encoded after it, which still reads less than two passes.  The grid is one
 // workgroup per CU, and a workgroup fills a CU's registers (kSpThreads
 // threads, up to 256 VGPRs each), so on an otherwise idle device all of them
 // are resident at once.  When they are not (another kernel holds CUs, e.g.
@@ -993,8 +995,11 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
 // maximum by reading the whole tensor itself, which is slow but gives the
 // same value, so the results stay exact and no wait can last.
 constexpr int kSpThreads = 512;
-constexpr int kSpRowHold = 48;   // 16-byte chunks (8 bf16) held per thread: 192 VGPRs
-constexpr int kSp2dHold = 3;     // 16 x 8 bf16 units held per thread: 192 VGPRs
+constexpr int kSpRowHold = 48;    // 16-byte chunks (8 bf16) held per thread: 192 VGPRs
+constexpr int kSpRowHoldSr = 42;  // the same with stochastic rounding (its encode needs more)
+constexpr int kSp2dHold = 3;      // 16 x 8 bf16 units held per thread: 192 VGPRs
+constexpr int kSpStream = 8;      // chunks in flight per thread in the rounds read twice
+constexpr int64_t kSpMaxBytes = int64_t(1) << 30;  // single pass up to 1 GiB of bf16 (31-bit offsets)
 
 // Max of |x| over n16 16-byte chunks of bf16 by the whole workgroup (the
 // fallback of a workgroup that gave up waiting at the grid barrier).
@@ -1091,43 +1096,62 @@ __device__ __forceinline__ void grid_outputs(float A, float* amax_out, float* gd
   }
 }
 
-// ROW blocks.  Thread t of the grid (P threads) holds chunks t + j P, j <
-// kSpRowHold (consecutive lanes: consecutive 16-byte chunks; lanes 2t and
-// 2t+1 hold the two halves of a block, as in quant_row_kernel).  Loads and
-// stores go through buffer resources sized to the tensor: the per-lane part
-// of an offset is the thread's, the per-round part (j P) a wave-uniform
-// scalar, so no per-round address stays live in vector registers; chunks
-// past the end read zeros and their stores are dropped by the range check.
-// The tensor is at most a few hundred MB here (it fits in the registers), so
-// 32-bit byte offsets suffice.
+// ROW blocks.  Thread t of the grid (P threads) takes chunks t + j P
+// (consecutive lanes: consecutive 16-byte chunks; lanes 2t and 2t+1 hold the
+// two halves of a block, as in quant_row_kernel).  Loads and stores go
+// through buffer resources sized to the tensor: the per-lane part of an
+// offset is the thread's, the per-round part (j P) a wave-uniform scalar, so
+// no per-round address stays live in vector registers; chunks past the end
+// read zeros and their stores are dropped by the range check.  The tensor is
+// at most kSpMaxBytes here, so the byte offsets fit 31 bits, also for the
+// rounds past the end that a streamed batch reads (kSpStream rounds further
+// at most).
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
 constexpr uint32_t kDropOff = 0x80000000u;  // past every range: the store is dropped
 
-// Block maxima are taken before the barrier (while the last workgroups are
-// still loading) and kept in LDS as bf16 bits (a block's maximum is one of
-// its bf16 values), two rounds per word; each thread reads back only its own
-// words.
+// Thread t takes the chunks of rounds j < J = ceil(chunks / P): rounds j < H
+// (kSpRowHold, or kSpRowHoldSr with stochastic rounding, whose encode needs
+// more registers) are loaded once and kept; rounds H .. J-1, when there are
+// more, are streamed first, before the held rounds are loaded, for their
+// maximum only, and again after the barrier to be encoded.  Block maxima of
+// the held rounds are taken before the barrier and kept in LDS as bf16 bits
+// (a block's maximum is one of its bf16 values), two rounds per word; each
+// thread reads back only its own words.  With stochastic rounding chunk i
+// draws Philox call i, as in quant_row_kernel.
+template <bool kSR>
 __global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
     const uint16_t* __restrict__ x, int64_t chunks, int slot, uint32_t epoch,
     float* __restrict__ amax_out, uint32_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ gdec, uint64_t wait_ticks) {
-  static_assert(kSpRowHold % 2 == 0, "rounds pair up in the LDS words");
+    float* __restrict__ gdec, uint64_t seed, uint64_t offset, uint32_t rounds,
+    uint64_t wait_ticks) {
+  constexpr int H = kSR ? kSpRowHoldSr : kSpRowHold;
+  static_assert(H % 2 == 0, "rounds pair up in the LDS words");
   __shared__ float rtab[128];
-  __shared__ uint32_t bmax[kSpRowHold / 2][kSpThreads];
+  __shared__ uint32_t bmax[H / 2][kSpThreads];
   const uint32_t P = gridDim.x * kSpThreads;
-  const uint32_t wg0 = blockIdx.x * kSpThreads;  // first chunk of the workgroup, round 0
+  const uint32_t J = (uint32_t)((chunks + P - 1) / P);  // rounds (wave-uniform)
+  const uint32_t wg0 = blockIdx.x * kSpThreads;          // first chunk of the workgroup, round 0
   const uint32_t tid = threadIdx.x;
   const int odd = (int)(tid & 1);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x), 0, (int)(chunks * 16), kBufFlags);
-  uint4 q[kSpRowHold];
-#pragma unroll
-  for (int j = 0; j < kSpRowHold; j++)
-    q[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+  auto load = [&](uint32_t j) {  // round j's chunk (past the end: zeros)
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                          xr, tid * 16, (int)((wg0 + j * P) * 16), 0));
-  float m = 0.0f;  // chunks past the end are zeros
+  };
+  float m = 0.0f;
+  for (uint32_t j0 = H; j0 < J; j0 += kSpStream) {  // the rounds read twice: maximum
+    uint4 sq[kSpStream];
 #pragma unroll
-  for (int j = 0; j < kSpRowHold; j += 2) {
+    for (int k = 0; k < kSpStream; k++) sq[k] = load(j0 + k);
+#pragma unroll
+    for (int k = 0; k < kSpStream; k++) m = fmaxf(m, max8_bf16_bits(sq[k]));
+  }
+  uint4 q[H];
+#pragma unroll
+  for (int j = 0; j < H; j++) q[j] = load(j);
+#pragma unroll
+  for (int j = 0; j < H; j += 2) {
     const float c0 = max8_bf16_bits(q[j]), c1 = max8_bf16_bits(q[j + 1]);
     const float b0 = fmaxf(c0, xor1(c0)), b1 = fmaxf(c1, xor1(c1));
     bmax[j / 2][tid] = (__float_as_uint(b0) >> 16) | (__float_as_uint(b1) & 0xFFFF0000u);
@@ -1142,25 +1166,41 @@ __global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
   const __amdgpu_buffer_rsrc_t sr =
       __builtin_amdgcn_make_buffer_rsrc(scales, 0, (int)(chunks / 2), kBufFlags);
   const uint32_t s_off = odd ? kDropOff : tid / 2;  // even lanes store the block's scale
-#pragma unroll
-  for (int j = 0; j < kSpRowHold; j++) {
+  // Encode round j's chunk v (8 values) with its block's maximum bm.
+  auto encode = [&](uint32_t j, const uint4& qq, float bm) {
     const uint32_t base = wg0 + j * P;  // wave-uniform
-    const uint32_t bw = bmax[j / 2][tid];
-    const float bm = __uint_as_float((j & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
     const uint32_t e = block_code(bm, ts.k);
     const float r = rtab[e];
     float v[8], y[8];
-    RawRow<uint16_t>{q[j]}.all(v);
+    RawRow<uint16_t>{qq}.all(v);
 #pragma unroll
     for (int u = 0; u < 8; u++) y[u] = v[u] * r;
+    if (kSR) sr_values8(y, sr_call((uint64_t)(base + tid), seed, offset, rounds));
     __builtin_amdgcn_raw_buffer_store_b32(pack8_rne(y), cr, tid * 4, (int)(base * 4), 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)e, sr, s_off, (int)(base / 2), 0);
+  };
+#pragma unroll
+  for (int j = 0; j < H; j++) {
+    const uint32_t bw = bmax[j / 2][tid];
+    encode(j, q[j], __uint_as_float((j & 1) ? (bw & 0xFFFF0000u) : (bw << 16)));
+  }
+  for (uint32_t j0 = H; j0 < J; j0 += kSpStream) {  // the rounds read twice: encode
+    uint4 sq[kSpStream];
+#pragma unroll
+    for (int k = 0; k < kSpStream; k++) sq[k] = load(j0 + k);
+#pragma unroll
+    for (int k = 0; k < kSpStream; k++) {
+      const float c = max8_bf16_bits(sq[k]);
+      encode(j0 + k, sq[k], fmaxf(c, xor1(c)));  // past the end: zeros, stores dropped
+    }
   }
 }
 
-// 16x16 blocks of one bf16 matrix.  Thread t of the grid holds units t + j P
+// 16x16 blocks of one bf16 matrix.  Thread t of the grid takes units t + j P
 // (16 rows x 8 columns, as in quant_2d_kernel; lanes 2t and 2t+1 hold the two
-// halves of a block).
+// halves of a block): rounds j < kSp2dHold are held, later ones (when there
+// are more) are streamed for the maximum first and read again after the
+// barrier, as in the ROW kernel.
 __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
     const uint16_t* __restrict__ w, int64_t rows, int64_t cols, int slot, uint32_t epoch,
     float* __restrict__ amax_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -1170,27 +1210,37 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
   const int64_t t0 = (int64_t)blockIdx.x * kSpThreads + threadIdx.x;
   const int64_t cg = cols / 8;  // a multiple of 4: pairs never straddle rows
   const int64_t units = (rows / 16) * cg;
-  uint4 q[kSp2dHold][16];
-#pragma unroll
-  for (int j = 0; j < kSp2dHold; j++) {
+  const int64_t J = (units + P - 1) / P;  // rounds (wave-uniform)
+  auto load_unit = [&](int64_t j, uint4 (&qq)[16]) {  // past the end: zeros
     const int64_t u = t0 + j * P;
     const int64_t uc = u < units ? u : 0;
     const int64_t g = uc / cg, c0 = (uc % cg) * 8;
 #pragma unroll
     for (int r = 0; r < 16; r++)
-      q[j][r] = u < units ? *reinterpret_cast<const uint4*>(w + (g * 16 + r) * cols + c0)
-                          : make_uint4(0, 0, 0, 0);
+      qq[r] = u < units ? *reinterpret_cast<const uint4*>(w + (g * 16 + r) * cols + c0)
+                        : make_uint4(0, 0, 0, 0);
+  };
+  auto unit_max = [&](const uint4 (&qq)[16]) {  // the block's maximum (both lanes)
+    float bm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, max8_bf16_bits(qq[r]));
+    return fmaxf(bm, xor1(bm));
+  };
+  float m = 0.0f;
+  for (int64_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: maximum
+    uint4 sq[16];
+    load_unit(j, sq);
+    m = fmaxf(m, unit_max(sq));
   }
+  uint4 q[kSp2dHold][16];
+#pragma unroll
+  for (int j = 0; j < kSp2dHold; j++) load_unit(j, q[j]);
   // Block maxima before the barrier, kept in LDS (each thread reads back
   // only its own entries).
   __shared__ float bmax[kSp2dHold][kSpThreads];
-  float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < kSp2dHold; j++) {
-    float bm = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; r++) bm = fmaxf(bm, max8_bf16_bits(q[j][r]));
-    bm = fmaxf(bm, xor1(bm));
+    const float bm = unit_max(q[j]);
     bmax[j][threadIdx.x] = bm;
     m = fmaxf(m, bm);
   }
@@ -1198,22 +1248,28 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
   grid_outputs(A, amax_out, gdec);
   const TensorScales ts = tensor_scales(A);
   build_recip_table(rtab, ts.S);
-#pragma unroll
-  for (int j = 0; j < kSp2dHold; j++) {
+  auto encode = [&](int64_t j, const uint4 (&qq)[16], float bm) {
     const int64_t u = t0 + j * P;
-    if (u >= units) break;  // units and P are even: the lanes of a pair agree
+    if (u >= units) return;  // units and P are even: the lanes of a pair agree
     const int64_t g = u / cg, c0 = (u % cg) * 8;
-    const uint32_t e = block_code(bmax[j][threadIdx.x], ts.k);
+    const uint32_t e = block_code(bm, ts.k);
     const float rcp = rtab[e];
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       float v[8], y[8];
-      RawRow<uint16_t>{q[j][r]}.all(v);
+      RawRow<uint16_t>{qq[r]}.all(v);
 #pragma unroll
       for (int k = 0; k < 8; k++) y[k] = v[k] * rcp;
       *reinterpret_cast<uint32_t*>(codes + (g * 16 + r) * (cols / 2) + c0 / 2) = pack8_rne(y);
     }
     if (((u % cg) & 1) == 0) scales[g * (cols / 16) + c0 / 16] = (uint8_t)e;
+  };
+#pragma unroll
+  for (int j = 0; j < kSp2dHold; j++) encode(j, q[j], bmax[j][threadIdx.x]);
+  for (int64_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: encode
+    uint4 sq[16];
+    load_unit(j, sq);
+    encode(j, sq, unit_max(sq));
   }
 }
 
@@ -1376,15 +1432,21 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     // Single pass when the tensor fits in the grid's registers.
     const int64_t chunks = a.rows * a.cols / 8;
     const int cus = device_cu_count();
-    // (RNE without the transform: with stochastic rounding or the transform
-    // the compiler does not keep the held chunks in registers.)
+    // (Not with the transform: the amax would need the transformed values.)
     const int wait_us = g_single_pass_wait_us.load(std::memory_order_relaxed);
-    if (a.axis == kBlockRow && !a.sr && !a.rht && !a.amax_is_input && cus > 0 &&
-        cus <= kBoardMax && wait_us >= 0 && chunks <= (int64_t)cus * kSpThreads * kSpRowHold) {
+    if (a.axis == kBlockRow && !a.rht && !a.amax_is_input && cus > 0 && cus <= kBoardMax &&
+        wait_us >= 0 && chunks * 16 <= kSpMaxBytes) {
       const Board b = next_board();
-      quant_row_1pass_kernel<<<cus, kSpThreads, 0, st>>>(
-          reinterpret_cast<const uint16_t*>(x), chunks, b.slot, b.epoch, a.amax,
-          reinterpret_cast<uint32_t*>(a.codes), a.scales, a.gdec, (uint64_t)wait_us * 100u);
+      const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+      uint32_t* cd = reinterpret_cast<uint32_t*>(a.codes);
+      const uint64_t ticks = (uint64_t)wait_us * 100u;
+      if (a.sr)
+        quant_row_1pass_kernel<true><<<cus, kSpThreads, 0, st>>>(
+            xb, chunks, b.slot, b.epoch, a.amax, cd, a.scales, a.gdec, a.seed, a.offset, a.rounds,
+            ticks);
+      else
+        quant_row_1pass_kernel<false><<<cus, kSpThreads, 0, st>>>(
+            xb, chunks, b.slot, b.epoch, a.amax, cd, a.scales, a.gdec, 0, 0, 0, ticks);
       return hipGetLastError();
     }
   }
@@ -1446,7 +1508,7 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
     const int cus = device_cu_count();
     const int wait_us = g_single_pass_wait_us.load(std::memory_order_relaxed);
     if (a.batch == 1 && !a.amax_is_input && cus > 0 && cus <= kBoardMax && wait_us >= 0 &&
-        units <= (int64_t)cus * kSpThreads * kSp2dHold) {
+        units * 256 <= kSpMaxBytes) {
       const Board b = next_board();
       quant_2d_1pass_kernel<<<cus, kSpThreads, 0, st>>>(
           reinterpret_cast<const uint16_t*>(w), a.rows, a.cols, b.slot, b.epoch, a.amax, a.codes,

@@ -1,13 +1,15 @@
 """GPU parity of the single-pass quantizers and of the per-call scratch slots
 that replace a cleared amax output.
 
-* Single pass (bf16 ROW RNE without transform, one bf16 16x16-blocked
-  matrix): bit-exact against the oracle on both sides of the size limit (the
-  largest tensor the grid's registers hold, and one row group more, which
-  takes the two-pass path), equal to the two-pass path, and exact when the
-  grid barrier's wait is forced to give up (every late workgroup takes the
-  tensor maximum by itself) and when two streams run single-pass calls at
-  the same time.
+* Single pass (bf16 ROW without transform, RNE or stochastic rounding; one
+  bf16 16x16-blocked matrix): bit-exact against the oracle on both sides of
+  the register capacity (the largest tensor the grid's registers hold, and
+  one row group more, whose last round is streamed: read for the maximum
+  before the grid barrier and again after it), at the Ultra size [8192^2]
+  (a quarter of it streamed) and at the wgrad-Super dY size with stochastic
+  rounding; equal to the two-pass path; exact when the grid barrier's wait is
+  forced to give up (every late workgroup takes the tensor maximum by
+  itself) and when two streams run single-pass calls at the same time.
 * Slots: hundreds of calls in a row, more than the slots, with tensor maxima
   going up and down (a slot left dirty would hand a stale, larger maximum to
   a later call), and repeated dual quantizations whose zero-code counts must
@@ -24,7 +26,7 @@ from _gpu import assert_same, device, make_input, to_np
 
 pytestmark = pytest.mark.gpu
 
-THREADS, ROW_HOLD, UNITS_HOLD = 512, 48, 3  # the single-pass kernels' capacity per CU
+THREADS, ROW_HOLD, ROW_HOLD_SR, UNITS_HOLD = 512, 48, 42, 3  # held per thread
 
 
 def _cus():
@@ -50,14 +52,20 @@ def _same(a, b):
 
 
 @pytest.mark.parametrize("extra_rows", [0, 16])
-def test_row_single_pass_size_limit(extra_rows):
-    """Rows of 4096: the largest ROW tensor held in registers (single pass)
-    and 16 rows more (two passes), both against the oracle."""
+@pytest.mark.parametrize("rounding", ["rne", "sr"])
+def test_row_single_pass_size_limit(extra_rows, rounding):
+    """Rows of 4096: the largest ROW tensor held in registers, and 16 rows
+    more (a partial last round, streamed), both against the oracle."""
     dev = device()
-    rows = _cus() * THREADS * ROW_HOLD * 8 // 4096 + extra_rows
+    hold = ROW_HOLD if rounding == "rne" else ROW_HOLD_SR
+    rows = _cus() * THREADS * hold * 8 // 4096 + extra_rows
     x = make_input("normal", (rows, 4096), seed=600 + extra_rows)
     t, xo = _bf16(x, dev)
-    _check(nv.quantize_1d(t, "row"), O.quantize(xo, "row"))
+    if rounding == "rne":
+        _check(nv.quantize_1d(t, "row"), O.quantize(xo, "row"))
+    else:
+        _check(nv.quantize_1d(t, "row", "sr", nv.Philox(31)),
+               O.quantize(xo, "row", rounding=O.SR, seed=31))
 
 
 @pytest.mark.parametrize("extra_rows", [0, 16])
@@ -69,6 +77,41 @@ def test_2d_single_pass_size_limit(extra_rows):
     _check(nv.quantize_2d(t), O.quantize(xo, "2d"))
 
 
+@pytest.mark.parametrize("kind", ["row", "row_sr", "2d"])
+def test_single_pass_ultra_size(kind):
+    """[8192 x 8192] bf16 (134 MB, a quarter of it streamed), against the
+    oracle: the Ultra-width X (ROW), dY (ROW, stochastic rounding) and W."""
+    dev = device()
+    scale = np.float32(0.015) if kind == "2d" else np.float32(1.0)
+    x = make_input("normal", (8192, 8192), seed=615) * scale
+    t, xo = _bf16(x, dev)
+    del x
+    if kind == "row":
+        _check(nv.quantize_1d(t, "row"), O.quantize(xo, "row"))
+    elif kind == "row_sr":
+        _check(nv.quantize_1d(t, "row", "sr", nv.Philox(14)),
+               O.quantize(xo, "row", rounding=O.SR, seed=14))
+    else:
+        _check(nv.quantize_2d(t), O.quantize(xo, "2d"))
+
+
+def test_single_pass_sr_wgrad_dy():
+    """The wgrad-Super dY [8192 x 6144] (Laplace, 7% zeros), ROW with
+    stochastic rounding, single pass with streamed rounds, against the
+    oracle and the two-pass path."""
+    dev = device()
+    x = make_input("laplace_zeros", (8192, 6144), seed=3)
+    t, xo = _bf16(x, dev)
+    one = nv.quantize_1d(t, "row", "sr", nv.Philox(7))
+    prev = nv.nvfp4_set_single_pass_wait(-1)
+    try:
+        two = nv.quantize_1d(t, "row", "sr", nv.Philox(7))
+    finally:
+        nv.nvfp4_set_single_pass_wait(prev)
+    _same(one, two)
+    _check(one, O.quantize(xo, "row", rounding=O.SR, seed=7))
+
+
 @pytest.mark.parametrize("shape", [(66, 1024), (2000, 6144), (4096, 4160), (1024, 32)])
 def test_single_pass_equals_two_pass(shape):
     """The same bits with the single-pass kernels turned off (tensors of
@@ -78,13 +121,16 @@ def test_single_pass_equals_two_pass(shape):
     t, xo = _bf16(x, dev)
     w = t[: shape[0] // 16 * 16]
     one_r, one_w = nv.quantize_1d(t, "row"), nv.quantize_2d(w)
+    one_s = nv.quantize_1d(t, "row", "sr", nv.Philox(shape[1]))
     prev = nv.nvfp4_set_single_pass_wait(-1)
     try:
         two_r, two_w = nv.quantize_1d(t, "row"), nv.quantize_2d(w)
+        two_s = nv.quantize_1d(t, "row", "sr", nv.Philox(shape[1]))
     finally:
         nv.nvfp4_set_single_pass_wait(prev)
     _same(one_r, two_r)
     _same(one_w, two_w)
+    _same(one_s, two_s)
     _check(one_r, O.quantize(xo, "row"))
 
 
