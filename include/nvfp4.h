@@ -68,6 +68,8 @@ extern "C" {
 #define NVFP4_ERR_LAYOUT (-4)      /* op letters / block kind do not fit    */
 #define NVFP4_ERR_UNSUPPORTED (-5) /* a valid-looking but unsupported mode  */
 #define NVFP4_ERR_DEVICE (-6)      /* a HIP launch failed                   */
+#define NVFP4_ERR_NONFINITE (-7)   /* debug checks only: an input holds an
+                                      infinity or a NaN                       */
 
 /* Element types of unquantized tensors. */
 #define NVFP4_BF16 0
@@ -386,19 +388,38 @@ int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16
 
 /*
  * Tuning of the single-pass quantizers (a performance setting: results are
- * the same either way).  A bf16 tensor that fits in the registers of one
- * workgroup per CU (ROW blocks with RNE and no transform; one 16x16-blocked
- * matrix) is quantized in one launch that reads it once: its workgroups
- * meet at a grid barrier to combine the tensor amax.  They wait there at
- * most wait_us microseconds (default 2000); a workgroup that gives up, which
- * only happens when other kernels hold CUs (e.g. on concurrent streams),
- * reads the whole tensor to take the amax itself, so the results are
- * unchanged but slower.  wait_us < 0 turns the single-pass kernels off
- * (every call then takes the two-pass path: amax, then encode).  Applies to
- * calls made after it, process-wide.  Returns the previous setting (-1 when
- * off).
+ * the same either way).  A bf16 tensor of at most 1 GiB quantized with ROW
+ * blocks and no transform (RNE or stochastic rounding), or one bf16
+ * 16x16-blocked matrix, is quantized in one launch: its workgroups keep
+ * what the registers hold, stream the rest for its maximum, and meet at a
+ * grid barrier to combine the tensor amax before encoding (the streamed part
+ * is read again).  They wait there at most wait_us microseconds (default
+ * 2000); a workgroup that gives up, which only happens when other kernels
+ * hold CUs (e.g. on concurrent streams), reads the whole tensor to take the
+ * amax itself, so the results are unchanged but slower.  wait_us < 0 turns
+ * the single-pass kernels off (every call then takes the two-pass path:
+ * amax, then encode).  Applies to calls made after it, process-wide.
+ * Returns the previous setting (-1 when off).
  */
 int32_t nvfp4_set_single_pass_wait(int32_t wait_us);
+
+/*
+ * Debug checks.  The method quantizes finite tensors: every block scale and
+ * code above is defined for finite inputs only, and a single infinity or NaN
+ * makes the tensor amax, and with it every code of the tensor, meaningless
+ * (the pages trace training divergences back through the numerics, "Nemotron
+ * 3 Ultra" report, section 2.7).  With on != 0, every quantizer entry point
+ * (nvfp4_quantize_1d, _2d, _dual, _mse and the gathering variants) first
+ * scans its whole input on the caller's stream for infinities and NaNs,
+ * waits for the result (a host synchronization), and returns
+ * NVFP4_ERR_NONFINITE, writing nothing, if it finds one; a gathering call
+ * scans all src_rows rows of x.  Off (the default), inputs are not checked
+ * and a non-finite input is the caller's error.  The flag a scan sets lives
+ * in a slot of device memory that the library owns; calls that overlap on
+ * one device use different slots unless more than 256 are in flight.
+ * Process-wide; returns the previous setting (0 or 1).
+ */
+int32_t nvfp4_set_debug_checks(int32_t on);
 
 #ifdef __cplusplus
 }

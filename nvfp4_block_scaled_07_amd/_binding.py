@@ -16,6 +16,7 @@ NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_BLOCK_ROW, NVFP4_BLOCK_COL, NVFP4_BLOCK_2D = 0, 1, 2
 NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN = 0, -1, -2, -3
 NVFP4_ERR_LAYOUT, NVFP4_ERR_UNSUPPORTED, NVFP4_ERR_DEVICE = -4, -5, -6
+NVFP4_ERR_NONFINITE = -7
 _BLOCKS = {"row": NVFP4_BLOCK_ROW, "col": NVFP4_BLOCK_COL, "2d": NVFP4_BLOCK_2D}
 _BLOCK_NAMES = {v: k for k, v in _BLOCKS.items()}
 
@@ -100,6 +101,8 @@ def load():
                                                    C.POINTER(_Operand), vp, vp]
     L.nvfp4_set_single_pass_wait.restype = i32
     L.nvfp4_set_single_pass_wait.argtypes = [i32]
+    L.nvfp4_set_debug_checks.restype = i32
+    L.nvfp4_set_debug_checks.argtypes = [i32]
     _lib = L
     return L
 
@@ -159,6 +162,12 @@ def nvfp4_set_single_pass_wait(wait_us):
     """Grid-barrier wait of the single-pass quantizers in microseconds (< 0:
     single-pass kernels off); returns the previous setting."""
     return load().nvfp4_set_single_pass_wait(int(wait_us))
+
+
+def nvfp4_set_debug_checks(on):
+    """Debug mode: quantizers first check their input for infinities and NaNs
+    (NVFP4_ERR_NONFINITE); returns the previous setting."""
+    return load().nvfp4_set_debug_checks(1 if on else 0)
 
 
 def nvfp4_abi_version():

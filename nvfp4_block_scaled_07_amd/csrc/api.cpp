@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <cstdint>
 
 #include "launch.hpp"
@@ -17,6 +19,21 @@ using nvfp4::DevOperand;
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int32_t device_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_DEVICE; }
+
+// Debug mode (nvfp4_set_debug_checks): the quantizers first check their
+// input for infinities and NaNs.
+std::atomic<int> g_debug_checks{0};
+
+// NVFP4_OK, NVFP4_ERR_NONFINITE, or NVFP4_ERR_DEVICE; a no-op unless debug
+// checks are on.
+int32_t debug_finite(const void* x, bool x_fp32, int64_t n, void* stream) {
+  if (!g_debug_checks.load(std::memory_order_relaxed)) return NVFP4_OK;
+  bool finite = true;
+  const hipError_t e =
+      nvfp4::check_finite(x, x_fp32, n, static_cast<hipStream_t>(stream), &finite);
+  if (e != hipSuccess) return NVFP4_ERR_DEVICE;
+  return finite ? NVFP4_OK : NVFP4_ERR_NONFINITE;
+}
 
 bool valid_dtype(int32_t t) { return t == NVFP4_BF16 || t == NVFP4_FP32; }
 
@@ -107,6 +124,7 @@ const char* nvfp4_status_string(int32_t s) {
     case NVFP4_ERR_LAYOUT: return "operand layout or block kind does not fit the op letters";
     case NVFP4_ERR_UNSUPPORTED: return "unsupported mode";
     case NVFP4_ERR_DEVICE: return "HIP launch failed";
+    case NVFP4_ERR_NONFINITE: return "input holds an infinity or a NaN (debug check)";
     default: return "unknown status";
   }
 }
@@ -145,6 +163,9 @@ int32_t quantize_1d(const void* x, int32_t x_dtype, const int64_t* row_index, in
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
       !aligned(global_dec, 4))
     return NVFP4_ERR_ALIGN;
+  const int32_t fin =
+      debug_finite(x, x_dtype == NVFP4_FP32, (row_index ? src_rows : rows) * cols, stream);
+  if (fin != NVFP4_OK) return fin;
   nvfp4::QuantArgs a{};
   a.x = x;
   a.x_fp32 = x_dtype == NVFP4_FP32;
@@ -212,6 +233,9 @@ int32_t quantize_dual(const void* x, int32_t x_dtype, const int64_t* row_index, 
       !aligned(row_scales, 4) || !aligned(col_scales, 4) || !aligned(amax, 4) ||
       !aligned(row_global_dec, 4) || !aligned(col_global_dec, 4) || !aligned(zero_codes, 8))
     return NVFP4_ERR_ALIGN;
+  const int32_t fin =
+      debug_finite(x, x_dtype == NVFP4_FP32, (row_index ? src_rows : rows) * cols, stream);
+  if (fin != NVFP4_OK) return fin;
   nvfp4::QuantDualArgs a{};
   a.x = x;
   a.x_fp32 = x_dtype == NVFP4_FP32;
@@ -278,6 +302,8 @@ int32_t nvfp4_quantize_mse(const void* w, int32_t w_dtype, int64_t rows, int64_t
   if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
       !aligned(global_dec, 4))
     return NVFP4_ERR_ALIGN;
+  const int32_t fin = debug_finite(w, w_dtype == NVFP4_FP32, rows * cols, stream);
+  if (fin != NVFP4_OK) return fin;
   return device_status(nvfp4::launch_quantize_mse(w, w_dtype == NVFP4_FP32, rows, cols, amax,
                                                   amax_is_input != 0, codes, scales, global_dec,
                                                   static_cast<hipStream_t>(stream)));
@@ -295,6 +321,8 @@ int32_t nvfp4_quantize_2d(const void* w, int32_t w_dtype, int64_t batch, int64_t
   if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(amax, 4) ||
       !aligned(global_dec, 4))
     return NVFP4_ERR_ALIGN;
+  const int32_t fin = debug_finite(w, w_dtype == NVFP4_FP32, batch * rows * cols, stream);
+  if (fin != NVFP4_OK) return fin;
   nvfp4::Quant2dArgs a{};
   a.w = w;
   a.w_fp32 = w_dtype == NVFP4_FP32;
@@ -436,6 +464,10 @@ int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16
   if (!aligned(x, 16) || !aligned(y, 16)) return NVFP4_ERR_ALIGN;
   return device_status(nvfp4::launch_sr_fp16(x, n, rng->seed, rng->offset, rng->rounds, y,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int32_t nvfp4_set_debug_checks(int32_t on) {
+  return g_debug_checks.exchange(on != 0 ? 1 : 0, std::memory_order_relaxed);
 }
 
 int32_t nvfp4_set_single_pass_wait(int32_t wait_us) {

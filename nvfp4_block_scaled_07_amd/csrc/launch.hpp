@@ -108,6 +108,9 @@ hipError_t launch_quantize_1d(const QuantArgs& a, hipStream_t st);
 // Sets the single-pass kernels' barrier wait (microseconds; negative: do not
 // use them) and returns the previous setting.
 int set_single_pass_wait_us(int us);
+// Debug check: *finite = false when any of the n elements (a multiple of 32)
+// of the bf16 / fp32 tensor x is an infinity or a NaN.  Synchronizes st.
+hipError_t check_finite(const void* x, bool x_fp32, int64_t n, hipStream_t st, bool* finite);
 hipError_t launch_quantize_2d(const Quant2dArgs& a, hipStream_t st);
 hipError_t launch_quantize_dual(const QuantDualArgs& a, hipStream_t st);
 hipError_t launch_quantize_mse(const void* x, bool x_fp32, int64_t rows, int64_t cols,

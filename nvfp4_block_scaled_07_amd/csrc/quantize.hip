@@ -1273,6 +1273,33 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
   }
 }
 
+// ---- debug check: non-finite inputs -----------------------------------------------------------
+// One flag per call slot, set when any element of the tensor is an infinity
+// or a NaN (exponent bits all ones).  The host reads the flag after the
+// kernel and clears it again; only the entry points' debug mode runs this.
+__device__ unsigned int g_nonfinite[kSlots];
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void nonfinite_kernel(const uint4* __restrict__ x,
+                                                             int64_t chunks,
+                                                             unsigned int* __restrict__ flag) {
+  bool bad = false;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < chunks; i += stride) {
+    const uint4 q = x[i];
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      if (std::is_same<T, float>::value) {
+        bad = bad || (w[k] & 0x7F800000u) == 0x7F800000u;
+      } else {
+        bad = bad || (w[k] & 0x7F80u) == 0x7F80u || (w[k] & 0x7F800000u) == 0x7F800000u;
+      }
+    }
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flag, 1u);
+}
+
 // ---- standalone transform ------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rht_row_kernel(const T* __restrict__ x, int64_t chunks,
@@ -1653,6 +1680,33 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
   dequant_kernel<<<(unsigned)cdiv(n, kThreads), kThreads, 0, st>>>(
       reinterpret_cast<const uint32_t*>(codes), scales, gdec, rows, cols, block, y);
   return hipGetLastError();
+}
+
+hipError_t check_finite(const void* x, bool x_fp32, int64_t n, hipStream_t st, bool* finite) {
+  *finite = true;
+  if (n <= 0) return hipSuccess;
+  unsigned int* flags = nullptr;  // this device's copy of the flags
+  hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&flags), HIP_SYMBOL(g_nonfinite));
+  if (e != hipSuccess) return e;
+  unsigned int* flag = flags + next_slot();
+  const int64_t chunks = n * (x_fp32 ? 4 : 2) / 16;  // n is a multiple of 32
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv(chunks, kThreads), 4096);
+  const uint4* xv = static_cast<const uint4*>(x);
+  if (x_fp32)
+    nonfinite_kernel<float><<<grid, kThreads, 0, st>>>(xv, chunks, flag);
+  else
+    nonfinite_kernel<uint16_t><<<grid, kThreads, 0, st>>>(xv, chunks, flag);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  unsigned int v = 0;
+  e = hipMemcpyAsync(&v, flag, sizeof v, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess || v == 0) return e;
+  *finite = false;
+  const unsigned int zero = 0;
+  e = hipMemcpyAsync(flag, &zero, sizeof zero, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e;
 }
 
 }  // namespace nvfp4

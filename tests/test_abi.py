@@ -53,8 +53,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.nvfp4_abi_version() == 1
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert lib.nvfp4_status_string(s)
+    assert b"NaN" in lib.nvfp4_status_string(-7)
     assert lib.nvfp4_status_string(-99) == b"unknown status"
 
 
@@ -228,3 +229,12 @@ def test_single_pass_wait_setting(lib):
     assert lib.nvfp4_set_single_pass_wait(-7) == 123
     assert lib.nvfp4_set_single_pass_wait(0) == -1
     assert lib.nvfp4_set_single_pass_wait(prev) == 0
+
+
+def test_debug_checks_setting(lib):
+    """The debug switch is host state only: it returns the previous setting,
+    normalized to 0 / 1, and starts off."""
+    prev = lib.nvfp4_set_debug_checks(5)
+    assert prev == 0
+    assert lib.nvfp4_set_debug_checks(0) == 1
+    assert lib.nvfp4_set_debug_checks(prev) == 0
