@@ -22,7 +22,12 @@
  * Conventions for every call:
  *  - Every pointer argument except the nvfp4_operand / nvfp4_philox structs
  *    themselves is DEVICE memory owned by the caller.  The library allocates
- *    nothing, keeps no global state and never synchronizes the device.
+ *    nothing and never synchronizes the device (except in the debug mode of
+ *    nvfp4_set_debug_checks).  Its only state is two process-wide settings
+ *    (nvfp4_set_single_pass_wait, nvfp4_set_debug_checks), the host counters
+ *    that hand out its scratch slots, and that scratch itself: static device
+ *    arrays (about 1 MB per device) through which the quantizers' workgroups
+ *    combine a tensor's maximum; each call leaves them ready for the next.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it and the call returns; outputs are valid in stream
  *    order.
