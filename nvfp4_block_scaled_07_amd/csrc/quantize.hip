@@ -1206,19 +1206,34 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
     float* __restrict__ amax_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ gdec, uint64_t wait_ticks) {
   __shared__ float rtab[128];
-  const int64_t P = (int64_t)gridDim.x * kSpThreads;
-  const int64_t t0 = (int64_t)blockIdx.x * kSpThreads + threadIdx.x;
-  const int64_t cg = cols / 8;  // a multiple of 4: pairs never straddle rows
-  const int64_t units = (rows / 16) * cg;
-  const int64_t J = (units + P - 1) / P;  // rounds (wave-uniform)
-  auto load_unit = [&](int64_t j, uint4 (&qq)[16]) {  // past the end: zeros
-    const int64_t u = t0 + j * P;
-    const int64_t uc = u < units ? u : 0;
-    const int64_t g = uc / cg, c0 = (uc % cg) * 8;
+  // At most kSpMaxBytes: unit indices and byte offsets fit 32 bits.  Loads
+  // and stores go through buffer resources: the unit's first row in the
+  // vector offset, the row step (wave-uniform) in the scalar one; a unit
+  // past the end gets an offset past the range (loads read zeros).
+  const uint32_t P = gridDim.x * kSpThreads;
+  const uint32_t t0 = blockIdx.x * kSpThreads + threadIdx.x;
+  const uint32_t cols32 = (uint32_t)cols;
+  const uint32_t cg = cols32 / 8;  // a multiple of 4: pairs never straddle rows
+  const uint32_t units = (uint32_t)(rows / 16) * cg;
+  const uint32_t J = (units + P - 1) / P;  // rounds (wave-uniform)
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w), 0, (int)(rows * cols * 2), kBufFlags);
+  // Element offset of the unit of round j (its row block's first row), or
+  // kDropOff past the end.
+  auto unit_at = [&](uint32_t j, uint32_t& g, uint32_t& c0) {
+    const uint32_t u = t0 + j * P;
+    g = u / cg;
+    c0 = (u - g * cg) * 8;
+    return u < units;
+  };
+  auto load_unit = [&](uint32_t j, uint4 (&qq)[16]) {  // past the end: zeros
+    uint32_t g, c0;
+    const bool ok = unit_at(j, g, c0);
+    const uint32_t voff = ok ? (g * 16 * cols32 + c0) * 2 : kDropOff;
 #pragma unroll
     for (int r = 0; r < 16; r++)
-      qq[r] = u < units ? *reinterpret_cast<const uint4*>(w + (g * 16 + r) * cols + c0)
-                        : make_uint4(0, 0, 0, 0);
+      qq[r] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, (int)(r * cols32 * 2), 0));
   };
   auto unit_max = [&](const uint4 (&qq)[16]) {  // the block's maximum (both lanes)
     float bm = 0.0f;
@@ -1227,7 +1242,7 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
     return fmaxf(bm, xor1(bm));
   };
   float m = 0.0f;
-  for (int64_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: maximum
+  for (uint32_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: maximum
     uint4 sq[16];
     load_unit(j, sq);
     m = fmaxf(m, unit_max(sq));
@@ -1248,25 +1263,27 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
   grid_outputs(A, amax_out, gdec);
   const TensorScales ts = tensor_scales(A);
   build_recip_table(rtab, ts.S);
-  auto encode = [&](int64_t j, const uint4 (&qq)[16], float bm) {
-    const int64_t u = t0 + j * P;
-    if (u >= units) return;  // units and P are even: the lanes of a pair agree
-    const int64_t g = u / cg, c0 = (u % cg) * 8;
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc(codes, 0, (int)(rows * cols / 2), kBufFlags);
+  auto encode = [&](uint32_t j, const uint4 (&qq)[16], float bm) {
+    uint32_t g, c0;
+    if (!unit_at(j, g, c0)) return;  // units and P are even: the lanes of a pair agree
     const uint32_t e = block_code(bm, ts.k);
     const float rcp = rtab[e];
+    const uint32_t voff = g * 16 * (cols32 / 2) + c0 / 2;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       float v[8], y[8];
       RawRow<uint16_t>{qq[r]}.all(v);
 #pragma unroll
       for (int k = 0; k < 8; k++) y[k] = v[k] * rcp;
-      *reinterpret_cast<uint32_t*>(codes + (g * 16 + r) * (cols / 2) + c0 / 2) = pack8_rne(y);
+      __builtin_amdgcn_raw_buffer_store_b32(pack8_rne(y), cr, voff, (int)(r * (cols32 / 2)), 0);
     }
-    if (((u % cg) & 1) == 0) scales[g * (cols / 16) + c0 / 16] = (uint8_t)e;
+    if ((c0 & 8) == 0) scales[g * (cols32 / 16) + c0 / 16] = (uint8_t)e;
   };
 #pragma unroll
   for (int j = 0; j < kSp2dHold; j++) encode(j, q[j], bmax[j][threadIdx.x]);
-  for (int64_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: encode
+  for (uint32_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: encode
     uint4 sq[16];
     load_unit(j, sq);
     encode(j, sq, unit_max(sq));
