@@ -432,6 +432,8 @@ struct RawRow<uint16_t> {  // 8 bf16 = 4 words; column pair p is word p
     const uint32_t m = neg ? 0x80008000u : 0u;
     q = make_uint4(q.x ^ m, q.y ^ m, q.z ^ m, q.w ^ m);
   }
+  // The next column pair becomes pair 0.
+  __device__ __forceinline__ void rotate() { q = make_uint4(q.y, q.z, q.w, q.x); }
   __device__ __forceinline__ float absmax() const { return max8_bf16_bits(q); }
 };
 
@@ -462,6 +464,11 @@ struct RawRow<float> {  // named words (no array, so selects stay in registers)
     const uint32_t m = neg ? 0x80000000u : 0u;
     lo = make_uint4(lo.x ^ m, lo.y ^ m, lo.z ^ m, lo.w ^ m);
     hi = make_uint4(hi.x ^ m, hi.y ^ m, hi.z ^ m, hi.w ^ m);
+  }
+  __device__ __forceinline__ void rotate() {
+    const uint4 l = lo;
+    lo = make_uint4(lo.z, lo.w, hi.x, hi.y);
+    hi = make_uint4(hi.z, hi.w, l.x, l.y);
   }
   __device__ __forceinline__ float absmax() const {
     float v[8];
@@ -758,9 +765,14 @@ __device__ __forceinline__ void col_encode(RawRow<T> (&raw)[16], int64_t rows, i
     for (int r = 0; r < 16; r++) raw[r].flip((mask >> r) & 1u);
 #pragma unroll 1
   for (int cp = 0; cp < 4; cp++) {  // column pairs (c, c+1) share one code byte per row
+    // Pair cp is pair 0 of the rotated words (a rolled loop cannot name a
+    // register by cp without selecting among all four).
     float col[2][16];
 #pragma unroll
-    for (int r = 0; r < 16; r++) raw[r].pair(cp, col[0][r], col[1][r]);
+    for (int r = 0; r < 16; r++) {
+      raw[r].pair(0, col[0][r], col[1][r]);
+      raw[r].rotate();
+    }
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const int c = 2 * cp + h;
