@@ -743,8 +743,9 @@ __global__ __launch_bounds__(kThreads) void quant_mse_row_kernel(
   scales[b] = (uint8_t)best;
 }
 
-// ---- COL quantizer (lane: 8 cols x 16 rows = 8 blocks) ---------------------------------------
-// COL encode of one lane's 8 columns x 16 rows (8 blocks), from its raw
+// ---- COL quantizer -----------------------------------------------------------------------------
+// COL encode of one lane's 8 columns x 16 rows (8 blocks; the dual
+// quantizer's unit, whose ROW blocks need whole row segments), from its raw
 // rows: out[r] gets the 8 codes of row r, sc[0..1] the 8 scale bytes.  With
 // the transform, its sign flips are applied to raw (in place: exact
 // negations of whole rows).  The loop over column pairs is kept rolled, so
@@ -803,6 +804,50 @@ __device__ __forceinline__ void col_encode(RawRow<T> (&raw)[16], int64_t rows, i
   }
 }
 
+// COL quantizer kernel: one lane per column pair and block row (2 blocks
+// of 16 rows), whose 16 raw rows are one word (bf16) or two (fp32) each.
+// With 8 columns per lane, a rolled loop over the column pairs has to pick
+// each pair's words out of the row's four (selects or rotations, about a
+// quarter of the loop's instructions); with one pair per lane there is
+// nothing to pick, the raw rows take 16 registers instead of 64, and
+// every load and store is still coalesced (consecutive lanes read
+// consecutive words of a row and write consecutive code bytes).  A
+// workgroup takes 256 column pairs of one block row, so that each row's
+// address is a scalar base plus the lane's 32-bit column offset.
+template <typename T>
+struct RawPair;
+
+template <>
+struct RawPair<uint16_t> {  // 2 bf16 = 1 word
+  uint32_t w;
+  __device__ __forceinline__ void load_or_zero(const uint16_t* p, bool ok) {  // p readable
+    const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
+    w = ok ? t : 0u;
+  }
+  __device__ __forceinline__ void get(float& a, float& b) const {
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ void flip(bool neg) { w ^= neg ? 0x80008000u : 0u; }
+};
+
+template <>
+struct RawPair<float> {
+  uint2 w;
+  __device__ __forceinline__ void load_or_zero(const float* p, bool ok) {  // p readable
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    w = ok ? t : make_uint2(0u, 0u);
+  }
+  __device__ __forceinline__ void get(float& a, float& b) const {
+    a = __uint_as_float(w.x);
+    b = __uint_as_float(w.y);
+  }
+  __device__ __forceinline__ void flip(bool neg) {
+    const uint32_t m = neg ? 0x80000000u : 0u;
+    w = make_uint2(w.x ^ m, w.y ^ m);
+  }
+};
+
 template <typename T, bool kSR, bool kRHT, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
@@ -811,27 +856,56 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
   __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
-  const int64_t cg = cols / 8;
-  const int64_t units = (rows / 16) * cg;
-  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t uc = u < units ? u : units - 1;
-  const int64_t g = uc / cg, c0 = (uc % cg) * 8;
-  RawRow<T> raw[16];
+  const uint32_t per_row = (uint32_t)((cols / 2 + kThreads - 1) / kThreads);  // workgroups per block row
+  const int64_t g = blockIdx.x / per_row;                                 // wave-uniform
+  const uint32_t cl = ((blockIdx.x % per_row) * kThreads + threadIdx.x) * 2;
+  const bool live = cl < cols;
+  const uint32_t c0 = live ? cl : (uint32_t)cols - 2;  // idle lanes re-read the last pair
+  RawPair<T> raw[16];
 #pragma unroll
   for (int r = 0; r < 16; r++) {
-    const int64_t sr = rs.at(g * 16 + r);
+    const int64_t sr = rs.at(g * 16 + r);  // wave-uniform
     raw[r].load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
   }
   build_recip_table(rtab, ts.S);
-  if (u >= units) return;
-  uint32_t out[16], sc[2];
-  col_encode<T, kSR, kRHT>(raw, rows, g, c0, ts, rtab, mask, seed, offset, rounds, out, sc);
+  if (!live) return;
+  // The transform's sign flips: exact negations of whole rows.
+  if (kRHT)
+#pragma unroll
+    for (int r = 0; r < 16; r++) raw[r].flip((mask >> r) & 1u);
+  float col[2][16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) raw[r].get(col[0][r], col[1][r]);
+  uint32_t sc = 0;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    if (kRHT) {
+      hadamard16_unscaled(col[h]);
+#pragma unroll
+      for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * 0.25f;
+    }
+    float bm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[h][r]));
+    const uint32_t e = block_code(bm, ts.k);
+    const float rcp = rtab[e];
+    sc |= e << (8 * h);
+#pragma unroll
+    for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp;
+    if (kSR) {  // rows 0..7 take call 2 * block, rows 8..15 call 2 * block + 1
+      const uint64_t blk = (uint64_t)(c0 + h) * (uint64_t)(rows / 16) + (uint64_t)g;  // COL-major
+      sr_values8(col[h], sr_call(2 * blk, seed, offset, rounds));
+      sr_values8(col[h] + 8, sr_call(2 * blk + 1, seed, offset, rounds));
+    }
+  }
+  // RNE, or (after stochastic rounding) the exact conversion of grid values:
+  // row r's code byte holds columns c0 (low nibble) and c0 + 1.
+  uint8_t* cp0 = codes + g * 16 * (cols / 2) + c0 / 2;
 #pragma unroll
   for (int r = 0; r < 16; r++)
-    *reinterpret_cast<uint32_t*>(codes + (g * 16 + r) * (cols / 2) + c0 / 2) = out[r];
-  uint32_t* sp = reinterpret_cast<uint32_t*>(scales + g * cols + c0);
-  sp[0] = sc[0];
-  sp[1] = sc[1];
+    cp0[r * (cols / 2)] =
+        (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0);
+  *reinterpret_cast<uint16_t*>(scales + g * cols + c0) = (uint16_t)sc;
 }
 
 // ---- both 1D quantizations of a gradient from one read ---------------------------------------
@@ -1540,8 +1614,9 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     else NVFP4_ROW(false, false);
 #undef NVFP4_ROW
   } else {
-    int64_t units = (a.rows / 16) * (a.cols / 8);
-    int grid = (int)cdiv(units, kThreads);
+    int64_t grid64 = (a.rows / 16) * cdiv(a.cols / 2, (int64_t)kThreads);
+    if (grid64 > 0x7FFFFFFF) return hipErrorInvalidValue;
+    int grid = (int)grid64;
 #define NVFP4_COL(SR, RHT)                                                                        \
   quant_col_kernel<T, SR, RHT, G><<<grid, kThreads, 0, st>>>(x, a.rows, a.cols, a.amax, a.codes, \
                                                              a.scales, a.gdec, a.mask, a.seed,   \
