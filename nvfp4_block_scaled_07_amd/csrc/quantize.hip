@@ -812,8 +812,13 @@ __device__ __forceinline__ void col_encode(RawRow<T> (&raw)[16], int64_t rows, i
 // nothing to pick, the raw rows take 16 registers instead of 64, and
 // every load and store is still coalesced (consecutive lanes read
 // consecutive words of a row and write consecutive code bytes).  A
-// workgroup takes 256 column pairs of one block row, so that each row's
-// address is a scalar base plus the lane's 32-bit column offset.
+// workgroup takes 256 column pairs of one block row, so that its 16 rows
+// (and their 16 code rows) sit in one buffer resource based at the block
+// row: the lane's column in the vector offset, the row step in the scalar
+// one, no address arithmetic per row (rows up to 2^25 bytes wide; wider
+// ones, and gathered rows, are addressed by pointer).
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
+
 template <typename T>
 struct RawPair;
 
@@ -823,6 +828,9 @@ struct RawPair<uint16_t> {  // 2 bf16 = 1 word
   __device__ __forceinline__ void load_or_zero(const uint16_t* p, bool ok) {  // p readable
     const uint32_t t = *reinterpret_cast<const uint32_t*>(p);
     w = ok ? t : 0u;
+  }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    w = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
   }
   __device__ __forceinline__ void get(float& a, float& b) const {
     a = __uint_as_float(w << 16);
@@ -837,6 +845,9 @@ struct RawPair<float> {
   __device__ __forceinline__ void load_or_zero(const float* p, bool ok) {  // p readable
     const uint2 t = *reinterpret_cast<const uint2*>(p);
     w = ok ? t : make_uint2(0u, 0u);
+  }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    w = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
   }
   __device__ __forceinline__ void get(float& a, float& b) const {
     a = __uint_as_float(w.x);
@@ -861,11 +872,20 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
   const uint32_t cl = ((blockIdx.x % per_row) * kThreads + threadIdx.x) * 2;
   const bool live = cl < cols;
   const uint32_t c0 = live ? cl : (uint32_t)cols - 2;  // idle lanes re-read the last pair
+  const int64_t rb = cols * (int64_t)sizeof(T);  // bytes per row
+  const bool buf = !kGather && rb <= (1 << 25);
   RawPair<T> raw[16];
+  if (buf) {
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(x + g * 16 * cols), 0, (int)(16 * rb), kBufFlags);
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int64_t sr = rs.at(g * 16 + r);  // wave-uniform
-    raw[r].load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
+    for (int r = 0; r < 16; r++) raw[r].load_buf(xr, c0 * (uint32_t)sizeof(T), (int)(r * rb));
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int64_t sr = rs.at(g * 16 + r);  // wave-uniform
+      raw[r].load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
+    }
   }
   build_recip_table(rtab, ts.S);
   if (!live) return;
@@ -900,11 +920,21 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
   }
   // RNE, or (after stochastic rounding) the exact conversion of grid values:
   // row r's code byte holds columns c0 (low nibble) and c0 + 1.
-  uint8_t* cp0 = codes + g * 16 * (cols / 2) + c0 / 2;
+  uint8_t* cp0 = codes + g * 16 * (cols / 2);
+  if (buf) {
+    const __amdgpu_buffer_rsrc_t cr =
+        __builtin_amdgcn_make_buffer_rsrc(cp0, 0, (int)(8 * cols), kBufFlags);
 #pragma unroll
-  for (int r = 0; r < 16; r++)
-    cp0[r * (cols / 2)] =
-        (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0);
+    for (int r = 0; r < 16; r++)
+      __builtin_amdgcn_raw_buffer_store_b8(
+          (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0),
+          cr, c0 / 2, (int)(r * (cols / 2)), 0);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      cp0[r * (cols / 2) + c0 / 2] =
+          (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0);
+  }
   *reinterpret_cast<uint16_t*>(scales + g * cols + c0) = (uint16_t)sc;
 }
 
@@ -1192,7 +1222,6 @@ __device__ __forceinline__ void grid_outputs(float A, float* amax_out, float* gd
 // at most kSpMaxBytes here, so the byte offsets fit 31 bits, also for the
 // rounds past the end that a streamed batch reads (kSpStream rounds further
 // at most).
-constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
 constexpr uint32_t kDropOff = 0x80000000u;  // past every range: the store is dropped
 
 // Thread t takes the chunks of rounds j < J = ceil(chunks / P): rounds j < H
