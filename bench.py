@@ -7,10 +7,14 @@ One step = the fprop of one Super-width linear layer from bf16 inputs:
   Y = X W^T with the NVFP4 GEMM (NT), bf16 out.
 Inputs are resident in HBM before timing starts; four input sets rotate so
 that the 256 MB Infinity Cache cannot serve a step's inputs from the step
-before.  In the timed region one HIP event is recorded before every library
-call, on the stream the library launches on (torch's current stream); a
-call's time runs to the next event, which gives the per-kernel averages used
-for the roofline fractions.
+before.  The timed steps hold no mark between calls (ms_per_step and value
+come from them alone).  The same number of steps then runs again with one
+HIP event recorded before every library call, on the stream the library
+launches on (torch's current stream); a call's time runs to the next event,
+which gives the per-kernel averages used for the roofline fractions (each
+holds one event boundary, a few us).  encode_only entries time the encode
+pass alone (amax supplied), launches back to back with no mark between
+them.
 
 `--rows` adds further rows of the hot path (wgrad with RHT + stochastic
 rounding, routed-expert grouped GEMM, Ultra-width fprop/dgrad, the SSM-state
@@ -66,11 +70,15 @@ class Timer:
     def __init__(self, torch, pairs=False):
         self.torch = torch
         self.pairs = pairs
+        self.enabled = True
         self.pending = []
         self.total = {}
         self.count = {}
 
     def run(self, label, fn):
+        if not self.enabled:
+            fn()
+            return
         t = self.torch
         e0 = t.cuda.Event(enable_timing=True)
         e0.record()
@@ -115,10 +123,14 @@ def fprop_step(nv, timer, xs, ws, qx, qw, y, M, N, K, i):
 
 
 def timed(torch, timer, step, steps, warmup):
+    """Warm up, then time exactly `steps` steps between two events with no
+    mark inside (each mark between calls idles the GPU for a few us); then
+    run `steps` more with the timer's per-call marks, which only attribute
+    time to the calls (their durations each hold one mark)."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    timer.pending = []
+    timer.enabled = False
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -128,7 +140,14 @@ def timed(torch, timer, step, steps, warmup):
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timer.collect(stop)
+    timer.enabled = True
+    timer.pending = []
+    for i in range(steps):
+        step(warmup + steps + i)
+    end = torch.cuda.Event(enable_timing=True)
+    end.record()
+    torch.cuda.synchronize()
+    timer.collect(end)
     return start.elapsed_time(stop) / steps, wall
 
 
@@ -142,22 +161,28 @@ def kernel_entry(ms, work, kind):
             "frac_mfma": round(tf / MFMA_PEAK_TFLOPS, 4), "flops": int(work)}
 
 
-def encode_only(nv, torch, qx, xs, reps=20):
-    """Quantize with the amax supplied (second pass only), rotating over the
-    input sets so that the input comes from HBM, not the Infinity Cache."""
+def back_to_back(torch, call, reps=20):
+    """Average ms of call(i) over reps launches in a row, between two events
+    (no mark between the calls).  The callers rotate over their input sets so
+    that the input comes from HBM, not the Infinity Cache."""
     for i in range(3):
-        nv.nvfp4_quantize_1d(xs[i % len(xs)], nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1,
-                             qx.amax, True, qx.codes, qx.scales, qx.global_dec)
+        call(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(reps):
-        nv.nvfp4_quantize_1d(xs[i % len(xs)], nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1,
-                             qx.amax, True, qx.codes, qx.scales, qx.global_dec)
+        call(i)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def encode_only(nv, torch, qx, xs, reps=20):
+    """ROW quantize with the amax supplied (the encode pass only)."""
+    return back_to_back(torch, lambda i: nv.nvfp4_quantize_1d(
+        xs[i % len(xs)], nv.NVFP4_BLOCK_ROW, nv.NVFP4_RNE, None, -1, qx.amax, True, qx.codes,
+        qx.scales, qx.global_dec), reps)
 
 
 def gemm_traffic():
@@ -273,12 +298,21 @@ def row_wgrad(nv, synth, torch, dev, steps, warmup):
                                                     qx.operand(), dw, nv.NVFP4_FP32))
 
     ms, _ = timed(torch, timer, step, steps, warmup)
+    # The encode pass alone (amax supplied), launches back to back.
+    enc_sr = back_to_back(torch, lambda i: nv.nvfp4_quantize_1d(
+        dys[i % 3], nv.NVFP4_BLOCK_COL, nv.NVFP4_SR, rng, mask, qdy.amax, True, qdy.codes,
+        qdy.scales, qdy.global_dec))
+    enc_rne = back_to_back(torch, lambda i: nv.nvfp4_quantize_1d(
+        xs[i % 3], nv.NVFP4_BLOCK_COL, nv.NVFP4_RNE, None, mask, qx.amax, True, qx.codes,
+        qx.scales, qx.global_dec))
+    e_sr = kernel_entry(timer.avg_ms("quantize_col_rht_sr"), q1d_bytes(T, Mo), "bytes")
+    e_sr["encode_only"] = kernel_entry(enc_sr, q1d_bytes(T, Mo), "bytes")
+    e_rne = kernel_entry(timer.avg_ms("quantize_col_rht"), q1d_bytes(T, Ni), "bytes")
+    e_rne["encode_only"] = kernel_entry(enc_rne, q1d_bytes(T, Ni), "bytes")
     return {"workload": "wgrad_super: dY, X bf16 [8192x6144] COL+RHT16 (SR on dY) -> dW fp32 TN",
             "ms_per_step": round(ms, 4),
-            "quantize_col_rht_sr": kernel_entry(timer.avg_ms("quantize_col_rht_sr"),
-                                                q1d_bytes(T, Mo), "bytes"),
-            "quantize_col_rht": kernel_entry(timer.avg_ms("quantize_col_rht"), q1d_bytes(T, Ni),
-                                             "bytes"),
+            "quantize_col_rht_sr": e_sr,
+            "quantize_col_rht": e_rne,
             "gemm_tn": kernel_entry(timer.avg_ms("gemm_tn"), 2.0 * Mo * Ni * T, "flops")}
 
 
@@ -614,7 +648,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The step time settles after ~25 steps on a freshly idle MI355X (0.58 ms
+    # after 5 warm-up steps, 0.53 ms after 30): the default warms up past that.
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,ssm_sr,ptq_decode,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
@@ -657,6 +693,9 @@ def main():
     qw_e = kernel_entry(timer.avg_ms("quantize_2d"), q2d_bytes(N, K), "bytes")
     enc_ms = encode_only(nv, torch, qx, xs)
     qx_e["encode_only"] = kernel_entry(enc_ms, q1d_bytes(M, K), "bytes")
+    enc_w = back_to_back(torch, lambda i: nv.nvfp4_quantize_2d(
+        ws[i % len(ws)], qw.amax, True, qw.codes, qw.scales, qw.global_dec))
+    qw_e["encode_only"] = kernel_entry(enc_w, q2d_bytes(N, K), "bytes")
     out = {
         "metric": METRIC,
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
