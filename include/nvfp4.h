@@ -26,7 +26,7 @@
  *    nvfp4_set_debug_checks).  Its only state is two process-wide settings
  *    (nvfp4_set_single_pass_wait, nvfp4_set_debug_checks), the host counters
  *    that hand out its scratch slots, and that scratch itself: static device
- *    arrays (about 1 MB per device) through which the quantizers' workgroups
+ *    arrays (about 1.8 MB per device) through which the quantizers' workgroups
  *    combine a tensor's maximum; each call leaves them ready for the next.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it and the call returns; outputs are valid in stream
@@ -394,11 +394,13 @@ int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16
 /*
  * Tuning of the single-pass quantizers (a performance setting: results are
  * the same either way).  A bf16 tensor of at most 1 GiB quantized with ROW
- * blocks and no transform (RNE or stochastic rounding), or one bf16
- * 16x16-blocked matrix, is quantized in one launch: its workgroups keep
- * what the registers hold, stream the rest for its maximum, and meet at a
- * grid barrier to combine the tensor amax before encoding (the streamed part
- * is read again).  They wait there at most wait_us microseconds (default
+ * blocks and no transform (RNE or stochastic rounding), or bf16
+ * 16x16-blocked matrices of at most 1 GiB each (one, or a batch), is
+ * quantized in one launch: its workgroups keep what the registers hold,
+ * stream the rest for its maximum, and meet at a grid barrier to combine the
+ * tensor amax before encoding (the streamed part is read again); a batch is
+ * split over groups of workgroups that each take one matrix at a time and
+ * meet at the group's barrier.  They wait there at most wait_us microseconds (default
  * 2000); a workgroup that gives up, which only happens when other kernels
  * hold CUs (e.g. on concurrent streams), reads the whole tensor to take the
  * amax itself, so the results are unchanged but slower.  wait_us < 0 turns

@@ -1139,23 +1139,23 @@ __device__ __noinline__ float own_tensor_max(const uint16_t* x, int64_t n16) {
 constexpr int kBoardMax = 256;  // workgroups (one per CU) a board holds
 __device__ unsigned long long g_board[kSlots][kBoardMax];
 
-// Tensor amax from every workgroup's max m (all threads call it; the result
-// is returned to all).  Wave 0 polls the board, bounded by wait_ticks of the
-// real-time counter and, independently of it, by a poll count (s_sleep 2
-// between polls: at least 0.05 us each).  x, n16: the tensor, for the
-// fallback of a workgroup that gives up.
-__device__ __forceinline__ float grid_amax(float m, int slot, uint32_t epoch, const uint16_t* x,
-                                           int64_t n16, uint64_t wait_ticks) {
+// Tensor amax from the maxima m of the n workgroups sharing board[0 .. n)
+// (this one is entry me; all threads call it, the result is returned to
+// all).  Wave 0 polls the board, bounded by wait_ticks of the real-time
+// counter and, independently of it, by a poll count (s_sleep 2 between
+// polls: at least 0.05 us each).  x, n16: the tensor, for the fallback of a
+// workgroup that gives up.
+__device__ __forceinline__ float board_amax(float m, unsigned long long* board, unsigned int n,
+                                            unsigned int me, uint32_t epoch, const uint16_t* x,
+                                            int64_t n16, uint64_t wait_ticks) {
   __shared__ float bcast;
   __shared__ int late;
   float m1 = 0.0f;
   block_max2(m, m1);
-  unsigned long long* board = g_board[slot];
   if (threadIdx.x == 0)
-    __hip_atomic_store(&board[blockIdx.x], ((unsigned long long)epoch << 32) | __float_as_uint(m),
+    __hip_atomic_store(&board[me], ((unsigned long long)epoch << 32) | __float_as_uint(m),
                        __ATOMIC_RELAXED, kAgent);
   if (threadIdx.x < 64) {
-    const unsigned int n = gridDim.x;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const uint64_t max_polls = wait_ticks * 20 + 1;
     uint64_t polls = 0;
@@ -1195,12 +1195,21 @@ __device__ __forceinline__ float grid_amax(float m, int slot, uint32_t epoch, co
     }
   }
   __syncthreads();
-  if (late) {  // workgroup-uniform
-    const float a = own_tensor_max(x, n16);
-    if (threadIdx.x == 0) bcast = a;
-    __syncthreads();
-  }
-  return bcast;
+  const bool gave_up = late;  // workgroup-uniform
+  const float a = gave_up ? own_tensor_max(x, n16) : bcast;
+  __syncthreads();  // every read of bcast and late is done before a later call writes them
+  if (!gave_up) return a;
+  if (threadIdx.x == 0) bcast = a;
+  __syncthreads();
+  const float r = bcast;
+  __syncthreads();
+  return r;
+}
+
+// The whole grid's tensor amax (one workgroup per board entry).
+__device__ __forceinline__ float grid_amax(float m, int slot, uint32_t epoch, const uint16_t* x,
+                                           int64_t n16, uint64_t wait_ticks) {
+  return board_amax(m, g_board[slot], gridDim.x, blockIdx.x, epoch, x, n16, wait_ticks);
 }
 
 // The caller's amax and g, from workgroup 0 (every workgroup holds the same
@@ -1405,6 +1414,117 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
   }
 }
 
+// 16x16 blocks of a batch of bf16 matrices (the routed experts' weights),
+// each with its own amax, in one pass.  The grid (one workgroup per CU) is
+// split into `groups` groups of gridDim.x / groups workgroups, each large
+// enough to hold one matrix in its registers (streamed rounds as above when
+// it is not); group k quantizes matrices k, k + groups, k + 2 groups, ...
+// exactly as quant_2d_1pass_kernel quantizes one: load and hold, the
+// matrix's maximum through the group's own barrier, encode.  Round i of a
+// group (its i-th matrix) uses board i % 2 of the call and epoch epoch + i:
+// a workgroup can only write round i + 2's entry after every workgroup of
+// its group has written round i + 1's, i.e. after all of them have read
+// round i's, so two boards suffice.  Workgroups past the groups idle.
+__device__ unsigned long long g_board2[kSlots][2][kBoardMax];
+
+__global__ __launch_bounds__(kSpThreads) void quant_2d_batch_1pass_kernel(
+    const uint16_t* __restrict__ w, int64_t batch, int64_t rows, int64_t cols, uint32_t groups,
+    int slot, uint32_t epoch, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gdec, uint64_t wait_ticks) {
+  __shared__ float rtab[128];
+  __shared__ float bmax[kSp2dHold][kSpThreads];
+  const uint32_t gsz = gridDim.x / groups;  // workgroups per group
+  const uint32_t grp = blockIdx.x / gsz;
+  if (grp >= groups) return;  // workgroup-uniform
+  const uint32_t me = blockIdx.x - grp * gsz;
+  // Per matrix at most kSpMaxBytes: unit indices and byte offsets fit 32
+  // bits; each matrix gets buffer resources based at its first element.
+  const uint32_t P = gsz * kSpThreads;
+  const uint32_t t0 = me * kSpThreads + threadIdx.x;
+  const uint32_t cols32 = (uint32_t)cols;
+  const uint32_t cg = cols32 / 8;  // a multiple of 4: pairs never straddle rows
+  const uint32_t units = (uint32_t)(rows / 16) * cg;
+  const uint32_t J = (units + P - 1) / P;  // rounds per matrix (wave-uniform)
+  const int64_t mat = rows * cols;
+  auto unit_at = [&](uint32_t j, uint32_t& g, uint32_t& c0) {
+    const uint32_t u = t0 + j * P;
+    g = u / cg;
+    c0 = (u - g * cg) * 8;
+    return u < units;
+  };
+  auto unit_max = [&](const uint4 (&qq)[16]) {  // the block's maximum (both lanes)
+    float bm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, max8_bf16_bits(qq[r]));
+    return fmaxf(bm, xor1(bm));
+  };
+  uint32_t round = 0;
+  for (int64_t b = grp; b < batch; b += groups, round++) {
+    const uint16_t* wb = w + b * mat;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wb), 0, (int)(mat * 2), kBufFlags);
+    auto load_unit = [&](uint32_t j, uint4 (&qq)[16]) {  // past the end: zeros
+      uint32_t g, c0;
+      const bool ok = unit_at(j, g, c0);
+      const uint32_t voff = ok ? (g * 16 * cols32 + c0) * 2 : kDropOff;
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        qq[r] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, (int)(r * cols32 * 2), 0));
+    };
+    float m = 0.0f;
+    for (uint32_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: maximum
+      uint4 sq[16];
+      load_unit(j, sq);
+      m = fmaxf(m, unit_max(sq));
+    }
+    uint4 q[kSp2dHold][16];
+#pragma unroll
+    for (int j = 0; j < kSp2dHold; j++) load_unit(j, q[j]);
+#pragma unroll
+    for (int j = 0; j < kSp2dHold; j++) {
+      const float bm = unit_max(q[j]);
+      bmax[j][threadIdx.x] = bm;
+      m = fmaxf(m, bm);
+    }
+    const float A = board_amax(m, g_board2[slot][round & 1] + grp * gsz, gsz, me, epoch + round,
+                               wb, mat / 8, wait_ticks);
+    if (me == 0 && threadIdx.x == 0) {
+      amax_out[b] = A;
+      gdec[b] = tensor_scales(A).g;
+    }
+    const TensorScales ts = tensor_scales(A);
+    build_recip_table(rtab, ts.S);
+    uint8_t* cb = codes + b * (mat / 2);
+    uint8_t* sb = scales + b * (mat / 256);
+    const __amdgpu_buffer_rsrc_t cr =
+        __builtin_amdgcn_make_buffer_rsrc(cb, 0, (int)(mat / 2), kBufFlags);
+    auto encode = [&](uint32_t j, const uint4 (&qq)[16], float bm) {
+      uint32_t g, c0;
+      if (!unit_at(j, g, c0)) return;  // units and P are even: the lanes of a pair agree
+      const uint32_t e = block_code(bm, ts.k);
+      const float rcp = rtab[e];
+      const uint32_t voff = g * 16 * (cols32 / 2) + c0 / 2;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        float v[8], y[8];
+        RawRow<uint16_t>{qq[r]}.all(v);
+#pragma unroll
+        for (int k = 0; k < 8; k++) y[k] = v[k] * rcp;
+        __builtin_amdgcn_raw_buffer_store_b32(pack8_rne(y), cr, voff, (int)(r * (cols32 / 2)), 0);
+      }
+      if ((c0 & 8) == 0) sb[g * (cols32 / 16) + c0 / 16] = (uint8_t)e;
+    };
+#pragma unroll
+    for (int j = 0; j < kSp2dHold; j++) encode(j, q[j], bmax[j][threadIdx.x]);
+    for (uint32_t j = kSp2dHold; j < J; j++) {  // the rounds read twice: encode
+      uint4 sq[16];
+      load_unit(j, sq);
+      encode(j, sq, unit_max(sq));
+    }
+  }
+}
+
 // ---- debug check: non-finite inputs -----------------------------------------------------------
 // One flag per call slot, set when any element of the tensor is an infinity
 // or a NaN (exponent bits all ones).  The host reads the flag after the
@@ -1532,6 +1652,19 @@ Board next_board() {
   static std::atomic<unsigned long long> counter{0};
   const unsigned long long c = counter.fetch_add(1u, std::memory_order_relaxed);
   return Board{(int)(c % kSlots), (uint32_t)((c / kSlots) % 0xFFFFFFFFull) + 1u};
+}
+
+// The next board pair of the batched single-pass kernel (round robin over
+// kSlots) and the first of its `rounds` epochs.  Epochs come from one
+// counter for all slots, so no call's epochs repeat an earlier call's (until
+// the counter wraps after ~4e9 rounds); never 0, the value of an unused
+// entry.  rounds < 2^20.
+Board next_batch_board(uint32_t rounds) {
+  static std::atomic<unsigned int> calls{0};
+  static std::atomic<unsigned long long> epochs{0};
+  const int slot = (int)(calls.fetch_add(1u, std::memory_order_relaxed) % kSlots);
+  const unsigned long long e = epochs.fetch_add(rounds, std::memory_order_relaxed);
+  return Board{slot, (uint32_t)(e % 0xFFF00000ull) + 1u};
 }
 
 // Compute units of the current device (the single-pass grid: one workgroup
@@ -1674,6 +1807,22 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
           reinterpret_cast<const uint16_t*>(w), a.rows, a.cols, b.slot, b.epoch, a.amax, a.codes,
           a.scales, a.gdec, (uint64_t)wait_us * 100u);
       return hipGetLastError();
+    }
+    // A batch: groups of workgroups that each hold one matrix (one group
+    // streaming when a matrix needs more than the whole grid).
+    if (a.batch > 1 && !a.amax_is_input && cus > 0 && cus <= kBoardMax && wait_us >= 0 &&
+        units * 256 <= kSpMaxBytes) {
+      const int64_t need = cdiv(units, (int64_t)kSpThreads * kSp2dHold);  // workgroups per matrix
+      int64_t groups = need <= cus ? cus / need : 1;
+      if (groups > a.batch) groups = a.batch;
+      const int64_t rounds = cdiv(a.batch, groups);
+      if (rounds < (int64_t(1) << 20)) {
+        const Board b = next_batch_board((uint32_t)rounds);
+        quant_2d_batch_1pass_kernel<<<cus, kSpThreads, 0, st>>>(
+            reinterpret_cast<const uint16_t*>(w), a.batch, a.rows, a.cols, (uint32_t)groups,
+            b.slot, b.epoch, a.amax, a.codes, a.scales, a.gdec, (uint64_t)wait_us * 100u);
+        return hipGetLastError();
+      }
     }
   }
   if (!a.amax_is_input) {

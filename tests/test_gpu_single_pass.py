@@ -10,6 +10,14 @@ that replace a cleared amax output.
   rounding; equal to the two-pass path; exact when the grid barrier's wait is
   forced to give up (every late workgroup takes the tensor maximum by
   itself) and when two streams run single-pass calls at the same time.
+* Batched single pass (bf16 16x16 blocks of a batch of matrices, one amax
+  each: groups of workgroups that each hold one matrix, several matrices per
+  group in turn): bit-exact against the oracle for batches that give each
+  group one, two and three matrices (the board alternates between rounds),
+  with slices scaled apart so that a maximum taken from the wrong slice
+  shows; equal to the two-pass path, also for matrices larger than the
+  grid's registers (one group, streamed rounds); exact when the group
+  barrier's wait is forced to give up.
 * Slots: hundreds of calls in a row, more than the slots, with tensor maxima
   going up and down (a slot left dirty would hand a stale, larger maximum to
   a later call), and repeated dual quantizations whose zero-code counts must
@@ -132,6 +140,65 @@ def test_single_pass_equals_two_pass(shape):
     _same(one_w, two_w)
     _same(one_s, two_s)
     _check(one_r, O.quantize(xo, "row"))
+
+
+def _batch_input(batch, rows, cols, seed, dev):
+    """Normal slices scaled 4^(i % 7): neighbouring slices' maxima differ."""
+    x = make_input("normal", (batch, rows, cols), seed=seed)
+    x *= np.float32(4.0) ** (np.arange(batch, dtype=np.float32) % 7)[:, None, None]
+    return _bf16(x, dev)
+
+
+def _check_batch(q, xo):
+    got, ref = to_np(q), O.quantize(xo, "2d")
+    assert_same(got["amax"], ref["amax"], "amax")
+    assert_same(got["g"], ref["g"], "g")
+    assert_same(got["scales"], ref["scales"], "scales")
+    assert_same(got["codes"], ref["codes"], "codes")
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(3, 48, 96), (300, 16, 32), (37, 2688, 1024),
+                                             (5, 1024, 4096), (64, 272, 160)])
+def test_batch_2d_single_pass(batch, rows, cols):
+    """Matrices per group (one workgroup holds 1536 units of 16 x 8):
+    [16 x 32] x 300 -> 256 groups, two rounds for 44 of them; [2688 x 1024]
+    x 37 (the Super experts' shape) -> 18 groups of 14 workgroups, three
+    rounds for one group; [1024 x 4096] x 5 -> 5 groups; ragged column
+    counts (96, 160) -> pairs and rows as in the single-matrix kernel."""
+    dev = device()
+    t, xo = _batch_input(batch, rows, cols, batch + rows, dev)
+    _check_batch(nv.quantize_2d(t), xo)
+
+
+@pytest.mark.parametrize("batch,rows,cols", [(300, 16, 32), (20, 2688, 1024), (2, 8192, 8192)])
+def test_batch_2d_single_pass_equals_two_pass(batch, rows, cols):
+    """The same bits with the single-pass kernels turned off; [8192^2] x 2 is
+    larger than the grid's registers (one group, the last round streamed)."""
+    dev = device()
+    t, _ = _batch_input(batch, rows, cols, 7 * batch, dev)
+    one = nv.quantize_2d(t)
+    prev = nv.nvfp4_set_single_pass_wait(-1)
+    try:
+        two = nv.quantize_2d(t)
+    finally:
+        nv.nvfp4_set_single_pass_wait(prev)
+    _same(one, two)
+    want = t.float().abs().amax(dim=(1, 2))
+    assert torch.equal(one.amax, want), "amax"
+
+
+def test_batch_2d_single_pass_gives_up():
+    """With no wait at the group barriers every late workgroup reads its
+    matrix for the maximum: the results are still exact."""
+    dev = device()
+    t, xo = _batch_input(24, 2688, 1024, 640, dev)
+    prev = nv.nvfp4_set_single_pass_wait(0)
+    try:
+        q = nv.quantize_2d(t)
+        torch.cuda.synchronize()
+    finally:
+        nv.nvfp4_set_single_pass_wait(prev)
+    _check_batch(q, xo)
 
 
 def test_single_pass_barrier_gives_up():
