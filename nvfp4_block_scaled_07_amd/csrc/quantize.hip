@@ -859,6 +859,73 @@ struct RawPair<float> {
   }
 };
 
+// COL encode of the column pair (c0, c0 + 1) of block row g from its 16 raw
+// rows (with the transform, its sign flips are applied to raw in place:
+// exact negations of whole rows): code[r] gets row r's code byte (column c0
+// in the low nibble), the result the two scale bytes (c0's low).
+template <typename T, bool kSR, bool kRHT>
+__device__ __forceinline__ uint32_t col_pair_encode(RawPair<T> (&raw)[16], int64_t rows,
+                                                    int64_t g, uint32_t c0,
+                                                    const TensorScales& ts, const float* rtab,
+                                                    uint32_t mask, uint64_t seed,
+                                                    uint64_t offset, uint32_t rounds,
+                                                    uint32_t (&code)[16]) {
+  if (kRHT)
+#pragma unroll
+    for (int r = 0; r < 16; r++) raw[r].flip((mask >> r) & 1u);
+  float col[2][16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) raw[r].get(col[0][r], col[1][r]);
+  uint32_t sc = 0;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    if (kRHT) {
+      hadamard16_unscaled(col[h]);
+#pragma unroll
+      for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * 0.25f;
+    }
+    float bm = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[h][r]));
+    const uint32_t e = block_code(bm, ts.k);
+    const float rcp = rtab[e];
+    sc |= e << (8 * h);
+#pragma unroll
+    for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp;
+    if (kSR) {  // rows 0..7 take call 2 * block, rows 8..15 call 2 * block + 1
+      const uint64_t blk = (uint64_t)(c0 + h) * (uint64_t)(rows / 16) + (uint64_t)g;  // COL-major
+      sr_values8(col[h], sr_call(2 * blk, seed, offset, rounds));
+      sr_values8(col[h] + 8, sr_call(2 * blk + 1, seed, offset, rounds));
+    }
+  }
+  // RNE, or (after stochastic rounding) the exact conversion of grid values.
+#pragma unroll
+  for (int r = 0; r < 16; r++)
+    code[r] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0) & 0xFFu;
+  return sc;
+}
+
+// The largest |value| of the pair's 32 elements, after the transform's
+// butterflies (unscaled: the caller multiplies the maximum by 1/4) when rht.
+template <typename T, bool kRHT>
+__device__ __forceinline__ float col_pair_max(const RawPair<T> (&raw)[16], uint32_t mask) {
+  float col[2][16];
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    RawPair<T> t = raw[r];  // the caller's words stay as loaded
+    if (kRHT) t.flip((mask >> r) & 1u);
+    t.get(col[0][r], col[1][r]);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    if (kRHT) hadamard16_unscaled(col[h]);
+#pragma unroll
+    for (int r = 0; r < 16; r++) m = fmaxf(m, __builtin_fabsf(col[h][r]));
+  }
+  return m;
+}
+
 template <typename T, bool kSR, bool kRHT, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
@@ -889,51 +956,19 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
   }
   build_recip_table(rtab, ts.S);
   if (!live) return;
-  // The transform's sign flips: exact negations of whole rows.
-  if (kRHT)
-#pragma unroll
-    for (int r = 0; r < 16; r++) raw[r].flip((mask >> r) & 1u);
-  float col[2][16];
-#pragma unroll
-  for (int r = 0; r < 16; r++) raw[r].get(col[0][r], col[1][r]);
-  uint32_t sc = 0;
-#pragma unroll
-  for (int h = 0; h < 2; h++) {
-    if (kRHT) {
-      hadamard16_unscaled(col[h]);
-#pragma unroll
-      for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * 0.25f;
-    }
-    float bm = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[h][r]));
-    const uint32_t e = block_code(bm, ts.k);
-    const float rcp = rtab[e];
-    sc |= e << (8 * h);
-#pragma unroll
-    for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp;
-    if (kSR) {  // rows 0..7 take call 2 * block, rows 8..15 call 2 * block + 1
-      const uint64_t blk = (uint64_t)(c0 + h) * (uint64_t)(rows / 16) + (uint64_t)g;  // COL-major
-      sr_values8(col[h], sr_call(2 * blk, seed, offset, rounds));
-      sr_values8(col[h] + 8, sr_call(2 * blk + 1, seed, offset, rounds));
-    }
-  }
-  // RNE, or (after stochastic rounding) the exact conversion of grid values:
-  // row r's code byte holds columns c0 (low nibble) and c0 + 1.
+  uint32_t code[16];
+  const uint32_t sc = col_pair_encode<T, kSR, kRHT>(raw, rows, g, c0, ts, rtab, mask, seed, offset,
+                                                    rounds, code);
   uint8_t* cp0 = codes + g * 16 * (cols / 2);
   if (buf) {
     const __amdgpu_buffer_rsrc_t cr =
         __builtin_amdgcn_make_buffer_rsrc(cp0, 0, (int)(8 * cols), kBufFlags);
 #pragma unroll
     for (int r = 0; r < 16; r++)
-      __builtin_amdgcn_raw_buffer_store_b8(
-          (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0),
-          cr, c0 / 2, (int)(r * (cols / 2)), 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code[r], cr, c0 / 2, (int)(r * (cols / 2)), 0);
   } else {
 #pragma unroll
-    for (int r = 0; r < 16; r++)
-      cp0[r * (cols / 2) + c0 / 2] =
-          (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0);
+    for (int r = 0; r < 16; r++) cp0[r * (cols / 2) + c0 / 2] = (uint8_t)code[r];
   }
   *reinterpret_cast<uint16_t*>(scales + g * cols + c0) = (uint16_t)sc;
 }
@@ -1114,11 +1149,14 @@ constexpr int kSpThreads = 512;
 constexpr int kSpRowHold = 48;    // 16-byte chunks (8 bf16) held per thread: 192 VGPRs
 constexpr int kSpRowHoldSr = 42;  // the same with stochastic rounding (its encode needs more)
 constexpr int kSp2dHold = 3;      // 16 x 8 bf16 units held per thread: 192 VGPRs
+constexpr int kSpColHold = 8;     // COL column-pair units (16 rows x 2 bf16) held per thread
+constexpr int kSpColStream = 4;   // COL units in flight per thread in the rounds read twice
 constexpr int kSpStream = 8;      // chunks in flight per thread in the rounds read twice
 constexpr int64_t kSpMaxBytes = int64_t(1) << 30;  // single pass up to 1 GiB of bf16 (31-bit offsets)
 
 // Max of |x| over n16 16-byte chunks of bf16 by the whole workgroup (the
-// fallback of a workgroup that gave up waiting at the grid barrier).
+// fallback of a workgroup that gave up waiting at a barrier).  Kept out of
+// line and small: the kernels' registers stay live across the call.
 __device__ __noinline__ float own_tensor_max(const uint16_t* x, int64_t n16) {
   float m = 0.0f;
   for (int64_t i = threadIdx.x; i < n16; i += blockDim.x)
@@ -1127,6 +1165,45 @@ __device__ __noinline__ float own_tensor_max(const uint16_t* x, int64_t n16) {
   block_max2(m, m1);
   return m;  // valid in thread 0
 }
+
+// The same fallback for COL blocks with the transform over a [rows x cols]
+// bf16 tensor: the maximum the COL amax pass takes (after the butterflies,
+// times 1/4).
+__device__ __noinline__ float own_col_rht_max(const uint16_t* x, int64_t rows, int64_t cols,
+                                              uint32_t mask) {
+  float m = 0.0f;
+  const int64_t cp = cols / 2, units = (rows / 16) * cp;
+  for (int64_t u = threadIdx.x; u < units; u += blockDim.x) {
+    const int64_t g = u / cp, c0 = (u % cp) * 2;
+    float col[2][16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      uint32_t w = *reinterpret_cast<const uint32_t*>(x + (g * 16 + r) * cols + c0);
+      w ^= ((mask >> r) & 1u) ? 0x80008000u : 0u;
+      col[0][r] = __uint_as_float(w << 16);
+      col[1][r] = __uint_as_float(w & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      hadamard16_unscaled(col[h]);
+#pragma unroll
+      for (int r = 0; r < 16; r++) m = fmaxf(m, __builtin_fabsf(col[h][r]));
+    }
+  }
+  float m1 = 0.0f;
+  block_max2(m, m1);
+  return m * 0.25f;  // valid in thread 0
+}
+
+// What a workgroup that gave up waiting at a barrier reads to take the
+// tensor maximum itself: max |x| over n16 16-byte chunks of bf16, or (for
+// kColRht) the COL-with-transform maximum of the [rows x cols] tensor x.
+struct MaxSource {
+  const uint16_t* x;
+  int64_t n16;
+  int64_t rows, cols;
+  uint32_t mask;
+};
 
 // The grid barrier is a board: one 8-byte entry per workgroup, holding
 // (epoch << 32) | the workgroup's maximum (fp32 bits), written with a single
@@ -1143,11 +1220,12 @@ __device__ unsigned long long g_board[kSlots][kBoardMax];
 // (this one is entry me; all threads call it, the result is returned to
 // all).  Wave 0 polls the board, bounded by wait_ticks of the real-time
 // counter and, independently of it, by a poll count (s_sleep 2 between
-// polls: at least 0.05 us each).  x, n16: the tensor, for the fallback of a
-// workgroup that gives up.
+// polls: at least 0.05 us each).  src: what a workgroup that gives up reads
+// for the maximum itself.
+template <bool kColRht = false>
 __device__ __forceinline__ float board_amax(float m, unsigned long long* board, unsigned int n,
-                                            unsigned int me, uint32_t epoch, const uint16_t* x,
-                                            int64_t n16, uint64_t wait_ticks) {
+                                            unsigned int me, uint32_t epoch, const MaxSource& src,
+                                            uint64_t wait_ticks) {
   __shared__ float bcast;
   __shared__ int late;
   float m1 = 0.0f;
@@ -1196,7 +1274,13 @@ __device__ __forceinline__ float board_amax(float m, unsigned long long* board, 
   }
   __syncthreads();
   const bool gave_up = late;  // workgroup-uniform
-  const float a = gave_up ? own_tensor_max(x, n16) : bcast;
+  float a = bcast;
+  if (gave_up) {
+    if constexpr (kColRht)
+      a = own_col_rht_max(src.x, src.rows, src.cols, src.mask);
+    else
+      a = own_tensor_max(src.x, src.n16);
+  }
   __syncthreads();  // every read of bcast and late is done before a later call writes them
   if (!gave_up) return a;
   if (threadIdx.x == 0) bcast = a;
@@ -1209,7 +1293,8 @@ __device__ __forceinline__ float board_amax(float m, unsigned long long* board, 
 // The whole grid's tensor amax (one workgroup per board entry).
 __device__ __forceinline__ float grid_amax(float m, int slot, uint32_t epoch, const uint16_t* x,
                                            int64_t n16, uint64_t wait_ticks) {
-  return board_amax(m, g_board[slot], gridDim.x, blockIdx.x, epoch, x, n16, wait_ticks);
+  return board_amax(m, g_board[slot], gridDim.x, blockIdx.x, epoch,
+                    MaxSource{x, n16, 0, 0, 0u}, wait_ticks);
 }
 
 // The caller's amax and g, from workgroup 0 (every workgroup holds the same
@@ -1488,7 +1573,7 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_batch_1pass_kernel(
       m = fmaxf(m, bm);
     }
     const float A = board_amax(m, g_board2[slot][round & 1] + grp * gsz, gsz, me, epoch + round,
-                               wb, mat / 8, wait_ticks);
+                               MaxSource{wb, mat / 8, 0, 0, 0u}, wait_ticks);
     if (me == 0 && threadIdx.x == 0) {
       amax_out[b] = A;
       gdec[b] = tensor_scales(A).g;
@@ -1522,6 +1607,110 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_batch_1pass_kernel(
       load_unit(j, sq);
       encode(j, sq, unit_max(sq));
     }
+  }
+}
+
+// COL blocks (16 x 1, with or without the transform, RNE) of one bf16 matrix.
+// Thread t of the grid takes column-pair units t + j P (16 rows x 2 columns,
+// as in quant_col_kernel): rounds j < kSpColHold are held, later ones are
+// streamed (kSpColStream units in flight) for the maximum first and read
+// again after the barrier.  The maximum is
+// taken after the transform's butterflies (times 1/4 at the end, as the COL
+// amax pass does); a workgroup that gives up at the barrier takes it the
+// same way from the whole tensor.  Then every held unit is encoded exactly
+// as quant_col_kernel encodes it (the transform computed again).
+template <bool kRHT>
+__global__ __launch_bounds__(kSpThreads) void quant_col_1pass_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint32_t mask, int slot,
+    uint32_t epoch, float* __restrict__ amax_out, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ gdec, uint64_t wait_ticks) {
+  constexpr int H = kSpColHold;
+  __shared__ float rtab[128];
+  // At most kSpMaxBytes: unit indices and byte offsets fit 32 bits.  Loads
+  // and stores go through buffer resources: the unit's first row in the
+  // vector offset, the row step (wave-uniform) in the scalar one; a unit
+  // past the end gets an offset past the range (loads read zeros, stores
+  // are dropped).
+  const uint32_t P = gridDim.x * kSpThreads;
+  const uint32_t t0 = blockIdx.x * kSpThreads + threadIdx.x;
+  const uint32_t cols32 = (uint32_t)cols;
+  const uint32_t cp = cols32 / 2;
+  const uint32_t units = (uint32_t)(rows / 16) * cp;
+  const uint32_t J = (units + P - 1) / P;  // rounds (wave-uniform)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x), 0, (int)(rows * cols * 2), kBufFlags);
+  auto unit_at = [&](uint32_t j, uint32_t& g, uint32_t& c0) {
+    const uint32_t u = t0 + j * P;
+    g = u / cp;
+    c0 = (u - g * cp) * 2;
+    return u < units;
+  };
+  auto load_unit = [&](uint32_t j, RawPair<uint16_t> (&raw)[16])
+                       __attribute__((always_inline)) {  // past the end: zeros
+    uint32_t g, c0;
+    const bool ok = unit_at(j, g, c0);
+    const uint32_t voff = ok ? (g * 16 * cols32 + c0) * 2 : kDropOff;
+#pragma unroll
+    for (int r = 0; r < 16; r++) raw[r].load_buf(xr, voff, (int)(r * cols32 * 2));
+  };
+  float m = 0.0f;
+  for (uint32_t j0 = H; j0 < J; j0 += kSpColStream) {  // the rounds read twice: maximum
+    RawPair<uint16_t> sq[kSpColStream][16];
+#pragma unroll
+    for (int k = 0; k < kSpColStream; k++) load_unit(j0 + k, sq[k]);  // past the end: zeros
+#pragma unroll
+    for (int k = 0; k < kSpColStream; k++) m = fmaxf(m, col_pair_max<uint16_t, kRHT>(sq[k], mask));
+  }
+  RawPair<uint16_t> q[H][16];
+#pragma unroll
+  for (int j = 0; j < H; j++) load_unit(j, q[j]);
+  // (One unit at a time: the scheduler would otherwise interleave the units'
+  // transforms and run out of registers.)
+#pragma unroll
+  for (int j = 0; j < H; j++) {
+    m = fmaxf(m, col_pair_max<uint16_t, kRHT>(q[j], mask));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float A =
+      board_amax<kRHT>(kRHT ? m * 0.25f : m, g_board[slot], gridDim.x, blockIdx.x, epoch,
+                       MaxSource{x, rows * cols / 8, rows, cols, mask}, wait_ticks);
+  grid_outputs(A, amax_out, gdec);
+  const TensorScales ts = tensor_scales(A);
+  build_recip_table(rtab, ts.S);
+  // The encode computes the transform again from the held words.  Kept
+  // opaque to the compiler, which would otherwise keep the maximum pass's
+  // transformed values (fp32: twice the registers of the words) across the
+  // barrier and spill them.
+#pragma unroll
+  for (int j = 0; j < H; j++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) __asm__ volatile("" : "+v"(q[j][r].w));
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc(codes, 0, (int)(rows * cols / 2), kBufFlags);
+  const __amdgpu_buffer_rsrc_t sr =
+      __builtin_amdgcn_make_buffer_rsrc(scales, 0, (int)(rows / 16 * cols), kBufFlags);
+  auto encode = [&](uint32_t j, RawPair<uint16_t> (&raw)[16]) __attribute__((always_inline)) {
+    uint32_t g, c0;
+    const bool ok = unit_at(j, g, c0);
+    uint32_t code[16];
+    const uint32_t sc =
+        col_pair_encode<uint16_t, false, kRHT>(raw, rows, g, c0, ts, rtab, mask, 0, 0, 0, code);
+    const uint32_t voff = ok ? g * 16 * cp + c0 / 2 : kDropOff;
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code[r], cr, voff, (int)(r * cp), 0);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sc, sr, ok ? g * cols32 + c0 : kDropOff, 0,
+                                          0);
+  };
+#pragma unroll
+  for (int j = 0; j < H; j++) {
+    encode(j, q[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (uint32_t j = H; j < J; j++) {  // the rounds read twice: encode
+    RawPair<uint16_t> sq[16];
+    load_unit(j, sq);
+    encode(j, sq);
   }
 }
 
@@ -1721,11 +1910,27 @@ hipError_t launch_quantize_1d_t(const QuantArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   if constexpr (!G && !std::is_same<T, float>::value) {
-    // Single pass when the tensor fits in the grid's registers.
+    // Single pass (the tensor held in the grid's registers as far as they
+    // go, the rest read twice): ROW without the transform, and COL with
+    // RNE.  (COL with stochastic rounding is ALU-bound: one workgroup per CU
+    // hides less of it than the two-pass encode's eight waves per SIMD, and
+    // the single pass measured 5% slower.)
     const int64_t chunks = a.rows * a.cols / 8;
     const int cus = device_cu_count();
-    // (Not with the transform: the amax would need the transformed values.)
     const int wait_us = g_single_pass_wait_us.load(std::memory_order_relaxed);
+    if (a.axis == kBlockCol && !a.sr && !a.amax_is_input && cus > 0 && cus <= kBoardMax &&
+        wait_us >= 0 && chunks * 16 <= kSpMaxBytes) {
+      const Board b = next_board();
+      const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+      const uint64_t ticks = (uint64_t)wait_us * 100u;
+      if (a.rht)
+        quant_col_1pass_kernel<true><<<cus, kSpThreads, 0, st>>>(
+            xb, a.rows, a.cols, a.mask, b.slot, b.epoch, a.amax, a.codes, a.scales, a.gdec, ticks);
+      else
+        quant_col_1pass_kernel<false><<<cus, kSpThreads, 0, st>>>(
+            xb, a.rows, a.cols, a.mask, b.slot, b.epoch, a.amax, a.codes, a.scales, a.gdec, ticks);
+      return hipGetLastError();
+    }
     if (a.axis == kBlockRow && !a.rht && !a.amax_is_input && cus > 0 && cus <= kBoardMax &&
         wait_us >= 0 && chunks * 16 <= kSpMaxBytes) {
       const Board b = next_board();

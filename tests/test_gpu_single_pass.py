@@ -18,6 +18,13 @@ that replace a cleared amax output.
   shows; equal to the two-pass path, also for matrices larger than the
   grid's registers (one group, streamed rounds); exact when the group
   barrier's wait is forced to give up.
+* COL single pass (bf16 16x1 blocks with RNE, with and without the
+  transform; the maximum taken after the transform): equal to
+  the two-pass path for tensors smaller and larger than the grid's registers
+  (the Super and Ultra sizes stream 4 and 8 of their 12 and 16 rounds) and
+  ragged against the grid; bit-exact against the oracle; exact when the
+  barrier's wait gives up (the late workgroups transform the whole tensor
+  for the maximum themselves).
 * Slots: hundreds of calls in a row, more than the slots, with tensor maxima
   going up and down (a slot left dirty would hand a stale, larger maximum to
   a later call), and repeated dual quantizations whose zero-code counts must
@@ -199,6 +206,61 @@ def test_batch_2d_single_pass_gives_up():
     finally:
         nv.nvfp4_set_single_pass_wait(prev)
     _check_batch(q, xo)
+
+
+@pytest.mark.parametrize("shape", [(16, 32), (2000, 6144), (8192, 6144), (8192, 8192), (4096, 4160)])
+def test_col_single_pass_equals_two_pass(shape):
+    """COL with and without the transform: the same bits with the single-pass
+    kernels turned off (RNE; the SR cases take the two-pass path either way
+    and check that the setting leaves them alone)."""
+    dev = device()
+    x = make_input("laplace_zeros", shape, seed=shape[1] + 3)
+    rows = shape[0] // 16 * 16
+    t, _ = _bf16(x[:rows], dev)
+    mask = synth.rht_mask(6)
+    cases = [("rne", None, -1), ("rne", None, mask), ("sr", 21, -1), ("sr", 22, mask)]
+
+    def run():
+        return [nv.quantize_1d(t, "col", r, nv.Philox(sd) if sd else None, m) for r, sd, m in cases]
+
+    one = run()
+    prev = nv.nvfp4_set_single_pass_wait(-1)
+    try:
+        two = run()
+    finally:
+        nv.nvfp4_set_single_pass_wait(prev)
+    for a, b in zip(one, two):
+        _same(a, b)
+
+
+def test_col_single_pass_oracle():
+    """COL + RHT16 RNE in one pass, bit-exact against the oracle, on a
+    tensor whose last round is streamed ([8192 x 4160]: 8 held rounds and a
+    partial ninth on 256 CUs)."""
+    dev = device()
+    x = make_input("normal", (8192, 4160), seed=650)
+    t, xo = _bf16(x, dev)
+    mask = synth.rht_mask(6)
+    q = nv.quantize_1d(t, "col", "rne", None, mask)
+    _check(q, O.quantize(xo, "col", rht_mask=mask))
+
+
+def test_col_single_pass_gives_up():
+    """With no wait at the grid barrier the late workgroups take the
+    transform's maximum from the whole tensor: still exact."""
+    dev = device()
+    x = make_input("normal", (2000, 6144), seed=660)
+    t, xo = _bf16(x[:1984], dev)
+    mask = synth.rht_mask(6)
+    prev = nv.nvfp4_set_single_pass_wait(0)
+    try:
+        qr = nv.quantize_1d(t, "col", "rne", None, mask)
+        qp = nv.quantize_1d(t, "col")
+        torch.cuda.synchronize()
+    finally:
+        nv.nvfp4_set_single_pass_wait(prev)
+    _check(qr, O.quantize(xo, "col", rht_mask=mask))
+    _check(qp, O.quantize(xo, "col"))
 
 
 def test_single_pass_barrier_gives_up():
