@@ -394,7 +394,8 @@ int32_t nvfp4_sr_fp16(const float* x, int64_t n, const nvfp4_philox* rng, uint16
 /*
  * Tuning of the single-pass quantizers (a performance setting: results are
  * the same either way).  A bf16 tensor of at most 1 GiB quantized with ROW
- * blocks and no transform (RNE or stochastic rounding), or bf16
+ * blocks and no transform (RNE or stochastic rounding) or with COL blocks
+ * and RNE (with or without the transform), or bf16
  * 16x16-blocked matrices of at most 1 GiB each (one, or a batch), is
  * quantized in one launch: its workgroups keep what the registers hold,
  * stream the rest for its maximum, and meet at a grid barrier to combine the
