@@ -66,3 +66,38 @@ def test_pairs_bracket_each_call():
         Clock.t += 10.0  # other work between calls is not counted
     timer.collect()
     assert timer.avg_ms("w") == 1.5
+
+
+class FakeCuda:
+    Event = FakeEvent
+
+    @staticmethod
+    def synchronize():
+        pass
+
+
+def test_timed_steps_hold_no_marks_and_attribution_runs_after():
+    """bench.timed: warm-up, then exactly `steps` steps between two events with
+    the timer disabled (no mark inside), then as many more with per-call marks,
+    whose durations are attributed to the labels."""
+    torch = types.SimpleNamespace(cuda=FakeCuda)
+    timer = bench.Timer(torch)
+    seen = []
+    marks_in_timed = []
+
+    def step(i):
+        seen.append(i)
+        n0 = len(timer.pending)
+        timer.run("q", lambda: setattr(Clock, "t", Clock.t + 1.0))
+        timer.run("g", lambda: setattr(Clock, "t", Clock.t + 4.0))
+        if not timer.enabled:
+            marks_in_timed.append(len(timer.pending) - n0)
+
+    Clock.t = 0.0
+    ms, _ = bench.timed(torch, timer, step, steps=3, warmup=2)
+    assert seen == [0, 1, 2, 3, 4, 5, 6, 7]  # 2 warm-up, 3 timed, 3 attributed
+    assert marks_in_timed == [0, 0, 0]
+    assert ms == 5.0
+    assert timer.count == {"q": 3, "g": 3}
+    assert timer.avg_ms("q") == 1.0 and timer.avg_ms("g") == 4.0
+    assert timer.enabled
