@@ -804,21 +804,9 @@ __device__ __forceinline__ void col_encode(RawRow<T> (&raw)[16], int64_t rows, i
   }
 }
 
-// COL quantizer kernel: one lane per column pair and block row (2 blocks
-// of 16 rows), whose 16 raw rows are one word (bf16) or two (fp32) each.
-// With 8 columns per lane, a rolled loop over the column pairs has to pick
-// each pair's words out of the row's four (selects or rotations, about a
-// quarter of the loop's instructions); with one pair per lane there is
-// nothing to pick, the raw rows take 16 registers instead of 64, and
-// every load and store is still coalesced (consecutive lanes read
-// consecutive words of a row and write consecutive code bytes).  A
-// workgroup takes 256 column pairs of one block row, so that its 16 rows
-// (and their 16 code rows) sit in one buffer resource based at the block
-// row: the lane's column in the vector offset, the row step in the scalar
-// one, no address arithmetic per row (rows up to 2^25 bytes wide; wider
-// ones, and gathered rows, are addressed by pointer).
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
 
+// The raw words of one column pair in one row (the COL kernels' lane unit).
 template <typename T>
 struct RawPair;
 
@@ -926,6 +914,19 @@ __device__ __forceinline__ float col_pair_max(const RawPair<T> (&raw)[16], uint3
   return m;
 }
 
+// COL quantizer kernel: one lane per column pair and block row (2 blocks
+// of 16 rows), whose 16 raw rows are one word (bf16) or two (fp32) each.
+// With 8 columns per lane, a rolled loop over the column pairs has to pick
+// each pair's words out of the row's four (selects or rotations, about a
+// quarter of the loop's instructions); with one pair per lane there is
+// nothing to pick, the raw rows take 16 registers instead of 64, and
+// every load and store is still coalesced (consecutive lanes read
+// consecutive words of a row and write consecutive code bytes).  A
+// workgroup takes 256 column pairs of one block row, so that its 16 rows
+// (and their 16 code rows) sit in one buffer resource based at the block
+// row: the lane's column in the vector offset, the row step in the scalar
+// one, no address arithmetic per row (rows up to 2^25 bytes wide; wider
+// ones, and gathered rows, are addressed by pointer).
 template <typename T, bool kSR, bool kRHT, bool kGather = false>
 __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
