@@ -805,6 +805,7 @@ __device__ __forceinline__ void col_encode(RawRow<T> (&raw)[16], int64_t rows, i
 }
 
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
+constexpr uint32_t kDropOff = 0x80000000u;  // past every range: loads read 0, stores are dropped
 
 // The raw words of one column pair in one row (the COL kernels' lane unit).
 template <typename T>
@@ -1131,6 +1132,55 @@ __global__ __launch_bounds__(kThreads) void quant_2d_kernel(
   if (((uc % cg) & 1) == 0) ss[g * (cols / 16) + c0 / 16] = (uint8_t)e;
 }
 
+// The same for bf16, a workgroup per 256 units of one block row: its 16 rows
+// (and their 16 code rows) sit in one buffer resource based at the block
+// row, the lane's column in the vector offset and the row step in the scalar
+// one, so no address arithmetic runs per row; the rows stay raw words (64
+// registers instead of 128 floats) until the encode converts them.  Lanes
+// past the row's end read zeros and store nothing.  Rows up to 2^26 bytes
+// wide (16 of them in one 31-bit range).
+__global__ __launch_bounds__(kThreads) void quant_2d_bf16_kernel(
+    const uint16_t* __restrict__ w, int64_t rows, int64_t cols, const float* __restrict__ amax,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec) {
+  __shared__ float rtab[128];
+  const int64_t slice = blockIdx.y;
+  const TensorScales ts = tensor_scales(amax[slice]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) gdec[slice] = ts.g;
+  const uint32_t cg = (uint32_t)(cols / 8);  // units per block row: even (pairs agree)
+  const uint32_t per_row = (cg + kThreads - 1) / kThreads;
+  const int64_t g = slice * (rows / 16) + blockIdx.x / per_row;  // block row (wave-uniform)
+  const uint32_t cu = (blockIdx.x % per_row) * kThreads + threadIdx.x;
+  const bool live = cu < cg;
+  const int rb = (int)(cols * 2);  // bytes per row
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w + g * 16 * cols), 0, 16 * rb, kBufFlags);
+  const uint32_t voff = live ? cu * 16 : kDropOff;
+  uint4 q[16];
+#pragma unroll
+  for (int r = 0; r < 16; r++)
+    q[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, r * rb, 0));
+  float bm = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; r++) bm = fmaxf(bm, max8_bf16_bits(q[r]));
+  bm = fmaxf(bm, xor1(bm));
+  build_recip_table(rtab, ts.S);
+  if (!live) return;
+  const uint32_t e = block_code(bm, ts.k);
+  const float rcp = rtab[e];
+  const int cb = (int)(cols / 2);  // code bytes per row
+  const __amdgpu_buffer_rsrc_t cr =
+      __builtin_amdgcn_make_buffer_rsrc(codes + g * 16 * cb, 0, 16 * cb, kBufFlags);
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    float v[8], y[8];
+    RawRow<uint16_t>{q[r]}.all(v);
+#pragma unroll
+    for (int k = 0; k < 8; k++) y[k] = v[k] * rcp;
+    __builtin_amdgcn_raw_buffer_store_b32(pack8_rne(y), cr, cu * 4, r * cb, 0);
+  }
+  if ((cu & 1) == 0) scales[g * (cols / 16) + cu / 2] = (uint8_t)e;
+}
+
 // ---- single-pass quantizers (tensor amax and encode in one launch) -------------------------
 // A bf16 tensor is read once as far as the registers of one workgroup per CU
 // hold it: every thread loads its share and keeps it, the workgroups combine
@@ -1317,7 +1367,6 @@ __device__ __forceinline__ void grid_outputs(float A, float* amax_out, float* gd
 // at most kSpMaxBytes here, so the byte offsets fit 31 bits, also for the
 // rounds past the end that a streamed batch reads (kSpStream rounds further
 // at most).
-constexpr uint32_t kDropOff = 0x80000000u;  // past every range: the store is dropped
 
 // Thread t takes the chunks of rounds j < J = ceil(chunks / P): rounds j < H
 // (kSpRowHold, or kSpRowHoldSr with stochastic rounding, whose encode needs
@@ -2043,6 +2092,15 @@ hipError_t launch_quantize_2d_t(const Quant2dArgs& a, hipStream_t st) {
       const int64_t per = a.batch >= 512 ? 1 : 512 / a.batch;
       dim3 grid((unsigned)amax_grid(chunks, u, per), (unsigned)a.batch);
       amax_flat_kernel<T, false><<<grid, kAmaxThreads, 0, st>>>(w, chunks, 0, a.amax, nullptr, -1);
+    }
+  }
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (a.cols < (int64_t(1) << 25)) {  // 16 rows of bf16 in a 31-bit range
+      const int64_t blocks = (a.rows / 16) * cdiv(a.cols / 8, kThreads);
+      if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+      quant_2d_bf16_kernel<<<dim3((unsigned)blocks, (unsigned)a.batch), kThreads, 0, st>>>(
+          w, a.rows, a.cols, a.amax, a.codes, a.scales, a.gdec);
+      return hipGetLastError();
     }
   }
   int64_t units = (a.rows / 16) * (a.cols / 8);
