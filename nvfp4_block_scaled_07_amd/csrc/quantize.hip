@@ -1455,11 +1455,44 @@ __global__ __launch_bounds__(kSpThreads) void quant_row_1pass_kernel(
   }
 }
 
-// 16x16 blocks of one bf16 matrix.  Thread t of the grid takes units t + j P
-// (16 rows x 8 columns, as in quant_2d_kernel; lanes 2t and 2t+1 hold the two
-// halves of a block): rounds j < kSp2dHold are held, later ones (when there
-// are more) are streamed for the maximum first and read again after the
-// barrier, as in the ROW kernel.
+// The units of a single pass over n workgroups of kSpThreads threads.
+// Whole rounds go over the grid as one stream (unit t + j P for grid thread
+// t, P = n kSpThreads: concurrent loads cover one contiguous span).  The
+// partial last round, when there is one, is split evenly: each workgroup
+// takes `per` consecutive units of it (ceil(rem / n), rounded up to even so
+// that the two lanes of a block agree), on its first `per` threads.  Handing
+// the partial round out as the whole ones left it to the first workgroups
+// only (a [6144 x 6144] matrix is 2.25 rounds: 64 CUs loaded 3 units per
+// thread, 192 loaded 2), and a pass runs at the pace of its busiest CUs.
+// Giving every workgroup one contiguous range of the whole tensor instead
+// made the [8192 x 8192] pass slower (51.7 -> 58.5 us): 256 concurrent
+// streams 512 KB apart.  unit() is false where the round has no unit for
+// the thread (the caller then loads zeros and stores nothing).  Unit
+// indices fit 32 bits: a matrix here is at most kSpMaxBytes.
+struct SpShare {
+  uint32_t units, P, full, tail0, per, b;
+  __device__ SpShare(uint32_t units_, uint32_t n, uint32_t b_) : units(units_), b(b_) {
+    P = n * kSpThreads;
+    full = units_ / P;
+    tail0 = full * P;
+    per = ((units_ - tail0 + n - 1) / n + 1) & ~1u;
+  }
+  __device__ uint32_t rounds() const { return full + (tail0 < units ? 1u : 0u); }
+  __device__ bool unit(uint32_t j, uint32_t t, uint32_t& u) const {
+    if (j < full) {
+      u = b * kSpThreads + t + j * P;
+      return true;
+    }
+    u = tail0 + b * per + t;
+    return j == full && t < per && u < units;
+  }
+};
+
+// 16x16 blocks of one bf16 matrix.  Units are 16 rows x 8 columns, as in
+// quant_2d_kernel (lanes 2t and 2t+1 hold the two halves of a block), handed
+// out in rounds as SpShare says: rounds j < kSp2dHold are held, later ones
+// (when there are more) are streamed for the maximum first and read again
+// after the barrier, as in the ROW kernel.
 __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
     const uint16_t* __restrict__ w, int64_t rows, int64_t cols, int slot, uint32_t epoch,
     float* __restrict__ amax_out, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -1469,21 +1502,21 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
   // and stores go through buffer resources: the unit's first row in the
   // vector offset, the row step (wave-uniform) in the scalar one; a unit
   // past the end gets an offset past the range (loads read zeros).
-  const uint32_t P = gridDim.x * kSpThreads;
-  const uint32_t t0 = blockIdx.x * kSpThreads + threadIdx.x;
   const uint32_t cols32 = (uint32_t)cols;
   const uint32_t cg = cols32 / 8;  // a multiple of 4: pairs never straddle rows
   const uint32_t units = (uint32_t)(rows / 16) * cg;
-  const uint32_t J = (units + P - 1) / P;  // rounds (wave-uniform)
+  const SpShare sh(units, gridDim.x, blockIdx.x);
+  const uint32_t J = sh.rounds();  // wave-uniform
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(w), 0, (int)(rows * cols * 2), kBufFlags);
-  // Element offset of the unit of round j (its row block's first row), or
-  // kDropOff past the end.
+  // Row block g and first column c0 of the thread's unit of round j; false
+  // when the round has no unit for the thread.
   auto unit_at = [&](uint32_t j, uint32_t& g, uint32_t& c0) {
-    const uint32_t u = t0 + j * P;
+    uint32_t u;
+    const bool ok = sh.unit(j, threadIdx.x, u);
     g = u / cg;
     c0 = (u - g * cg) * 8;
-    return u < units;
+    return ok;
   };
   auto load_unit = [&](uint32_t j, uint4 (&qq)[16]) {  // past the end: zeros
     uint32_t g, c0;
@@ -1526,7 +1559,7 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_1pass_kernel(
       __builtin_amdgcn_make_buffer_rsrc(codes, 0, (int)(rows * cols / 2), kBufFlags);
   auto encode = [&](uint32_t j, const uint4 (&qq)[16], float bm) {
     uint32_t g, c0;
-    if (!unit_at(j, g, c0)) return;  // units and P are even: the lanes of a pair agree
+    if (!unit_at(j, g, c0)) return;  // share and units are even: the lanes of a pair agree
     const uint32_t e = block_code(bm, ts.k);
     const float rcp = rtab[e];
     const uint32_t voff = g * 16 * (cols32 / 2) + c0 / 2;
@@ -1574,18 +1607,18 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_batch_1pass_kernel(
   const uint32_t me = blockIdx.x - grp * gsz;
   // Per matrix at most kSpMaxBytes: unit indices and byte offsets fit 32
   // bits; each matrix gets buffer resources based at its first element.
-  const uint32_t P = gsz * kSpThreads;
-  const uint32_t t0 = me * kSpThreads + threadIdx.x;
   const uint32_t cols32 = (uint32_t)cols;
   const uint32_t cg = cols32 / 8;  // a multiple of 4: pairs never straddle rows
   const uint32_t units = (uint32_t)(rows / 16) * cg;
-  const uint32_t J = (units + P - 1) / P;  // rounds per matrix (wave-uniform)
+  const SpShare sh(units, gsz, me);  // the group's workgroups share a matrix
+  const uint32_t J = sh.rounds();      // rounds per matrix (wave-uniform)
   const int64_t mat = rows * cols;
   auto unit_at = [&](uint32_t j, uint32_t& g, uint32_t& c0) {
-    const uint32_t u = t0 + j * P;
+    uint32_t u;
+    const bool ok = sh.unit(j, threadIdx.x, u);
     g = u / cg;
     c0 = (u - g * cg) * 8;
-    return u < units;
+    return ok;
   };
   auto unit_max = [&](const uint4 (&qq)[16]) {  // the block's maximum (both lanes)
     float bm = 0.0f;
@@ -1636,7 +1669,7 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_batch_1pass_kernel(
         __builtin_amdgcn_make_buffer_rsrc(cb, 0, (int)(mat / 2), kBufFlags);
     auto encode = [&](uint32_t j, const uint4 (&qq)[16], float bm) {
       uint32_t g, c0;
-      if (!unit_at(j, g, c0)) return;  // units and P are even: the lanes of a pair agree
+      if (!unit_at(j, g, c0)) return;  // share and units are even: the lanes of a pair agree
       const uint32_t e = block_code(bm, ts.k);
       const float rcp = rtab[e];
       const uint32_t voff = g * 16 * (cols32 / 2) + c0 / 2;
@@ -1661,8 +1694,8 @@ __global__ __launch_bounds__(kSpThreads) void quant_2d_batch_1pass_kernel(
 }
 
 // COL blocks (16 x 1, with or without the transform, RNE) of one bf16 matrix.
-// Thread t of the grid takes column-pair units t + j P (16 rows x 2 columns,
-// as in quant_col_kernel): rounds j < kSpColHold are held, later ones are
+// Column-pair units (16 rows x 2 columns, as in quant_col_kernel) are handed
+// out in rounds as SpShare says: rounds j < kSpColHold are held, later ones are
 // streamed (kSpColStream units in flight) for the maximum first and read
 // again after the barrier.  The maximum is
 // taken after the transform's butterflies (times 1/4 at the end, as the COL
@@ -1681,19 +1714,19 @@ __global__ __launch_bounds__(kSpThreads) void quant_col_1pass_kernel(
   // vector offset, the row step (wave-uniform) in the scalar one; a unit
   // past the end gets an offset past the range (loads read zeros, stores
   // are dropped).
-  const uint32_t P = gridDim.x * kSpThreads;
-  const uint32_t t0 = blockIdx.x * kSpThreads + threadIdx.x;
   const uint32_t cols32 = (uint32_t)cols;
   const uint32_t cp = cols32 / 2;
   const uint32_t units = (uint32_t)(rows / 16) * cp;
-  const uint32_t J = (units + P - 1) / P;  // rounds (wave-uniform)
+  const SpShare sh(units, gridDim.x, blockIdx.x);
+  const uint32_t J = sh.rounds();  // wave-uniform
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x), 0, (int)(rows * cols * 2), kBufFlags);
   auto unit_at = [&](uint32_t j, uint32_t& g, uint32_t& c0) {
-    const uint32_t u = t0 + j * P;
+    uint32_t u;
+    const bool ok = sh.unit(j, threadIdx.x, u);
     g = u / cp;
     c0 = (u - g * cp) * 2;
-    return u < units;
+    return ok;
   };
   auto load_unit = [&](uint32_t j, RawPair<uint16_t> (&raw)[16])
                        __attribute__((always_inline)) {  // past the end: zeros
