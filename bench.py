@@ -40,6 +40,12 @@ METRIC = "NVFP4 GEMM TFLOP/s + quantize GB/s at 1 MI355X, % of MFMA/HBM roofline
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 COPY_BYTES = 256 * 1024 * 1024  # calibration copy: reads and writes this many bytes
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+# On a freshly idle MI355X the fprop GEMM's launches run 470 -> 600 us and
+# settle at ~458 us only after about 30 of them (~15 ms of MFMA work; hipBLASLt's
+# GEMMs show the same ramp), so at least this many untimed steps (settle steps
+# plus warm-up steps) run before the timed ones.  The JSON line reports the
+# settle steps beside the requested warm-up.
+SETTLE_STEPS = 40
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "fprop_super_hbm_traffic.txt")
@@ -122,11 +128,17 @@ def fprop_step(nv, timer, xs, ws, qx, qw, y, M, N, K, i):
                                                 nv.NVFP4_BF16))
 
 
-def timed(torch, timer, step, steps, warmup):
-    """Warm up, then time exactly `steps` steps between two events with no
-    mark inside (each mark between calls idles the GPU for a few us); then
-    run `steps` more with the timer's per-call marks, which only attribute
-    time to the calls (their durations each hold one mark)."""
+def timed(torch, timer, step, steps, warmup, settle=0):
+    """Settle and warm up, then time exactly `steps` steps between two events
+    with no mark inside (each mark between calls idles the GPU for a few us);
+    then run `steps` more with the timer's per-call marks, which only
+    attribute time to the calls (their durations each hold one mark).
+    settle: steps run before the warm-up, untimed and unmarked, so that the
+    timed steps start at the device's steady clock (see SETTLE_STEPS)."""
+    timer.enabled = False
+    for i in range(settle):
+        step(i)
+    timer.enabled = True
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -648,8 +660,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The step time settles after ~25 steps on a freshly idle MI355X (0.58 ms
-    # after 5 warm-up steps, 0.53 ms after 30): the default warms up past that.
+    # Fewer than SETTLE_STEPS warm-up steps are topped up by settle steps.
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--rows", default="", help="comma list of extra rows: wgrad,dy_dual,grouped,grouped_bwd,ultra,grouped_ultra,ssm_sr,ptq_decode,all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -683,10 +694,11 @@ def main():
     log("generating inputs")
     xs, ws, qx, qw, y = fprop_setup(nv, synth, torch, dev, M, N, K, sets=4)
     timer = Timer(torch)
-    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    settle = max(0, SETTLE_STEPS - args.warmup)
+    log(f"timing {args.steps} steps after {settle} settle and {args.warmup} warm-up steps")
     ms, wall = timed(torch, timer,
                      lambda i: fprop_step(nv, timer, xs, ws, qx, qw, y, M, N, K, i),
-                     args.steps, args.warmup)
+                     args.steps, args.warmup, settle)
     flops = 2.0 * M * N * K
     g = kernel_entry(timer.avg_ms("gemm_nt"), flops, "flops")
     qx_e = kernel_entry(timer.avg_ms("quantize_1d"), q1d_bytes(M, K), "bytes")
@@ -701,6 +713,7 @@ def main():
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "nvfp4 codes -> f16 MFMA, f32 accumulate",
