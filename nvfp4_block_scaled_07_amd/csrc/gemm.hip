@@ -1384,7 +1384,7 @@ hipError_t launch_depth(const GemmArgs& a, int cus, hipStream_t st) {
     if (a.b_kmajor) return launch_dense<Cfg<128, 256, 1, 8, BK>, true, true>(a, st);
     return launch_dense<Cfg<128, 256, 1, 8, BK>, true, false>(a, st);
   }
-  if (c192 < c256) return launch_layout<Cfg<192, 256, 2, 4, BK, BK>>(a, st);
+  if (c192 < c256) return launch_layout<Cfg<192, 256, 1, 8, BK, BK>>(a, st);
   return launch_layout<Cfg<256, 256, 2, 4, BK>>(a, st);
 }
 
@@ -1410,7 +1410,10 @@ hipError_t launch_grouped(const GroupedArgs& a, int cus, hipStream_t st) {
 // A images (48 KB each) fill the 160 KB of LDS exactly, and a barrier then
 // comes every 48 MFMAs of a wave instead of 24 (6144 x 6144 x 8192: TN
 // 0.531 -> 0.513 ms, NN 0.518 -> 0.503 ms, NT unchanged).  The 256-row
-// tile's 128-k images would not fit beside its stages.  Tile: the 256- and 192-row shapes run at
+// tile's 128-k images would not fit beside its stages.  Its eight waves sit
+// side by side (192 x 32 each: 6 MFMAs and one B decode per step, where
+// 2 x 4 waves of 96 x 64 decoded each B fragment twice, two per 6 MFMAs):
+// TN 0.529 -> 0.497 ms, NN 0.509 -> 0.492 ms, NT unchanged.  Tile: the 256- and 192-row shapes run at
 // about the same rate per output, so take the one whose last round of
 // workgroups leaves the fewest CUs idle (cost = rounds of tiles times tile
 // area).  With A K-major (NT, NN) a 128-row tile also competes, at a 5/4
