@@ -214,13 +214,14 @@ def gemm_traffic():
 
 
 # ---- CPU baseline: the oracle on a bounded sample of the same step ---------------------------
-def cpu_baseline(torch, synth, xs, ws, M, N, K, q_rows=1024, g_rows=64):
-    """The oracle on fixed slices of the fprop step: ROW quantization of
-    q_rows rows of X and 16x16 quantization of q_rows rows of W (one core
-    each, amax given: those blocks only see their own rows), and the fp64
-    GEMM reference of g_rows full rows of Y (g_rows x N outputs over all of K,
-    OpenMP over all host cores).  Each part is timed and scaled to the full
-    step by its share of rows."""
+def cpu_baseline(torch, synth, xs, ws, M, N, K, q_rows=2048, g_rows=128, g1_rows=8):
+    """The oracle on fixed slices of the fprop step (about 15 s of host work):
+    ROW quantization of q_rows rows of X and 16x16 quantization of q_rows
+    rows of W (one core each, amax given: those blocks only see their own
+    rows), and the fp64 GEMM reference of g_rows full rows of Y (g_rows x N
+    outputs over all of K, OpenMP over all host cores).  Each part is timed
+    and scaled to the full step by its share of rows.  The GEMM reference is
+    also timed on one core over g1_rows rows, reported beside it."""
     import numpy as np
 
     import oracle as O
@@ -240,24 +241,35 @@ def cpu_baseline(torch, synth, xs, ws, M, N, K, q_rows=1024, g_rows=64):
     qw_full = O.quantize(wb_all, "2d", amax=amax_w)  # the GEMM's B (not timed)
     A = dict(codes=qa["codes"], scales=qa["scales"], block="row", g=qa["g"])
     B = dict(codes=qw_full["codes"], scales=qw_full["scales"], block="2d", g=qw_full["g"])
-    ii = np.repeat(np.arange(g_rows), N)
-    jj = np.tile(np.arange(N), g_rows)
-    t0 = time.perf_counter()
-    O.gemm_entries("N", "T", q_rows, N, K, A, B, ii, jj)
-    t_g = time.perf_counter() - t0
+
+    def gemm_rows(rows):
+        ii = np.repeat(np.arange(rows), N)
+        jj = np.tile(np.arange(N), rows)
+        t0 = time.perf_counter()
+        O.gemm_entries("N", "T", q_rows, N, K, A, B, ii, jj)
+        return time.perf_counter() - t0
+
+    used = O.set_threads(threads)
+    t_g = gemm_rows(g_rows)
+    O.set_threads(1)
+    t_g1 = gemm_rows(g1_rows)
+    O.set_threads(used)
     est = t_qx * (M / q_rows) + t_qw * (N / q_rows) + t_g * (M / g_rows)
     flops = 2.0 * M * N * K
     return {
-        "value": round(flops / est / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+        "value": round(flops / est / 1e12, 6), "unit": "TFLOP/s", "cores": used,
         "kind": "oracle",
         "sample": (f"oracle ROW quantize of {q_rows} of {M} rows of X and 16x16 quantize of "
                    f"{q_rows} of {N} rows of W (1 core each), fp64 GEMM reference of {g_rows} "
-                   f"full rows of Y ({g_rows} x {N} outputs, K = {K}; {threads} OpenMP "
+                   f"full rows of Y ({g_rows} x {N} outputs, K = {K}; {used} OpenMP "
                    f"threads); each part scaled to the full step by rows"),
         "est_step_s": round(est, 2),
-        "sample_seconds": round(t_qx + t_qw + t_g, 2),
+        "sample_seconds": round(t_qx + t_qw + t_g + t_g1, 2),
         "parts_s": {"quantize_x": round(t_qx, 3), "quantize_w": round(t_qw, 3),
                     "gemm_rows": round(t_g, 3)},
+        "gemm_1core": {"rows": g1_rows, "s": round(t_g1, 3),
+                       "est_full_gemm_s": round(t_g1 * (M / g1_rows), 1),
+                       "speedup_all_cores": round((t_g1 / g1_rows) / (t_g / g_rows), 2)},
     }
 
 

@@ -74,6 +74,8 @@ def lib():
                                           vp, vp, C.c_int, C.c_float,
                                           vp, vp, C.c_int, C.c_float,
                                           vp, vp, i64, vp, vp]
+        L.oracle_set_threads.restype = C.c_int
+        L.oracle_set_threads.argtypes = [C.c_int]
         L.oracle_gemm_full.restype = C.c_int
         L.oracle_gemm_full.argtypes = [C.c_char, C.c_char, i64, i64, i64,
                                        vp, vp, C.c_int, C.c_float,
@@ -323,6 +325,12 @@ def gemm_entries(opA, opB, M, N, K, A, B, ii, jj):
                                    _ptr(R), _ptr(D))
     _check(rc, "gemm_entries")
     return R, D
+
+
+def set_threads(n):
+    """OpenMP threads of the oracle's parallel loops for later calls from this
+    thread (n <= 0: unchanged); returns the count in force."""
+    return lib().oracle_set_threads(int(n))
 
 
 def gemm_full(opA, opB, M, N, K, A, B):

@@ -15,6 +15,9 @@
 #include <float.h>
 #include <string.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ========================================================================
  * Element formats
@@ -519,6 +522,16 @@ int oracle_gemm_entries(char opA, char opB, int64_t M, int64_t N, int64_t K,
     D[t] = gg * mag;
   }
   return 0;
+}
+
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
 }
 
 int oracle_gemm_full(char opA, char opB, int64_t M, int64_t N, int64_t K,

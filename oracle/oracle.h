@@ -132,6 +132,12 @@ int oracle_gemm_entries(char opA, char opB, int64_t M, int64_t N, int64_t K,
                         const int64_t* ii, const int64_t* jj, int64_t n,
                         double* R, double* D);
 
+/* Threads of the OpenMP loops above (the fp64 GEMM references and the
+ * array encoders): n > 0 sets them for later calls from this host thread,
+ * n <= 0 leaves them.  Returns the count now in force.  Used to time the
+ * reference on one core and on all of them; results do not depend on it. */
+int oracle_set_threads(int n);
+
 /* Whole-matrix fp64 reference (R and D both [M][N]); threads over rows. */
 int oracle_gemm_full(char opA, char opB, int64_t M, int64_t N, int64_t K,
                      const uint8_t* a_codes, const uint8_t* a_scales,

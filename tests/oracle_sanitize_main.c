@@ -109,6 +109,14 @@ int main(void) {
     CHECK(oracle_gemm_entries('N', 'T', M, N, K, ac, as, ORACLE_ROW, ga, bc, bs, ORACLE_2D, gb,
                               ii, jj, 3, Re, De) == 0);
     for (int t = 0; t < 3; t++) CHECK(Re[t] == R_[ii[t] * N + jj[t]]);
+    /* One thread: the same values (the thread count only splits the outputs) */
+    const int threads = oracle_set_threads(0);
+    CHECK(threads >= 1);
+    CHECK(oracle_set_threads(1) == 1);
+    CHECK(oracle_gemm_entries('N', 'T', M, N, K, ac, as, ORACLE_ROW, ga, bc, bs, ORACLE_2D, gb,
+                              ii, jj, 3, Re, De) == 0);
+    for (int t = 0; t < 3; t++) CHECK(Re[t] == R_[ii[t] * N + jj[t]]);
+    CHECK(oracle_set_threads(threads) == threads);
     /* B stored [K][N] with COL blocks (NN), A stored [K][M] with COL (TN) */
     float* bt = xmalloc(K * N * sizeof(float));
     float* at = xmalloc(K * M * sizeof(float));
