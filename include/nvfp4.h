@@ -158,8 +158,9 @@ int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t 
                           uint8_t* codes, uint8_t* scales, float* global_dec, void* stream);
 
 /*
- * Both 1D quantizations of one gradient tensor (dY) from a single read of it
- * (Super summary, Infra table; Ultra report section 2.2: dgrad and wgrad
+ * Both 1D quantizations of one gradient tensor (dY), with both tensor
+ * maxima taken in one read of it (Super summary, Infra table; Ultra report
+ * section 2.2: dgrad and wgrad
  * both consume dY in NVFP4, stochastically rounded, the wgrad operand after
  * the Random Hadamard Transform), plus the count of zero-valued codes, the
  * health signal of the Super report summary, section 2.2 (NVFP4
@@ -179,6 +180,9 @@ int32_t nvfp4_quantize_1d(const void* x, int32_t x_dtype, int64_t rows, int64_t 
  *   zero_codes NULL, or device uint64[2] overwritten with the number of
  *              codes of magnitude zero (0x0 or 0x8) in the ROW and in the
  *              COL output.
+ * The two encodes then run as the two 1D quantizers' encode kernels (both are
+ * ALU-bound: an encode reading x once for both outputs was slower), which
+ * count the zero codes as they write them.
  * Shapes: rows % 16 == 0, cols % 32 == 0; rows == 0 or cols == 0 is a no-op
  * (nothing is written, zero_codes included).  Alignment: x and codes 16
  * bytes, scales and amax 4, zero_codes 8.

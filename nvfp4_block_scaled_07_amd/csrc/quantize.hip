@@ -152,8 +152,7 @@ constexpr int kAmaxThreads = 1024;
 // maxima (atomicMax on the fp32 bits: non-negative floats order like
 // integers, so the result does not depend on the order) and counts itself
 // in; the last one to arrive copies the maxima to the caller's outputs and
-// clears the slot for its next use.  The zero-code counts of the dual
-// quantizer are gathered the same way.  The host hands slots out round
+// clears the slot for its next use.  The host hands slots out round
 // robin (next_slot), so calls in flight at the same time on different
 // streams use different slots unless more than kSlots of them overlap.  The
 // array starts zeroed when the code object loads and every completed use
@@ -164,11 +163,9 @@ constexpr int kAmaxThreads = 1024;
 // and the last of each group carries the group's maxima and counts up to the
 // top line.  A line sees at most a few dozen atomics.
 struct alignas(128) Line {
-  unsigned int bits0;           // running maximum
-  unsigned int arrive;          // workgroups counted in
-  unsigned int bits1;           // second running maximum
-  unsigned int done;            // workgroups that added their zero-code counts
-  unsigned long long zeros[2];  // zero-code counts (dual quantizer)
+  unsigned int bits0;   // running maximum
+  unsigned int arrive;  // workgroups counted in
+  unsigned int bits1;   // second running maximum
 };
 constexpr int kGroups = 8;
 struct Slot {
@@ -187,7 +184,6 @@ constexpr int kAgent = __HIP_MEMORY_SCOPE_AGENT;
 // next one is issued (a maximum before the arrival that announces it), the
 // first returns its old value and the wave waits for it (done()).
 __device__ __forceinline__ void done(unsigned int v) { asm volatile("" ::"v"(v)); }
-__device__ __forceinline__ void done(unsigned long long v) { asm volatile("" ::"v"(v)); }
 
 __device__ __forceinline__ unsigned int ld(const unsigned int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, kAgent);
@@ -202,40 +198,24 @@ __device__ __forceinline__ void raise_max(unsigned int* p, unsigned int v) {
   if (ld(p) < v) done(__hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, kAgent));
 }
 
-// Counter fields of a line.
-enum Field { kArrive, kDone };
-__device__ __forceinline__ unsigned int* field(Line& l, Field f) {
-  return f == kArrive ? &l.arrive : &l.done;
-}
-
-// Counts workgroup blockIdx.x (of `count`) in on field f: at its group
-// line, then, for the last of the group, at the top line.  Before counting
-// in at a level, the maxima (nmax of them) and zero-code counts (when zc)
-// are added there: a workgroup's own values at its group line, a group's
-// totals at the top line.  Returns true in the one workgroup that completes
-// the count; the top line then holds the totals.  Thread 0 only.
-__device__ __forceinline__ bool count_in(Slot& s, Field f, unsigned int count, int nmax,
-                                         const unsigned int* mx, bool zc,
-                                         const unsigned long long* z) {
+// Counts workgroup blockIdx.x (of `count`) in: at its group line, then, for
+// the last of the group, at the top line.  Before counting in at a level,
+// the maxima (nmax of them) are raised there: a workgroup's own at its group
+// line, a group's at the top line.  Returns true in the one workgroup that
+// completes the count; the top line then holds the maxima.  Thread 0 only.
+__device__ __forceinline__ bool count_in(Slot& s, unsigned int count, int nmax,
+                                         const unsigned int* mx) {
   const unsigned int g = blockIdx.x % kGroups;
   const unsigned int ng = (count - g + kGroups - 1) / kGroups;  // workgroups of group g
   Line& L = s.group[g];
   if (nmax > 0) raise_max(&L.bits0, mx[0]);
   if (nmax > 1) raise_max(&L.bits1, mx[1]);
-  if (zc)
-    for (int k = 0; k < 2; k++)
-      if (z[k]) done(__hip_atomic_fetch_add(&L.zeros[k], z[k], __ATOMIC_RELAXED, kAgent));
-  if (__hip_atomic_fetch_add(field(L, f), 1u, __ATOMIC_RELAXED, kAgent) != ng - 1) return false;
+  if (__hip_atomic_fetch_add(&L.arrive, 1u, __ATOMIC_RELAXED, kAgent) != ng - 1) return false;
   Line& T = s.top;
   if (nmax > 0) raise_max(&T.bits0, ld(&L.bits0));
   if (nmax > 1) raise_max(&T.bits1, ld(&L.bits1));
-  if (zc)
-    for (int k = 0; k < 2; k++) {
-      const unsigned long long v = __hip_atomic_load(&L.zeros[k], __ATOMIC_RELAXED, kAgent);
-      if (v) done(__hip_atomic_fetch_add(&T.zeros[k], v, __ATOMIC_RELAXED, kAgent));
-    }
   const unsigned int groups = count < kGroups ? count : kGroups;
-  return __hip_atomic_fetch_add(field(T, f), 1u, __ATOMIC_RELAXED, kAgent) == groups - 1;
+  return __hip_atomic_fetch_add(&T.arrive, 1u, __ATOMIC_RELAXED, kAgent) == groups - 1;
 }
 
 // Zeroes every line of a slot (by the workgroup that completed its use).
@@ -245,9 +225,6 @@ __device__ __forceinline__ void slot_clear(Slot& s) {
     st(&l[i].bits0, 0u);
     st(&l[i].arrive, 0u);
     st(&l[i].bits1, 0u);
-    st(&l[i].done, 0u);
-    __hip_atomic_store(&l[i].zeros[0], 0ull, __ATOMIC_RELAXED, kAgent);
-    __hip_atomic_store(&l[i].zeros[1], 0ull, __ATOMIC_RELAXED, kAgent);
   }
 }
 
@@ -288,7 +265,7 @@ __device__ __forceinline__ void block_max_to(float m0, float* out0, float m1, fl
   }
   Slot& s = g_slots[slot];
   const unsigned int mx[2] = {__float_as_uint(m0), __float_as_uint(m1)};
-  if (count_in(s, kArrive, count, out1 ? 2 : 1, mx, false, nullptr)) {
+  if (count_in(s, count, out1 ? 2 : 1, mx)) {
     *out0 = __uint_as_float(ld(&s.top.bits0));
     if (out1) *out1 = __uint_as_float(ld(&s.top.bits1));
     slot_clear(s);
@@ -404,8 +381,8 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_flat_kernel(const T* __rest
 }
 
 // ---- a lane's 16 x 8 tile, kept as loaded ------------------------------------------------------
-// The COL kernels hold 16 rows of 8 columns per lane as raw input words and
-// work them one column pair at a time.
+// The COL+RHT amax pass holds 16 rows of 8 columns per lane as raw input
+// words and works them one column pair at a time.
 template <typename T>
 struct RawRow;
 
@@ -432,8 +409,6 @@ struct RawRow<uint16_t> {  // 8 bf16 = 4 words; column pair p is word p
     const uint32_t m = neg ? 0x80008000u : 0u;
     q = make_uint4(q.x ^ m, q.y ^ m, q.z ^ m, q.w ^ m);
   }
-  // The next column pair becomes pair 0.
-  __device__ __forceinline__ void rotate() { q = make_uint4(q.y, q.z, q.w, q.x); }
   __device__ __forceinline__ float absmax() const { return max8_bf16_bits(q); }
 };
 
@@ -464,11 +439,6 @@ struct RawRow<float> {  // named words (no array, so selects stay in registers)
     const uint32_t m = neg ? 0x80000000u : 0u;
     lo = make_uint4(lo.x ^ m, lo.y ^ m, lo.z ^ m, lo.w ^ m);
     hi = make_uint4(hi.x ^ m, hi.y ^ m, hi.z ^ m, hi.w ^ m);
-  }
-  __device__ __forceinline__ void rotate() {
-    const uint4 l = lo;
-    lo = make_uint4(lo.z, lo.w, hi.x, hi.y);
-    hi = make_uint4(hi.z, hi.w, l.x, l.y);
   }
   __device__ __forceinline__ float absmax() const {
     float v[8];
@@ -577,21 +547,85 @@ __global__ __launch_bounds__(kThreads) void amax_col_rht_kernel(const T* __restr
   block_max_to(m * 0.25f, amax, mp, kPlain ? amax_plain : nullptr, slot, gridDim.x);
 }
 
+// Zero-magnitude codes (0x0 or 0x8) among the 8 nibbles of w.
+__device__ __forceinline__ uint32_t zero_nibbles(uint32_t w) {
+  const uint32_t m = w & 0x77777777u;
+  return 8u - (uint32_t)__builtin_popcount((m | (m >> 1) | (m >> 2)) & 0x11111111u);
+}
+
+// Zero-code counts of the dual quantizer's two encode kernels, which run
+// thousands of workgroups each (6144 for an [8192 x 6144] tensor).  Every
+// wave adds its count to one line of a slot with an atomic whose result it
+// does not wait for; after both kernels, one small kernel
+// (zero_count_finish_kernel) sums the lines, writes the totals and clears
+// the lines.  Finding the last workgroup in the encode kernels instead (two
+// returning atomics per workgroup, as the amax passes do) kept every
+// workgroup resident until its atomics returned and cost about 7 us per
+// kernel.  Slots are indexed by the amax slots' round-robin numbers
+// (next_slot), so calls in flight use different ones; 32 lines of 128
+// bytes per slot.
+constexpr int kZGroups = 32;
+struct alignas(128) ZLine {
+  unsigned long long sum;
+};
+struct ZSlot {
+  ZLine group[kZGroups];
+};
+__device__ ZSlot g_zslots[kSlots];
+
+// Zero-code count z of each thread, summed over the wave and added by its
+// first lane to zero-count slot `slot` (line = the wave's number in the grid
+// mod kZGroups).  No barrier: a workgroup-wide sum made the waves that
+// finish first wait for the others, which cost more than the atomics.
+__device__ __forceinline__ void grid_zero_count(uint32_t z, int slot) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+  if ((threadIdx.x & 63) == 0 && z) {
+    const unsigned int w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    (void)__hip_atomic_fetch_add(&g_zslots[slot].group[w % kZGroups].sum,
+                                 (unsigned long long)z, __ATOMIC_RELAXED, kAgent);
+  }
+}
+
+// The totals of zero-count slots s0 and s1 into out[0] and out[1], and the
+// slots' lines cleared for their next use.  One wave; it runs after the
+// kernels that counted (stream order), so their atomics are complete.
+__global__ __launch_bounds__(64) void zero_count_finish_kernel(int s0, int s1,
+                                                               unsigned long long* out) {
+  static_assert(kZGroups <= 64, "one line per lane");
+  const int l = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    ZLine* lines = g_zslots[k == 0 ? s0 : s1].group;
+    unsigned long long v = 0;
+    if (l < kZGroups) {
+      v = __hip_atomic_load(&lines[l].sum, __ATOMIC_RELAXED, kAgent);
+      __hip_atomic_store(&lines[l].sum, 0ull, __ATOMIC_RELAXED, kAgent);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (l == 0) out[k] = v;
+  }
+}
+
 // ---- ROW quantizer ---------------------------------------------------------------------------
 // Lane chunk i (8 elements) belongs to block i >> 1; with stochastic rounding
 // its Philox counter is 2 * block + (i & 1) = i.
 constexpr int kRowUnroll = 4;
 
-template <typename T, bool kSR, bool kRHT, bool kGather = false>
+// kZeros: also the number of zero-magnitude codes written, added to
+// zero-count slot zslot (grid_zero_count).
+template <typename T, bool kSR, bool kRHT, bool kGather = false, bool kZeros = false>
 __global__ __launch_bounds__(kThreads) void quant_row_kernel(
     const T* __restrict__ x, int64_t chunks, const float* __restrict__ amax,
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
     uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds, RowSrc<kGather> rs = {},
-    uint32_t cpr = 1) {
+    uint32_t cpr = 1, int zslot = 0) {
   __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
   const int64_t base = (int64_t)blockIdx.x * kThreads * kRowUnroll + threadIdx.x;
+  uint32_t zc = 0;  // zero codes written (kZeros)
   // Loads first (kRowUnroll 16-byte loads in flight), then the table.
   float v[kRowUnroll][8];
   float bm[kRowUnroll];
@@ -629,7 +663,9 @@ __global__ __launch_bounds__(kThreads) void quant_row_kernel(
     const uint32_t packed = pack8_rne(y);
     codes[i] = packed;
     if (!odd) scales[i >> 1] = (uint8_t)e;
+    if (kZeros) zc += zero_nibbles(packed);
   }
+  if constexpr (kZeros) grid_zero_count(zc, zslot);
 }
 
 // ---- small tensors: ROW quantization in one workgroup --------------------------------------------
@@ -793,66 +829,6 @@ __global__ __launch_bounds__(kThreads) void quant_mse_row_kernel(
 }
 
 // ---- COL quantizer -----------------------------------------------------------------------------
-// COL encode of one lane's 8 columns x 16 rows (8 blocks; the dual
-// quantizer's unit, whose ROW blocks need whole row segments), from its raw
-// rows: out[r] gets the 8 codes of row r, sc[0..1] the 8 scale bytes.  With
-// the transform, its sign flips are applied to raw (in place: exact
-// negations of whole rows).  The loop over column pairs is kept rolled, so
-// that only one pair's transform and random bits are live: unrolled, the
-// lane holds more of them and its occupancy drops from three waves per SIMD
-// to two.
-template <typename T, bool kSR, bool kRHT>
-__device__ __forceinline__ void col_encode(RawRow<T> (&raw)[16], int64_t rows, int64_t g,
-                                           int64_t c0, const TensorScales& ts,
-                                           const float* rtab, uint32_t mask, uint64_t seed,
-                                           uint64_t offset, uint32_t rounds, uint32_t (&out)[16],
-                                           uint32_t (&sc)[2]) {
-#pragma unroll
-  for (int r = 0; r < 16; r++) out[r] = 0;
-  sc[0] = sc[1] = 0;
-  if (kRHT)
-#pragma unroll
-    for (int r = 0; r < 16; r++) raw[r].flip((mask >> r) & 1u);
-#pragma unroll 1
-  for (int cp = 0; cp < 4; cp++) {  // column pairs (c, c+1) share one code byte per row
-    // Pair cp is pair 0 of the rotated words (a rolled loop cannot name a
-    // register by cp without selecting among all four).
-    float col[2][16];
-#pragma unroll
-    for (int r = 0; r < 16; r++) {
-      raw[r].pair(0, col[0][r], col[1][r]);
-      raw[r].rotate();
-    }
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      const int c = 2 * cp + h;
-      if (kRHT) {
-        hadamard16_unscaled(col[h]);
-#pragma unroll
-        for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * 0.25f;
-      }
-      float bm = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; r++) bm = fmaxf(bm, __builtin_fabsf(col[h][r]));
-      const uint32_t e = block_code(bm, ts.k);
-      const float rcp = rtab[e];
-      sc[cp >> 1] |= e << (8 * (c & 3));
-#pragma unroll
-      for (int r = 0; r < 16; r++) col[h][r] = col[h][r] * rcp;
-      if (kSR) {  // rows 0..7 take call 2 * block, rows 8..15 call 2 * block + 1
-        const uint64_t blk = (uint64_t)(c0 + c) * (uint64_t)(rows / 16) + (uint64_t)g;
-        sr_values8(col[h], sr_call(2 * blk, seed, offset, rounds));
-        sr_values8(col[h] + 8, sr_call(2 * blk + 1, seed, offset, rounds));
-      }
-    }
-    // RNE, or (after stochastic rounding) the exact conversion of grid values.
-#pragma unroll
-    for (int r = 0; r < 16; r++)
-      out[r] |= __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, col[0][r], col[1][r], 1.0f, 0)
-                << (8 * cp);
-  }
-}
-
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format (gfx9 dword3)
 constexpr uint32_t kDropOff = 0x80000000u;  // past every range: loads read 0, stores are dropped
 
@@ -977,11 +953,14 @@ __device__ __forceinline__ float col_pair_max(const RawPair<T> (&raw)[16], uint3
 // row: the lane's column in the vector offset, the row step in the scalar
 // one, no address arithmetic per row (rows up to 2^25 bytes wide; wider
 // ones, and gathered rows, are addressed by pointer).
-template <typename T, bool kSR, bool kRHT, bool kGather = false>
+// kZeros: also the number of zero-magnitude codes written, as in
+// quant_row_kernel.
+template <typename T, bool kSR, bool kRHT, bool kGather = false, bool kZeros = false>
 __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ gdec,
-    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds, RowSrc<kGather> rs = {}) {
+    uint32_t mask, uint64_t seed, uint64_t offset, uint32_t rounds, RowSrc<kGather> rs = {},
+    int zslot = 0) {
   __shared__ float rtab[128];
   const TensorScales ts = tensor_scales(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0) *gdec = ts.g;
@@ -1006,140 +985,32 @@ __global__ __launch_bounds__(kThreads) void quant_col_kernel(
     }
   }
   build_recip_table(rtab, ts.S);
-  if (!live) return;
-  uint32_t code[16];
-  const uint32_t sc = col_pair_encode<T, kSR, kRHT>(raw, rows, g, c0, ts, rtab, mask, seed, offset,
-                                                    rounds, code);
-  uint8_t* cp0 = codes + g * 16 * (cols / 2);
-  if (buf) {
-    const __amdgpu_buffer_rsrc_t cr =
-        __builtin_amdgcn_make_buffer_rsrc(cp0, 0, (int)(8 * cols), kBufFlags);
+  if (!kZeros && !live) return;  // with kZeros every thread reaches the count
+  uint32_t zc = 0;
+  if (live) {
+    uint32_t code[16];
+    const uint32_t sc = col_pair_encode<T, kSR, kRHT>(raw, rows, g, c0, ts, rtab, mask, seed,
+                                                      offset, rounds, code);
+    uint8_t* cp0 = codes + g * 16 * (cols / 2);
+    if (buf) {
+      const __amdgpu_buffer_rsrc_t cr =
+          __builtin_amdgcn_make_buffer_rsrc(cp0, 0, (int)(8 * cols), kBufFlags);
 #pragma unroll
-    for (int r = 0; r < 16; r++)
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code[r], cr, c0 / 2, (int)(r * (cols / 2)), 0);
-  } else {
+      for (int r = 0; r < 16; r++)
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)code[r], cr, c0 / 2, (int)(r * (cols / 2)),
+                                             0);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 16; r++) cp0[r * (cols / 2) + c0 / 2] = (uint8_t)code[r];
-  }
-  *reinterpret_cast<uint16_t*>(scales + g * cols + c0) = (uint16_t)sc;
-}
-
-// ---- both 1D quantizations of a gradient from one read ---------------------------------------
-// Zero-magnitude codes (0x0 or 0x8) among the 8 nibbles of w.
-__device__ __forceinline__ uint32_t zero_nibbles(uint32_t w) {
-  const uint32_t m = w & 0x77777777u;
-  return 8u - (uint32_t)__builtin_popcount((m | (m >> 1) | (m >> 2)) & 0x11111111u);
-}
-
-// Lane: 8 columns x 16 rows, as the COL quantizer.  First its COL blocks,
-// exactly as the COL quantizer (transform when kRHT).  Then the ROW blocks
-// (1 x 16 along columns, no transform, stochastic rounding) of each of its 16
-// rows, which span lanes 2t and 2t+1 (cols % 16 == 0 keeps the pairs in one
-// row), exactly as the ROW quantizer forms them: block max across the pair,
-// chunk i = (row * cols + c0) / 8 draws Philox call i of the ROW stream.  The
-// ROW pass takes one row at a time and reads its 16 bytes again (a cache hit:
-// the workgroup has just loaded them), which keeps it out of the COL pass's
-// registers.  Both outputs are bit-identical to the two separate calls.
-// zeros (nullable): the zero-magnitude codes of each output, summed per
-// workgroup and added with one atomic each (an atomic per wave on the same
-// two addresses serializes in L2 and doubled the kernel's time).
-template <typename T, bool kRHT, bool kGather = false>
-__global__ __launch_bounds__(kThreads) void quant_dual_kernel(
-    const T* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ amax,
-    uint32_t* __restrict__ row_codes, uint8_t* __restrict__ row_scales,
-    float* __restrict__ row_gdec, uint8_t* __restrict__ col_codes,
-    uint8_t* __restrict__ col_scales, float* __restrict__ col_gdec, uint32_t mask,
-    uint64_t seed_r, uint64_t offset_r, uint32_t rounds_r, uint64_t seed_c, uint64_t offset_c,
-    uint32_t rounds_c, unsigned long long* __restrict__ zeros, int slot, RowSrc<kGather> rs = {}) {
-  __shared__ float rtab_r[128], rtab_c[128];
-  const TensorScales tr = tensor_scales(amax[0]), tc = tensor_scales(amax[1]);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    *row_gdec = tr.g;
-    *col_gdec = tc.g;
-  }
-  const int64_t cg = cols / 8;
-  const int64_t units = (rows / 16) * cg;  // even (cols % 16 == 0): lane pairs agree below
-  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const bool active = u < units;
-  const int64_t uc = active ? u : units - 2 + (u & 1);  // the last pair, same parity
-  const int64_t g = uc / cg, c0 = (uc % cg) * 8;
-  RawRow<T> raw[16];
-#pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int64_t sr = rs.at(g * 16 + r);
-    raw[r].load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
-  }
-  for (int e = threadIdx.x; e < 128; e += blockDim.x) {
-    const float d = e4m3_decode((uint32_t)e);
-    rtab_r[e] = block_recip(tr.S, d);
-    rtab_c[e] = block_recip(tc.S, d);
-  }
-  __syncthreads();
-  uint32_t zr = 0, zc = 0;
-  {
-    uint32_t out[16], sc[2];
-    col_encode<T, true, kRHT>(raw, rows, g, c0, tc, rtab_c, mask, seed_c, offset_c, rounds_c,
-                              out, sc);
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        *reinterpret_cast<uint32_t*>(col_codes + (g * 16 + r) * (cols / 2) + c0 / 2) = out[r];
-        zc += zero_nibbles(out[r]);
-      }
-      uint32_t* sp = reinterpret_cast<uint32_t*>(col_scales + g * cols + c0);
-      sp[0] = sc[0];
-      sp[1] = sc[1];
+      for (int r = 0; r < 16; r++) cp0[r * (cols / 2) + c0 / 2] = (uint8_t)code[r];
     }
+    *reinterpret_cast<uint16_t*>(scales + g * cols + c0) = (uint16_t)sc;
+    if (kZeros)
+#pragma unroll
+      for (int q = 0; q < 4; q++)  // 4 rows of 2 codes per word
+        zc += zero_nibbles((code[4 * q] & 0xFFu) | ((code[4 * q + 1] & 0xFFu) << 8) |
+                           ((code[4 * q + 2] & 0xFFu) << 16) | ((code[4 * q + 3] & 0xFFu) << 24));
   }
-  const bool even = (uc & 1) == 0;
-#pragma unroll 1
-  for (int r = 0; r < 16; r++) {
-    RawRow<T> rr;  // this row's segment again (just loaded: a cache hit)
-    const int64_t sr = rs.at(g * 16 + r);
-    rr.load_or_zero(x + (kGather && sr < 0 ? 0 : sr) * cols + c0, !kGather || sr >= 0);
-    float v[8];
-    rr.all(v);
-    const float m = max8(v);
-    const uint32_t e = block_code(fmaxf(m, xor1(m)), tr.k);
-    const float rc = rtab_r[e];
-    const int64_t chunk = (g * 16 + r) * cg + c0 / 8;
-#pragma unroll
-    for (int t = 0; t < 8; t++) v[t] = v[t] * rc;
-    sr_values8(v, sr_call((uint64_t)chunk, seed_r, offset_r, rounds_r));
-    const uint32_t packed = pack8_rne(v);
-    if (active) {
-      row_codes[chunk] = packed;
-      if (even) row_scales[(g * 16 + r) * (cols / 16) + c0 / 16] = (uint8_t)e;
-      zr += zero_nibbles(packed);
-    }
-  }
-  if (zeros) {  // per workgroup: one atomic per output
-    __shared__ uint32_t wz[2][kThreads / 64];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      zr += __shfl_xor(zr, o);
-      zc += __shfl_xor(zc, o);
-    }
-    if ((threadIdx.x & 63) == 0) {
-      wz[0][threadIdx.x >> 6] = zr;
-      wz[1][threadIdx.x >> 6] = zc;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {  // through the slot: the last workgroup writes the totals
-      Slot& sl = g_slots[slot];
-      unsigned long long t[2] = {0, 0};
-#pragma unroll
-      for (int k = 0; k < 2; k++)
-#pragma unroll
-        for (int w = 0; w < kThreads / 64; w++) t[k] += wz[k][w];
-      if (count_in(sl, kDone, gridDim.x, 0, nullptr, true, t)) {
-#pragma unroll
-        for (int k = 0; k < 2; k++)
-          zeros[k] = __hip_atomic_load(&sl.top.zeros[k], __ATOMIC_RELAXED, kAgent);
-        slot_clear(sl);
-      }
-    }
-  }
+  if constexpr (kZeros) grid_zero_count(zc, zslot);
 }
 
 // ---- 2D quantizer (lane: 8 cols x 16 rows; lanes 2t, 2t+1 = one 16x16 block) ------------------
@@ -2229,16 +2100,39 @@ hipError_t launch_quantize_dual_t(const QuantDualArgs& a, hipStream_t st) {
           x, chunks, 0, a.amax, a.amax + 1, slot, rs, (uint32_t)(a.cols / 8));
     }
   }
-  const int grid = (int)cdiv(units, kThreads);
+  // The two encodes, each as its own 1D quantizer does it (bit-identical to
+  // the separate calls), with the maxima of the pass above.  Both are
+  // ALU-bound (stochastic rounding, the transform), so a single encode
+  // reading x once for both was slower than the two: the saved read is not
+  // what bounds them.
+  const int64_t chunks = a.rows * a.cols / 8;
+  const int grid_r = (int)cdiv(chunks, (int64_t)kThreads * kRowUnroll);
+  const int64_t grid_c = (a.rows / 16) * cdiv(a.cols / 2, (int64_t)kThreads);
+  if (grid_c > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const bool z = a.zeros != nullptr;
+  const int slot_r = z ? next_slot() : 0, slot_c = z ? next_slot() : 0;
   uint32_t* rc = reinterpret_cast<uint32_t*>(a.row_codes);
-#define NVFP4_DUAL(RHT)                                                                       \
-  quant_dual_kernel<T, RHT, G><<<grid, kThreads, 0, st>>>(                                    \
-      x, a.rows, a.cols, a.amax, rc, a.row_scales, a.row_gdec, a.col_codes, a.col_scales,     \
-      a.col_gdec, a.mask, a.seed_r, a.offset_r, a.rounds_r, a.seed_c, a.offset_c, a.rounds_c, \
-      a.zeros, slot, rs)
-  if (a.rht) NVFP4_DUAL(true);
-  else NVFP4_DUAL(false);
-#undef NVFP4_DUAL
+  const uint32_t cpr = (uint32_t)(a.cols / 8);
+#define NVFP4_DUAL_ROW(Z)                                                                        \
+  quant_row_kernel<T, true, false, G, Z><<<grid_r, kThreads, 0, st>>>(                           \
+      x, chunks, a.amax, rc, a.row_scales, a.row_gdec, 0, a.seed_r, a.offset_r, a.rounds_r, rs, \
+      cpr, slot_r)
+#define NVFP4_DUAL_COL(RHT, Z)                                                                  \
+  quant_col_kernel<T, true, RHT, G, Z><<<(int)grid_c, kThreads, 0, st>>>(                       \
+      x, a.rows, a.cols, a.amax + 1, a.col_codes, a.col_scales, a.col_gdec, a.mask, a.seed_c,   \
+      a.offset_c, a.rounds_c, rs, slot_c)
+  if (z) {
+    NVFP4_DUAL_ROW(true);
+    if (a.rht) NVFP4_DUAL_COL(true, true);
+    else NVFP4_DUAL_COL(false, true);
+  } else {
+    NVFP4_DUAL_ROW(false);
+    if (a.rht) NVFP4_DUAL_COL(true, false);
+    else NVFP4_DUAL_COL(false, false);
+  }
+#undef NVFP4_DUAL_ROW
+#undef NVFP4_DUAL_COL
+  if (z) zero_count_finish_kernel<<<1, 64, 0, st>>>(slot_r, slot_c, a.zeros);
   return hipGetLastError();
 }
 
