@@ -139,3 +139,25 @@ def test_rel_err_flags_a_dropped_block():
     A2["scales"][5, 3] = A2["scales"][5, 3] + 1
     off = (_decode(A2, M, K).astype(np.float32) @ Bd.T) * g
     assert O.gemm_rel_err(off, R, D) > 1e-3
+
+
+def test_thread_count_does_not_change_the_reference():
+    """set_threads only splits the outputs over threads: one thread and all
+    of them give the same R and D, bit for bit (the CPU baseline times both)."""
+    rng = np.random.default_rng(77)
+    a = rng.standard_normal((48, 256)).astype(np.float32)
+    b = rng.standard_normal((64, 256)).astype(np.float32)
+    A, B = _q(a, "row"), _q(b, "2d")
+    ii = np.repeat(np.arange(48), 64)
+    jj = np.tile(np.arange(64), 48)
+    before = O.set_threads(0)
+    try:
+        assert O.set_threads(1) == 1
+        R1, D1 = O.gemm_entries("N", "T", 48, 64, 256, A, B, ii, jj)
+        O.set_threads(max(before, 2))
+        Rn, Dn = O.gemm_entries("N", "T", 48, 64, 256, A, B, ii, jj)
+    finally:
+        O.set_threads(before)
+    assert np.array_equal(R1, Rn) and np.array_equal(D1, Dn)
+    Rf, Df = O.gemm_full("N", "T", 48, 64, 256, A, B)
+    assert np.array_equal(R1, Rf.reshape(-1)) and np.array_equal(D1, Df.reshape(-1))
